@@ -1,0 +1,206 @@
+"""CPU oracle for the fused-QKV-projection + grouped-query-attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product path (the
+HIP library and its Python binding) never imports, calls or links it, and
+this package imports nothing from the product path: the two share no code.
+
+Everything here is plain numpy in float64 (inputs are up-cast exactly from
+the fp32 / bf16 values the device receives).  Each function is the plain
+definition of what it computes, with no tiling, online softmax, splitting or
+reordering: the tiled and split methods reach the same result up to rounding
+order, so the definition is the oracle.
+
+Sources (page title, then the part of the page):
+  * "Optimize LlamaAttention by fusing QKV projections" (transformers PR
+    #40092), the review diff of LlamaAttention.forward: one qkv_proj linear
+    layer, then query/key/value taken as consecutive column slices whose
+    widths are num_attention_heads*head_dim, num_key_value_heads*head_dim and
+    the remainder.
+  * "MHA -> GQA" blog, section 3.2 (GQA attention computation): H_q query
+    heads share H_kv KV heads, groups of H_q/H_kv query heads per KV head;
+    the PR thread's repeat_kv remark fixes the contiguous grouping.
+  * FlashAttention-3 news page, HN comment thread (the answer on what
+    FlashAttention computes): attention is Softmax(Q K^T) V and is exact;
+    the 1/sqrt(d) scale and the causal flag are parameters of the op.
+
+Readings where the pages are silent (all listed in the design notes):
+  * W is [hidden, N] row-major (x . W orientation), optional bias [N].
+  * query head h reads KV head floor(h / (H_q/H_kv)).
+  * causal masking is bottom-right aligned: query i of L_q sits at absolute
+    position L_kv - L_q + i and sees keys j <= that position.
+  * decode: the new token is already in the cache; sequence b attends to
+    keys [0, seq_lens[b]).
+
+Parity pins for every function live in tests/test_oracle.py (brute force,
+closed forms, invariants, a library-routine reduction); none is unpinned.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+__all__ = ["qkv_proj", "split_qkv", "attention", "attention_rows", "decode",
+           "brute_attention", "kv_head_of"]
+
+F64 = np.float64
+
+
+def qkv_proj(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Fused projection qkv = x . W (+ bias), one product for Q, K and V together.
+
+    PR #40092 "Optimize LlamaAttention by fusing QKV projections", diff of
+    LlamaAttention.forward: a single qkv_proj replaces q_proj, k_proj, v_proj.
+    x: [..., hidden], w: [hidden, N], bias: [N] or None -> [..., N] float64.
+    """
+    x = np.asarray(x, dtype=F64)
+    w = np.asarray(w, dtype=F64)
+    out = x @ w
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=F64)
+    return out
+
+
+def split_qkv(qkv: np.ndarray, H_q: int, H_kv: int, d: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Split the fused output by column offset into Q, K, V heads.
+
+    PR #40092, diff of LlamaAttention.forward: query = columns [0, H_q*d),
+    key = [H_q*d, (H_q+H_kv)*d), value = the rest; within a block the column
+    is head*d + c.  Returns [..., H, d] views.
+    """
+    qe = H_q * d
+    ke = qe + H_kv * d
+    if qkv.shape[-1] != ke + H_kv * d:
+        raise ValueError("qkv width does not match (H_q + 2*H_kv)*d")
+    lead = qkv.shape[:-1]
+    q = qkv[..., :qe].reshape(*lead, H_q, d)
+    k = qkv[..., qe:ke].reshape(*lead, H_kv, d)
+    v = qkv[..., ke:].reshape(*lead, H_kv, d)
+    return q, k, v
+
+
+def kv_head_of(h: int, H_q: int, H_kv: int) -> int:
+    """KV head read by query head h: contiguous groups of G = H_q/H_kv heads.
+
+    "MHA -> GQA" blog, section 3.2 (query heads of one group share one KV
+    head); the grouping is the one repeat_kv produces (PR #40092 thread)."""
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    return h // (H_q // H_kv)
+
+
+def _softmax_rows(S: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Row softmax of a score block and its natural-log normaliser (LSE).
+
+    Rows with every entry -inf cannot occur (causal needs L_q <= L_kv)."""
+    m = np.max(S, axis=-1, keepdims=True)
+    E = np.exp(S - m)
+    s = np.sum(E, axis=-1, keepdims=True)
+    return E / s, (m + np.log(s))[..., 0]
+
+
+def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, b: int, h: int,
+                   rows: np.ndarray, causal: bool, scale: float,
+                   L_q: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact attention for selected query rows of one (batch, head).
+
+    softmax(scale * q K^T) V over the keys visible to each row (FlashAttention-3
+    page, HN thread: attention = Softmax(QK^T)V).  q: [B, L_q, H_q, d] (only
+    row indices in `rows` are read), k/v: [B, L_kv, H_kv, d].
+    Returns O [len(rows), d] and LSE [len(rows)] (natural log).
+    """
+    H_q = q.shape[2]
+    H_kv = k.shape[2]
+    L_q = q.shape[1] if L_q is None else L_q
+    L_kv = k.shape[1]
+    g = kv_head_of(h, H_q, H_kv)
+    rows = np.asarray(rows, dtype=np.int64)
+    Q = np.asarray(q[b, rows, h, :], dtype=F64)
+    K = np.asarray(k[b, :, g, :], dtype=F64)
+    V = np.asarray(v[b, :, g, :], dtype=F64)
+    S = float(scale) * (Q @ K.T)
+    if causal:
+        if L_q > L_kv:
+            raise ValueError("causal attention needs L_q <= L_kv")
+        limit = rows + (L_kv - L_q)                       # last visible key per row
+        cols = np.arange(L_kv)
+        S = np.where(cols[None, :] <= limit[:, None], S, -np.inf)
+    P, lse = _softmax_rows(S)
+    return P @ V, lse
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
+              row_block: int = 1024) -> Tuple[np.ndarray, np.ndarray]:
+    """Grouped-query attention for all rows.
+
+    q [B, L_q, H_q, d], k/v [B, L_kv, H_kv, d] -> O [B, L_q, H_q, d] float64 and
+    LSE [B, H_q, L_q].  H_kv = H_q is MHA, H_kv = 1 is MQA.  Rows are handled
+    in blocks only to bound memory; every row takes its full softmax.
+    """
+    B, L_q, H_q, d = q.shape
+    if k.shape[0] != B or v.shape != k.shape or k.shape[3] != d:
+        raise ValueError("shape mismatch")
+    O = np.empty((B, L_q, H_q, d), dtype=F64)
+    LSE = np.empty((B, H_q, L_q), dtype=F64)
+    for b in range(B):
+        for h in range(H_q):
+            for r0 in range(0, L_q, row_block):
+                rows = np.arange(r0, min(L_q, r0 + row_block))
+                o, l = attention_rows(q, k, v, b, h, rows, causal, scale)
+                O[b, rows, h, :] = o
+                LSE[b, h, rows] = l
+    return O, LSE
+
+
+def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, seq_lens: np.ndarray,
+           scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One decode step: each sequence's single query attends to its first seq_lens[b] keys.
+
+    The per-token decode of the "MHA -> GQA" blog, section 3.1 (batched
+    matrix-vector attention with per-request lengths).  q [B, H_q, d], caches
+    [B, L_max, H_kv, d], seq_lens [B] -> O [B, H_q, d], LSE [B, H_q].
+    """
+    B, H_q, d = q.shape
+    O = np.empty((B, H_q, d), dtype=F64)
+    LSE = np.empty((B, H_q), dtype=F64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if not 1 <= n <= k_cache.shape[1]:
+            raise ValueError("seq_lens out of range")
+        kb = k_cache[b:b + 1, :n]
+        vb = v_cache[b:b + 1, :n]
+        qb = q[b:b + 1, None]                              # [1, 1, H_q, d]
+        for h in range(H_q):
+            o, l = attention_rows(qb, kb, vb, 0, h, np.array([0]), False, scale)
+            O[b, h] = o[0]
+            LSE[b, h] = l[0]
+    return O, LSE
+
+
+def brute_attention(q, k, v, causal: bool, scale: float):
+    """Pure-Python loop version of `attention` for tiny inputs (math.exp, math.fsum).
+
+    Written independently of numpy's vector routines; the oracle is pinned to it."""
+    B, L_q, H_q, d = (len(q), len(q[0]), len(q[0][0]), len(q[0][0][0]))
+    L_kv, H_kv = len(k[0]), len(k[0][0])
+    G = H_q // H_kv
+    O = [[[[0.0] * d for _ in range(H_q)] for _ in range(L_q)] for _ in range(B)]
+    LSE = [[[0.0] * L_q for _ in range(H_q)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H_q):
+            g = h // G
+            for i in range(L_q):
+                last = i + (L_kv - L_q) if causal else L_kv - 1
+                scores = []
+                for j in range(last + 1):
+                    scores.append(scale * math.fsum(float(q[b][i][h][c]) * float(k[b][j][g][c])
+                                                    for c in range(d)))
+                mx = max(scores)
+                w = [math.exp(s - mx) for s in scores]
+                tot = math.fsum(w)
+                for c in range(d):
+                    O[b][i][h][c] = math.fsum(w[j] * float(v[b][j][g][c]) for j in range(len(w))) / tot
+                LSE[b][h][i] = mx + math.log(tot)
+    return O, LSE

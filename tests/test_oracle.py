@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle against facts fixed outside it (runs on the CPU, no GPU).
+
+Each test ties the oracle to something other than itself: a pure-Python loop
+implementation, an independent library routine (torch's CPU attention in
+float64), closed forms, invariants the pages assert, and golden layout
+fixtures.  The mutation tests at the end plant plausible mistakes in the
+oracle and check that the pins catch them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+RNG = np.random.default_rng(12345)
+
+
+def _rand(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+def _tolist(a):
+    return np.asarray(a).tolist()
+
+
+# ----------------------------------------------------------------------------- brute force
+
+TINY = [  # B, L_q, L_kv, H_q, H_kv, d, causal
+    (1, 1, 1, 1, 1, 3, True),
+    (2, 5, 5, 4, 4, 4, True),      # MHA
+    (2, 5, 5, 4, 2, 4, False),     # GQA G=2
+    (1, 7, 7, 4, 1, 8, True),      # MQA
+    (2, 3, 9, 4, 2, 5, True),      # L_q < L_kv, bottom-right causal
+    (1, 4, 9, 2, 1, 6, False),
+    (2, 9, 9, 3, 3, 2, True),
+]
+
+
+@pytest.mark.parametrize("B,L_q,L_kv,H_q,H_kv,d,causal", TINY)
+def test_oracle_matches_brute_force(B, L_q, L_kv, H_q, H_kv, d, causal):
+    rng = np.random.default_rng(B * 1000 + L_q * 100 + L_kv * 10 + H_kv)
+    q, k, v = (rng.standard_normal((B, L_q, H_q, d)), rng.standard_normal((B, L_kv, H_kv, d)),
+               rng.standard_normal((B, L_kv, H_kv, d)))
+    scale = 0.7
+    O, LSE = oracle.attention(q, k, v, causal, scale)
+    Ob, LSEb = oracle.brute_attention(_tolist(q), _tolist(k), _tolist(v), causal, scale)
+    np.testing.assert_allclose(O, np.array(Ob), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(LSE, np.array(LSEb), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- library routine
+
+@pytest.mark.parametrize("H_q,H_kv,causal", [(8, 8, True), (8, 2, True), (8, 1, False), (6, 3, False)])
+def test_oracle_matches_torch_sdpa_fp64(H_q, H_kv, causal):
+    """Reduction to torch's CPU scaled_dot_product_attention (float64, GQA via enable_gqa).
+
+    With L_q = L_kv the library's causal mask coincides with the bottom-right reading."""
+    rng = np.random.default_rng(77 + H_kv)
+    B, L, d = 2, 37, 16
+    q, k, v = (rng.standard_normal((B, L, H_q, d)), rng.standard_normal((B, L, H_kv, d)),
+               rng.standard_normal((B, L, H_kv, d)))
+    scale = 1.0 / math.sqrt(d)
+    O, _ = oracle.attention(q, k, v, causal, scale)
+    tq, tk, tv = (torch.from_numpy(a).permute(0, 2, 1, 3) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=causal, scale=scale, enable_gqa=(H_kv != H_q))
+    np.testing.assert_allclose(O, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+
+
+def test_oracle_bottom_right_causal_matches_sdpa_explicit_mask():
+    """L_q < L_kv: query i sees keys j <= i + L_kv - L_q (explicit boolean mask in the library)."""
+    rng = np.random.default_rng(5)
+    B, L_q, L_kv, H, d = 1, 4, 11, 2, 8
+    q, k, v = (rng.standard_normal((B, L_q, H, d)), rng.standard_normal((B, L_kv, H, d)),
+               rng.standard_normal((B, L_kv, H, d)))
+    O, _ = oracle.attention(q, k, v, True, 0.5)
+    mask = torch.tensor([[j <= i + L_kv - L_q for j in range(L_kv)] for i in range(L_q)])
+    tq, tk, tv = (torch.from_numpy(a).permute(0, 2, 1, 3) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.5)
+    np.testing.assert_allclose(O, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- projection + split
+
+def test_fused_projection_equals_three_projections_bitwise():
+    """One x.[Wq|Wk|Wv] product equals [x.Wq | x.Wk | x.Wv] (integer data: exact in fp64)."""
+    rng = np.random.default_rng(3)
+    H_q, H_kv, d, hidden = 4, 2, 8, 24
+    x = rng.integers(-3, 4, size=(10, hidden)).astype(np.float64)
+    Wq, Wk, Wv = (rng.integers(-2, 3, size=(hidden, n)).astype(np.float64)
+                  for n in (H_q * d, H_kv * d, H_kv * d))
+    fused = oracle.qkv_proj(x, np.concatenate([Wq, Wk, Wv], axis=1))
+    sep = np.concatenate([oracle.qkv_proj(x, Wq), oracle.qkv_proj(x, Wk), oracle.qkv_proj(x, Wv)], axis=1)
+    assert np.array_equal(fused, sep)
+    # and the fused result equals the exact integer product
+    exact = np.array([[sum(int(x[i, t]) * int(Wc[t]) for t in range(hidden))
+                       for Wc in np.concatenate([Wq, Wk, Wv], axis=1).T] for i in range(10)], dtype=np.float64)
+    assert np.array_equal(fused, exact)
+
+
+def test_projection_bias_and_one_hot_selection():
+    hidden, N = 16, 40
+    x = np.arange(3 * hidden, dtype=np.float64).reshape(3, hidden) - 7.0
+    w = np.zeros((hidden, N))
+    for n in range(N):
+        w[n % hidden, n] = 1.0
+    bias = np.arange(N, dtype=np.float64) * 0.5
+    out = oracle.qkv_proj(x, w, bias)
+    for n in range(N):
+        np.testing.assert_array_equal(out[:, n], x[:, n % hidden] + bias[n])
+
+
+def test_split_offsets_golden():
+    """Column ranges of Q, K, V for the workload shapes (tests/golden/split_offsets.json)."""
+    with open(os.path.join(HERE, "golden", "split_offsets.json")) as f:
+        gold = json.load(f)
+    for case in gold["cases"]:
+        H_q, H_kv, d = case["H_q"], case["H_kv"], case["d"]
+        N = (H_q + 2 * H_kv) * d
+        assert N == case["N"]
+        row = np.arange(N, dtype=np.float64)[None, :]
+        q, k, v = oracle.split_qkv(row, H_q, H_kv, d)
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            lo, hi = case[name]
+            np.testing.assert_array_equal(t.reshape(-1), np.arange(lo, hi))
+        # head h, column c of Q is fused column h*d + c
+        assert q[0, H_q - 1, d - 1] == H_q * d - 1
+        assert k[0, 0, 0] == H_q * d and v[0, 0, 0] == (H_q + H_kv) * d
+
+
+# ----------------------------------------------------------------------------- GQA family
+
+@pytest.mark.parametrize("H_q,H_kv", [(8, 2), (8, 4), (6, 3), (4, 1)])
+def test_gqa_equals_mha_on_repeated_kv(H_q, H_kv):
+    rng = np.random.default_rng(H_q * 10 + H_kv)
+    B, L, d = 2, 13, 8
+    q, k, v = (rng.standard_normal((B, L, H_q, d)), rng.standard_normal((B, L, H_kv, d)),
+               rng.standard_normal((B, L, H_kv, d)))
+    G = H_q // H_kv
+    O, L1 = oracle.attention(q, k, v, True, 0.4)
+    O2, L2 = oracle.attention(q, np.repeat(k, G, axis=2), np.repeat(v, G, axis=2), True, 0.4)
+    assert np.array_equal(O, O2) and np.array_equal(L1, L2)
+
+
+def test_mqa_equals_single_head_attention_per_head():
+    rng = np.random.default_rng(9)
+    B, L, H_q, d = 2, 11, 5, 6
+    q, k, v = rng.standard_normal((B, L, H_q, d)), rng.standard_normal((B, L, 1, d)), rng.standard_normal((B, L, 1, d))
+    O, _ = oracle.attention(q, k, v, False, 0.3)
+    for h in range(H_q):
+        Oh, _ = oracle.attention(q[:, :, h:h + 1], k, v, False, 0.3)
+        assert np.array_equal(O[:, :, h:h + 1], Oh)
+
+
+def test_head_mapping_closed_form():
+    """V of KV head g is the constant g+1  =>  O of query head h is floor(h/G)+1."""
+    rng = np.random.default_rng(2)
+    B, L, H_q, H_kv, d = 1, 9, 8, 4, 4
+    q, k = rng.standard_normal((B, L, H_q, d)), rng.standard_normal((B, L, H_kv, d))
+    v = np.zeros((B, L, H_kv, d))
+    for g in range(H_kv):
+        v[:, :, g, :] = g + 1
+    O, _ = oracle.attention(q, k, v, True, 1.0)
+    for h in range(H_q):
+        np.testing.assert_allclose(O[:, :, h, :], h // (H_q // H_kv) + 1, rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- softmax invariants
+
+def test_softmax_rows_sum_to_one_via_lse():
+    rng = np.random.default_rng(4)
+    B, L, H_q, H_kv, d = 2, 10, 4, 2, 8
+    q, k, v = (rng.standard_normal((B, L, H_q, d)), rng.standard_normal((B, L, H_kv, d)),
+               rng.standard_normal((B, L, H_kv, d)))
+    scale = 0.35
+    _, LSE = oracle.attention(q, k, v, True, scale)
+    for b in range(B):
+        for h in range(H_q):
+            g = h // 2
+            for i in range(L):
+                s = math.fsum(math.exp(scale * float(q[b, i, h] @ k[b, j, g]) - LSE[b, h, i]) for j in range(i + 1))
+                assert abs(s - 1.0) < 1e-13
+
+
+def test_causal_rows_ignore_future_keys():
+    rng = np.random.default_rng(6)
+    B, L, H_q, H_kv, d = 1, 12, 4, 2, 8
+    q, k, v = (rng.standard_normal((B, L, H_q, d)), rng.standard_normal((B, L, H_kv, d)),
+               rng.standard_normal((B, L, H_kv, d)))
+    O, LSE = oracle.attention(q, k, v, True, 0.5)
+    for i in range(L - 1):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, i + 1:] += 100.0 * rng.standard_normal(k2[:, i + 1:].shape)
+        v2[:, i + 1:] -= 50.0
+        O2, LSE2 = oracle.attention(q, k2, v2, True, 0.5)
+        assert np.array_equal(O[:, i], O2[:, i]) and np.array_equal(LSE[:, :, i], LSE2[:, :, i])
+    # non-causal rows do see them
+    On, _ = oracle.attention(q, k, v, False, 0.5)
+    assert not np.allclose(On[:, 0], O[:, 0])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_zero_keys_give_prefix_means(causal):
+    """K = 0 (or scale = 0): uniform weights, O_i = mean of the visible V rows, LSE = ln(count)."""
+    rng = np.random.default_rng(8)
+    B, L_q, L_kv, H, d = 2, 6, 10, 2, 5
+    q, v = rng.standard_normal((B, L_q, H, d)), rng.standard_normal((B, L_kv, H, d))
+    k = np.zeros((B, L_kv, H, d))
+    for kk, sc in ((k, 0.9), (rng.standard_normal((B, L_kv, H, d)), 0.0)):
+        O, LSE = oracle.attention(q, kk, v, causal, sc)
+        for i in range(L_q):
+            n = i + (L_kv - L_q) + 1 if causal else L_kv
+            np.testing.assert_allclose(O[:, i], v[:, :n].mean(axis=1), rtol=0, atol=1e-13)
+            np.testing.assert_allclose(LSE[:, :, i], math.log(n), rtol=0, atol=1e-13)
+
+
+def test_constant_v_single_key_and_dominant_key():
+    rng = np.random.default_rng(10)
+    B, L, H, d = 1, 7, 2, 4
+    q, k = rng.standard_normal((B, L, H, d)), rng.standard_normal((B, L, H, d))
+    O, _ = oracle.attention(q, k, np.full((B, L, H, d), -2.5), True, 0.8)
+    np.testing.assert_allclose(O, -2.5, rtol=0, atol=1e-14)
+    v = rng.standard_normal((B, L, H, d))
+    O1, LSE1 = oracle.attention(q[:, :1], k[:, :1], v[:, :1], True, 0.8)
+    np.testing.assert_array_equal(O1[:, 0], v[:, 0])
+    # one key scoring ~1000 above the others takes all the weight
+    k2 = k.copy()
+    k2[:, 3] = 200.0 * q[:, 6]
+    O2, _ = oracle.attention(q[:, 6:7], k2, v, False, 1.0)
+    np.testing.assert_allclose(O2[:, 0], v[:, 3], rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- decode
+
+def test_decode_matches_attention_and_ignores_cache_tail():
+    rng = np.random.default_rng(11)
+    B, L_max, H_q, H_kv, d = 3, 20, 4, 2, 8
+    kc, vc = rng.standard_normal((B, L_max, H_kv, d)), rng.standard_normal((B, L_max, H_kv, d))
+    q = rng.standard_normal((B, H_q, d))
+    lens = np.array([1, 13, 20], dtype=np.int32)
+    O, LSE = oracle.decode(q, kc, vc, lens, 0.3)
+    for b in range(B):
+        n = lens[b]
+        # the last query of an n-long causal prefill sees exactly the same keys
+        Ob, Lb = oracle.attention(q[b:b + 1, None], kc[b:b + 1, :n], vc[b:b + 1, :n], True, 0.3)
+        np.testing.assert_allclose(O[b], Ob[0, 0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(LSE[b], Lb[0, :, 0], rtol=0, atol=1e-14)
+        Obr, _ = oracle.brute_attention(_tolist(q[b:b + 1, None]), _tolist(kc[b:b + 1, :n]),
+                                        _tolist(vc[b:b + 1, :n]), False, 0.3)
+        np.testing.assert_allclose(O[b], np.array(Obr)[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(O[0], vc[0, 0][np.array([0, 0, 1, 1])])
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[0, 1:] = 1e3
+    vc2[1, 13:] = -7.0
+    O2, LSE2 = oracle.decode(q, kc2, vc2, lens, 0.3)
+    assert np.array_equal(O, O2) and np.array_equal(LSE, LSE2)
+
+
+def _split_combine(q, kc, vc, lens, scale, chunk, n_split):
+    """Test-local fp64 split-KV partial softmax + combine (the exact rescaling identity)."""
+    B, H_q, d = q.shape
+    H_kv = kc.shape[2]
+    O = np.zeros((B, H_q, d))
+    LSE = np.zeros((B, H_q))
+    for b in range(B):
+        for h in range(H_q):
+            g = h // (H_q // H_kv)
+            ms, ls, os_ = [], [], []
+            for s in range(n_split):
+                lo, hi = s * chunk, min((s + 1) * chunk, int(lens[b]))
+                if lo >= hi:
+                    ms.append(-np.inf); ls.append(0.0); os_.append(np.zeros(d))
+                    continue
+                sc = scale * (kc[b, lo:hi, g] @ q[b, h])
+                m = sc.max()
+                e = np.exp(sc - m)
+                ms.append(m); ls.append(e.sum()); os_.append(e @ vc[b, lo:hi, g])
+            M = max(ms)
+            wts = [math.exp(m - M) if m != -np.inf else 0.0 for m in ms]
+            Lsum = sum(w * l for w, l in zip(wts, ls))
+            O[b, h] = sum(w * o for w, o in zip(wts, os_)) / Lsum
+            LSE[b, h] = M + math.log(Lsum)
+    return O, LSE
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 7, 64])
+def test_split_kv_combine_identity(chunk):
+    rng = np.random.default_rng(chunk)
+    B, L_max, H_q, H_kv, d = 3, 40, 4, 1, 8
+    kc, vc = rng.standard_normal((B, L_max, H_kv, d)), rng.standard_normal((B, L_max, H_kv, d))
+    q = 3.0 * rng.standard_normal((B, H_q, d))
+    lens = np.array([1, 17, 40], dtype=np.int32)
+    O, LSE = oracle.decode(q, kc, vc, lens, 0.5)
+    n_split = -(-L_max // chunk)
+    O2, LSE2 = _split_combine(q, kc, vc, lens, 0.5, chunk, n_split)
+    np.testing.assert_allclose(O2, O, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(LSE2, LSE, rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    a = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 37,
+                        np.array([1.00390625, 1.01171875, -1.00390625, 0.0, -0.0, 3.0e38], np.float32)])
+    ours = W.bf16_bits(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(W.bf16_to_f32(ours), torch.from_numpy(a).to(torch.bfloat16).float().numpy())
+
+
+def test_generators_reproducible_and_sliceable():
+    wl = W.WORKLOADS["long_kv4_causal"]
+    a = W.normal(wl.seed, 4, (3, 5, 2, 8))
+    b = W.normal(wl.seed, 4, (3, 5, 2, 8))
+    c = W.normal(wl.seed, 4, (3, 5, 2, 8), lead=range(1, 3))
+    assert np.array_equal(a, b) and np.array_equal(a[1:3], c)
+    ch = W.outlier_channels(wl.seed, 4, 16 * 128)
+    assert len(ch) == 2 and len(set(ch.tolist())) == 2
+    assert len(W.outlier_channels(wl.seed, 4, 4 * 128)) == 1
+    lens = W.decode_lengths(W.WORKLOADS["llama7b_decode_kv8"])
+    assert lens.min() >= 1024 and lens.max() <= 4096 and len(lens) == 32
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def _pins_pass(monkeypatch_ctx) -> bool:
+    """Run a representative subset of pins; False if any fails."""
+    checks = [
+        lambda: test_oracle_matches_brute_force(2, 5, 5, 4, 2, 4, False),
+        lambda: test_oracle_matches_brute_force(2, 3, 9, 4, 2, 5, True),
+        lambda: test_oracle_matches_torch_sdpa_fp64(8, 2, True),
+        lambda: test_head_mapping_closed_form(),
+        lambda: test_zero_keys_give_prefix_means(True),
+        lambda: test_softmax_rows_sum_to_one_via_lse(),
+    ]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    assert _pins_pass(None)
+    real_rows = oracle.attention_rows
+
+    mutations = {
+        # wrong head mapping: h mod H_kv instead of floor(h/G)
+        "head_mod": lambda: monkeypatch.setattr(oracle, "kv_head_of", lambda h, Hq, Hkv: h % Hkv),
+        # dropped scale
+        "no_scale": lambda: monkeypatch.setattr(
+            oracle, "attention_rows",
+            lambda q, k, v, b, h, rows, causal, scale, L_q=None: real_rows(q, k, v, b, h, rows, causal, 1.0, L_q)),
+        # causal aligned top-left instead of bottom-right
+        "top_left": lambda: monkeypatch.setattr(
+            oracle, "attention_rows",
+            lambda q, k, v, b, h, rows, causal, scale, L_q=None: real_rows(q, k, v, b, h, rows, causal, scale,
+                                                                          k.shape[1] if L_q is None else L_q)),
+        # transposed softmax normaliser: LSE without the max term
+        "lse_no_max": lambda: monkeypatch.setattr(
+            oracle, "_softmax_rows",
+            lambda S: (lambda P, l: (P, l - np.max(S, axis=-1)))(*_real_softmax(S))),
+    }
+    _real_softmax = oracle._softmax_rows
+    for name, apply in mutations.items():
+        monkeypatch.undo()
+        apply()
+        assert not _pins_pass(None), f"planted mistake {name} not caught"
+    monkeypatch.undo()
+    assert _pins_pass(None)
