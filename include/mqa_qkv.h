@@ -1,0 +1,144 @@
+/*
+ * mqa_qkv.h -- C ABI of the fused QKV projection + grouped-query attention
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the hot path of one attention layer:
+ *   1. qkv_proj          one GEMM  qkv = x . W_qkv  replacing the separate
+ *                        q/k/v projections ("Optimize LlamaAttention by fusing
+ *                        QKV projections", transformers PR #40092, the diff of
+ *                        LlamaAttention.forward);
+ *   2. the split into Q, K, V is not a call: Q, K and V are strided views of
+ *      the packed qkv rows (same diff: query columns first, then key, then
+ *      value; within a block the column is head*d + c).  The attention calls
+ *      take a token stride, so no copy is ever made;
+ *   3. gqa_attn_prefill  exact softmax(scale . Q K^T) V with H_q query heads
+ *                        sharing H_kv KV heads ("MHA -> GQA" blog, section 3.2;
+ *                        FlashAttention-3 page, the recap of tiling with
+ *                        softmax rescaling being exact);
+ *   4. gqa_attn_decode   one new query per sequence against a contiguous KV
+ *                        cache with per-sequence lengths ("MHA -> GQA" blog,
+ *                        section 3.1), split over the keys with an exact
+ *                        partial-softmax combine (FlashAttention-3 page, HN
+ *                        thread: the softmax is split and recombined).
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers owned by the caller; outputs are
+ *     fully overwritten (never accumulated), in the style of an op that
+ *     mutates a caller-allocated `out` ("custom op overhead" gist).
+ *   - The library never allocates device memory, never synchronises and keeps
+ *     no mutable global state; calls are asynchronous on `stream`
+ *     (a hipStream_t; NULL = the default stream) and reentrant.
+ *   - Arguments are validated on the host before any HIP call.  A rejected
+ *     call launches nothing and returns MQKV_ERR_INVALID (malformed) or
+ *     MQKV_ERR_UNSUPPORTED (well-formed but not implemented); a failed launch
+ *     returns MQKV_ERR_HIP.  mqkv_last_error() gives the thread-local detail.
+ *   - Device-side data (seq_lens values) is trusted: values outside
+ *     [1, L_max] are undefined behaviour.
+ *   - dtypes: MQKV_BF16 (bf16 storage, fp32 accumulation, round-to-nearest-
+ *     even outputs) or MQKV_F32 (fp32 throughout).
+ *   - Alignment: every data pointer 16-byte aligned; element strides multiples
+ *     of 8 (bf16) or 4 (fp32) elements.
+ */
+#ifndef MQA_QKV_H
+#define MQA_QKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mqkv_status {
+  MQKV_OK = 0,
+  MQKV_ERR_INVALID = 1,      /* malformed arguments; nothing launched            */
+  MQKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d not 64/128)    */
+  MQKV_ERR_HIP = 3           /* a HIP runtime call or launch failed              */
+} mqkv_status;
+
+typedef enum mqkv_dtype { MQKV_F32 = 0, MQKV_BF16 = 1 } mqkv_dtype;
+
+/*
+ * Fused QKV projection (PR #40092, LlamaAttention.forward diff).
+ *
+ *   qkv[m, n] = sum_k x[m, k] * w_qkv[k, n] (+ bias[n]),   N = (H_q + 2*H_kv) * d
+ *
+ * x      [M, hidden]  row-major, dtype `dtype`
+ * w_qkv  [hidden, N]  row-major (the x . W orientation; a torch nn.Linear
+ *                     weight is its transpose), columns [Q | K | V], head-major
+ * bias   [N] or NULL
+ * qkv    [M, N]       row-major output
+ * Requires hidden >= 1 and hidden a multiple of 8 (bf16) / 4 (fp32), d in {64, 128},
+ * H_q % H_kv == 0.  M == 0 is a no-op.
+ */
+mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv,
+                     int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
+                     mqkv_dtype dtype, void* stream);
+
+/*
+ * Grouped-query attention over a whole sequence (prefill).
+ *
+ *   q(b,i,h,c) = q[(b*L_q  + i)*q_tok_stride  + h*d + c]
+ *   k(b,j,g,c) = k[(b*L_kv + j)*kv_tok_stride + g*d + c]   (v likewise)
+ *   query head h reads KV head g = h / (H_q / H_kv)  (contiguous groups)
+ *   O(b,i,h,:) = sum_j softmax_j(scale * q(b,i,h,:) . k(b,j,g,:)) v(b,j,g,:)
+ *   causal: key j is visible to query i iff j <= i + (L_kv - L_q)
+ *           (bottom-right alignment; requires L_q <= L_kv)
+ *
+ * With q = qkv, k = qkv + H_q*d, v = qkv + (H_q+H_kv)*d and both strides = N,
+ * this consumes qkv_proj's output in place.
+ * o    [B, L_q, H_q, d] contiguous, dtype o_dtype (bf16 or fp32 for bf16 inputs;
+ *      fp32 for fp32 inputs)
+ * lse  [B, H_q, L_q] fp32 natural-log normaliser ln sum_j exp(scale q.k_j), or NULL
+ * scale must be finite and >= 0.  B == 0 or L_q == 0 is a no-op; L_kv >= 1.
+ */
+mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t B, int32_t L_q, int32_t L_kv, int32_t H_q, int32_t H_kv,
+                             int32_t d, int64_t q_tok_stride, int64_t kv_tok_stride,
+                             int32_t causal, float scale, mqkv_dtype in_dtype,
+                             mqkv_dtype o_dtype, void* stream);
+
+/*
+ * Bytes of device workspace gqa_attn_decode needs for these sizes
+ * (fp32 partial outputs and softmax statistics of every key split).
+ * kv_split: keys per split, 0 = the library's choice.  Returns 0 for
+ * arguments gqa_attn_decode would reject.
+ */
+size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
+                                       int32_t L_max, int32_t kv_split);
+
+/*
+ * One decode step of grouped-query attention over a contiguous KV cache.
+ *
+ *   q(b,h,c)       = q[b*q_tok_stride + h*d + c]          (e.g. a view of qkv rows)
+ *   k_cache, v_cache [B, L_max, H_kv, d] contiguous
+ *   seq_lens [B] device int32, each in [1, L_max]: sequence b attends to keys
+ *   [0, seq_lens[b]) (the new token's K/V are already in the cache)
+ *   o   [B, H_q, d] contiguous (o_dtype), lse [B, H_q] fp32 or NULL
+ *
+ * The keys are processed in splits of kv_split keys (0 = library choice; else a
+ * multiple of 64 in [64, 65536]); partial (max, sum, output) triples go to
+ * `workspace` and a second kernel combines them exactly.
+ * workspace_bytes must be >= gqa_attn_decode_workspace_bytes(...).
+ */
+mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, void* o, float* lse, int32_t B,
+                            int32_t H_q, int32_t H_kv, int32_t d, int32_t L_max,
+                            int64_t q_tok_stride, float scale, int32_t kv_split,
+                            void* workspace, size_t workspace_bytes, mqkv_dtype in_dtype,
+                            mqkv_dtype o_dtype, void* stream);
+
+/* Static description of a status code. */
+const char* mqkv_status_string(mqkv_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char* mqkv_last_error(void);
+
+/* ABI version of this header (major*100 + minor). */
+int32_t mqkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQA_QKV_H */

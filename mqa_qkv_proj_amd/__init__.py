@@ -1,0 +1,239 @@
+"""Python binding of libmqa_qkv.so: fused QKV projection + grouped-query attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library (`include/mqa_qkv.h`).  PyTorch provides device memory and the current
+stream.  Importing this module loads the built library and fails loudly if it
+is missing (build it with `python -m mqa_qkv_proj_amd.build`); there is no
+fallback implementation.
+
+Functions mirror the C ABI:
+    qkv_proj(x, w_qkv, bias=None, H_q, H_kv, d)     -> qkv [..., (H_q+2H_kv)*d]
+    split_qkv(qkv, H_q, H_kv, d)                     -> (q, k, v) strided views, no copy
+    gqa_attn_prefill(q, k, v, causal, scale, ...)    -> o [B, L_q, H_q, d] (, lse)
+    gqa_attn_decode(q, k_cache, v_cache, seq_lens, ...) -> o [B, H_q, d] (, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmqa_qkv.so")
+
+MQKV_OK, MQKV_ERR_INVALID, MQKV_ERR_UNSUPPORTED, MQKV_ERR_HIP = 0, 1, 2, 3
+MQKV_F32, MQKV_BF16 = 0, 1
+
+EXPORTS = ("qkv_proj", "gqa_attn_prefill", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode",
+           "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version")
+
+
+class MqkvError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {_status_string(status)}: {detail}")
+
+
+class MqkvInvalid(MqkvError, ValueError):
+    pass
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m mqa_qkv_proj_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.qkv_proj.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
+    lib.qkv_proj.restype = i32
+    lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32,
+                                     f32, i32, i32, vp]
+    lib.gqa_attn_prefill.restype = i32
+    lib.gqa_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.gqa_attn_decode_workspace_bytes.restype = sz
+    lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, i32, vp,
+                                    sz, i32, i32, vp]
+    lib.gqa_attn_decode.restype = i32
+    lib.mqkv_status_string.argtypes = [i32]
+    lib.mqkv_status_string.restype = ctypes.c_char_p
+    lib.mqkv_last_error.argtypes = []
+    lib.mqkv_last_error.restype = ctypes.c_char_p
+    lib.mqkv_abi_version.argtypes = []
+    lib.mqkv_abi_version.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def _status_string(st: int) -> str:
+    return lib.mqkv_status_string(st).decode()
+
+
+def check(st: int, fn: str) -> None:
+    """Raise for a non-OK status (ValueError subclass for INVALID/UNSUPPORTED)."""
+    if st == MQKV_OK:
+        return
+    detail = lib.mqkv_last_error().decode()
+    if st in (MQKV_ERR_INVALID, MQKV_ERR_UNSUPPORTED):
+        raise MqkvInvalid(st, fn, detail)
+    raise MqkvError(st, fn, detail)
+
+
+# ----------------------------------------------------------------------------- torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.bfloat16:
+        return MQKV_BF16
+    if t == torch.float32:
+        return MQKV_F32
+    raise TypeError(f"unsupported dtype {t} (bfloat16 or float32)")
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on a HIP device")
+
+
+def _tok_stride(t, L: int, H: int, d: int, name: str) -> int:
+    """Token stride of a [B, L, H, d] tensor whose rows may be views into packed qkv."""
+    B = t.shape[0]
+    s = t.stride()
+    if s[3] != 1 or (H > 1 and s[2] != d):
+        raise ValueError(f"{name}: heads must be contiguous [.., H, d] rows")
+    if L > 1:
+        if B > 1 and s[0] != L * s[1]:
+            raise ValueError(f"{name}: batch stride must equal L * token stride")
+        return s[1]
+    if B > 1:
+        return s[0]
+    return H * d  # a single row: any stride >= H*d describes it
+
+
+# ----------------------------------------------------------------------------- public API
+
+def qkv_proj(x, w_qkv, H_q: int, H_kv: int, d: int, bias=None, out=None):
+    """Fused projection qkv = x . W_qkv (+ bias): one GEMM for Q, K and V.
+
+    x [..., hidden] (contiguous), w_qkv [hidden, N] row-major, N = (H_q + 2*H_kv)*d.
+    Returns qkv [..., N] (or writes `out`)."""
+    torch = _torch()
+    _require_cuda(x, w_qkv, bias, out)
+    hidden = x.shape[-1]
+    N = (H_q + 2 * H_kv) * d
+    if w_qkv.shape != (hidden, N):
+        raise ValueError(f"w_qkv must be [{hidden}, {N}], got {tuple(w_qkv.shape)}")
+    if not (x.is_contiguous() and w_qkv.is_contiguous()):
+        raise ValueError("x and w_qkv must be contiguous")
+    if w_qkv.dtype != x.dtype or (bias is not None and (bias.dtype != x.dtype or bias.shape != (N,))):
+        raise ValueError("x, w_qkv and bias must share a dtype; bias is [N]")
+    M = x.numel() // hidden if hidden else 0
+    if out is None:
+        out = torch.empty(*x.shape[:-1], N, dtype=x.dtype, device=x.device)
+    elif out.shape != (*x.shape[:-1], N) or not out.is_contiguous() or out.dtype != x.dtype:
+        raise ValueError("out has the wrong shape, dtype or layout")
+    st = lib.qkv_proj(x.data_ptr(), w_qkv.data_ptr(), bias.data_ptr() if bias is not None else None,
+                      out.data_ptr(), M, hidden, H_q, H_kv, d, _dtype_code(x.dtype), _stream(x.device))
+    check(st, "qkv_proj")
+    return out
+
+
+def split_qkv(qkv, H_q: int, H_kv: int, d: int):
+    """Q, K, V as strided views of the packed rows (column blocks Q | K | V); no copy.
+
+    qkv [B, L, N] -> q [B, L, H_q, d], k [B, L, H_kv, d], v [B, L, H_kv, d]."""
+    qe, ke = H_q * d, (H_q + H_kv) * d
+    if qkv.shape[-1] != ke + H_kv * d:
+        raise ValueError("qkv width does not match (H_q + 2*H_kv)*d")
+    q = qkv[..., :qe].unflatten(-1, (H_q, d))
+    k = qkv[..., qe:ke].unflatten(-1, (H_kv, d))
+    v = qkv[..., ke:].unflatten(-1, (H_kv, d))
+    return q, k, v
+
+
+def gqa_attn_prefill(q, k, v, causal: bool = True, scale: Optional[float] = None,
+                     return_lse: bool = False, out_dtype=None, out=None):
+    """Exact grouped-query attention over whole sequences.
+
+    q [B, L_q, H_q, d], k/v [B, L_kv, H_kv, d]; token strides may be views into qkv.
+    Returns o [B, L_q, H_q, d] (dtype out_dtype, default q.dtype) and, if asked,
+    lse [B, H_q, L_q] float32."""
+    torch = _torch()
+    _require_cuda(q, k, v, out)
+    B, L_q, H_q, d = q.shape
+    _, L_kv, H_kv, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, L_kv, H_kv, d] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+    qs = _tok_stride(q, L_q, H_q, d, "q")
+    ks = _tok_stride(k, L_kv, H_kv, d, "k")
+    if _tok_stride(v, L_kv, H_kv, d, "v") != ks:
+        raise ValueError("k and v must share a token stride")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, L_q, H_q, d, dtype=out_dtype, device=q.device)
+    elif out.shape != (B, L_q, H_q, d) or not out.is_contiguous() or out.dtype != out_dtype:
+        raise ValueError("out must be a contiguous [B, L_q, H_q, d] tensor of out_dtype")
+    lse = torch.empty(B, H_q, L_q, dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr() if lse is not None else None, B, L_q, L_kv, H_q, H_kv, d,
+                              qs, ks, int(bool(causal)), scale, _dtype_code(q.dtype),
+                              _dtype_code(out_dtype), _stream(q.device))
+    check(st, "gqa_attn_prefill")
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_bytes(B: int, H_q: int, H_kv: int, d: int, L_max: int, kv_split: int = 0) -> int:
+    return int(lib.gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split))
+
+
+def gqa_attn_decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None, out_dtype=None,
+                    kv_split: int = 0, return_lse: bool = False, workspace=None, out=None):
+    """One decode step over a contiguous KV cache.
+
+    q [B, H_q, d] (rows may be views into qkv, i.e. any token stride), caches
+    [B, L_max, H_kv, d] contiguous, seq_lens [B] int32 on the device.
+    Returns o [B, H_q, d] (and lse [B, H_q] if asked)."""
+    torch = _torch()
+    _require_cuda(q, k_cache, v_cache, seq_lens, workspace, out)
+    B, H_q, d = q.shape
+    _, L_max, H_kv, _ = k_cache.shape
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("caches must be [B, L_max, H_kv, d] matching q")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    if q.stride(2) != 1 or (H_q > 1 and q.stride(1) != d):
+        raise ValueError("q rows must hold contiguous [H_q, d] heads")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=out_dtype, device=q.device)
+    lse = torch.empty(B, H_q, dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.gqa_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                             out.data_ptr(), lse.data_ptr() if lse is not None else None, B, H_q, H_kv, d,
+                             L_max, q.stride(0), scale, kv_split, workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _dtype_code(q.dtype),
+                             _dtype_code(out_dtype), _stream(q.device))
+    check(st, "gqa_attn_decode")
+    return (out, lse) if return_lse else out

@@ -1,0 +1,180 @@
+// C ABI of the library: host-side validation and dispatch to the gfx950 kernels.
+// Every check runs before any HIP call, so a rejected call touches no device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "launch.h"
+#include "mqa_qkv.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mqkv_status fail(mqkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mqkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MQKV_OK;
+  return fail(MQKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(mqkv_dtype t) { return t == MQKV_F32 || t == MQKV_BF16; }
+int elem_align(mqkv_dtype t) { return t == MQKV_BF16 ? 8 : 4; }  // elements per 16 bytes
+
+// Shared head-shape checks.
+mqkv_status check_heads(int32_t H_q, int32_t H_kv, int32_t d) {
+  if (H_q < 1 || H_kv < 1) return fail(MQKV_ERR_INVALID, "H_q=%d and H_kv=%d must be >= 1", H_q, H_kv);
+  if (H_q % H_kv != 0) return fail(MQKV_ERR_INVALID, "H_q=%d is not a multiple of H_kv=%d", H_q, H_kv);
+  if (d < 1) return fail(MQKV_ERR_INVALID, "d=%d must be >= 1", d);
+  if (d != 64 && d != 128) return fail(MQKV_ERR_UNSUPPORTED, "head dim d=%d not supported (64 or 128)", d);
+  return MQKV_OK;
+}
+
+// Keys per decode split chosen by the library: enough (sequence, KV head, split)
+// units to cover the chip about twice, in multiples of the 64-key tile.
+int32_t auto_split(int32_t B, int32_t H_kv, int32_t L_max) {
+  const int64_t target_units = 2048;
+  const int64_t work = (int64_t)L_max * B * H_kv;
+  int64_t split = 64 * ((work + 64 * target_units - 1) / (64 * target_units));
+  if (split < 64) split = 64;
+  if (split > 2048) split = 2048;
+  return (int32_t)split;
+}
+
+bool split_ok(int32_t s) { return s >= 64 && s <= 65536 && s % 64 == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mqkv_status_string(mqkv_status s) {
+  switch (s) {
+    case MQKV_OK: return "ok";
+    case MQKV_ERR_INVALID: return "invalid argument";
+    case MQKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MQKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* mqkv_last_error(void) { return g_err; }
+
+int32_t mqkv_abi_version(void) { return 100; }
+
+mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, int64_t M,
+                     int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype,
+                     void* stream) {
+  g_err[0] = 0;
+  if (!dtype_ok(dtype)) return fail(MQKV_ERR_INVALID, "dtype %d unknown", (int)dtype);
+  mqkv_status st = check_heads(H_q, H_kv, d);
+  if (st != MQKV_OK) return st;
+  if (M < 0) return fail(MQKV_ERR_INVALID, "M=%lld < 0", (long long)M);
+  if (hidden < 1) return fail(MQKV_ERR_INVALID, "hidden=%lld < 1", (long long)hidden);
+  if (hidden % elem_align(dtype) != 0)
+    return fail(MQKV_ERR_INVALID, "hidden=%lld must be a multiple of %d", (long long)hidden, elem_align(dtype));
+  if (!x || !w_qkv || !qkv) return fail(MQKV_ERR_INVALID, "x, w_qkv and qkv must be non-NULL");
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(qkv) || (bias && !aligned16(bias)))
+    return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned");
+  const int64_t N = (int64_t)(H_q + 2 * (int64_t)H_kv) * d;
+  if (M > 0x7fffffff || hidden > 0x7fffffff || N > 0x7fffffff)
+    return fail(MQKV_ERR_UNSUPPORTED, "sizes beyond 2^31-1 are not supported");
+  if (M == 0) return MQKV_OK;
+  return hip_status(mqkv::launch_qkv_gemm(x, w_qkv, bias, qkv, M, hidden, N, dtype == MQKV_BF16,
+                                          (hipStream_t)stream),
+                    "qkv_proj launch");
+}
+
+mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t B, int32_t L_q, int32_t L_kv, int32_t H_q, int32_t H_kv,
+                             int32_t d, int64_t q_tok_stride, int64_t kv_tok_stride, int32_t causal,
+                             float scale, mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream) {
+  g_err[0] = 0;
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
+    return fail(MQKV_ERR_INVALID, "dtype %d/%d unknown", (int)in_dtype, (int)o_dtype);
+  mqkv_status st = check_heads(H_q, H_kv, d);
+  if (st != MQKV_OK) return st;
+  if (B < 0 || L_q < 0) return fail(MQKV_ERR_INVALID, "B=%d and L_q=%d must be >= 0", B, L_q);
+  if (L_kv < 1) return fail(MQKV_ERR_INVALID, "L_kv=%d must be >= 1", L_kv);
+  if (causal != 0 && causal != 1) return fail(MQKV_ERR_INVALID, "causal must be 0 or 1");
+  if (causal && L_q > L_kv)
+    return fail(MQKV_ERR_INVALID, "causal attention needs L_q (%d) <= L_kv (%d)", L_q, L_kv);
+  if (!isfinite(scale) || scale < 0.0f) return fail(MQKV_ERR_INVALID, "scale must be finite and >= 0");
+  if (!q || !k || !v || !o) return fail(MQKV_ERR_INVALID, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned");
+  const int ea = elem_align(in_dtype);
+  if (q_tok_stride < (int64_t)H_q * d || kv_tok_stride < (int64_t)H_kv * d)
+    return fail(MQKV_ERR_INVALID, "token strides must cover all heads (q >= %d, kv >= %d)", H_q * d,
+                H_kv * d);
+  if (q_tok_stride % ea != 0 || kv_tok_stride % ea != 0)
+    return fail(MQKV_ERR_INVALID, "token strides must be multiples of %d elements", ea);
+  if (in_dtype == MQKV_F32 && o_dtype != MQKV_F32)
+    return fail(MQKV_ERR_UNSUPPORTED, "fp32 inputs need an fp32 output");
+  if (B == 0 || L_q == 0) return MQKV_OK;
+  mqkv::PrefillArgs a{q, k, v, o, lse, B, L_q, L_kv, H_q, H_kv, d, q_tok_stride, kv_tok_stride,
+                      causal != 0, scale, in_dtype == MQKV_BF16, o_dtype == MQKV_BF16};
+  return hip_status(mqkv::launch_prefill(a, (hipStream_t)stream), "gqa_attn_prefill launch");
+}
+
+size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
+                                       int32_t L_max, int32_t kv_split) {
+  if (B < 0 || L_max < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
+    return 0;
+  if (kv_split != 0 && !split_ok(kv_split)) return 0;
+  const int32_t split = kv_split ? kv_split : auto_split(B, H_kv, L_max);
+  const int64_t n_split = ((int64_t)L_max + split - 1) / split;
+  const int64_t per = (int64_t)B * H_q * n_split;
+  return (size_t)(per * d * 4 + per * 2 * 4 + 256);  // outputs, then (max, sum) pairs
+}
+
+mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, void* o, float* lse, int32_t B, int32_t H_q,
+                            int32_t H_kv, int32_t d, int32_t L_max, int64_t q_tok_stride,
+                            float scale, int32_t kv_split, void* workspace, size_t workspace_bytes,
+                            mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream) {
+  g_err[0] = 0;
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
+    return fail(MQKV_ERR_INVALID, "dtype %d/%d unknown", (int)in_dtype, (int)o_dtype);
+  mqkv_status st = check_heads(H_q, H_kv, d);
+  if (st != MQKV_OK) return st;
+  if (B < 0) return fail(MQKV_ERR_INVALID, "B=%d must be >= 0", B);
+  if (L_max < 1) return fail(MQKV_ERR_INVALID, "L_max=%d must be >= 1", L_max);
+  if (kv_split != 0 && !split_ok(kv_split))
+    return fail(MQKV_ERR_INVALID, "kv_split=%d must be 0 or a multiple of 64 in [64, 65536]", kv_split);
+  if (!isfinite(scale) || scale < 0.0f) return fail(MQKV_ERR_INVALID, "scale must be finite and >= 0");
+  if (!q || !k_cache || !v_cache || !seq_lens || !o)
+    return fail(MQKV_ERR_INVALID, "q, k_cache, v_cache, seq_lens and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned (seq_lens 4-byte)");
+  const int ea = elem_align(in_dtype);
+  if (q_tok_stride < (int64_t)H_q * d || q_tok_stride % ea != 0)
+    return fail(MQKV_ERR_INVALID, "q_tok_stride must be >= H_q*d and a multiple of %d", ea);
+  if (in_dtype == MQKV_F32 && o_dtype != MQKV_F32)
+    return fail(MQKV_ERR_UNSUPPORTED, "fp32 inputs need an fp32 output");
+  if ((int64_t)B * L_max * H_kv * d > ((int64_t)1 << 40))
+    return fail(MQKV_ERR_UNSUPPORTED, "cache too large");
+  if (B == 0) return MQKV_OK;
+  const size_t need = gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(MQKV_ERR_INVALID, "workspace must be 16-byte aligned and >= %zu bytes (got %zu)", need,
+                workspace_bytes);
+  const int32_t split = kv_split ? kv_split : auto_split(B, H_kv, L_max);
+  const int32_t n_split = (L_max + split - 1) / split;
+  const int64_t per = (int64_t)B * H_q * n_split;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = part_o + per * d;
+  mqkv::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, H_q, H_kv, d, L_max, q_tok_stride,
+                     scale, split, n_split, part_o, part_ml, in_dtype == MQKV_BF16,
+                     o_dtype == MQKV_BF16};
+  return hip_status(mqkv::launch_decode(a, (hipStream_t)stream), "gqa_attn_decode launch");
+}
+
+}  // extern "C"

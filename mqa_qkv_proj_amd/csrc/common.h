@@ -1,0 +1,92 @@
+// Device helpers shared by the gfx950 kernels: MFMA wrappers, bf16/fp16
+// packing, XCD-aware block remapping and wave-level LDS ordering.
+//
+// MFMA 32x32x16 operand convention used throughout (CDNA4 wave64):
+//   A (32 x 16): lane l holds row (l % 32), eight k values "slot j" (j = 0..7)
+//                of k-half (l / 32);
+//   B (16 x 32): lane l holds column (l % 32), the same eight k slots;
+//   D (32 x 32): lane l holds column (l % 32), rows 8*(i/4) + 4*(l/32) + (i%4)
+//                for accumulator element i = 0..15.
+// Only the row/column placement matters for correctness: A and B always put
+// the same k in the same (lane half, slot), so the hardware's k order cancels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16_t mfma32_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma32_f16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// bf16 halves of a packed dword -> exact fp32.
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even), first value in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two fp32 -> packed fp16 pair (round to nearest even), first value in the low half.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f16x2_t r;
+  r[0] = (_Float16)a;
+  r[1] = (_Float16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float a) {
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)0.0f;
+  return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xffffu);
+}
+
+// Exchange with the lane 32 positions away (the other k-half of an MFMA tile).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Order a wave's own LDS writes before its later LDS reads (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Remap so that
+// each XCD receives a contiguous range of logical ids: neighbouring logical
+// blocks (which share K/V or weight tiles) then share one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int full = (nblocks / 8) * 8;
+  if (bid >= full) return bid;
+  return (bid % 8) * (full / 8) + bid / 8;
+}
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, u32x2_t v) { *reinterpret_cast<u32x2_t*>(p) = v; }
+
+}  // namespace mqkv

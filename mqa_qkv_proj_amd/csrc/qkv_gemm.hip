@@ -1,0 +1,271 @@
+// Fused QKV projection GEMM for gfx950.
+//
+// qkv[M, N] = x[M, K] . W[K, N] (+ bias[N]) -- one GEMM for Q, K and V together
+// ("Optimize LlamaAttention by fusing QKV projections", transformers PR #40092,
+// the diff of LlamaAttention.forward).  The split into Q/K/V is free: callers
+// address the packed rows with a token stride.
+//
+// bf16 path: bf16 MFMA 32x32x16 with fp32 accumulation, bf16 output (RNE).
+//   x tiles are k-contiguous and go to LDS unchanged.  W is n-contiguous; each
+//   thread loads a 4(k) x 8(n) block with 16-byte loads and writes it to LDS
+//   transposed (n-major, k-contiguous), so both MFMA operands are read from LDS
+//   with one 16-byte read per lane.  Tiles are double buffered in LDS with a
+//   register prefetch of the next tile.  Small M uses a split of the k range
+//   over the workgroup's waves, reduced through LDS at the end.
+// fp32 path: plain LDS-tiled fp32 FMA (a correctness path for the tiny fp32 layer).
+#include "common.h"
+#include "launch.h"
+
+namespace mqkv {
+
+template <int BM, int BN, int BK, int WM, int WN, int KS>
+struct GemmCfg {
+  static constexpr int kWaves = WM * WN * KS;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kPad = 8;                 // bf16 elements of padding per LDS row
+  static constexpr int kLd = BK + kPad;
+  static constexpr int kMI = BM / WM / 32;       // 32x32 blocks per wave (rows)
+  static constexpr int kNI = BN / WN / 32;       // 32x32 blocks per wave (cols)
+  static constexpr int kSteps = BK / 16;         // MFMA k-steps per tile
+  static constexpr int kStepsPerWave = kSteps / KS;
+  static constexpr int kAChunks = BM * BK / 8 / kThreads;     // 16B chunks of x per thread
+  static constexpr int kBTasks = (BK / 4) * (BN / 8);          // 4x8 W blocks per tile
+  static constexpr int kBTasksPerThread = (kBTasks + kThreads - 1) / kThreads;
+  static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "tile");
+  static_assert(kSteps % KS == 0, "k split");
+  static_assert((BM * BK / 8) % kThreads == 0, "x chunks");
+  static constexpr int kLdsTile = (BM + BN) * kLd;  // elements per stage
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int KS>
+__global__ __launch_bounds__(WM* WN* KS * 64) void qkv_gemm_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int K, int N) {
+  using C = GemmCfg<BM, BN, BK, WM, WN, KS>;
+  extern __shared__ __align__(16) uint16_t smem[];
+  // stage s: x tile at smem + s*kLdsTile, transposed W tile right after it
+  auto As = [&](int st) { return smem + st * C::kLdsTile; };
+  auto Bs = [&](int st) { return smem + st * C::kLdsTile + BM * C::kLd; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wk = wave / (WM * WN);
+  const int wmn = wave % (WM * WN);
+  const int wm = wmn / WN, wn = wmn % WN;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int nbn = (N + BN - 1) / BN;
+  const int nbm = (M + BM - 1) / BM;
+  const int lid = xcd_remap(blockIdx.x, nbn * nbm);
+  // logical order: the n-tiles of one m-row are neighbours (they share x rows).
+  const int bm = lid / nbn, bn = lid % nbn;
+  const int m0 = bm * BM, n0 = bn * BN;
+  const int nk = (K + BK - 1) / BK;
+
+  u32x4_t ra[C::kAChunks];
+  u32x4_t rb[C::kBTasksPerThread][4];
+
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < C::kAChunks; ++j) {
+      const int ci = tid + j * C::kThreads;
+      const int r = ci / (BK / 8), kc = ci % (BK / 8);
+      const int gm = m0 + r, gk = k0 + kc * 8;
+      ra[j] = (gm < M && gk < K) ? ld16(x + (int64_t)gm * K + gk) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < C::kBTasksPerThread; ++j) {
+      const int ti = tid + j * C::kThreads;
+      const int kg = ti / (BN / 8), ng = ti % (BN / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gk = k0 + kg * 4 + r, gn = n0 + ng * 8;
+        rb[j][r] = (ti < C::kBTasks && gk < K && gn < N) ? ld16(w + (int64_t)gk * N + gn)
+                                                         : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < C::kAChunks; ++j) {
+      const int ci = tid + j * C::kThreads;
+      const int r = ci / (BK / 8), kc = ci % (BK / 8);
+      st16(As(buf) + r * C::kLd + kc * 8, ra[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < C::kBTasksPerThread; ++j) {
+      const int ti = tid + j * C::kThreads;
+      if (ti < C::kBTasks) {
+        const int kg = ti / (BN / 8), ng = ti % (BN / 8);
+        // rb[j][r].e holds W[k0+4kg+r][n0+8ng+2e .. +1]; write column n as 4 k values.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u32x2_t lo, hi;
+          lo[0] = __builtin_amdgcn_perm(rb[j][1][e], rb[j][0][e], 0x05040100u);
+          lo[1] = __builtin_amdgcn_perm(rb[j][3][e], rb[j][2][e], 0x05040100u);
+          hi[0] = __builtin_amdgcn_perm(rb[j][1][e], rb[j][0][e], 0x07060302u);
+          hi[1] = __builtin_amdgcn_perm(rb[j][3][e], rb[j][2][e], 0x07060302u);
+          st8(Bs(buf) + (ng * 8 + 2 * e) * C::kLd + kg * 4, lo);
+          st8(Bs(buf) + (ng * 8 + 2 * e + 1) * C::kLd + kg * 4, hi);
+        }
+      }
+    }
+  };
+
+  f32x16_t acc[C::kMI][C::kNI];
+#pragma unroll
+  for (int i = 0; i < C::kMI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kNI; ++j) acc[i][j] = f32x16_t{};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+    const uint16_t* A = As(buf);
+    const uint16_t* Bt = Bs(buf);
+#pragma unroll
+    for (int s = 0; s < C::kStepsPerWave; ++s) {
+      const int ks = wk * C::kStepsPerWave + s;
+      u32x4_t af[C::kMI], bfr[C::kNI];
+#pragma unroll
+      for (int i = 0; i < C::kMI; ++i)
+        af[i] = ld16(A + (wm * (BM / WM) + i * 32 + l32) * C::kLd + ks * 16 + hf * 8);
+#pragma unroll
+      for (int j = 0; j < C::kNI; ++j)
+        bfr[j] = ld16(Bt + (wn * (BN / WN) + j * 32 + l32) * C::kLd + ks * 16 + hf * 8);
+#pragma unroll
+      for (int i = 0; i < C::kMI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kNI; ++j) acc[i][j] = mfma32_bf16(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if constexpr (KS > 1) {
+    // Reduce the k-split partial sums through LDS (the tile buffers are free now).
+    float* red = reinterpret_cast<float*>(smem);
+    constexpr int kTileF = (BM / WM) * (BN / WN);
+    if (wk > 0) {
+#pragma unroll
+      for (int i = 0; i < C::kMI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kNI; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            red[((wk - 1) * WM * WN + wmn) * kTileF + ((i * C::kNI + j) * 16 + e) * 64 + lane] =
+                acc[i][j][e];
+    }
+    __syncthreads();
+    if (wk > 0) return;
+#pragma unroll
+    for (int p = 1; p < KS; ++p)
+#pragma unroll
+      for (int i = 0; i < C::kMI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kNI; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc[i][j][e] += red[((p - 1) * WM * WN + wmn) * kTileF + ((i * C::kNI + j) * 16 + e) * 64 + lane];
+  }
+
+#pragma unroll
+  for (int j = 0; j < C::kNI; ++j) {
+    const int gn = n0 + wn * (BN / WN) + j * 32 + l32;
+    if (gn >= N) continue;
+    const float bv = bias ? bf16_to_f32(bias[gn]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < C::kMI; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int gm = m0 + wm * (BM / WM) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
+        if (gm < M) out[(int64_t)gm * N + gn] = f32_to_bf16(acc[i][j][e] + bv);
+      }
+    }
+  }
+}
+
+// fp32 path: 64x64 tile, 256 threads, 4x4 outputs per thread, k tile 16.
+__global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restrict__ x,
+                                                           const float* __restrict__ w,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ out, int M, int K,
+                                                           int N) {
+  __shared__ float As[16][64 + 1];
+  __shared__ float Bs[16][64 + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int e = tid; e < 64 * 16; e += 256) {
+      const int r = e / 16, kk = e % 16;
+      As[kk][r] = (m0 + r < M && k0 + kk < K) ? x[(int64_t)(m0 + r) * K + k0 + kk] : 0.0f;
+      const int kr = e / 64, nn = e % 64;
+      Bs[kr][nn] = (k0 + kr < K && n0 + nn < N) ? w[(int64_t)(k0 + kr) * N + n0 + nn] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gm = m0 + ty * 4 + i;
+    if (gm >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + tx * 4 + j;
+      if (gn < N) out[(int64_t)gm * N + gn] = acc[i][j] + (bias ? bias[gn] : 0.0f);
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int KS>
+static hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, void* out,
+                                   int M, int K, int N, hipStream_t s) {
+  using C = GemmCfg<BM, BN, BK, WM, WN, KS>;
+  const size_t lds = 2 * C::kLdsTile * sizeof(uint16_t);
+  auto kern = qkv_gemm_bf16_kernel<BM, BN, BK, WM, WN, KS>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  const int nblk = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(C::kThreads), lds, s, (const uint16_t*)x,
+                     (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, M, K, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void* out, int64_t M,
+                           int64_t K, int64_t N, bool bf16, hipStream_t s) {
+  if (!bf16) {
+    dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+    hipLaunchKernelGGL(qkv_gemm_f32_kernel, grid, dim3(256), 0, s, (const float*)x, (const float*)w,
+                       (const float*)bias, (float*)out, (int)M, (int)K, (int)N);
+    return hipGetLastError();
+  }
+  const int m = (int)M, k = (int)K, n = (int)N;
+  // Pick the largest tile that still gives the chip (256 CUs) a full wave of workgroups.
+  const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
+  if (big >= 256) return launch_gemm_bf16<128, 128, 64, 2, 2, 1>(x, w, bias, out, m, k, n, s);
+  if (M > 32 && mid >= 128) return launch_gemm_bf16<64, 64, 64, 2, 2, 1>(x, w, bias, out, m, k, n, s);
+  return launch_gemm_bf16<32, 32, 256, 1, 1, 4>(x, w, bias, out, m, k, n, s);
+}
+
+}  // namespace mqkv

@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects malformed arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mqa_qkv.h")
+
+INV, UNS = 1, 2
+F32, BF16 = 0, 1
+A = 0x1000  # a 16-byte aligned fake device address; never dereferenced on rejection
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", src, flags=re.M)) - {"if"})
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("qkv_proj", "gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
+              "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(raw, n), f"{n} declared in mqa_qkv.h but not exported"
+    assert set(lib.EXPORTS) <= set(declared_functions())
+
+
+def test_status_strings(lib):
+    L = lib.lib
+    assert L.mqkv_status_string(0) == b"ok"
+    assert L.mqkv_status_string(1) == b"invalid argument"
+    assert L.mqkv_status_string(2) == b"unsupported configuration"
+    assert L.mqkv_status_string(3) == b"HIP runtime error"
+    assert L.mqkv_abi_version() == 100
+
+
+def proj(lib, **kw):
+    a = dict(x=A, w=A, bias=None, out=A, M=16, hidden=256, H_q=4, H_kv=2, d=64, dtype=BF16)
+    a.update(kw)
+    return lib.lib.qkv_proj(a["x"], a["w"], a["bias"], a["out"], a["M"], a["hidden"], a["H_q"], a["H_kv"],
+                            a["d"], a["dtype"], None)
+
+
+def prefill(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=None, B=1, Lq=16, Lkv=16, H_q=4, H_kv=2, d=64, qs=512, ks=512,
+             causal=1, scale=0.125, dt=BF16, odt=BF16)
+    a.update(kw)
+    return lib.lib.gqa_attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"], a["Lkv"],
+                                    a["H_q"], a["H_kv"], a["d"], a["qs"], a["ks"], a["causal"], a["scale"],
+                                    a["dt"], a["odt"], None)
+
+
+def decode(lib, **kw):
+    a = dict(q=A, k=A, v=A, lens=A, o=A, lse=None, B=2, H_q=8, H_kv=2, d=128, Lmax=100, qs=1024,
+             scale=0.1, split=0, ws=A, wsb=1 << 20, dt=BF16, odt=BF16)
+    a.update(kw)
+    return lib.lib.gqa_attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["H_q"],
+                                   a["H_kv"], a["d"], a["Lmax"], a["qs"], a["scale"], a["split"], a["ws"],
+                                   a["wsb"], a["dt"], a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), INV), (dict(out=None), INV), (dict(w=A + 2), INV), (dict(M=-1), INV),
+    (dict(hidden=0), INV), (dict(hidden=260), INV), (dict(H_q=3, H_kv=2), INV), (dict(H_kv=0), INV),
+    (dict(d=96), UNS), (dict(d=0), INV), (dict(dtype=7), INV), (dict(M=1 << 40), UNS),
+])
+def test_qkv_proj_rejects(lib, kw, code):
+    assert proj(lib, **kw) == code
+    assert lib.lib.mqkv_last_error() != b""
+
+
+def test_qkv_proj_empty_is_noop(lib):
+    assert proj(lib, M=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(o=A + 8), INV), (dict(lse=A + 4), INV), (dict(Lkv=0), INV),
+    (dict(causal=1, Lq=17, Lkv=16), INV), (dict(causal=2), INV), (dict(scale=float("nan")), INV),
+    (dict(scale=float("inf")), INV), (dict(scale=-1.0), INV), (dict(qs=100), INV), (dict(qs=516), INV),
+    (dict(ks=130), INV), (dict(H_q=4, H_kv=3), INV), (dict(d=256, qs=1024, ks=512), UNS),
+    (dict(dt=F32, odt=BF16), UNS), (dict(B=-1), INV), (dict(dt=3), INV),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill(lib, **kw) == code
+
+
+def test_prefill_empty_is_noop(lib):
+    assert prefill(lib, B=0) == 0
+    assert prefill(lib, Lq=0) == 0
+
+
+def test_decode_workspace_query(lib):
+    f = lib.decode_workspace_bytes
+    n = f(32, 32, 8, 128, 4096, 0)
+    assert n > 32 * 32 * 128 * 4
+    assert f(32, 32, 8, 128, 4096, 64) == 32 * 32 * 64 * (128 * 4 + 8) + 256
+    assert f(2, 8, 3, 128, 100, 0) == 0       # H_q % H_kv
+    assert f(2, 8, 2, 128, 100, 100) == 0     # split not a multiple of 64
+    assert f(2, 8, 2, 96, 100, 0) == 0        # d
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=None), INV), (dict(lens=A + 2), INV), (dict(ws=None), INV), (dict(wsb=16), INV),
+    (dict(split=100), INV), (dict(split=32), INV), (dict(Lmax=0), INV), (dict(qs=1000), INV),
+    (dict(qs=512), INV), (dict(scale=float("nan")), INV), (dict(d=80, qs=1024), UNS),
+    (dict(dt=F32, odt=BF16), UNS), (dict(H_q=8, H_kv=3), INV), (dict(ws=A + 8), INV),
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def test_decode_empty_is_noop(lib):
+    assert decode(lib, B=0) == 0
+
+
+def test_python_layer_validates_without_gpu(lib):
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lib.qkv_proj(x, torch.zeros(256, 512, dtype=torch.bfloat16), 4, 2, 64)  # CPU tensors
+    qkv = torch.zeros(2, 5, (8 + 2 * 2) * 64, dtype=torch.bfloat16)
+    q, k, v = lib.split_qkv(qkv, 8, 2, 64)
+    assert q.shape == (2, 5, 8, 64) and k.shape == (2, 5, 2, 64) and v.shape == (2, 5, 2, 64)
+    assert q.data_ptr() == qkv.data_ptr()
+    assert k.data_ptr() == qkv.data_ptr() + 8 * 64 * 2 and v.data_ptr() == qkv.data_ptr() + 10 * 64 * 2
+    assert q.stride(1) == k.stride(1) == (8 + 4) * 64

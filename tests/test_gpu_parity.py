@@ -1,0 +1,210 @@
+"""Parity of the HIP path with the CPU oracle at sizes the oracle finishes in
+seconds: several tiles, ragged tails, every head grouping, both dtypes.
+
+The attention stages are fed the GPU's own inputs (stage-wise parity); the
+projection stage compares the GPU GEMM with the fp64 product of the same
+values."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import assert_close, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import mqa_qkv_proj_amd
+    return mqa_qkv_proj_amd
+
+
+def torch():
+    import torch as t
+    return t
+
+
+# ----------------------------------------------------------------------------- projection
+
+PROJ = [  # M, hidden, H_q, H_kv, d, dtype
+    (1, 256, 4, 2, 64, "bf16"), (7, 512, 8, 1, 128, "bf16"), (33, 256, 4, 4, 64, "bf16"),
+    (130, 384, 8, 2, 64, "bf16"), (300, 1024, 16, 2, 128, "bf16"), (1029, 264, 4, 2, 64, "bf16"),
+    (128, 256, 4, 2, 64, "f32"), (45, 100, 2, 1, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("M,hidden,H_q,H_kv,d,dtype", PROJ)
+def test_qkv_proj_matches_oracle(m, M, hidden, H_q, H_kv, d, dtype):
+    say("qkv_proj", M, hidden, H_q, H_kv, d, dtype)
+    N = (H_q + 2 * H_kv) * d
+    enc = W.round_bf16 if dtype == "bf16" else (lambda a: a)
+    x = enc(W.normal(11, M, (M, hidden)))
+    w = enc(W.normal(12, hidden, (hidden, N), std=1.0 / math.sqrt(hidden)))
+    got = m.qkv_proj(dev(x, dtype), dev(w, dtype), H_q, H_kv, d)
+    ref = oracle.qkv_proj(x, w)
+    assert_close(host(got), ref, dtype, f"qkv_proj M={M}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_qkv_proj_bias(m, dtype):
+    M, hidden, H_q, H_kv, d = 70, 256, 4, 2, 64
+    N = (H_q + 2 * H_kv) * d
+    enc = W.round_bf16 if dtype == "bf16" else (lambda a: a)
+    x, w = enc(W.normal(1, 1, (M, hidden))), enc(W.normal(1, 2, (hidden, N), std=0.0625))
+    bias = enc(W.normal(1, 3, (1, N))[0])
+    got = m.qkv_proj(dev(x, dtype), dev(w, dtype), H_q, H_kv, d, bias=dev(bias, dtype))
+    assert_close(host(got), oracle.qkv_proj(x, w, bias), dtype, "qkv_proj+bias")
+
+
+@pytest.mark.parametrize("M", [5, 64, 700])
+def test_qkv_proj_exact_on_integers(m, M):
+    """Small-integer x and sparse {-1,0,1} W: every sum is an integer <= 256, exact in bf16."""
+    rng = np.random.default_rng(M)
+    hidden, H_q, H_kv, d = 512, 4, 2, 64
+    N = (H_q + 2 * H_kv) * d
+    x = rng.integers(-2, 3, size=(M, hidden)).astype(np.float32)
+    w = (rng.integers(-1, 2, size=(hidden, N)) * (rng.random((hidden, N)) < 0.2)).astype(np.float32)
+    for dtype in ("bf16", "f32"):
+        got = host(m.qkv_proj(dev(x, dtype), dev(w, dtype), H_q, H_kv, d))
+        assert np.array_equal(got, oracle.qkv_proj(x, w)), dtype
+
+
+def test_qkv_proj_one_hot_column_selection(m):
+    M, hidden, H_q, H_kv, d = 96, 256, 4, 2, 64
+    N = (H_q + 2 * H_kv) * d
+    x = W.round_bf16(W.normal(5, 5, (M, hidden)))
+    w = np.zeros((hidden, N), np.float32)
+    w[np.arange(N) % hidden, np.arange(N)] = 1.0
+    got = host(m.qkv_proj(dev(x, "bf16"), dev(w, "bf16"), H_q, H_kv, d))
+    assert np.array_equal(got, x[:, np.arange(N) % hidden].astype(np.float64))
+
+
+def test_fused_equals_three_separate_projections(m):
+    """One fused call vs three calls on the column blocks of W (the pages' claim).
+
+    Each block W_q, W_k, W_v is run as its own projection (zero-padded to a width
+    the call accepts, the padding columns dropped afterwards)."""
+    M, hidden, H_q, H_kv, d = 200, 512, 8, 2, 64
+    N = (H_q + 2 * H_kv) * d
+    x = W.round_bf16(W.normal(9, 9, (M, hidden)))
+    w = W.round_bf16(W.normal(9, 10, (hidden, N), std=0.04))
+    xd = dev(x, "bf16")
+    fused = host(m.qkv_proj(xd, dev(w, "bf16"), H_q, H_kv, d))
+    parts = []
+    for lo, hi in ((0, H_q * d), (H_q * d, (H_q + H_kv) * d), ((H_q + H_kv) * d, N)):
+        n = hi - lo
+        pad = max(0, 3 * d - n)
+        wb = np.concatenate([w[:, lo:hi], np.zeros((hidden, pad), np.float32)], axis=1)
+        heads = wb.shape[1] // d
+        parts.append(host(m.qkv_proj(xd, dev(wb, "bf16"), heads - 2, 1, d))[:, :n])
+    sep = np.concatenate(parts, axis=1)
+    assert_close(fused, sep, "bf16", "fused vs separate", max_abs=1e-2, rel_l2=1e-3)
+
+
+# ----------------------------------------------------------------------------- prefill
+
+PREFILL = [  # B, L_q, L_kv, H_q, H_kv, d, causal
+    (2, 200, 200, 8, 2, 64, True),
+    (2, 200, 200, 8, 2, 128, False),
+    (1, 130, 130, 4, 4, 128, True),     # MHA
+    (1, 257, 257, 16, 1, 64, True),     # MQA, G=16
+    (1, 97, 97, 8, 1, 128, False),      # MQA G=8
+    (2, 65, 65, 6, 2, 64, True),        # G=3 (not a power of two)
+    (1, 77, 300, 4, 2, 128, True),      # L_q < L_kv: bottom-right causal
+    (1, 1, 1, 2, 1, 64, True),          # single token
+    (3, 1, 129, 4, 2, 128, False),      # one query row
+    (1, 64, 64, 64, 2, 64, True),       # G=32
+]
+
+
+@pytest.mark.parametrize("B,L_q,L_kv,H_q,H_kv,d,causal", PREFILL)
+@pytest.mark.parametrize("odt", ["bf16", "f32"])
+def test_prefill_bf16_matches_oracle(m, B, L_q, L_kv, H_q, H_kv, d, causal, odt):
+    t = torch()
+    say("prefill", B, L_q, L_kv, H_q, H_kv, d, causal, odt)
+    inp = W.small("bf16", 100 + L_q + H_q, B, L_q, L_kv, H_q, H_kv, d)
+    q, k, v = (dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = m.gqa_attn_prefill(q, k, v, causal=causal, scale=scale, return_lse=True,
+                                out_dtype=t.float32 if odt == "f32" else t.bfloat16)
+    ref_o, ref_l = oracle.attention(inp["q"], inp["k"], inp["v"], causal, scale)
+    assert_close(host(o), ref_o, "bf16", "O")
+    assert_close(host(lse), ref_l, "bf16", "LSE", max_abs=1e-3, rel_l2=1e-4)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_f32_matches_oracle(m, causal, d):
+    B, L, H_q, H_kv = 2, 150, 4, 2
+    inp = W.small("f32", 3, B, L, L, H_q, H_kv, d)
+    q, k, v = (dev(inp[n], "f32") for n in ("q", "k", "v"))
+    o, lse = m.gqa_attn_prefill(q, k, v, causal=causal, return_lse=True)
+    ref_o, ref_l = oracle.attention(inp["q"], inp["k"], inp["v"], causal, 1.0 / math.sqrt(d))
+    assert_close(host(o), ref_o, "f32", "O f32")
+    assert_close(host(lse), ref_l, "f32", "LSE f32")
+
+
+def test_prefill_on_qkv_views_equals_contiguous_copies(m):
+    """The split is zero-copy: strided views of qkv give the same bits as packed copies."""
+    t = torch()
+    B, L, H_q, H_kv, d = 2, 150, 8, 2, 64
+    N = (H_q + 2 * H_kv) * d
+    qkv = dev(W.round_bf16(W.normal(4, 4, (B, L, N))), "bf16")
+    q, k, v = m.split_qkv(qkv, H_q, H_kv, d)
+    assert q.data_ptr() == qkv.data_ptr()
+    o1 = m.gqa_attn_prefill(q, k, v, causal=True)
+    o2 = m.gqa_attn_prefill(q.contiguous(), k.contiguous(), v.contiguous(), causal=True)
+    assert t.equal(o1, o2)
+
+
+# ----------------------------------------------------------------------------- decode
+
+DECODE = [  # B, H_q, H_kv, d, L_max, lens, split
+    (3, 8, 2, 128, 300, [1, 77, 300], 0),
+    (3, 8, 2, 128, 300, [1, 77, 300], 64),
+    (3, 8, 2, 128, 300, [1, 77, 300], 128),
+    (2, 16, 1, 128, 1040, [17, 1040], 0),
+    (4, 4, 4, 64, 200, [200, 5, 64, 65], 64),
+    (2, 6, 3, 64, 130, [129, 130], 0),
+    (1, 64, 1, 128, 100, [100], 64),     # G = 64 > 32: two query blocks
+]
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,d,L_max,lens,split", DECODE)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_matches_oracle(m, B, H_q, H_kv, d, L_max, lens, split, dtype):
+    t = torch()
+    say("decode", B, H_q, H_kv, d, L_max, lens, split, dtype)
+    enc = W.round_bf16 if dtype == "bf16" else (lambda a: a)
+    kc = enc(W.normal(21, L_max, (B, L_max, H_kv, d)))
+    vc = enc(W.normal(22, L_max, (B, L_max, H_kv, d)))
+    q = enc(W.normal(23, L_max, (B, H_q, d)))
+    seq = np.array(lens, np.int32)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = m.gqa_attn_decode(dev(q, dtype), dev(kc, dtype), dev(vc, dtype),
+                               t.from_numpy(seq).cuda(), scale=scale, kv_split=split,
+                               return_lse=True, out_dtype=t.float32)
+    ref_o, ref_l = oracle.decode(q, kc, vc, seq, scale)
+    assert_close(host(o), ref_o, dtype, "decode O")
+    assert_close(host(lse), ref_l, dtype, "decode LSE", max_abs=1e-3 if dtype == "bf16" else 1e-4)
+
+
+def test_decode_q_as_view_of_qkv_rows(m):
+    t = torch()
+    B, H_q, H_kv, d, L_max = 4, 8, 2, 64, 150
+    N = (H_q + 2 * H_kv) * d
+    qkv = W.round_bf16(W.normal(31, 1, (B, N)))
+    kc = W.round_bf16(W.normal(31, 2, (B, L_max, H_kv, d)))
+    vc = W.round_bf16(W.normal(31, 3, (B, L_max, H_kv, d)))
+    seq = np.array([150, 1, 64, 100], np.int32)
+    qkv_d = dev(qkv, "bf16")
+    q_view = qkv_d[:, :H_q * d].unflatten(-1, (H_q, d))
+    o = m.gqa_attn_decode(q_view, dev(kc, "bf16"), dev(vc, "bf16"), t.from_numpy(seq).cuda(),
+                          out_dtype=t.float32)
+    ref, _ = oracle.decode(qkv[:, :H_q * d].reshape(B, H_q, d), kc, vc, seq, 1 / math.sqrt(d))
+    assert_close(host(o), ref, "bf16", "decode q view")
