@@ -1,0 +1,295 @@
+"""Benchmark of the attention-layer hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--sweep]
+
+One step is one pass of the whole path over one batch of synthetic input, in
+the two shapes the headline metric is quoted on:
+  * prefill phase -- long-context grouped-query prefill, B=2, L=8192, H_q=16,
+    H_kv=4, d=128, causal, bf16 (Q, K, V given; 0.1% of feature channels x20);
+  * decode phase  -- Llama-2-7B-shaped GQA decode, B=32, H_q=32, H_kv=8, d=128,
+    hidden 4096: fused QKV GEMM of the 32 new tokens, the query heads taken as a
+    strided view of the packed qkv rows (no copy), then split-KV attention over
+    a contiguous cache of 4096 slots with lengths drawn from U{1024..4096}.
+Inputs are resident in HBM before timing.  Warm-up steps run first; then K
+steps are timed between two device synchronisations.  Per-kernel durations
+come from HIP events recorded on the stream the kernels run on.
+
+Prints ONE JSON line: `value` is the whole step's algorithmic TFLOP/s (prefill
++ GEMM + decode FLOPs over the step time); `prefill`, `decode` and `qkv_proj`
+give each kernel's own rate and roofline fraction; `roofline` is the dominant
+kernel (prefill, MFMA-bound); `cpu_baseline` times the CPU oracle on a bounded
+sample of the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--sweep", action="store_true", help="also time every configuration (stderr)")
+    return p.parse_args()
+
+
+def prefill_flops(B, H_q, d, L_q, L_kv, causal):
+    off = L_kv - L_q
+    pairs = sum(min(L_kv, i + off + 1) for i in range(L_q)) if causal else L_q * L_kv
+    return 4.0 * B * H_q * d * pairs
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU "
+              "collectives to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mqa_qkv_proj_amd as m
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+
+    def up(a):
+        bits = W.bf16_bits(np.ascontiguousarray(a, dtype=np.float32))
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    wp = W.WORKLOADS["long_kv4_causal"]
+    pin = W.prefill_inputs(wp)
+    Qp, Kp, Vp = up(pin["q"]), up(pin["k"]), up(pin["v"])
+    del pin
+    wd = W.WORKLOADS["llama7b_decode_kv8"]
+    din = W.decode_inputs(wd)
+    kc, vc = up(din["k_cache"]), up(din["v_cache"])
+    lens_np = din["seq_lens"]
+    lens = torch.from_numpy(lens_np).to(dev)
+    del din
+    pj = W.proj_inputs(wd)
+    x, wq = up(pj["x"]), up(pj["w"])
+    del pj
+    Op = torch.empty(wp.B, wp.L, wp.H_q, wp.d, dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty(wd.B, wd.N, dtype=torch.bfloat16, device=dev)
+    Od = torch.empty(wd.B, wd.H_q, wd.d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(m.decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.L_max), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    scale_p = 1.0 / math.sqrt(wp.d)
+    scale_d = 1.0 / math.sqrt(wd.d)
+
+    # ---------------------------------------------------------------- work per step
+    fl_prefill = prefill_flops(wp.B, wp.H_q, wp.d, wp.L, wp.L, wp.causal)
+    fl_gemm = 2.0 * wd.B * wd.hidden * wd.N
+    by_gemm = 2.0 * (wd.hidden * wd.N + wd.B * wd.hidden + wd.B * wd.N)
+    kv_tokens = int(lens_np.astype(np.int64).sum())
+    by_decode = 2.0 * (kv_tokens * wd.H_kv * wd.d * 2 + 2 * wd.B * wd.H_q * wd.d)
+    fl_decode = 4.0 * wd.H_q * wd.d * kv_tokens
+    by_prefill = 2.0 * (wp.B * wp.L * (wp.H_q + 2 * wp.H_kv) * wp.d + wp.B * wp.L * wp.H_q * wp.d)
+
+    ev = {k: [] for k in ("p0", "p1", "g0", "g1", "d1")}
+
+    def step(record):
+        e = {k: torch.cuda.Event(enable_timing=True) for k in ev} if record else None
+        if record:
+            e["p0"].record(stream)
+        m.gqa_attn_prefill(Qp, Kp, Vp, causal=True, scale=scale_p, out=Op)
+        if record:
+            e["p1"].record(stream)
+            e["g0"].record(stream)
+        m.qkv_proj(x, wq, wd.H_q, wd.H_kv, wd.d, out=qkv)
+        q_view = qkv[:, :wd.H_q * wd.d].unflatten(-1, (wd.H_q, wd.d))  # split: a strided view
+        if record:
+            e["g1"].record(stream)
+        m.gqa_attn_decode(q_view, kc, vc, lens, scale=scale_d, workspace=ws, out=Od)
+        if record:
+            e["d1"].record(stream)
+            for k in ev:
+                ev[k].append(e[k])
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step(False)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            step(True)
+        torch.cuda.synchronize()
+        t_total = time.perf_counter() - t_start
+
+    def avg_ms(a, b):
+        return sum(x.elapsed_time(y) for x, y in zip(ev[a], ev[b])) / len(ev[a])
+
+    ms_prefill = avg_ms("p0", "p1")
+    ms_gemm = avg_ms("g0", "g1")
+    ms_decode = avg_ms("g1", "d1")
+    ms_step = t_total * 1e3 / args.steps
+    fl_step = fl_prefill + fl_gemm + fl_decode
+
+    pre_tf = fl_prefill / (ms_prefill * 1e-3) / 1e12
+    dec_gbs = by_decode / (ms_decode * 1e-3) / 1e9
+    gemm_tf = fl_gemm / (ms_gemm * 1e-3) / 1e12
+    gemm_gbs = by_gemm / (ms_gemm * 1e-3) / 1e9
+
+    out = {
+        "metric": "prefill attn TFLOPS + decode KV GB/s (frac. of roofline), 1 MI355X",
+        "value": round(fl_step / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs, random-init weights)",
+        "config": {
+            "workload": "long-context GQA prefill (B=2, L=8192, H_q=16, H_kv=4, d=128, causal) + "
+                        "Llama-2-7B GQA decode step (B=32, H_q=32, H_kv=8, d=128, hidden=4096, "
+                        "KV lengths U{1024..4096} of 4096)",
+            "prefill": {"B": wp.B, "L": wp.L, "H_q": wp.H_q, "H_kv": wp.H_kv, "d": wp.d, "causal": True},
+            "decode": {"B": wd.B, "H_q": wd.H_q, "H_kv": wd.H_kv, "d": wd.d, "L_max": wd.L_max,
+                       "hidden": wd.hidden, "kv_tokens": kv_tokens},
+        },
+        "prefill": {"tflops": round(pre_tf, 2), "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4),
+                    "us": round(ms_prefill * 1e3, 1), "gflop": round(fl_prefill / 1e9, 2)},
+        "decode": {"gbps": round(dec_gbs, 1), "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                   "us": round(ms_decode * 1e3, 2), "mbytes": round(by_decode / 1e6, 2)},
+        "qkv_proj": {"tflops": round(gemm_tf, 2), "gbps": round(gemm_gbs, 1),
+                     "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "us": round(ms_gemm * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(pre_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_prefill_bf16 (d=128, causal)"},
+        "cpu_baseline": None,
+    }
+    if args.sweep:
+        sweep(m, W, torch, dev, stream)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, wp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(W, wp, seconds):
+    """Time the fp64 CPU oracle on a bounded sample of the prefill workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    inp = W.prefill_inputs(wp, batch=range(0, 1))
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    scale = 1.0 / math.sqrt(wp.d)
+    flops, rows_done, t0 = 0.0, 0, time.perf_counter()
+    blk = 512
+    # causal row blocks, from the last (heaviest) block backwards, head by head
+    order = [(h, r0) for r0 in range(wp.L - blk, -1, -blk) for h in range(wp.H_q)]
+    for h, r0 in order:
+        rows = np.arange(r0, r0 + blk)
+        oracle.attention_rows(q, k, v, 0, h, rows, True, scale)
+        flops += 4.0 * wp.d * float((rows + 1).sum())
+        rows_done += blk
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows_done} query rows (blocks of {blk}, heaviest first) of batch 0 of the "
+                      f"causal prefill, fp64 numpy, {dt:.1f}s"}
+
+
+def sweep(m, W, torch, dev, stream):
+    """Time every configuration's kernels (to stderr); used for the design tables."""
+    import numpy as np
+
+    def up(a):
+        bits = W.bf16_bits(np.ascontiguousarray(a, dtype=np.float32))
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def timeit(fn, n=20):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            for _ in range(n):
+                fn()
+            e.record(stream)
+            e.synchronize()
+        return s.elapsed_time(e) / n * 1e3  # us
+
+    for name, wl in W.WORKLOADS.items():
+        if wl.dtype != "bf16":
+            continue
+        if wl.kind == "prefill":
+            pin = W.prefill_inputs(wl)
+            q, k, v = up(pin["q"]), up(pin["k"]), up(pin["v"])
+            o = torch.empty_like(q)
+            us = timeit(lambda: m.gqa_attn_prefill(q, k, v, causal=wl.causal, out=o))
+            fl = prefill_flops(wl.B, wl.H_q, wl.d, wl.L, wl.L, wl.causal)
+            log(json.dumps({"sweep": name, "kernel": "prefill", "us": round(us, 2),
+                            "tflops": round(fl / us / 1e6, 2), "frac": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}))
+            if wl.hidden:
+                pj = W.proj_inputs(wl)
+                x, w = up(pj["x"]), up(pj["w"])
+                us = timeit(lambda: m.qkv_proj(x, w, wl.H_q, wl.H_kv, wl.d))
+                fl = 2.0 * x.shape[0] * wl.hidden * wl.N
+                log(json.dumps({"sweep": name, "kernel": "qkv_proj", "us": round(us, 2),
+                                "tflops": round(fl / us / 1e6, 2)}))
+            del q, k, v, o
+        else:
+            din = W.decode_inputs(wl)
+            kc, vc = up(din["k_cache"]), up(din["v_cache"])
+            lens_np = din["seq_lens"]
+            if name == "mqa_decode":
+                lens_np = np.full(wl.B, wl.len_hi, np.int32)
+            lens = torch.from_numpy(lens_np).to(dev)
+            q = up(din["q"])
+            o = torch.empty_like(q)
+            ws = torch.empty(m.decode_workspace_bytes(wl.B, wl.H_q, wl.H_kv, wl.d, wl.L_max), dtype=torch.uint8,
+                             device=dev)
+            us = timeit(lambda: m.gqa_attn_decode(q, kc, vc, lens, workspace=ws, out=o))
+            by = 2.0 * (int(lens_np.sum()) * wl.H_kv * wl.d * 2 + 2 * wl.B * wl.H_q * wl.d)
+            log(json.dumps({"sweep": name, "kernel": "decode", "us": round(us, 2),
+                            "gbps": round(by / us / 1e3, 1), "frac": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}))
+            pj = W.proj_inputs(wl)
+            x, w = up(pj["x"]), up(pj["w"])
+            us = timeit(lambda: m.qkv_proj(x, w, wl.H_q, wl.H_kv, wl.d))
+            by = 2.0 * (wl.hidden * wl.N + x.shape[0] * (wl.hidden + wl.N))
+            log(json.dumps({"sweep": name, "kernel": "qkv_proj", "us": round(us, 2),
+                            "gbps": round(by / us / 1e3, 1)}))
+            del kc, vc
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()
