@@ -117,7 +117,7 @@ size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int
  *   o   [B, H_q, d] contiguous (o_dtype), lse [B, H_q] fp32 or NULL
  *
  * The keys are processed in splits of kv_split keys (0 = library choice; else a
- * multiple of 64 in [64, 65536]); partial (max, sum, output) triples go to
+ * multiple of 32 in [32, 65536]); partial (max, sum, output) triples go to
  * `workspace` and a second kernel combines them exactly.
  * workspace_bytes must be >= gqa_attn_decode_workspace_bytes(...).
  */

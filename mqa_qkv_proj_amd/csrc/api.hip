@@ -37,18 +37,21 @@ mqkv_status check_heads(int32_t H_q, int32_t H_kv, int32_t d) {
   return MQKV_OK;
 }
 
-// Keys per decode split chosen by the library: enough (sequence, KV head, split)
-// units to cover the chip about twice, in multiples of the 64-key tile.
+// Keys per decode split chosen by the library: about 8192 (sequence, KV head,
+// split) units at full cache length, i.e. several per single-wave slot of the
+// chip, so that waves whose split lies beyond a short sequence's length are
+// back-filled; multiples of the 32-key tile, at least 96 keys so that the
+// partial outputs stay a small part of the traffic.
 int32_t auto_split(int32_t B, int32_t H_kv, int32_t L_max) {
-  const int64_t target_units = 2048;
+  const int64_t target_units = 8192;
   const int64_t work = (int64_t)L_max * B * H_kv;
-  int64_t split = 64 * ((work + 64 * target_units - 1) / (64 * target_units));
-  if (split < 64) split = 64;
-  if (split > 2048) split = 2048;
+  int64_t split = 32 * ((work + 32 * target_units - 1) / (32 * target_units));
+  if (split < 96) split = 96;
+  if (split > 8192) split = 8192;
   return (int32_t)split;
 }
 
-bool split_ok(int32_t s) { return s >= 64 && s <= 65536 && s % 64 == 0; }
+bool split_ok(int32_t s) { return s >= 32 && s <= 65536 && s % 32 == 0; }
 
 }  // namespace
 
@@ -147,7 +150,7 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
   if (B < 0) return fail(MQKV_ERR_INVALID, "B=%d must be >= 0", B);
   if (L_max < 1) return fail(MQKV_ERR_INVALID, "L_max=%d must be >= 1", L_max);
   if (kv_split != 0 && !split_ok(kv_split))
-    return fail(MQKV_ERR_INVALID, "kv_split=%d must be 0 or a multiple of 64 in [64, 65536]", kv_split);
+    return fail(MQKV_ERR_INVALID, "kv_split=%d must be 0 or a multiple of 32 in [32, 65536]", kv_split);
   if (!isfinite(scale) || scale < 0.0f) return fail(MQKV_ERR_INVALID, "scale must be finite and >= 0");
   if (!q || !k_cache || !v_cache || !seq_lens || !o)
     return fail(MQKV_ERR_INVALID, "q, k_cache, v_cache, seq_lens and o must be non-NULL");

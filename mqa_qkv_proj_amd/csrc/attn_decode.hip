@@ -10,15 +10,15 @@
 // of tiling + softmax rescaling and the HN remark on splitting/combining the
 // softmax).
 //
-// Split kernel (bf16): one wave per (sequence, KV head, split, block of 32
-// query heads of the group).  Each K/V row is read from HBM once and serves
-// all G query heads of its group through MFMA: S^T = K . Q^T (bf16 MFMA with
-// the heads as the 32 columns) and O^T += V^T . P^T (fp16 MFMA).  K/V tiles of
-// 64 keys are loaded with coalesced 16-byte loads (the next tile is prefetched
-// into registers while the current one is computed) and staged in the wave's
-// own LDS region: K as-is, V transposed and converted to fp16.  No workgroup
-// barrier is used, so waves with different split lengths never wait on each
-// other.  Splits that start beyond seq_lens[b] exit at once.
+// Split kernel (bf16): one single-wave workgroup per (sequence, KV head, split,
+// block of 16 query heads of the group).  Each K/V row is read from HBM once
+// and serves all G query heads of its group through MFMA 16x16x32: S^T = K . Q^T
+// (bf16, the heads as the 16 columns) and O^T += V^T . P^T (fp16, P rounded to
+// fp16 as in the prefill kernel).  K rows are loaded straight into the MFMA
+// operand registers; V rows are staged through the wave's LDS, transposed and
+// converted to fp16.  Tiles are 32 keys; the next tile's loads are in flight
+// while the current one is finished.  Splits that start beyond seq_lens[b] exit
+// at once and free their slot; three waves fit per SIMD.
 // Combine kernel: one workgroup per (sequence, query head), one thread per
 // output element.
 #include "common.h"
@@ -28,42 +28,52 @@ namespace mqkv {
 
 namespace {
 
-constexpr int kTK = 64;  // keys per tile
-constexpr int kWaves = 4;
+constexpr int kTK = 32;  // keys per tile: two 16-key MFMA blocks
 
 template <int D>
 struct DecodeLds {
-  static constexpr int kKld = D + 8;
-  static constexpr int kVld = kTK + 8;
-  static constexpr int kK = kTK * kKld;
-  static constexpr int kWave = kK + D * kVld;  // elements per wave
-  static constexpr size_t kBytes = (size_t)kWaves * kWave * sizeof(uint16_t);
+  static constexpr int kVld = kTK + 8;  // V^T row stride (fp16 elements)
+  static constexpr size_t kBytes = (size_t)D * kVld * sizeof(uint16_t);
 };
 
-__device__ __forceinline__ int vt_pos(int a) { return ((a & 1) << 3) | ((a >> 1) << 2); }
+// Position in a V^T row of key k (0..31) of a tile: the P^T operand lane group
+// kg holds keys {4kg..4kg+3} of the first 16-key block then the same of the
+// second block, so those eight keys are stored contiguously.
+__device__ __forceinline__ int vt_pos32(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
 
+__device__ __forceinline__ f32x4_t mfma16_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// One single-wave workgroup (a finished wave frees its slot at once) per
+// (sequence, KV head, block of 16 query heads, split).  MFMA 16x16x32 layout:
+// A (16 x 32): lane l holds row l%16, k slot group l/16; B (32 x 16): column
+// l%16, the same k group; D (16 x 16): column l%16, rows 4*(l/16) + i.
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) void attn_decode_split_bf16_kernel(
+__global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_split, int n_qblk,
-    int n_sgrp) {
+    int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_split, int n_qblk) {
   using S = DecodeLds<D>;
-  constexpr int DS = D / 16, DB = D / 32;
-  constexpr int KCH = kTK * D / 8 / 64;          // K chunks per lane
-  constexpr int VTASK = (kTK / 4) * (D / 8) / 64;  // V 4x8 tasks per lane
+  constexpr int DS = D / 32;                       // k-steps of the score MFMA
+  constexpr int DB = D / 16;                       // 16-row blocks of O^T
+  constexpr int VTASK = (kTK / 4) * (D / 8) / 64;  // V 4x8 blocks per lane
   extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* Vt = smem;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, hf = lane >> 5;
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  // splits of one (sequence, KV head) are neighbours; each XCD gets a contiguous range
   int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int sgrp = lid % n_sgrp;
-  lid /= n_sgrp;
+  const int s = lid % n_split;
+  lid /= n_split;
   const int qblk = lid % n_qblk;
   const int bg = lid / n_qblk;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int s = sgrp * kWaves + wave;
-  if (s >= n_split) return;
   const int len = min(seq_lens[b], Lmax);  // lengths beyond the cache are clamped (caller error)
   const int kbeg = s * split;
   if (kbeg >= len) return;
@@ -71,58 +81,53 @@ __global__ __launch_bounds__(kWaves * 64) void attn_decode_split_bf16_kernel(
   const int nt = (kend - kbeg + kTK - 1) / kTK;
 
   const int G = Hq / Hkv;
-  const int col = qblk * 32 + l32;  // query head within the group
+  const int col = qblk * 16 + l16;  // query head within the group
   const bool hvalid = col < G;
   const int h = g * G + (hvalid ? col : 0);
 
-  uint16_t* Ks = smem + wave * S::kWave;
-  uint16_t* Vt = Ks + S::kK;
-
+  // Q^T operand: at k-step st lane (col, g4) holds d-chunk 4*st + g4 of its head
+  // (the four lanes of a row then read 64 contiguous bytes per K load)
   u32x4_t qf[DS];
   {
-    const uint16_t* qp = q + (int64_t)b * q_stride + (int64_t)h * D + hf * 8;
+    const uint16_t* qp = q + (int64_t)b * q_stride + (int64_t)h * D + g4 * 8;
 #pragma unroll
-    for (int t = 0; t < DS; ++t) qf[t] = hvalid ? ld16(qp + t * 16) : u32x4_t{0, 0, 0, 0};
+    for (int st = 0; st < DS; ++st) qf[st] = hvalid ? ld16(qp + st * 32) : u32x4_t{0, 0, 0, 0};
   }
 
   const int64_t row_stride = (int64_t)Hkv * D;
-  const uint16_t* kbase = kc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D;
+  const uint16_t* kbase = kc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D + g4 * 8;
   const uint16_t* vbase = vc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D;
 
-  u32x4_t rk[KCH];
+  // K goes straight into the A-operand registers (lane = key row); V is staged
+  // through LDS to be transposed.
+  u32x4_t kr[2][DS];
   u32x4_t rv[VTASK][4];
   auto load_tile = [&](int t) {
     const int k0 = kbeg + t * kTK;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int ci = lane + j * 64;
-      const int key = ci / (D / 8), dc = ci % (D / 8);
-      const int gk = k0 + key;
-      rk[j] = (gk < kend) ? ld16(kbase + (int64_t)gk * row_stride + dc * 8) : u32x4_t{0, 0, 0, 0};
+    for (int kb = 0; kb < 2; ++kb) {
+      const int gk = k0 + kb * 16 + l16;
+#pragma unroll
+      for (int st = 0; st < DS; ++st)
+        kr[kb][st] = (gk < kend) ? ld16(kbase + (int64_t)gk * row_stride + st * 32) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < VTASK; ++j) {
       const int ti = lane + j * 64;
-      const int kg = ti / (D / 8), dg = ti % (D / 8);
+      const int a = ti / (D / 8), dg = ti % (D / 8);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int gk = k0 + kg * 4 + jj;
+        const int gk = k0 + a * 4 + jj;
         rv[j][jj] = (gk < kend) ? ld16(vbase + (int64_t)gk * row_stride + dg * 8) : u32x4_t{0, 0, 0, 0};
       }
     }
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int ci = lane + j * 64;
-      const int key = ci / (D / 8), dc = ci % (D / 8);
-      st16(Ks + key * S::kKld + dc * 8, rk[j]);
-    }
+  auto store_v = [&]() {
 #pragma unroll
     for (int j = 0; j < VTASK; ++j) {
       const int ti = lane + j * 64;
-      const int kg = ti / (D / 8), dg = ti % (D / 8);
-      const int cpos = (kg >> 2) * 16 + vt_pos(kg & 3);
+      const int a = ti / (D / 8), dg = ti % (D / 8);
+      const int cpos = vt_pos32(a * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         u32x2_t lo, hi;
@@ -136,44 +141,38 @@ __global__ __launch_bounds__(kWaves * 64) void attn_decode_split_bf16_kernel(
     }
   };
 
-  f32x16_t acc[DB];
+  f32x4_t acc[DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) acc[i] = f32x16_t{};
+  for (int i = 0; i < DB; ++i) acc[i] = f32x4_t{};
   float m_run = -INFINITY, l_run = 0.0f;
+  const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   load_tile(0);
   for (int t = 0; t < nt; ++t) {
-    wave_lds_sync();  // previous tile's LDS reads are done before overwriting
-    store_tile();
+    wave_lds_sync();  // the previous tile's V^T reads are done before overwriting
+    store_v();
     wave_lds_sync();
-    if (t + 1 < nt) load_tile(t + 1);
     const int k0 = kbeg + t * kTK;
-
-    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
+    f32x4_t sb[2] = {f32x4_t{}, f32x4_t{}};
 #pragma unroll
     for (int st = 0; st < DS; ++st)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4_t a = ld16(Ks + (kb * 32 + l32) * S::kKld + st * 16 + hf * 8);
-        sacc[kb] = mfma32_bf16(a, qf[st], sacc[kb]);
-      }
+      for (int kb = 0; kb < 2; ++kb) sb[kb] = mfma16_bf16(kr[kb][st], qf[st], sb[kb]);
+    if (t + 1 < nt) load_tile(t + 1);  // in flight while this tile is finished
 
-    const bool masked = (k0 + kTK > kend);
-    if (masked) {
+    // lane (col, g4) holds keys kb*16 + 4*g4 + i of its query head
+    if (k0 + kTK > kend) {
+      const int rel = kend - 1 - k0 - 4 * g4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (key >= kend) sacc[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i)
+          if (kb * 16 + i > rel) sb[kb][i] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, xor32(mx));
+    float mx = fmaxf(fmaxf(fmaxf(sb[0][0], sb[0][1]), fmaxf(sb[0][2], sb[0][3])),
+                     fmaxf(fmaxf(sb[1][0], sb[1][1]), fmaxf(sb[1][2], sb[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mt = mx * c;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.0f) != 0) {
       const float mn = fmaxf(m_run, mt);
@@ -183,48 +182,32 @@ __global__ __launch_bounds__(kWaves * 64) void attn_decode_split_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < DB; ++i) acc[i] *= alpha;
     }
-    u32x4_t pf[4];
-    float ls = 0.0f;
+    // P^T operand: slots 0-3 = keys 4*g4+i of block 0, slots 4-7 = the same of block 1
+    u32x4_t pf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, -m_run));
-        if (masked) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          p[i] = (key >= kend) ? 0.0f : p[i];
-        }
-        ls += p[i];
-      }
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pf[kb * 2 + hb][e] = pack_f16(p[hb * 8 + 2 * e], p[hb * 8 + 2 * e + 1]);
+    for (int e = 0; e < 4; ++e) {
+      const int kb = e >> 1, i = (e & 1) * 2;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[kb][i], c, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[kb][i + 1], c, -m_run));
+      const uint32_t w = pack_f16(p0, p1);
+      pf[e] = w;
+      l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
     }
-    l_run += ls;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4_t a = ld16(Vt + (db * 32 + l32) * S::kVld + ks * 16 + hf * 8);
-        acc[db] = mfma32_f16(a, pf[ks], acc[db]);
-      }
+    for (int db = 0; db < DB; ++db)
+      acc[db] = mfma16_f16(ld16(Vt + (db * 16 + l16) * S::kVld + g4 * 8), pf, acc[db]);
   }
 
-  const float l_tot = l_run + xor32(l_run);
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
   if (!hvalid) return;
   const int64_t pidx = ((int64_t)b * Hq + h) * n_split + s;
   float* po = part_o + pidx * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = db * 32 + 8 * g4 + 4 * hf;
-      st16(po + d0, u32x4_t{__float_as_uint(acc[db][4 * g4]), __float_as_uint(acc[db][4 * g4 + 1]),
-                            __float_as_uint(acc[db][4 * g4 + 2]), __float_as_uint(acc[db][4 * g4 + 3])});
-    }
-  if (hf == 0) {
+    st16(po + db * 16 + 4 * g4, u32x4_t{__float_as_uint(acc[db][0]), __float_as_uint(acc[db][1]),
+                                        __float_as_uint(acc[db][2]), __float_as_uint(acc[db][3])});
+  if (g4 == 0) {
     part_ml[pidx * 2 + 0] = m_run;
     part_ml[pidx * 2 + 1] = l_tot;
   }
@@ -291,49 +274,85 @@ __global__ __launch_bounds__(64) void attn_decode_split_f32_kernel(
   }
 }
 
-// Combine the partials of every split of one (sequence, query head).
-template <bool OUT_BF16>
-__global__ void attn_decode_combine_kernel(const int32_t* __restrict__ seq_lens,
-                                           const float* __restrict__ part_o,
-                                           const float* __restrict__ part_ml, void* __restrict__ o,
-                                           float* __restrict__ lse, int Hq, int D, int split,
-                                           int n_split) {
-  const int bh = blockIdx.x;
-  const int b = bh / Hq;
-  const int dd = threadIdx.x;
-  const int n = min((seq_lens[b] + split - 1) / split, n_split);
-  const float* ml = part_ml + (int64_t)bh * n_split * 2;
+// Combine the partials of every split: one wave per (sequence, query head).
+// Lanes first reduce the per-split (max, sum) statistics in parallel; then
+// each lane owns D/64 output elements and accumulates the splits' weighted
+// partial outputs with 8 loads in flight.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(64) void attn_decode_combine_kernel(
+    const int32_t* __restrict__ seq_lens, const float* __restrict__ part_o,
+    const float* __restrict__ part_ml, void* __restrict__ o, float* __restrict__ lse, int Hq,
+    int Lmax, int split, int n_split) {
+  constexpr int EPL = D / 64;  // output elements per lane
+  __shared__ float wsh[64];
+  const int lane = threadIdx.x;
+  const int b = blockIdx.y, h = blockIdx.x;
+  const int64_t bh = (int64_t)b * Hq + h;
+  const int len = min(seq_lens[b], Lmax);
+  const int n = min((len + split - 1) / split, n_split);
+  const float* ml = part_ml + bh * n_split * 2;
+  const float* po = part_o + bh * n_split * D;
+
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.0f, acc = 0.0f;
-  const float* po = part_o + (int64_t)bh * n_split * D;
-  for (int s = 0; s < n; ++s) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-    L = __builtin_fmaf(w, ml[2 * s + 1], L);
-    acc = __builtin_fmaf(w, po[(int64_t)s * D + dd], acc);
+  for (int s0 = lane; s0 < n; s0 += 64) M = fmaxf(M, ml[2 * s0]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+  float L = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int sl = c0 + lane;
+    const float w = (sl < n) ? __builtin_amdgcn_exp2f(ml[2 * sl] - M) : 0.0f;
+    float lw = (sl < n) ? w * ml[2 * sl + 1] : 0.0f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off, 64);
+    L += lw;
+    wsh[lane] = w;
+    __syncthreads();
+    const int cnt = min(64, n - c0);
+    int s = 0;
+    for (; s + 8 <= cnt; s += 8) {
+      float v[8][EPL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[u][e] = po[(int64_t)(c0 + s + u) * D + e * 64 + lane];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(wsh[s + u], v[u][e], acc[e]);
+    }
+    for (; s < cnt; ++s)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        acc[e] = __builtin_fmaf(wsh[s], po[(int64_t)(c0 + s) * D + e * 64 + lane], acc[e]);
+    __syncthreads();
   }
-  const float val = acc / L;
-  if constexpr (OUT_BF16)
-    static_cast<uint16_t*>(o)[(int64_t)bh * D + dd] = f32_to_bf16(val);
-  else
-    static_cast<float*>(o)[(int64_t)bh * D + dd] = val;
-  if (lse != nullptr && dd == 0) lse[bh] = (M + __builtin_log2f(L)) * kLn2;
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int64_t oi = bh * D + e * 64 + lane;
+    if constexpr (OUT_BF16)
+      static_cast<uint16_t*>(o)[oi] = f32_to_bf16(acc[e] * inv);
+    else
+      static_cast<float*>(o)[oi] = acc[e] * inv;
+  }
+  if (lse != nullptr && lane == 0) lse[bh] = (M + __builtin_log2f(L)) * kLn2;
 }
 
 template <int D>
 hipError_t launch_split_bf16(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const int n_qblk = (G + 31) / 32;
-  const int n_sgrp = (a.n_split + kWaves - 1) / kWaves;
-  const int64_t nblk = (int64_t)a.B * a.Hkv * n_qblk * n_sgrp;
+  const int n_qblk = (G + 15) / 16;
+  const int64_t nblk = (int64_t)a.B * a.Hkv * n_qblk * a.n_split;
   if (nblk > 0x7fffffff) return hipErrorInvalidValue;
   auto kern = attn_decode_split_bf16_kernel<D>;
   const size_t lds = DecodeLds<D>::kBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kWaves * 64), lds, s, (const uint16_t*)a.q,
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_lens, a.part_o, a.part_ml, a.Hq,
-                     a.Hkv, a.Lmax, a.q_stride, a.scale * kLog2e, a.split, a.n_split, n_qblk, n_sgrp);
+                     a.Hkv, a.Lmax, a.q_stride, fmaxf(a.scale * kLog2e, 1e-30f), a.split, a.n_split,
+                     n_qblk);
   return hipGetLastError();
 }
 
@@ -355,13 +374,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   else
     e = a.d == 64 ? launch_split_f32<64>(a, s) : launch_split_f32<128>(a, s);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)(a.B * a.Hq));
-  if (a.out_bf16)
-    hipLaunchKernelGGL(attn_decode_combine_kernel<true>, grid, dim3(a.d), 0, s, a.seq_lens, a.part_o,
-                       a.part_ml, a.o, a.lse, a.Hq, a.d, a.split, a.n_split);
-  else
-    hipLaunchKernelGGL(attn_decode_combine_kernel<false>, grid, dim3(a.d), 0, s, a.seq_lens,
-                       a.part_o, a.part_ml, a.o, a.lse, a.Hq, a.d, a.split, a.n_split);
+  const dim3 grid((unsigned)a.Hq, (unsigned)a.B);  // (query head, sequence)
+#define MQKV_COMB(DD, OB)                                                                        \
+  if (a.d == DD && a.out_bf16 == OB)                                                            \
+    hipLaunchKernelGGL((attn_decode_combine_kernel<DD, OB>), grid, dim3(64), 0, s, a.seq_lens,   \
+                       a.part_o, a.part_ml, a.o, a.lse, a.Hq, a.Lmax, a.split, a.n_split);
+  MQKV_COMB(64, true)
+  MQKV_COMB(64, false)
+  MQKV_COMB(128, true)
+  MQKV_COMB(128, false)
+#undef MQKV_COMB
   return hipGetLastError();
 }
 

@@ -30,6 +30,8 @@
 //    dispatched first.  Workgroup ids are remapped so that each XCD serves a
 //    contiguous range of (batch, KV head) blocks and keeps their K/V in its L2.
 // fp32 inputs use a plain one-row-per-thread kernel (fp32 throughout).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -37,11 +39,20 @@ namespace mqkv {
 
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef MQKV_PF_WAVES
+#define MQKV_PF_WAVES 8  // waves per workgroup (32 query rows each)
+#endif
+#ifndef MQKV_PF_BK
+#define MQKV_PF_BK 64    // keys per K/V tile (a multiple of 64)
+#endif
+constexpr int kWaves = MQKV_PF_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = kWaves * 32;  // query rows per workgroup
-constexpr int kBK = 64;             // keys per tile
+constexpr int kBK = MQKV_PF_BK;
 constexpr float kTau = 8.0f;        // lazy-rescale threshold (log2 units)
+#ifndef MQKV_PF_OCC
+#define MQKV_PF_OCC 2  // minimum waves per SIMD the register budget must allow
+#endif
 
 template <int D>
 struct PrefillLds {
@@ -58,7 +69,7 @@ struct PrefillLds {
 __device__ __forceinline__ int vt_pos(int a) { return ((a & 1) << 3) | ((a >> 1) << 2); }
 
 template <int D, bool CAUSAL, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
+__global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, float* __restrict__ lse, int Lq, int Lkv, int Hq, int Hkv,
     int64_t q_stride, int64_t kv_stride, float c, int F, int n_hg, int n_qb) {
@@ -66,7 +77,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   constexpr int DS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   constexpr int KCH = kBK * D / 8 / kThreads;  // 16B K chunks per thread
+  static_assert(KCH >= 1 && KCH * kThreads == kBK * D / 8, "K tile split over threads");
   constexpr int VT = (kBK / 4) * (D / 8);      // 4x8 V tasks per tile
+  constexpr int VTPT = (VT + kThreads - 1) / kThreads;  // V tasks per thread
   extern __shared__ __align__(16) uint16_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   const uint16_t* vbase = v + (int64_t)b * Lkv * kv_stride + (int64_t)g * D;
 
   u32x4_t rk[KCH];
-  u32x4_t rv[4];
+  u32x4_t rv[VTPT][4];
   auto load_tile = [&](int t) {
     const int k0 = t * kBK;
 #pragma unroll
@@ -118,12 +131,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
       rk[j] = (k0 + key < Lkv) ? ld16(kbase + (int64_t)(k0 + key) * kv_stride + dc * 8)
                                : u32x4_t{0, 0, 0, 0};
     }
-    if (tid < VT) {
-      const int kg = tid / (D / 8), dg = tid % (D / 8);
+#pragma unroll
+    for (int j = 0; j < VTPT; ++j) {
+      const int ti = tid + j * kThreads;
+      const int kg = ti / (D / 8), dg = ti % (D / 8);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int key = k0 + kg * 4 + jj;
-        rv[jj] = (key < Lkv) ? ld16(vbase + (int64_t)key * kv_stride + dg * 8) : u32x4_t{0, 0, 0, 0};
+        rv[j][jj] = (ti < VT && key < Lkv) ? ld16(vbase + (int64_t)key * kv_stride + dg * 8)
+                                           : u32x4_t{0, 0, 0, 0};
       }
     }
   };
@@ -136,19 +152,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
       const int key = ci / (D / 8), dc = ci % (D / 8);
       st16(Ks + key * S::kKld + dc * 8, rk[j]);
     }
-    if (tid < VT) {
-      const int kg = tid / (D / 8), dg = tid % (D / 8);
-      const int col = (kg >> 2) * 16 + vt_pos(kg & 3);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // rv[jj][e] = V[key jj][d = 8dg+2e, 8dg+2e+1] (bf16 pair)
-        u32x2_t lo, hi;
-        lo[0] = pack_f16(bf16lo(rv[0][e]), bf16lo(rv[1][e]));
-        lo[1] = pack_f16(bf16lo(rv[2][e]), bf16lo(rv[3][e]));
-        hi[0] = pack_f16(bf16hi(rv[0][e]), bf16hi(rv[1][e]));
-        hi[1] = pack_f16(bf16hi(rv[2][e]), bf16hi(rv[3][e]));
-        st8(Vt + (dg * 8 + 2 * e) * S::kVld + col, lo);
-        st8(Vt + (dg * 8 + 2 * e + 1) * S::kVld + col, hi);
+    for (int j = 0; j < VTPT; ++j) {
+      const int ti = tid + j * kThreads;
+      if (ti < VT) {
+        const int kg = ti / (D / 8), dg = ti % (D / 8);
+        const int col = (kg >> 2) * 16 + vt_pos(kg & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // rv[j][jj][e] = V[key jj][d = 8dg+2e, 8dg+2e+1] (bf16 pair)
+          u32x2_t lo, hi;
+          lo[0] = pack_f16(bf16lo(rv[j][0][e]), bf16lo(rv[j][1][e]));
+          lo[1] = pack_f16(bf16lo(rv[j][2][e]), bf16lo(rv[j][3][e]));
+          hi[0] = pack_f16(bf16hi(rv[j][0][e]), bf16hi(rv[j][1][e]));
+          hi[1] = pack_f16(bf16hi(rv[j][2][e]), bf16hi(rv[j][3][e]));
+          st8(Vt + (dg * 8 + 2 * e) * S::kVld + col, lo);
+          st8(Vt + (dg * 8 + 2 * e + 1) * S::kVld + col, hi);
+        }
       }
     }
   };
@@ -159,88 +179,99 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   float m_run = -INFINITY;  // running max of S*c (log2 units)
   float l_run = 0.0f;       // this lane's share of the running sum
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) load_tile(t + 1);
-    const uint16_t* Ks = smem + buf * S::kStage;
-    const uint16_t* Vt = Ks + S::kK;
-    const int k0 = t * kBK;
-
-    // S^T = K . Q^T for 64 keys (two 32-key blocks)
-    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
+  // One 32-key half: scores -> online softmax -> O^T += V^T P^T.  The two halves
+  // are issued back to back so that one half's softmax (VALU) runs while the
+  // other half's MFMAs are in flight.
+  const uint16_t* Ks;
+  const uint16_t* Vt;
+  int k0;
+    auto half = [&](f32x16_t sc, int kb, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      if constexpr (MASK) {
+        // key - k0 - 4*hf of element i is 32kb + 8(i/4) + (i%4); mask keys beyond lim
+        const int rel = lim - k0 - 4 * hf - 32 * kb;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4_t a = ld16(Ks + (kb * 32 + l32) * S::kKld + s * 16 + hf * 8);
-        sacc[kb] = mfma32_bf16(a, qf[s], sacc[kb]);
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) > rel) sc[i] = -INFINITY;
       }
-    }
-
-    const bool masked = (k0 + kBK > mask_from);
-    float mx = -INFINITY;
-    if (masked) {
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
+      mx = fmaxf(mx, sc[15]);
+      mx = fmaxf(mx, xor32(mx));
+      const float mt = mx * c;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
+        const float mn = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        m_run = mn;
+        l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (key > lim) sacc[kb][i] = -INFINITY;
-        }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, xor32(mx));
-    const float mt = mx * c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      m_run = mn;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DB; ++i) acc[i] *= alpha;
-    }
-
-    // p = exp2(S*c - m), rounded to fp16 pairs in the P^T operand order
-    u32x4_t pf[4];
-    float ls = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, -m_run));
-        if (masked) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          p[i] = (key > lim) ? 0.0f : p[i];
-        }
-        ls += p[i];
+        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
       }
+      u32x4_t pf[2];
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pf[kb * 2 + hb][e] = pack_f16(p[hb * 8 + 2 * e], p[hb * 8 + 2 * e + 1]);
-    }
-    l_run += ls;
-
-    // O^T += V^T . P^T
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
+          pf[hb][e] = pack_f16(p0, p1);
+        }
+      // row sum of the fp16-rounded P actually multiplied into V (fp32 accumulation)
+      const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4_t a = ld16(Vt + (db * 32 + l32) * S::kVld + ks * 16 + hf * 8);
-        acc[db] = mfma32_f16(a, pf[ks], acc[db]);
+        for (int e = 0; e < 4; ++e) {
+          // copy the element out first: a bit_cast applied to a vector element
+          // lvalue reads element 0 with this compiler
+          const uint32_t w = pf[hb][e];
+          l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
+        }
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        u32x4_t vf[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          vf[db] = ld16(Vt + (db * 32 + l32) * S::kVld + (kb * 2 + hb) * 16 + hf * 8);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32_f16(vf[db], pf[hb], acc[db]);
       }
-    }
+    };
+    auto tile = [&](auto mask_tag) {
+#pragma unroll
+      for (int sub = 0; sub < kBK / 64; ++sub) {
+        f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+          s0 = mfma32_bf16(ld16(Ks + (sub * 64 + l32) * S::kKld + st * 16 + hf * 8), qf[st], s0);
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+          s1 = mfma32_bf16(ld16(Ks + (sub * 64 + 32 + l32) * S::kKld + st * 16 + hf * 8), qf[st], s1);
+        half(s0, 2 * sub, mask_tag);
+        half(s1, 2 * sub + 1, mask_tag);
+      }
+    };
 
+  // Tiles below every row's causal limit run without masking; the loop is split
+  // so that the masked body is a separate piece of code.
+  auto iter = [&](int t, auto mask_tag) {
+    const int buf = t & 1;
+    if (t + 1 < nt) load_tile(t + 1);
+    Ks = smem + buf * S::kStage;
+    Vt = Ks + S::kK;
+    k0 = t * kBK;
+    tile(mask_tag);
     if (t + 1 < nt) store_tile(buf ^ 1);
     __syncthreads();
-  }
+  };
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  const int t_mask = min(nt, mask_from / kBK);
+  int t = 0;
+  for (; t < t_mask; ++t) iter(t, std::false_type{});
+  for (; t < nt; ++t) iter(t, std::true_type{});
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + xor32(l_run);
@@ -347,7 +378,9 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const size_t lds = PrefillLds<D>::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const float c = a.scale * kLog2e;
+  // scale 0 is run as a tiny positive scale: masked scores stay -inf after the
+  // multiply and every visible score maps to exp2(0) = 1 exactly.
+  const float c = fmaxf(a.scale * kLog2e, 1e-30f);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kThreads), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv,
                      a.q_stride, a.kv_stride, c, F, n_hg, n_qb);

@@ -104,13 +104,13 @@ def test_decode_workspace_query(lib):
     assert n > 32 * 32 * 128 * 4
     assert f(32, 32, 8, 128, 4096, 64) == 32 * 32 * 64 * (128 * 4 + 8) + 256
     assert f(2, 8, 3, 128, 100, 0) == 0       # H_q % H_kv
-    assert f(2, 8, 2, 128, 100, 100) == 0     # split not a multiple of 64
+    assert f(2, 8, 2, 128, 100, 100) == 0     # split not a multiple of 32
     assert f(2, 8, 2, 96, 100, 0) == 0        # d
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(lens=None), INV), (dict(lens=A + 2), INV), (dict(ws=None), INV), (dict(wsb=16), INV),
-    (dict(split=100), INV), (dict(split=32), INV), (dict(Lmax=0), INV), (dict(qs=1000), INV),
+    (dict(split=100), INV), (dict(split=16), INV), (dict(split=48), INV), (dict(Lmax=0), INV), (dict(qs=1000), INV),
     (dict(qs=512), INV), (dict(scale=float("nan")), INV), (dict(d=80, qs=1024), UNS),
     (dict(dt=F32, odt=BF16), UNS), (dict(H_q=8, H_kv=3), INV), (dict(ws=A + 8), INV),
 ])

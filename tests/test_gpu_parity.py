@@ -168,6 +168,7 @@ DECODE = [  # B, H_q, H_kv, d, L_max, lens, split
     (3, 8, 2, 128, 300, [1, 77, 300], 0),
     (3, 8, 2, 128, 300, [1, 77, 300], 64),
     (3, 8, 2, 128, 300, [1, 77, 300], 128),
+    (3, 8, 2, 128, 300, [1, 33, 300], 32),
     (2, 16, 1, 128, 1040, [17, 1040], 0),
     (4, 4, 4, 64, 200, [200, 5, 64, 65], 64),
     (2, 6, 3, 64, 130, [129, 130], 0),
