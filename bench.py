@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_BYTES = 256 << 20      # calibration copy: reads and writes this many bytes
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_long_kv4_causal_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "mqa_qkv_proj_amd", "csrc", "attn_prefill.hip")
 
 
 def log(*a):
@@ -43,11 +46,14 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--sweep", action="store_true", help="also time every configuration (stderr)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="run one 256 MiB device-to-device copy first (known-size reference for HBM "
+                        "byte counters)")
     return p.parse_args()
 
 
@@ -100,6 +106,13 @@ def main():
                      device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
+    if args.calib_copy:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     scale_p = 1.0 / math.sqrt(wp.d)
     scale_d = 1.0 / math.sqrt(wd.d)
@@ -185,7 +198,8 @@ def main():
         "qkv_proj": {"tflops": round(gemm_tf, 2), "gbps": round(gemm_gbs, 1),
                      "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "us": round(ms_gemm * 1e3, 2)},
         "roofline": {"bound": "mfma", "achieved": round(pre_tf, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(),
                      "kernel": "attn_prefill_bf16 (d=128, causal)"},
         "cpu_baseline": None,
     }
@@ -194,6 +208,22 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SRC, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(W, wp, seconds):

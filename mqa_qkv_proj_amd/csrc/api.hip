@@ -27,6 +27,7 @@ mqkv_status hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dtype_ok(mqkv_dtype t) { return t == MQKV_F32 || t == MQKV_BF16; }
 int elem_align(mqkv_dtype t) { return t == MQKV_BF16 ? 8 : 4; }  // elements per 16 bytes
+int elem_size(mqkv_dtype t) { return t == MQKV_BF16 ? 2 : 4; }
 
 // Shared head-shape checks.
 mqkv_status check_heads(int32_t H_q, int32_t H_kv, int32_t d) {
@@ -120,6 +121,9 @@ mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* 
     return fail(MQKV_ERR_INVALID, "token strides must be multiples of %d elements", ea);
   if (in_dtype == MQKV_F32 && o_dtype != MQKV_F32)
     return fail(MQKV_ERR_UNSUPPORTED, "fp32 inputs need an fp32 output");
+  if ((int64_t)L_kv * kv_tok_stride * elem_size(in_dtype) >= ((int64_t)1 << 31) ||
+      (int64_t)L_q * q_tok_stride * elem_size(in_dtype) >= ((int64_t)1 << 31))
+    return fail(MQKV_ERR_UNSUPPORTED, "one sequence's rows must span less than 2 GiB");
   if (B == 0 || L_q == 0) return MQKV_OK;
   mqkv::PrefillArgs a{q, k, v, o, lse, B, L_q, L_kv, H_q, H_kv, d, q_tok_stride, kv_tok_stride,
                       causal != 0, scale, in_dtype == MQKV_BF16, o_dtype == MQKV_BF16};

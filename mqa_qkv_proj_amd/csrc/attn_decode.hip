@@ -175,7 +175,8 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mt = mx * c;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.0f) != 0) {
-      const float mn = fmaxf(m_run, mt);
+      // only this row's own growth moves its max (rows sharing the wave do not matter)
+      const float mn = (mt > m_run + 8.0f) ? mt : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;

@@ -49,6 +49,7 @@ constexpr int kWaves = MQKV_PF_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = kWaves * 32;  // query rows per workgroup
 constexpr int kBK = MQKV_PF_BK;
+constexpr int kStages = 2;  // K/V tiles resident in LDS (double buffer)
 constexpr float kTau = 8.0f;        // lazy-rescale threshold (log2 units)
 #ifndef MQKV_PF_OCC
 #define MQKV_PF_OCC 2  // minimum waves per SIMD the register budget must allow
@@ -61,7 +62,7 @@ struct PrefillLds {
   static constexpr int kK = kBK * kKld;     // elements per K stage
   static constexpr int kV = D * kVld;       // elements per V^T stage
   static constexpr int kStage = kK + kV;
-  static constexpr size_t kBytes = 2 * kStage * sizeof(uint16_t);
+  static constexpr size_t kBytes = kStages * kStage * sizeof(uint16_t);
 };
 
 // Position, inside a 16-key group, of key 4a + j (a = 0..3) in the V^T rows:
@@ -117,8 +118,13 @@ __global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kerne
   const int mask_from = CAUSAL ? min(Lkv, p0 + off + 1) : Lkv;  // first key some row cannot see
   const int nt = (kv_end + kBK - 1) / kBK;
 
-  const uint16_t* kbase = k + (int64_t)b * Lkv * kv_stride + (int64_t)g * D;
-  const uint16_t* vbase = v + (int64_t)b * Lkv * kv_stride + (int64_t)g * D;
+  // K/V rows of batch b through bounds-checked buffer resources: a key >= L_kv
+  // lands at or past the resource end and reads zeros.
+  const uint32_t kv_bytes = (uint32_t)((int64_t)Lkv * kv_stride * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (int64_t)b * Lkv * kv_stride, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (int64_t)b * Lkv * kv_stride, kv_bytes);
+  const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+  const uint32_t head_off = (uint32_t)(g * D * 2);
 
   u32x4_t rk[KCH];
   u32x4_t rv[VTPT][4];
@@ -128,8 +134,7 @@ __global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kerne
     for (int j = 0; j < KCH; ++j) {
       const int ci = tid + j * kThreads;
       const int key = ci / (D / 8), dc = ci % (D / 8);
-      rk[j] = (k0 + key < Lkv) ? ld16(kbase + (int64_t)(k0 + key) * kv_stride + dc * 8)
-                               : u32x4_t{0, 0, 0, 0};
+      rk[j] = bld16(krs, (uint32_t)(k0 + key) * row_bytes + head_off + dc * 16);
     }
 #pragma unroll
     for (int j = 0; j < VTPT; ++j) {
@@ -138,8 +143,7 @@ __global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kerne
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int key = k0 + kg * 4 + jj;
-        rv[j][jj] = (ti < VT && key < Lkv) ? ld16(vbase + (int64_t)key * kv_stride + dg * 8)
-                                           : u32x4_t{0, 0, 0, 0};
+        rv[j][jj] = bld16(vrs, (ti < VT ? (uint32_t)key * row_bytes : kv_bytes) + head_off + dg * 16);
       }
     }
   };
@@ -201,7 +205,9 @@ __global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kerne
       mx = fmaxf(mx, xor32(mx));
       const float mt = mx * c;
       if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
-        const float mn = fmaxf(m_run, mt);
+        // only this row's own growth moves its max, so a row's result does not
+        // depend on the other rows that share the wave
+        const float mn = (mt > m_run + kTau) ? mt : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
         m_run = mn;
         l_run *= alpha;
@@ -255,6 +261,7 @@ __global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kerne
 
   // Tiles below every row's causal limit run without masking; the loop is split
   // so that the masked body is a separate piece of code.
+  const int t_mask = min(nt, mask_from / kBK);
   auto iter = [&](int t, auto mask_tag) {
     const int buf = t & 1;
     if (t + 1 < nt) load_tile(t + 1);
@@ -268,7 +275,6 @@ __global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kerne
   load_tile(0);
   store_tile(0);
   __syncthreads();
-  const int t_mask = min(nt, mask_from / kBK);
   int t = 0;
   for (; t < t_mask; ++t) iter(t, std::false_type{});
   for (; t < nt; ++t) iter(t, std::true_type{});
