@@ -104,6 +104,8 @@ def main():
     Od = torch.empty(wd.B, wd.H_q, wd.d, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(m.decode_workspace_bytes(wd.B, wd.H_q, wd.H_kv, wd.d, wd.L_max), dtype=torch.uint8,
                      device=dev)
+    ws_proj = torch.empty(max(16, m.qkv_proj_workspace_bytes(wd.B, wd.hidden, wd.H_q, wd.H_kv, wd.d)),
+                          dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     if args.calib_copy:
@@ -136,7 +138,7 @@ def main():
         if record:
             e["p1"].record(stream)
             e["g0"].record(stream)
-        m.qkv_proj(x, wq, wd.H_q, wd.H_kv, wd.d, out=qkv)
+        m.qkv_proj(x, wq, wd.H_q, wd.H_kv, wd.d, out=qkv, workspace=ws_proj)
         q_view = qkv[:, :wd.H_q * wd.d].unflatten(-1, (wd.H_q, wd.d))  # split: a strided view
         if record:
             e["g1"].record(stream)

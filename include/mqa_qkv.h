@@ -68,12 +68,20 @@ typedef enum mqkv_dtype { MQKV_F32 = 0, MQKV_BF16 = 1 } mqkv_dtype;
  *                     weight is its transpose), columns [Q | K | V], head-major
  * bias   [N] or NULL
  * qkv    [M, N]       row-major output
+ * workspace, workspace_bytes: optional device scratch (NULL/0 allowed).  With
+ *   at least qkv_proj_workspace_bytes(...) bytes, small-M (<= 128 rows) bf16
+ *   calls split the hidden dimension over more workgroups and reduce the fp32
+ *   partials in a second kernel (fixed order, deterministic); otherwise a
+ *   single-pass kernel runs.  The result is within rounding either way.
  * Requires hidden >= 1 and hidden a multiple of 8 (bf16) / 4 (fp32), d in {64, 128},
  * H_q % H_kv == 0.  M == 0 is a no-op.
  */
+size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
+                                mqkv_dtype dtype);
+
 mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv,
                      int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
-                     mqkv_dtype dtype, void* stream);
+                     mqkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Grouped-query attention over a whole sequence (prefill).

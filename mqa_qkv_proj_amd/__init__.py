@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the computation runs in the HIP
 library (`include/mqa_qkv.h`).  PyTorch provides device memory and the current
 stream.  Importing this module loads the built library and fails loudly if it
-is missing (build it with `python -m mqa_qkv_proj_amd.build`); there is no
+is missing (build it with `python mqa_qkv_proj_amd/build.py`); there is no
 fallback implementation.
 
 Functions mirror the C ABI:
@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libmqa_qkv.so")
 MQKV_OK, MQKV_ERR_INVALID, MQKV_ERR_UNSUPPORTED, MQKV_ERR_HIP = 0, 1, 2, 3
 MQKV_F32, MQKV_BF16 = 0, 1
 
-EXPORTS = ("qkv_proj", "gqa_attn_prefill", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode",
+EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "gqa_attn_prefill", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode",
            "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version")
 
 
@@ -43,10 +43,12 @@ class MqkvInvalid(MqkvError, ValueError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m mqa_qkv_proj_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python mqa_qkv_proj_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-    lib.qkv_proj.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp]
+    lib.qkv_proj_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+    lib.qkv_proj_workspace_bytes.restype = sz
+    lib.qkv_proj.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, sz, vp]
     lib.qkv_proj.restype = i32
     lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32,
                                      f32, i32, i32, vp]
@@ -126,13 +128,18 @@ def _tok_stride(t, L: int, H: int, d: int, name: str) -> int:
 
 # ----------------------------------------------------------------------------- public API
 
-def qkv_proj(x, w_qkv, H_q: int, H_kv: int, d: int, bias=None, out=None):
+def qkv_proj_workspace_bytes(M: int, hidden: int, H_q: int, H_kv: int, d: int, dtype_code: int = MQKV_BF16) -> int:
+    return int(lib.qkv_proj_workspace_bytes(M, hidden, H_q, H_kv, d, dtype_code))
+
+
+def qkv_proj(x, w_qkv, H_q: int, H_kv: int, d: int, bias=None, out=None, workspace=None):
     """Fused projection qkv = x . W_qkv (+ bias): one GEMM for Q, K and V.
 
     x [..., hidden] (contiguous), w_qkv [hidden, N] row-major, N = (H_q + 2*H_kv)*d.
-    Returns qkv [..., N] (or writes `out`)."""
+    Returns qkv [..., N] (or writes `out`).  `workspace` (uint8 device tensor) is
+    allocated when the call can use one and none is given."""
     torch = _torch()
-    _require_cuda(x, w_qkv, bias, out)
+    _require_cuda(x, w_qkv, bias, out, workspace)
     hidden = x.shape[-1]
     N = (H_q + 2 * H_kv) * d
     if w_qkv.shape != (hidden, N):
@@ -146,8 +153,15 @@ def qkv_proj(x, w_qkv, H_q: int, H_kv: int, d: int, bias=None, out=None):
         out = torch.empty(*x.shape[:-1], N, dtype=x.dtype, device=x.device)
     elif out.shape != (*x.shape[:-1], N) or not out.is_contiguous() or out.dtype != x.dtype:
         raise ValueError("out has the wrong shape, dtype or layout")
+    if workspace is None:
+        need = qkv_proj_workspace_bytes(M, hidden, H_q, H_kv, d, _dtype_code(x.dtype))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.qkv_proj(x.data_ptr(), w_qkv.data_ptr(), bias.data_ptr() if bias is not None else None,
-                      out.data_ptr(), M, hidden, H_q, H_kv, d, _dtype_code(x.dtype), _stream(x.device))
+                      out.data_ptr(), M, hidden, H_q, H_kv, d, _dtype_code(x.dtype), ws_ptr, ws_bytes,
+                      _stream(x.device))
     check(st, "qkv_proj")
     return out
 

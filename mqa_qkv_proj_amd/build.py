@@ -1,6 +1,6 @@
 """Build the HIP library libmqa_qkv.so in-tree for gfx950.
 
-    python -m mqa_qkv_proj_amd.build          # or __graft_entry__.build()
+    python mqa_qkv_proj_amd/build.py          # or __graft_entry__.build()
 
 Each source is compiled to an object with hipcc in parallel, then linked into
 mqa_qkv_proj_amd/libmqa_qkv.so (written atomically).  Needs no GPU.

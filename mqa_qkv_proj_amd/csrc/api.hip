@@ -70,11 +70,21 @@ const char* mqkv_status_string(mqkv_status s) {
 
 const char* mqkv_last_error(void) { return g_err; }
 
-int32_t mqkv_abi_version(void) { return 100; }
+int32_t mqkv_abi_version(void) { return 101; }
+
+size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
+                                mqkv_dtype dtype) {
+  if (M < 0 || hidden < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128) ||
+      dtype != MQKV_BF16)
+    return 0;
+  const int64_t N = (int64_t)(H_q + 2 * (int64_t)H_kv) * d;
+  const mqkv::SkinnyPlan p = mqkv::plan_skinny(M, hidden, N);
+  return p.ok ? p.ws_bytes : 0;
+}
 
 mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, int64_t M,
                      int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype,
-                     void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   if (!dtype_ok(dtype)) return fail(MQKV_ERR_INVALID, "dtype %d unknown", (int)dtype);
   mqkv_status st = check_heads(H_q, H_kv, d);
@@ -84,13 +94,15 @@ mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* q
   if (hidden % elem_align(dtype) != 0)
     return fail(MQKV_ERR_INVALID, "hidden=%lld must be a multiple of %d", (long long)hidden, elem_align(dtype));
   if (!x || !w_qkv || !qkv) return fail(MQKV_ERR_INVALID, "x, w_qkv and qkv must be non-NULL");
-  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(qkv) || (bias && !aligned16(bias)))
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(qkv) || (bias && !aligned16(bias)) ||
+      (workspace && !aligned16(workspace)))
     return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned");
   const int64_t N = (int64_t)(H_q + 2 * (int64_t)H_kv) * d;
   if (M > 0x7fffffff || hidden > 0x7fffffff || N > 0x7fffffff)
     return fail(MQKV_ERR_UNSUPPORTED, "sizes beyond 2^31-1 are not supported");
   if (M == 0) return MQKV_OK;
   return hip_status(mqkv::launch_qkv_gemm(x, w_qkv, bias, qkv, M, hidden, N, dtype == MQKV_BF16,
+                                          workspace, workspace ? workspace_bytes : 0,
                                           (hipStream_t)stream),
                     "qkv_proj launch");
 }

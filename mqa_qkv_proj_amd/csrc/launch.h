@@ -5,8 +5,18 @@
 
 namespace mqkv {
 
+// Skinny-M (<= 128 rows) projection plan: k range split over workgroups.
+struct SkinnyPlan {
+  bool ok;        // the skinny path applies
+  int nbm;        // 32-row blocks
+  int ksplit;     // k ranges
+  int krange;     // rows of W per k range (a multiple of 128)
+  size_t ws_bytes;  // fp32 partials needed when ksplit > 1
+};
+SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N);
+
 hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void* out, int64_t M,
-                           int64_t K, int64_t N, bool bf16, hipStream_t s);
+                           int64_t K, int64_t N, bool bf16, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct PrefillArgs {
   const void* q;

@@ -236,6 +236,133 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
   }
 }
 
+// ----------------------------------------------------------------------------- skinny M
+// M <= 128 (decode batches, short prompts): the weight is streamed once and is
+// the whole cost, so the grid is widened by splitting the k range over
+// workgroups.  Workgroup = 2 waves, tile = 32 rows x 32 columns x a k range;
+// each 128-deep chunk of W is loaded with 16-byte loads two chunks ahead and
+// written to LDS transposed; x fragments come straight from L2 in MFMA layout.
+// With several k ranges, fp32 partial tiles go to the workspace and a second
+// kernel adds them (fixed order), adds the bias and rounds to bf16.
+constexpr int kSkBN = 32, kSkBK = 128, kSkLd = kSkBK + 8, kSkThreads = 128;
+constexpr int kSkMaxChunks = 8;  // k range <= 1024 rows
+constexpr int kSkDepth = 3;      // chunks in flight ahead of the one being multiplied
+
+__global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, float* __restrict__ part, int M, int K, int N, int krange, int ksplit,
+    int nbm) {
+  __shared__ __align__(16) uint16_t Bs[2][kSkBN * kSkLd];
+  __shared__ __align__(16) float red[16 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bm = lid % nbm;  // row blocks of one (column block, k range) are neighbours: W reuse in L2
+  lid /= nbm;
+  const int ks = lid % ksplit;
+  const int bn = lid / ksplit;
+  const int m0 = bm * 32, n0 = bn * kSkBN;
+  const int kbeg = ks * krange, kend = min(K, kbeg + krange);
+  const int nchunk = (kend - kbeg + kSkBK - 1) / kSkBK;
+
+  const uint32_t wbytes = (uint32_t)((int64_t)K * N * 2);
+  const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, wbytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, xbytes);
+  // W task of this thread: rows 4*kg..4*kg+3 of a chunk, columns 8*ng..8*ng+7 of the tile
+  const int kg = tid >> 2, ng = tid & 3;
+  const int xrow = m0 + l32;
+
+  // A chunk = 4 W rows-segments (16 B each) + this wave's 4 x fragments; every
+  // load is issued unconditionally (out-of-range offsets read zeros), so the
+  // waits on the in-order load counter stay exact.
+  u32x4_t rw[kSkDepth][4], rx[kSkDepth][4];
+  auto load_chunk = [&](int c, u32x4_t (&w4)[4], u32x4_t (&x4)[4]) {
+    const int kw = kbeg + c * kSkBK + kg * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = kw + j;
+      w4[j] = bld16(wr, (c < nchunk && kk < kend) ? (uint32_t)((int64_t)kk * N + n0 + ng * 8) * 2 : wbytes);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kk = kbeg + c * kSkBK + (wave * 4 + st) * 16 + hf * 8;
+      x4[st] = bld16(xr, (c < nchunk && xrow < M && kk < kend) ? (uint32_t)((int64_t)xrow * K + kk) * 2 : xbytes);
+    }
+  };
+  auto store_chunk = [&](int buf, const u32x4_t (&w4)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u32x2_t lo, hi;
+      lo[0] = __builtin_amdgcn_perm(w4[1][e], w4[0][e], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(w4[3][e], w4[2][e], 0x05040100u);
+      hi[0] = __builtin_amdgcn_perm(w4[1][e], w4[0][e], 0x07060302u);
+      hi[1] = __builtin_amdgcn_perm(w4[3][e], w4[2][e], 0x07060302u);
+      st8(&Bs[buf][(ng * 8 + 2 * e) * kSkLd + kg * 4], lo);
+      st8(&Bs[buf][(ng * 8 + 2 * e + 1) * kSkLd + kg * 4], hi);
+    }
+  };
+
+  f32x16_t acc = f32x16_t{};
+#pragma unroll
+  for (int c = 0; c < kSkDepth; ++c) load_chunk(c, rw[c], rx[c]);
+#pragma unroll
+  for (int c = 0; c < kSkMaxChunks; ++c) {
+    if (c >= nchunk) break;
+    const int r = c % kSkDepth;
+    store_chunk(c & 1, rw[r]);
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      acc = mfma32_bf16(rx[r][st], ld16(&Bs[c & 1][l32 * kSkLd + (wave * 4 + st) * 16 + hf * 8]), acc);
+    if (c + kSkDepth < kSkMaxChunks) load_chunk(c + kSkDepth, rw[r], rx[r]);
+  }
+  // add the two waves' k-step halves
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[e * 64 + lane] = acc[e];
+  }
+  __syncthreads();
+  if (wave == 1) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] += red[e * 64 + lane];
+  const int n = n0 + l32;
+  if (ksplit == 1) {
+    const float bv = bias ? bf16_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + 8 * (e >> 2) + 4 * hf + (e & 3);
+      if (m < M) out[(int64_t)m * N + n] = f32_to_bf16(acc[e] + bv);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + 8 * (e >> 2) + 4 * hf + (e & 3);
+      if (m < M) part[((int64_t)ks * M + m) * N + n] = acc[e];
+    }
+  }
+}
+
+// Sum the k-range partials in a fixed order, add the bias, round to bf16.
+__global__ __launch_bounds__(256) void qkv_gemm_reduce_kernel(const float* __restrict__ part,
+                                                              const uint16_t* __restrict__ bias,
+                                                              uint16_t* __restrict__ out, int M, int N,
+                                                              int ksplit) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // 4 consecutive outputs
+  const int64_t total = (int64_t)M * N;
+  if (i >= total) return;
+  const int n = (int)(i % N);
+  f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + i);
+  for (int k = 1; k < ksplit; ++k) s += *reinterpret_cast<const f32x4_t*>(part + (int64_t)k * total + i);
+  u32x2_t pk;
+  const float b0 = bias ? bf16_to_f32(bias[n]) : 0.0f, b1 = bias ? bf16_to_f32(bias[n + 1]) : 0.0f;
+  const float b2 = bias ? bf16_to_f32(bias[n + 2]) : 0.0f, b3 = bias ? bf16_to_f32(bias[n + 3]) : 0.0f;
+  pk[0] = pack_bf16(s[0] + b0, s[1] + b1);
+  pk[1] = pack_bf16(s[2] + b2, s[3] + b3);
+  st8(out + i, pk);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int KS>
 static hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, void* out,
                                    int M, int K, int N, hipStream_t s) {
@@ -251,8 +378,31 @@ static hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bia
   return hipGetLastError();
 }
 
+SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
+  SkinnyPlan p{};
+  // 32-bit buffer offsets cover W and x
+  if (M > 128 || N % kSkBN != 0 || K * N * 2 >= ((int64_t)1 << 32)) return p;
+  p.nbm = (int)((M + 31) / 32);
+  const int64_t base = (N / kSkBN) * p.nbm;
+  // about three workgroups per CU; each k range a multiple of the 128-deep chunk
+  // and at most kSkMaxChunks chunks
+  int64_t ks = (768 + base - 1) / base;
+  const int64_t kmin = (K + kSkMaxChunks * kSkBK - 1) / (kSkMaxChunks * kSkBK);
+  const int64_t kmax = (K + 255) / 256;
+  if (ks > kmax) ks = kmax;
+  if (ks < kmin) ks = kmin;
+  if (ks < 1) ks = 1;
+  int64_t kr = (K + ks - 1) / ks;
+  kr = (kr + kSkBK - 1) / kSkBK * kSkBK;
+  p.krange = (int)kr;
+  p.ksplit = (int)((K + kr - 1) / kr);
+  p.ws_bytes = p.ksplit > 1 ? (size_t)p.ksplit * M * N * 4 : 0;
+  p.ok = true;
+  return p;
+}
+
 hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void* out, int64_t M,
-                           int64_t K, int64_t N, bool bf16, hipStream_t s) {
+                           int64_t K, int64_t N, bool bf16, void* ws, size_t ws_bytes, hipStream_t s) {
   if (!bf16) {
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     hipLaunchKernelGGL(qkv_gemm_f32_kernel, grid, dim3(256), 0, s, (const float*)x, (const float*)w,
@@ -260,6 +410,19 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
     return hipGetLastError();
   }
   const int m = (int)M, k = (int)K, n = (int)N;
+  const SkinnyPlan p = plan_skinny(M, K, N);
+  if (p.ok && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
+    const int64_t nblk = (N / kSkBN) * p.nbm * p.ksplit;
+    hipLaunchKernelGGL(qkv_gemm_skinny_kernel, dim3((unsigned)nblk), dim3(kSkThreads), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out,
+                       (float*)ws, m, k, n, p.krange, p.ksplit, p.nbm);
+    if (p.ksplit > 1) {
+      const int64_t quads = (M * N + 3) / 4;
+      hipLaunchKernelGGL(qkv_gemm_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                         (const float*)ws, (const uint16_t*)bias, (uint16_t*)out, m, n, p.ksplit);
+    }
+    return hipGetLastError();
+  }
   // Pick the largest tile that still gives the chip (256 CUs) a full wave of workgroups.
   const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);

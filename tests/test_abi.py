@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("qkv_proj", "gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
+    for n in ("qkv_proj", "qkv_proj_workspace_bytes", "gqa_attn_prefill", "gqa_attn_decode",
+              "gqa_attn_decode_workspace_bytes",
               "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version"):
         assert n in names
 
@@ -40,14 +41,14 @@ def test_status_strings(lib):
     assert L.mqkv_status_string(1) == b"invalid argument"
     assert L.mqkv_status_string(2) == b"unsupported configuration"
     assert L.mqkv_status_string(3) == b"HIP runtime error"
-    assert L.mqkv_abi_version() == 100
+    assert L.mqkv_abi_version() == 101
 
 
 def proj(lib, **kw):
     a = dict(x=A, w=A, bias=None, out=A, M=16, hidden=256, H_q=4, H_kv=2, d=64, dtype=BF16)
     a.update(kw)
     return lib.lib.qkv_proj(a["x"], a["w"], a["bias"], a["out"], a["M"], a["hidden"], a["H_q"], a["H_kv"],
-                            a["d"], a["dtype"], None)
+                            a["d"], a["dtype"], a.get("ws"), a.get("wsb", 0), None)
 
 
 def prefill(lib, **kw):
@@ -72,6 +73,7 @@ def decode(lib, **kw):
     (dict(x=None), INV), (dict(out=None), INV), (dict(w=A + 2), INV), (dict(M=-1), INV),
     (dict(hidden=0), INV), (dict(hidden=260), INV), (dict(H_q=3, H_kv=2), INV), (dict(H_kv=0), INV),
     (dict(d=96), UNS), (dict(d=0), INV), (dict(dtype=7), INV), (dict(M=1 << 40), UNS),
+    (dict(ws=A + 4, wsb=1 << 20), INV),
 ])
 def test_qkv_proj_rejects(lib, kw, code):
     assert proj(lib, **kw) == code
@@ -96,6 +98,16 @@ def test_prefill_rejects(lib, kw, code):
 def test_prefill_empty_is_noop(lib):
     assert prefill(lib, B=0) == 0
     assert prefill(lib, Lq=0) == 0
+
+
+def test_projection_workspace_query(lib):
+    f = lib.qkv_proj_workspace_bytes
+    # decode-sized M: the hidden dimension is split, partials need M*N*4 bytes per k range
+    n = f(32, 4096, 32, 8, 128)
+    assert n > 0 and n % (32 * 6144 * 4) == 0
+    assert f(4096, 4096, 32, 8, 128) == 0      # large M: single pass, no workspace
+    assert f(32, 4096, 32, 8, 128, 0) == 0     # fp32 path: no workspace
+    assert f(32, 4096, 32, 3, 128) == 0        # invalid heads
 
 
 def test_decode_workspace_query(lib):
