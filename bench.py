@@ -106,6 +106,7 @@ def main():
                      device=dev)
     ws_proj = torch.empty(max(16, m.qkv_proj_workspace_bytes(wd.B, wd.hidden, wd.H_q, wd.H_kv, wd.d)),
                           dtype=torch.uint8, device=dev)
+    ws_pf = torch.empty(m.prefill_workspace_bytes(wp.B, wp.L, wp.H_kv, wp.d), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
     if args.calib_copy:
@@ -134,7 +135,7 @@ def main():
         e = {k: torch.cuda.Event(enable_timing=True) for k in ev} if record else None
         if record:
             e["p0"].record(stream)
-        m.gqa_attn_prefill(Qp, Kp, Vp, causal=True, scale=scale_p, out=Op)
+        m.gqa_attn_prefill(Qp, Kp, Vp, causal=True, scale=scale_p, out=Op, workspace=ws_pf)
         if record:
             e["p1"].record(stream)
             e["g0"].record(stream)
@@ -202,7 +203,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(pre_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "attn_prefill_bf16 (d=128, causal)"},
+                     "kernel": "gqa_attn_prefill (d=128, causal): V-image pre-pass + attention kernel"},
         "cpu_baseline": None,
     }
     if args.sweep:
@@ -238,16 +239,16 @@ def cpu_baseline(W, wp, seconds):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    inp = W.prefill_inputs(wp, batch=range(0, 1))
+    inp = W.prefill_inputs(wp, batch=range(0, wp.B))
     q, k, v = inp["q"], inp["k"], inp["v"]
     scale = 1.0 / math.sqrt(wp.d)
     flops, rows_done, t0 = 0.0, 0, time.perf_counter()
     blk = 512
-    # causal row blocks, from the last (heaviest) block backwards, head by head
-    order = [(h, r0) for r0 in range(wp.L - blk, -1, -blk) for h in range(wp.H_q)]
-    for h, r0 in order:
+    # causal row blocks, from the last (heaviest) block backwards, head by head, batch by batch
+    order = [(b, h, r0) for b in range(wp.B) for r0 in range(wp.L - blk, -1, -blk) for h in range(wp.H_q)]
+    for b, h, r0 in order:
         rows = np.arange(r0, r0 + blk)
-        oracle.attention_rows(q, k, v, 0, h, rows, True, scale)
+        oracle.attention_rows(q, k, v, b, h, rows, True, scale)
         flops += 4.0 * wp.d * float((rows + 1).sum())
         rows_done += blk
         if time.perf_counter() - t0 >= seconds:
@@ -255,7 +256,7 @@ def cpu_baseline(W, wp, seconds):
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rows_done} query rows (blocks of {blk}, heaviest first) of batch 0 of the "
+            "sample": f"{rows_done} query rows (blocks of {blk}, heaviest first, batch by batch) of the "
                       f"causal prefill, fp64 numpy, {dt:.1f}s"}
 
 
@@ -286,7 +287,8 @@ def sweep(m, W, torch, dev, stream):
             pin = W.prefill_inputs(wl)
             q, k, v = up(pin["q"]), up(pin["k"]), up(pin["v"])
             o = torch.empty_like(q)
-            us = timeit(lambda: m.gqa_attn_prefill(q, k, v, causal=wl.causal, out=o))
+            wsp = torch.empty(m.prefill_workspace_bytes(wl.B, wl.L, wl.H_kv, wl.d), dtype=torch.uint8, device=dev)
+            us = timeit(lambda: m.gqa_attn_prefill(q, k, v, causal=wl.causal, out=o, workspace=wsp))
             fl = prefill_flops(wl.B, wl.H_q, wl.d, wl.L, wl.L, wl.causal)
             log(json.dumps({"sweep": name, "kernel": "prefill", "us": round(us, 2),
                             "tflops": round(fl / us / 1e6, 2), "frac": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}))
@@ -297,7 +299,7 @@ def sweep(m, W, torch, dev, stream):
                 fl = 2.0 * x.shape[0] * wl.hidden * wl.N
                 log(json.dumps({"sweep": name, "kernel": "qkv_proj", "us": round(us, 2),
                                 "tflops": round(fl / us / 1e6, 2)}))
-            del q, k, v, o
+            del q, k, v, o, wsp
         else:
             din = W.decode_inputs(wl)
             kc, vc = up(din["k_cache"]), up(din["v_cache"])

@@ -98,13 +98,22 @@ mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* q
  * o    [B, L_q, H_q, d] contiguous, dtype o_dtype (bf16 or fp32 for bf16 inputs;
  *      fp32 for fp32 inputs)
  * lse  [B, H_q, L_q] fp32 natural-log normaliser ln sum_j exp(scale q.k_j), or NULL
+ * workspace: device scratch, 16-byte aligned, at least
+ *   gqa_attn_prefill_workspace_bytes(B, L_kv, H_kv, d, in_dtype) bytes (0 for
+ *   fp32 inputs, where NULL is allowed).  bf16 calls first write V there once
+ *   more, as fp16 key-major tiles ready to be copied into LDS; its contents are
+ *   dead after the call.  Calls that share a workspace must not overlap.
  * scale must be finite and >= 0.  B == 0 or L_q == 0 is a no-op; L_kv >= 1.
  */
+size_t gqa_attn_prefill_workspace_bytes(int32_t B, int32_t L_kv, int32_t H_kv, int32_t d,
+                                        mqkv_dtype in_dtype);
+
 mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                              int32_t B, int32_t L_q, int32_t L_kv, int32_t H_q, int32_t H_kv,
                              int32_t d, int64_t q_tok_stride, int64_t kv_tok_stride,
                              int32_t causal, float scale, mqkv_dtype in_dtype,
-                             mqkv_dtype o_dtype, void* stream);
+                             mqkv_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * Bytes of device workspace gqa_attn_decode needs for these sizes

@@ -25,8 +25,9 @@ LIB_PATH = os.path.join(_HERE, "libmqa_qkv.so")
 MQKV_OK, MQKV_ERR_INVALID, MQKV_ERR_UNSUPPORTED, MQKV_ERR_HIP = 0, 1, 2, 3
 MQKV_F32, MQKV_BF16 = 0, 1
 
-EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "gqa_attn_prefill", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode",
-           "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version")
+EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "gqa_attn_prefill_workspace_bytes", "gqa_attn_prefill",
+           "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "mqkv_status_string", "mqkv_last_error",
+           "mqkv_abi_version")
 
 
 class MqkvError(RuntimeError):
@@ -50,8 +51,10 @@ def _load() -> ctypes.CDLL:
     lib.qkv_proj_workspace_bytes.restype = sz
     lib.qkv_proj.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, sz, vp]
     lib.qkv_proj.restype = i32
+    lib.gqa_attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.gqa_attn_prefill_workspace_bytes.restype = sz
     lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32,
-                                     f32, i32, i32, vp]
+                                     f32, i32, i32, vp, sz, vp]
     lib.gqa_attn_prefill.restype = i32
     lib.gqa_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.gqa_attn_decode_workspace_bytes.restype = sz
@@ -179,15 +182,20 @@ def split_qkv(qkv, H_q: int, H_kv: int, d: int):
     return q, k, v
 
 
+def prefill_workspace_bytes(B: int, L_kv: int, H_kv: int, d: int, dtype_code: int = MQKV_BF16) -> int:
+    return int(lib.gqa_attn_prefill_workspace_bytes(B, L_kv, H_kv, d, dtype_code))
+
+
 def gqa_attn_prefill(q, k, v, causal: bool = True, scale: Optional[float] = None,
-                     return_lse: bool = False, out_dtype=None, out=None):
+                     return_lse: bool = False, out_dtype=None, out=None, workspace=None):
     """Exact grouped-query attention over whole sequences.
 
     q [B, L_q, H_q, d], k/v [B, L_kv, H_kv, d]; token strides may be views into qkv.
     Returns o [B, L_q, H_q, d] (dtype out_dtype, default q.dtype) and, if asked,
-    lse [B, H_q, L_q] float32."""
+    lse [B, H_q, L_q] float32.  `workspace` (uint8 device tensor of at least
+    prefill_workspace_bytes(...) bytes) is allocated per call when not given."""
     torch = _torch()
-    _require_cuda(q, k, v, out)
+    _require_cuda(q, k, v, out, workspace)
     B, L_q, H_q, d = q.shape
     _, L_kv, H_kv, _ = k.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
@@ -205,10 +213,16 @@ def gqa_attn_prefill(q, k, v, causal: bool = True, scale: Optional[float] = None
     elif out.shape != (B, L_q, H_q, d) or not out.is_contiguous() or out.dtype != out_dtype:
         raise ValueError("out must be a contiguous [B, L_q, H_q, d] tensor of out_dtype")
     lse = torch.empty(B, H_q, L_q, dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        need = prefill_workspace_bytes(B, L_kv, H_kv, d, _dtype_code(q.dtype))
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               lse.data_ptr() if lse is not None else None, B, L_q, L_kv, H_q, H_kv, d,
                               qs, ks, int(bool(causal)), scale, _dtype_code(q.dtype),
-                              _dtype_code(out_dtype), _stream(q.device))
+                              _dtype_code(out_dtype), ws_ptr, ws_bytes, _stream(q.device))
     check(st, "gqa_attn_prefill")
     return (out, lse) if return_lse else out
 

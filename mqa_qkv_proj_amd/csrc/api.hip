@@ -70,7 +70,7 @@ const char* mqkv_status_string(mqkv_status s) {
 
 const char* mqkv_last_error(void) { return g_err; }
 
-int32_t mqkv_abi_version(void) { return 101; }
+int32_t mqkv_abi_version(void) { return 102; }
 
 size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                                 mqkv_dtype dtype) {
@@ -107,10 +107,17 @@ mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* q
                     "qkv_proj launch");
 }
 
+size_t gqa_attn_prefill_workspace_bytes(int32_t B, int32_t L_kv, int32_t H_kv, int32_t d,
+                                        mqkv_dtype in_dtype) {
+  if (!dtype_ok(in_dtype) || B < 0 || L_kv < 1 || H_kv < 1 || (d != 64 && d != 128)) return 0;
+  return mqkv::prefill_workspace_bytes(B, L_kv, H_kv, d, in_dtype == MQKV_BF16);
+}
+
 mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                              int32_t B, int32_t L_q, int32_t L_kv, int32_t H_q, int32_t H_kv,
                              int32_t d, int64_t q_tok_stride, int64_t kv_tok_stride, int32_t causal,
-                             float scale, mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream) {
+                             float scale, mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
     return fail(MQKV_ERR_INVALID, "dtype %d/%d unknown", (int)in_dtype, (int)o_dtype);
@@ -137,8 +144,14 @@ mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* 
       (int64_t)L_q * q_tok_stride * elem_size(in_dtype) >= ((int64_t)1 << 31))
     return fail(MQKV_ERR_UNSUPPORTED, "one sequence's rows must span less than 2 GiB");
   if (B == 0 || L_q == 0) return MQKV_OK;
-  mqkv::PrefillArgs a{q, k, v, o, lse, B, L_q, L_kv, H_q, H_kv, d, q_tok_stride, kv_tok_stride,
-                      causal != 0, scale, in_dtype == MQKV_BF16, o_dtype == MQKV_BF16};
+  const size_t need = mqkv::prefill_workspace_bytes(B, L_kv, H_kv, d, in_dtype == MQKV_BF16);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(MQKV_ERR_INVALID, "workspace must be 16-byte aligned and >= %zu bytes (got %zu)", need,
+                workspace_bytes);
+  mqkv::PrefillArgs a{q,      k,     v,         o,         lse,       B,         L_q,
+                      L_kv,   H_q,   H_kv,      d,         q_tok_stride, kv_tok_stride,
+                      causal != 0, scale, in_dtype == MQKV_BF16, o_dtype == MQKV_BF16,
+                      workspace, workspace_bytes};
   return hip_status(mqkv::launch_prefill(a, (hipStream_t)stream), "gqa_attn_prefill launch");
 }
 

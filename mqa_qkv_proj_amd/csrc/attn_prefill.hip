@@ -8,8 +8,8 @@
 // sequence length (FlashAttention-3 page, "FlashAttention recap").
 //
 // Design (bf16 inputs, CDNA4 wave64, MFMA 32x32x16):
-//  * One workgroup = 4 waves = 128 query rows of one KV head: F query heads of
-//    the group x (128/F) positions, F = the largest power of two dividing
+//  * One workgroup = 8 waves = 256 query rows of one KV head: F query heads of
+//    the group x (256/F) positions, F = the largest power of two dividing
 //    G = H_q/H_kv (at most 32).  Every LDS K/V tile is reused by all F heads.
 //  * Scores are computed transposed, S^T = K . Q^T: the accumulator then holds
 //    one query per lane column, so the row max and row sum are in-lane
@@ -18,17 +18,28 @@
 //    per score.  The running max is only raised when a row's max grows by more
 //    than 8 (log2 units); until then p <= 2^8, which keeps fp32 sums exact in
 //    form and skips most accumulator rescales.
-//  * P is rounded to fp16 and O^T += V^T . P^T runs as an fp16 MFMA: V is
-//    converted bf16 -> fp16 (exact for |v| in fp16's normal range) while it is
-//    transposed into LDS.  fp16 P carries 3 more mantissa bits than bf16,
-//    which keeps the error of outlier-heavy rows inside the bf16 tolerance.
-//  * K tiles go to LDS as-is; V tiles are transposed (d-major, keys
-//    contiguous, in the order the P operand holds them).  Both are double
-//    buffered with a register prefetch of the next tile.
+//  * P is rounded to fp16 and O^T += V^T . P^T runs as an fp16 MFMA.  fp16 P
+//    carries 3 more mantissa bits than bf16, which keeps the error of
+//    outlier-heavy rows inside the bf16 tolerance.  A small pre-pass writes V
+//    once as fp16 V^T tile images (exact for |v| in fp16's normal range), in
+//    the key order the P operand holds, into caller-provided workspace.
+//  * Software pipeline over 32-key halves: the softmax of one half runs on the
+//    vector unit while the matrix cores compute the next half's scores and
+//    this half's P.V; the operands of each MFMA are read from LDS one slot
+//    ahead.  The pipeline runs across tile boundaries: three LDS stages hold
+//    the tile being consumed, the next tile (complete) and the tile being
+//    copied in, with one barrier per 64-key tile.
+//  * Tiles reach LDS by LDS-DMA (buffer loads that write LDS directly): no
+//    staging registers and no LDS store instructions.  K rows keep 16 bytes of
+//    padding per row (the pad lanes of a copy point past the buffer and write
+//    nothing) so that the operand reads of 16 consecutive rows hit distinct
+//    banks; the V^T images carry the same padding.  The copies are issued by
+//    the four older waves, between the MFMAs of the pipelined steps.
 //  * Causal: tiles beyond the block's diagonal are never visited, only tiles
-//    that cross a row's limit are masked, and the heaviest query blocks are
-//    dispatched first.  Workgroup ids are remapped so that each XCD serves a
-//    contiguous range of (batch, KV head) blocks and keeps their K/V in its L2.
+//    that cross a row's limit are masked (a separate, unpipelined loop), and
+//    the heaviest query blocks are dispatched first.  Workgroup ids are
+//    remapped so that each XCD serves a contiguous range of (batch, KV head)
+//    blocks and keeps their K/V in its L2.
 // fp32 inputs use a plain one-row-per-thread kernel (fp32 throughout).
 #include <type_traits>
 
@@ -39,52 +50,103 @@ namespace mqkv {
 
 namespace {
 
-#ifndef MQKV_PF_WAVES
-#define MQKV_PF_WAVES 8  // waves per workgroup (32 query rows each)
-#endif
-#ifndef MQKV_PF_BK
-#define MQKV_PF_BK 64    // keys per K/V tile (a multiple of 64)
-#endif
-constexpr int kWaves = MQKV_PF_WAVES;
+constexpr int kWaves = 8;           // waves per workgroup (32 query rows each)
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = kWaves * 32;  // query rows per workgroup
-constexpr int kBK = MQKV_PF_BK;
-constexpr int kStages = 2;  // K/V tiles resident in LDS (double buffer)
+constexpr int kBK = 64;             // keys per K/V tile: two 32-key halves
+constexpr int kStages = 3;          // K/V tiles resident in LDS
 constexpr float kTau = 8.0f;        // lazy-rescale threshold (log2 units)
-#ifndef MQKV_PF_OCC
-#define MQKV_PF_OCC 2  // minimum waves per SIMD the register budget must allow
+#ifndef MQKV_PF_FILL_WAVES
+#define MQKV_PF_FILL_WAVES 4
 #endif
 
+// LDS image of one K/V tile.  Rows carry 16 bytes of padding, which keeps the
+// MFMA operand reads of 16 consecutive rows on distinct banks.  LDS-DMA copies
+// 1 KB per instruction (64 lanes x 16 bytes, lane-linear), so each image is a
+// whole number of copies.
 template <int D>
 struct PrefillLds {
-  static constexpr int kKld = D + 8;        // K row stride (bf16 elements)
-  static constexpr int kVld = kBK + 8;      // V^T row stride (fp16 elements)
-  static constexpr int kK = kBK * kKld;     // elements per K stage
-  static constexpr int kV = D * kVld;       // elements per V^T stage
+  static constexpr int kKld = D + 8;    // K row pitch (bf16 elements)
+  static constexpr int kVld = kBK + 8;  // V^T row pitch (fp16 elements)
+  static constexpr int kK = kBK * kKld;
+  static constexpr int kV = D * kVld;
   static constexpr int kStage = kK + kV;
   static constexpr size_t kBytes = kStages * kStage * sizeof(uint16_t);
+  static constexpr int kKChunks = kKld / 8;  // 16-byte chunks per K row, padding included
+  static constexpr int kKCopies = kK * 2 / 1024;
+  static constexpr int kVCopies = kV * 2 / 1024;
+  static_assert(kK * 2 % 1024 == 0 && kV * 2 % 1024 == 0, "tile images are whole 1 KB copies");
 };
 
 // Position, inside a 16-key group, of key 4a + j (a = 0..3) in the V^T rows:
 // keys {0-3, 8-11} first (lane half 0 of the P operand), then {4-7, 12-15}.
 __device__ __forceinline__ int vt_pos(int a) { return ((a & 1) << 3) | ((a >> 1) << 2); }
 
-template <int D, bool CAUSAL, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    void* __restrict__ o, float* __restrict__ lse, int Lq, int Lkv, int Hq, int Hkv,
-    int64_t q_stride, int64_t kv_stride, float c, int F, int n_hg, int n_qb) {
+// V of one (batch, KV head, 64-key tile) written as the LDS image the prefill
+// kernel uses for P.V: V^T in fp16 (bf16 -> fp16 is exact for |v| in fp16's
+// normal range), one padded row per head dimension, keys in P-operand order.
+// Keys at or past L_kv are zeros, so every image is a full tile.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_v_image_kernel(const uint16_t* __restrict__ v,
+                                                              uint16_t* __restrict__ img, int Lkv,
+                                                              int Hkv, int64_t kv_stride, int ntiles) {
   using S = PrefillLds<D>;
-  constexpr int DS = D / 16;   // MFMA k-steps over the head dimension
-  constexpr int DB = D / 32;   // 32-row blocks of O^T
-  constexpr int KCH = kBK * D / 8 / kThreads;  // 16B K chunks per thread
-  static_assert(KCH >= 1 && KCH * kThreads == kBK * D / 8, "K tile split over threads");
-  constexpr int VT = (kBK / 4) * (D / 8);      // 4x8 V tasks per tile
-  constexpr int VTPT = (VT + kThreads - 1) / kThreads;  // V tasks per thread
+  constexpr int VT = (kBK / 4) * (D / 8);  // tasks of 4 keys x 8 dimensions
+  const int ti = threadIdx.x;
+  if (ti >= VT) return;
+  int id = blockIdx.x;
+  const int t = id % ntiles;
+  id /= ntiles;
+  const int g = id % Hkv;
+  const int b = id / Hkv;
+  // consecutive lanes take consecutive key groups: one store instruction then
+  // covers whole image rows
+  const int kg = ti % (kBK / 4), dg = ti / (kBK / 4);
+  const uint32_t kv_bytes = (uint32_t)((int64_t)Lkv * kv_stride * 2);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(v + (int64_t)b * Lkv * kv_stride, kv_bytes);
+  const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+  u32x4_t rv[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    rv[jj] = bld16(rs, (uint32_t)(t * kBK + kg * 4 + jj) * row_bytes + (uint32_t)(g * D * 2) + dg * 16);
+  uint16_t* out = img + (((int64_t)b * Hkv + g) * ntiles + t) * S::kV;
+  const int col = (kg >> 2) * 16 + vt_pos(kg & 3);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // rv[jj][e] = V[key jj][d = 8dg+2e, 8dg+2e+1] (bf16 pair)
+    u32x2_t lo, hi;
+    lo[0] = pack_f16(bf16lo(rv[0][e]), bf16lo(rv[1][e]));
+    lo[1] = pack_f16(bf16lo(rv[2][e]), bf16lo(rv[3][e]));
+    hi[0] = pack_f16(bf16hi(rv[0][e]), bf16hi(rv[1][e]));
+    hi[1] = pack_f16(bf16hi(rv[2][e]), bf16hi(rv[3][e]));
+    st8(out + (dg * 8 + 2 * e) * S::kVld + col, lo);
+    st8(out + (dg * 8 + 2 * e + 1) * S::kVld + col, hi);
+  }
+}
+
+// s_waitcnt vmcnt(0) with the other counters left alone: the LDS-DMA copies a
+// wave issued have landed.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int D, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vimg,
+    void* __restrict__ o, float* __restrict__ lse, int Lq, int Lkv, int Hq, int Hkv,
+    int64_t q_stride, int64_t kv_stride, float c, int F, int n_hg, int n_qb, int ntiles) {
+  using S = PrefillLds<D>;
+  constexpr int DS = D / 16;  // MFMA k-steps over the head dimension
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  // Tile copies are issued by the first kFillWaves waves only: the hardware
+  // favours the older wave of the two that share a SIMD, so those waves run
+  // ahead and would otherwise wait at the tile barrier.
+  constexpr int kFillWaves = MQKV_PF_FILL_WAVES;
+  constexpr int KCP = (S::kKCopies + kFillWaves - 1) / kFillWaves;  // K copies per filling wave
+  constexpr int VCP = (S::kVCopies + kFillWaves - 1) / kFillWaves;  // V copies per filling wave
   extern __shared__ __align__(16) uint16_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
+  const int wq = __builtin_amdgcn_readfirstlane(wave);
 
   // ---- block -> (b, g, head group, query block), heaviest causal blocks first
   const int G = Hq / Hkv;
@@ -118,63 +180,50 @@ __global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kerne
   const int mask_from = CAUSAL ? min(Lkv, p0 + off + 1) : Lkv;  // first key some row cannot see
   const int nt = (kv_end + kBK - 1) / kBK;
 
-  // K/V rows of batch b through bounds-checked buffer resources: a key >= L_kv
-  // lands at or past the resource end and reads zeros.
-  const uint32_t kv_bytes = (uint32_t)((int64_t)Lkv * kv_stride * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (int64_t)b * Lkv * kv_stride, kv_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (int64_t)b * Lkv * kv_stride, kv_bytes);
+  // ---- tile copies (LDS-DMA, no registers): K straight from the K rows, with
+  // the lanes that fall on row padding pointed past the buffer so they write
+  // nothing; V from its prepared image.  Rows at or past L_kv are past the
+  // buffer end too and leave stale LDS rows, which only ever meet masked keys.
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
-  const uint32_t head_off = (uint32_t)(g * D * 2);
-
-  u32x4_t rk[KCH];
-  u32x4_t rv[VTPT][4];
-  auto load_tile = [&](int t) {
-    const int k0 = t * kBK;
+  const uint32_t kv_bytes = (uint32_t)((int64_t)Lkv * kv_stride * 2);
+  const char* kbase = reinterpret_cast<const char*>(k + (int64_t)b * Lkv * kv_stride);
+  const uint16_t* vbase = vimg + ((int64_t)b * Hkv + g) * ntiles * S::kV;
+  constexpr uint32_t kNoCopy = 0x80000000u;  // beyond any buffer (spans are below 2 GiB)
+  uint32_t koff[KCP];
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int ci = tid + j * kThreads;
-      const int key = ci / (D / 8), dc = ci % (D / 8);
-      rk[j] = bld16(krs, (uint32_t)(k0 + key) * row_bytes + head_off + dc * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < VTPT; ++j) {
-      const int ti = tid + j * kThreads;
-      const int kg = ti / (D / 8), dg = ti % (D / 8);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = k0 + kg * 4 + jj;
-        rv[j][jj] = bld16(vrs, (ti < VT ? (uint32_t)key * row_bytes : kv_bytes) + head_off + dg * 16);
-      }
+  for (int i = 0; i < KCP; ++i) {
+    const int slot = (wave + i * kFillWaves) * 64 + lane;
+    const int row = slot / S::kKChunks, ch = slot % S::kKChunks;
+    koff[i] = ch < D / 8 ? (uint32_t)row * row_bytes + (uint32_t)(g * D * 2) + ch * 16 : kNoCopy;
+  }
+  // A tile copy is split into numbered parts (K copies, then V copies) so that
+  // the pipelined steps can issue them one at a time between MFMAs.
+  constexpr int kParts = KCP + VCP;
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  uint16_t* ks_dst = smem;
+  uint16_t* vs_dst = smem;
+  bool fill_on = false;
+  auto fill_begin = [&](int t, int st) {
+    fill_on = wq < kFillWaves && t < nt;
+    ks_dst = smem + st * S::kStage;
+    vs_dst = ks_dst + S::kK;
+    const uint32_t k0b = (uint32_t)(t * kBK) * row_bytes;
+    krs = make_rsrc(kbase + k0b, kv_bytes - k0b);
+    vrs = make_rsrc(vbase + (int64_t)t * S::kV, S::kV * 2);
+  };
+  auto fill_part = [&](auto part) {
+    constexpr int i = part;
+    if constexpr (i < KCP) {
+      const int cp = wq + i * kFillWaves;
+      if (fill_on && cp < S::kKCopies) dma16(krs, ks_dst + cp * 512, koff[i], 0);
+    } else if constexpr (i < kParts) {
+      const int cp = wq + (i - KCP) * kFillWaves;
+      if (fill_on && cp < S::kVCopies) dma16(vrs, vs_dst + cp * 512, (uint32_t)lane * 16, cp * 1024);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = smem + buf * S::kStage;
-    uint16_t* Vt = Ks + S::kK;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int ci = tid + j * kThreads;
-      const int key = ci / (D / 8), dc = ci % (D / 8);
-      st16(Ks + key * S::kKld + dc * 8, rk[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < VTPT; ++j) {
-      const int ti = tid + j * kThreads;
-      if (ti < VT) {
-        const int kg = ti / (D / 8), dg = ti % (D / 8);
-        const int col = (kg >> 2) * 16 + vt_pos(kg & 3);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // rv[j][jj][e] = V[key jj][d = 8dg+2e, 8dg+2e+1] (bf16 pair)
-          u32x2_t lo, hi;
-          lo[0] = pack_f16(bf16lo(rv[j][0][e]), bf16lo(rv[j][1][e]));
-          lo[1] = pack_f16(bf16lo(rv[j][2][e]), bf16lo(rv[j][3][e]));
-          hi[0] = pack_f16(bf16hi(rv[j][0][e]), bf16hi(rv[j][1][e]));
-          hi[1] = pack_f16(bf16hi(rv[j][2][e]), bf16hi(rv[j][3][e]));
-          st8(Vt + (dg * 8 + 2 * e) * S::kVld + col, lo);
-          st8(Vt + (dg * 8 + 2 * e + 1) * S::kVld + col, hi);
-        }
-      }
-    }
+  auto fill = [&](int t, int st) {
+    fill_begin(t, st);
+    static_for<0, kParts>([&](auto i) { fill_part(i); });
   };
 
   f32x16_t acc[DB];
@@ -183,101 +232,194 @@ __global__ __launch_bounds__(kThreads, MQKV_PF_OCC) void attn_prefill_bf16_kerne
   float m_run = -INFINITY;  // running max of S*c (log2 units)
   float l_run = 0.0f;       // this lane's share of the running sum
 
-  // One 32-key half: scores -> online softmax -> O^T += V^T P^T.  The two halves
-  // are issued back to back so that one half's softmax (VALU) runs while the
-  // other half's MFMAs are in flight.
-  const uint16_t* Ks;
-  const uint16_t* Vt;
-  int k0;
-    auto half = [&](f32x16_t sc, int kb, auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      if constexpr (MASK) {
-        // key - k0 - 4*hf of element i is 32kb + 8(i/4) + (i%4); mask keys beyond lim
-        const int rel = lim - k0 - 4 * hf - 32 * kb;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (8 * (i >> 2) + (i & 3) > rel) sc[i] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-#pragma unroll
-      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
-      mx = fmaxf(mx, sc[15]);
-      mx = fmaxf(mx, xor32(mx));
-      const float mt = mx * c;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
-        // only this row's own growth moves its max, so a row's result does not
-        // depend on the other rows that share the wave
-        const float mn = (mt > m_run + kTau) ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-        m_run = mn;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
-      }
-      u32x4_t pf[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
-          pf[hb][e] = pack_f16(p0, p1);
-        }
-      // row sum of the fp16-rounded P actually multiplied into V (fp32 accumulation)
-      const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // copy the element out first: a bit_cast applied to a vector element
-          // lvalue reads element 0 with this compiler
-          const uint32_t w = pf[hb][e];
-          l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
-        }
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        u32x4_t vf[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          vf[db] = ld16(Vt + (db * 32 + l32) * S::kVld + (kb * 2 + hb) * 16 + hf * 8);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = mfma32_f16(vf[db], pf[hb], acc[db]);
-      }
-    };
-    auto tile = [&](auto mask_tag) {
-#pragma unroll
-      for (int sub = 0; sub < kBK / 64; ++sub) {
-        f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-#pragma unroll
-        for (int st = 0; st < DS; ++st)
-          s0 = mfma32_bf16(ld16(Ks + (sub * 64 + l32) * S::kKld + st * 16 + hf * 8), qf[st], s0);
-#pragma unroll
-        for (int st = 0; st < DS; ++st)
-          s1 = mfma32_bf16(ld16(Ks + (sub * 64 + 32 + l32) * S::kKld + st * 16 + hf * 8), qf[st], s1);
-        half(s0, 2 * sub, mask_tag);
-        half(s1, 2 * sub + 1, mask_tag);
-      }
-    };
+  auto k_of = [&](int st) -> const uint16_t* { return smem + st * S::kStage; };
+  auto v_of = [&](int st) -> const uint16_t* { return smem + st * S::kStage + S::kK; };
 
-  // Tiles below every row's causal limit run without masking; the loop is split
-  // so that the masked body is a separate piece of code.
-  const int t_mask = min(nt, mask_from / kBK);
-  auto iter = [&](int t, auto mask_tag) {
-    const int buf = t & 1;
-    if (t + 1 < nt) load_tile(t + 1);
-    Ks = smem + buf * S::kStage;
-    Vt = Ks + S::kK;
-    k0 = t * kBK;
-    tile(mask_tag);
-    if (t + 1 < nt) store_tile(buf ^ 1);
-    __syncthreads();
+  // S^T for the 32 keys [32j, 32j + 32) of the tile held in K rows `ks`.
+  auto qk = [&](const uint16_t* ks, int j) {
+    f32x16_t sc = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < DS; ++st)
+      sc = mfma32_bf16(ld16(ks + (j * 32 + l32) * S::kKld + st * 16 + hf * 8), qf[st], sc);
+    return sc;
   };
-  load_tile(0);
-  store_tile(0);
+  // Element i of a half starting at key kbase is key kbase + 8(i/4) + 4hf + (i%4);
+  // keys past this row's limit get -inf.
+  auto mask = [&](f32x16_t& sc, int kb) {
+    const int rel = lim - kb - 4 * hf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (8 * (i >> 2) + (i & 3) > rel) sc[i] = -INFINITY;
+  };
+  // Row max of a half (log2 units).  The running max moves only when a row's
+  // max grows by more than kTau, and then only for that row, so a row's result
+  // does not depend on the other rows that share the wave.
+  auto update_max = [&](const f32x16_t& sc) {
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
+    mx = fmaxf(mx, sc[15]);
+    mx = max_xor32(mx);
+    const float mt = mx * c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
+      const float mn = (mt > m_run + kTau) ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+    }
+  };
+  // P = exp2(S*c - m) rounded to fp16 (the MFMA B operand), and its row sum.
+  auto softmax = [&](const f32x16_t& sc, u32x4_t (&pf)[2]) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
+        pf[hb][e] = pack_f16(p0, p1);
+      }
+    // row sum of the fp16-rounded P actually multiplied into V (fp32 accumulation)
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // copy the element out first: a bit_cast applied to a vector element
+        // lvalue reads element 0 with this compiler
+        const uint32_t w = pf[hb][e];
+        l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
+      }
+  };
+  // O^T += V^T P^T over the 32 keys [32j, 32j + 32) of the tile held in `vt`.
+  auto pv = [&](const uint16_t* vt, int j, const u32x4_t (&pf)[2]) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      u32x4_t vf[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        vf[db] = ld16(vt + (db * 32 + l32) * S::kVld + (j * 2 + hb) * 16 + hf * 8);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = mfma32_f16(vf[db], pf[hb], acc[db]);
+    }
+  };
+  // K fragments (MFMA A operand) of the 32 keys [32j, 32j + 32) of a tile.
+  auto load_kf = [&](u32x4_t (&kf)[DS], const uint16_t* ks, int j) {
+    static_for<0, DS>([&](auto st) { kf[st] = ld16(ks + (j * 32 + l32) * S::kKld + st * 16 + hf * 8); });
+  };
+  // One pipelined step.  On entry `sc` holds the scores of the current half
+  // (its row max already folded into m_run) and `kf` the K fragments of the
+  // next half.  The step turns `sc` into P, computes the next half's scores
+  // into `sc`, adds P V for the current half (V^T `vc`, keys 32jc..) and, when
+  // NEXT, reads the K fragments of the half after that (`kn`, keys 32jn..)
+  // into `kf`.  The source order is the issue order: each score MFMA is
+  // followed by one pair of softmax values and one V read, each P.V MFMA by a
+  // row-sum step and one K read, so the vector and LDS units work while the
+  // matrix cores run and every operand is in flight long before it is used.
+  // Fences keep the compiler from regrouping.
+  auto step = [&](f32x16_t& sc, u32x4_t (&kf)[DS], const uint16_t* vc, int jc, const uint16_t* kn,
+                  int jn, auto next_tag, auto part0) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr int PART0 = part0;
+    u32x4_t pf[2];
+    u32x4_t vf[2 * DB];
+    f32x16_t sn = f32x16_t{};
+    static_for<0, 8>([&](auto i) {
+      constexpr int hb = i >> 2, e = i & 3;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
+      pf[hb][e] = pack_f16(p0, p1);
+      if constexpr (i < DS) sn = mfma32_bf16(kf[i], qf[i], sn);
+      if constexpr (i < 2 * DB)
+        vf[i] = ld16(vc + ((i % DB) * 32 + l32) * S::kVld + (jc * 2 + i / DB) * 16 + hf * 8);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    static_for<0, 2 * DB>([&](auto i) {
+      constexpr int hb = i / DB, db = i % DB;
+      acc[db] = mfma32_f16(vf[i], pf[hb], acc[db]);
+      static_for<db * 4 / DB, (db + 1) * 4 / DB>([&](auto e) {
+        const uint32_t w = pf[hb][(int)e];
+        l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
+      });
+      if constexpr (NEXT && i < DS) kf[i] = ld16(kn + (jn * 32 + l32) * S::kKld + i * 16 + hf * 8);
+      if constexpr (PART0 >= 0) fill_part(std::integral_constant<int, PART0 + i>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    sc = sn;
+  };
+  // Last step of the pipeline: P V for the current half only.
+  auto drain = [&](const f32x16_t& sc, const uint16_t* vc, int jc) {
+    u32x4_t pf[2];
+    softmax(sc, pf);
+    pv(vc, jc, pf);
+  };
+
+  // Three LDS stages: while tile t is consumed, tile t + 1 is complete in LDS
+  // (its first scores are computed under tile t's second half) and tile t + 2
+  // is being copied in.  One barrier per tile publishes the copy.
+  fill(0, 0);
+  if (nt > 1) fill(1, 1);
+  wait_dma();
   __syncthreads();
-  int t = 0;
-  for (; t < t_mask; ++t) iter(t, std::false_type{});
-  for (; t < nt; ++t) iter(t, std::true_type{});
+
+  // Tiles below every row's causal limit run software-pipelined: the softmax of
+  // one 32-key half is computed while the scores of the next half and the
+  // P.V products of this half are in the matrix cores.
+  const int t_mask = min(nt, mask_from / kBK);
+  int t = 0, st0 = 0;
+  f32x16_t sc = f32x16_t{};
+  u32x4_t pf[2];
+  u32x4_t kf[DS];
+  if (t_mask > 0) {
+    sc = qk(k_of(0), 0);
+    update_max(sc);
+    load_kf(kf, k_of(0), 1);
+  }
+  for (; t + 1 < t_mask; ++t) {
+    const int st1 = st0 == 2 ? 0 : st0 + 1;
+    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    fill_begin(t + 2, st2);
+    step(sc, kf, v_of(st0), 0, k_of(st1), 0, std::true_type{}, std::integral_constant<int, 0>{});
+    update_max(sc);
+    step(sc, kf, v_of(st0), 1, k_of(st1), 1, std::true_type{}, std::integral_constant<int, 2 * DB>{});
+    update_max(sc);
+    static_for<4 * DB, kParts>([&](auto i) { fill_part(i); });
+    wait_dma();
+    __syncthreads();
+    st0 = st1;
+  }
+  if (t < t_mask) {  // last unmasked tile: the pipeline drains
+    const int st1 = st0 == 2 ? 0 : st0 + 1;
+    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    if (t + 2 < nt) fill(t + 2, st2);
+    step(sc, kf, v_of(st0), 0, k_of(st1), 0, std::false_type{}, std::integral_constant<int, -1>{});
+    update_max(sc);
+    drain(sc, v_of(st0), 1);
+    wait_dma();
+    __syncthreads();
+    st0 = st1;
+    ++t;
+  }
+  // Tiles that cross some row's limit (at most a few per workgroup): masked,
+  // one half after the other.
+  for (; t < nt; ++t) {
+    const int st1 = st0 == 2 ? 0 : st0 + 1;
+    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    if (t + 2 < nt) fill(t + 2, st2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sc = qk(k_of(st0), j);
+      mask(sc, t * kBK + 32 * j);
+      update_max(sc);
+      softmax(sc, pf);
+      pv(v_of(st0), j, pf);
+    }
+    wait_dma();
+    __syncthreads();
+    st0 = st1;
+  }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + xor32(l_run);
@@ -378,8 +520,14 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const int P = kRows / F;
   const int n_hg = G / F;
   const int n_qb = (a.Lq + P - 1) / P;
+  const int ntiles = (a.Lkv + kBK - 1) / kBK;
   const int64_t nblk = (int64_t)a.B * a.Hkv * n_hg * n_qb;
-  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t nimg = (int64_t)a.B * a.Hkv * ntiles;
+  if (nblk > 0x7fffffff || nimg > 0x7fffffff) return hipErrorInvalidValue;
+  if (a.ws_bytes < prefill_workspace_bytes(a.B, a.Lkv, a.Hkv, D, true)) return hipErrorInvalidValue;
+  uint16_t* img = static_cast<uint16_t*>(a.ws);
+  hipLaunchKernelGGL(prefill_v_image_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s,
+                     (const uint16_t*)a.v, img, a.Lkv, a.Hkv, a.kv_stride, ntiles);
   auto kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16>;
   const size_t lds = PrefillLds<D>::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -388,8 +536,8 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   // multiply and every visible score maps to exp2(0) = 1 exactly.
   const float c = fmaxf(a.scale * kLog2e, 1e-30f);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kThreads), lds, s, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv,
-                     a.q_stride, a.kv_stride, c, F, n_hg, n_qb);
+                     (const uint16_t*)a.k, img, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv,
+                     a.q_stride, a.kv_stride, c, F, n_hg, n_qb, ntiles);
   return hipGetLastError();
 }
 
@@ -403,6 +551,13 @@ hipError_t launch_f32(const PrefillArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+size_t prefill_workspace_bytes(int B, int Lkv, int Hkv, int d, bool bf16) {
+  if (!bf16 || B <= 0 || Lkv <= 0 || Hkv <= 0) return 0;
+  const int64_t ntiles = (Lkv + kBK - 1) / kBK;
+  const int64_t per = d == 64 ? PrefillLds<64>::kV : PrefillLds<128>::kV;
+  return (size_t)((int64_t)B * Hkv * ntiles * per * 2);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (!a.in_bf16) return a.d == 64 ? launch_f32<64>(a, s) : launch_f32<128>(a, s);

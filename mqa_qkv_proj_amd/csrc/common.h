@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mqkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -69,6 +71,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
 // Exchange with the lane 32 positions away (the other k-half of an MFMA tile).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max(x, x of the lane 32 away) without a trip through LDS: permlane32_swap on
+// two copies of x leaves, in every lane, x and its partner's x in the two
+// results (which one is in which depends on the lane half).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Order a wave's own LDS writes before its later LDS reads (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -85,6 +95,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % 8) * (full / 8) + bid / 8;
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1 as straight-line code.  Unlike an
+// unrolled loop, this leaves no loop structure for the optimizer to move
+// instructions out of, so the written order is the order the scheduler sees.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
 // Buffer resource over `bytes` bytes from a wave-uniform base: 16-byte loads at
@@ -96,6 +117,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t bld16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+// LDS-DMA: every lane's 16 bytes at buffer offset voff + soff land at
+// lds + 16 * lane (lds is wave-uniform).  Lanes whose offset is out of range
+// write nothing.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, u32x2_t v) { *reinterpret_cast<u32x2_t*>(p) = v; }
 

@@ -29,7 +29,10 @@ struct PrefillArgs {
   bool causal;
   float scale;
   bool in_bf16, out_bf16;
+  void* ws;         // bf16 inputs: V^T tile images (prefill_workspace_bytes)
+  size_t ws_bytes;
 };
+size_t prefill_workspace_bytes(int B, int Lkv, int Hkv, int d, bool bf16);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 struct DecodeArgs {

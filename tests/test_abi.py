@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("qkv_proj", "qkv_proj_workspace_bytes", "gqa_attn_prefill", "gqa_attn_decode",
-              "gqa_attn_decode_workspace_bytes",
+    for n in ("qkv_proj", "qkv_proj_workspace_bytes", "gqa_attn_prefill", "gqa_attn_prefill_workspace_bytes",
+              "gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
               "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version"):
         assert n in names
 
@@ -41,7 +41,7 @@ def test_status_strings(lib):
     assert L.mqkv_status_string(1) == b"invalid argument"
     assert L.mqkv_status_string(2) == b"unsupported configuration"
     assert L.mqkv_status_string(3) == b"HIP runtime error"
-    assert L.mqkv_abi_version() == 101
+    assert L.mqkv_abi_version() == 102
 
 
 def proj(lib, **kw):
@@ -53,11 +53,11 @@ def proj(lib, **kw):
 
 def prefill(lib, **kw):
     a = dict(q=A, k=A, v=A, o=A, lse=None, B=1, Lq=16, Lkv=16, H_q=4, H_kv=2, d=64, qs=512, ks=512,
-             causal=1, scale=0.125, dt=BF16, odt=BF16)
+             causal=1, scale=0.125, dt=BF16, odt=BF16, ws=A, wsb=1 << 20)
     a.update(kw)
     return lib.lib.gqa_attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"], a["Lkv"],
                                     a["H_q"], a["H_kv"], a["d"], a["qs"], a["ks"], a["causal"], a["scale"],
-                                    a["dt"], a["odt"], None)
+                                    a["dt"], a["odt"], a["ws"], a["wsb"], None)
 
 
 def decode(lib, **kw):
@@ -90,6 +90,7 @@ def test_qkv_proj_empty_is_noop(lib):
     (dict(scale=float("inf")), INV), (dict(scale=-1.0), INV), (dict(qs=100), INV), (dict(qs=516), INV),
     (dict(ks=130), INV), (dict(H_q=4, H_kv=3), INV), (dict(d=256, qs=1024, ks=512), UNS),
     (dict(dt=F32, odt=BF16), UNS), (dict(B=-1), INV), (dict(dt=3), INV),
+    (dict(ws=None), INV), (dict(ws=A + 8), INV), (dict(wsb=18431), INV),
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(lib, **kw) == code
@@ -108,6 +109,17 @@ def test_projection_workspace_query(lib):
     assert f(4096, 4096, 32, 8, 128) == 0      # large M: single pass, no workspace
     assert f(32, 4096, 32, 8, 128, 0) == 0     # fp32 path: no workspace
     assert f(32, 4096, 32, 3, 128) == 0        # invalid heads
+
+
+def test_prefill_workspace_query(lib):
+    f = lib.prefill_workspace_bytes
+    # bf16: one fp16 V^T image of (d rows x (64 + 8) keys) per 64-key tile, batch and KV head
+    assert f(2, 100, 4, 128) == 2 * 4 * 2 * 128 * 72 * 2
+    assert f(1, 16, 2, 64) == 1 * 2 * 1 * 64 * 72 * 2 == 18432
+    assert f(1, 64, 1, 64) == 9216 and f(1, 65, 1, 64) == 2 * 9216
+    assert f(2, 100, 4, 128, 0) == 0          # fp32 inputs need none
+    assert f(2, 100, 4, 96) == 0              # unsupported d
+    assert f(2, 0, 4, 128) == 0               # L_kv < 1
 
 
 def test_decode_workspace_query(lib):

@@ -119,6 +119,8 @@ PREFILL = [  # B, L_q, L_kv, H_q, H_kv, d, causal
     (1, 1, 1, 2, 1, 64, True),          # single token
     (3, 1, 129, 4, 2, 128, False),      # one query row
     (1, 64, 64, 64, 2, 64, True),       # G=32
+    (1, 640, 640, 8, 2, 128, False),    # ten full tiles: every LDS stage reused several times
+    (1, 700, 900, 4, 1, 64, True),      # long pipelined run, L_q < L_kv, ragged last tile
 ]
 
 
@@ -147,6 +149,29 @@ def test_prefill_f32_matches_oracle(m, causal, d):
     ref_o, ref_l = oracle.attention(inp["q"], inp["k"], inp["v"], causal, 1.0 / math.sqrt(d))
     assert_close(host(o), ref_o, "f32", "O f32")
     assert_close(host(lse), ref_l, "f32", "LSE f32")
+
+
+def test_prefill_workspace_reuse(m):
+    """One caller-owned workspace serves calls of different sizes in a row; each
+    call rewrites every V^T image it reads, so results equal fresh-workspace ones
+    bit for bit.  A workspace that is too small is rejected on the host."""
+    t = torch()
+    say("prefill workspace reuse")
+    cases = [(2, 300, 300, 8, 2, 128, True), (1, 70, 130, 4, 4, 64, False), (2, 65, 65, 8, 1, 128, True)]
+    need = max(m.prefill_workspace_bytes(B, Lkv, Hkv, d) for B, _, Lkv, _, Hkv, d, _ in cases)
+    ws = t.full((need,), 0xFF, dtype=t.uint8, device="cuda")  # NaN-pattern garbage to start from
+    for i, (B, L_q, L_kv, H_q, H_kv, d, causal) in enumerate(cases):
+        inp = W.small("bf16", 40 + i, B, L_q, L_kv, H_q, H_kv, d)
+        q, k, v = (dev(inp[n], "bf16") for n in ("q", "k", "v"))
+        o1 = m.gqa_attn_prefill(q, k, v, causal=causal, out_dtype=t.float32, workspace=ws)
+        o2 = m.gqa_attn_prefill(q, k, v, causal=causal, out_dtype=t.float32)
+        assert t.equal(o1, o2), f"case {i}"
+        assert t.isfinite(o1).all()
+    small = t.empty(m.prefill_workspace_bytes(2, 300, 2, 128) - 16, dtype=t.uint8, device="cuda")
+    inp = W.small("bf16", 40, 2, 300, 300, 8, 2, 128)
+    q, k, v = (dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    with pytest.raises(m.MqkvInvalid):
+        m.gqa_attn_prefill(q, k, v, workspace=small)
 
 
 def test_prefill_on_qkv_views_equals_contiguous_copies(m):
