@@ -116,10 +116,10 @@ mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* 
                              void* stream);
 
 /*
- * Bytes of device workspace gqa_attn_decode needs for these sizes
- * (fp32 partial outputs and softmax statistics of every key split).
- * kv_split: keys per split, 0 = the library's choice.  Returns 0 for
- * arguments gqa_attn_decode would reject.
+ * Bytes of device workspace gqa_attn_decode needs for these sizes: fp32
+ * partial outputs and softmax statistics of every work unit.  kv_split: keys
+ * per split, 0 = the library's choice.  Returns 0 for arguments
+ * gqa_attn_decode would reject.
  */
 size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
                                        int32_t L_max, int32_t kv_split);
@@ -133,10 +133,14 @@ size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int
  *   [0, seq_lens[b]) (the new token's K/V are already in the cache)
  *   o   [B, H_q, d] contiguous (o_dtype), lse [B, H_q] fp32 or NULL
  *
- * The keys are processed in splits of kv_split keys (0 = library choice; else a
- * multiple of 32 in [32, 65536]); partial (max, sum, output) triples go to
- * `workspace` and a second kernel combines them exactly.
- * workspace_bytes must be >= gqa_attn_decode_workspace_bytes(...).
+ * The keys of every (sequence, KV head) are cut into work units: splits of
+ * kv_split keys (a multiple of 32 in [32, 65536]), or with kv_split = 0 the
+ * library's choice -- for large caches an equal share of all attended keys per
+ * resident workgroup, crossing sequence boundaries, so that ragged lengths
+ * stay balanced.  Each unit writes a partial (max, sum, output) triple to
+ * `workspace` and a second kernel combines them exactly (softmax rescaling).
+ * workspace: >= gqa_attn_decode_workspace_bytes(...) bytes, 16-byte aligned;
+ *   no initial contents needed; calls that overlap must not share one.
  */
 mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seq_lens, void* o, float* lse, int32_t B,

@@ -231,6 +231,13 @@ def decode_workspace_bytes(B: int, H_q: int, H_kv: int, d: int, L_max: int, kv_s
     return int(lib.gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split))
 
 
+def decode_workspace(B: int, H_q: int, H_kv: int, d: int, L_max: int, kv_split: int = 0, device="cuda"):
+    """A decode workspace of the right size (its contents need no initialisation)."""
+    torch = _torch()
+    return torch.empty(max(decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split), 16), dtype=torch.uint8,
+                       device=device)
+
+
 def gqa_attn_decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None, out_dtype=None,
                     kv_split: int = 0, return_lse: bool = False, workspace=None, out=None):
     """One decode step over a contiguous KV cache.

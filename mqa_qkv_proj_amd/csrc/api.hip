@@ -1,5 +1,6 @@
 // C ABI of the library: host-side validation and dispatch to the gfx950 kernels.
 // Every check runs before any HIP call, so a rejected call touches no device.
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -36,20 +37,6 @@ mqkv_status check_heads(int32_t H_q, int32_t H_kv, int32_t d) {
   if (d < 1) return fail(MQKV_ERR_INVALID, "d=%d must be >= 1", d);
   if (d != 64 && d != 128) return fail(MQKV_ERR_UNSUPPORTED, "head dim d=%d not supported (64 or 128)", d);
   return MQKV_OK;
-}
-
-// Keys per decode split chosen by the library: about 8192 (sequence, KV head,
-// split) units at full cache length, i.e. several per single-wave slot of the
-// chip, so that waves whose split lies beyond a short sequence's length are
-// back-filled; multiples of the 32-key tile, at least 96 keys so that the
-// partial outputs stay a small part of the traffic.
-int32_t auto_split(int32_t B, int32_t H_kv, int32_t L_max) {
-  const int64_t target_units = 8192;
-  const int64_t work = (int64_t)L_max * B * H_kv;
-  int64_t split = 32 * ((work + 32 * target_units - 1) / (32 * target_units));
-  if (split < 96) split = 96;
-  if (split > 8192) split = 8192;
-  return (int32_t)split;
 }
 
 bool split_ok(int32_t s) { return s >= 32 && s <= 65536 && s % 32 == 0; }
@@ -160,9 +147,9 @@ size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int
   if (B < 0 || L_max < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
     return 0;
   if (kv_split != 0 && !split_ok(kv_split)) return 0;
-  const int32_t split = kv_split ? kv_split : auto_split(B, H_kv, L_max);
-  const int64_t n_split = ((int64_t)L_max + split - 1) / split;
-  const int64_t per = (int64_t)B * H_q * n_split;
+  const int slots = std::max(mqkv::decode_slots(B, H_q, H_kv, L_max, kv_split, true),
+                             mqkv::decode_slots(B, H_q, H_kv, L_max, kv_split, false));
+  const int64_t per = (int64_t)B * H_q * slots;
   return (size_t)(per * d * 4 + per * 2 * 4 + 256);  // outputs, then (max, sum) pairs
 }
 
@@ -198,13 +185,15 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(MQKV_ERR_INVALID, "workspace must be 16-byte aligned and >= %zu bytes (got %zu)", need,
                 workspace_bytes);
-  const int32_t split = kv_split ? kv_split : auto_split(B, H_kv, L_max);
-  const int32_t n_split = (L_max + split - 1) / split;
-  const int64_t per = (int64_t)B * H_q * n_split;
+  const bool bf16 = in_dtype == MQKV_BF16;
+  const int32_t n_slot = mqkv::decode_slots(B, H_q, H_kv, L_max, kv_split, bf16);
+  const int32_t split = kv_split > 0 ? kv_split : mqkv::decode_auto_split(B, H_q, H_kv, L_max, bf16);
+  const int64_t per = (int64_t)B * H_q * n_slot;
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = part_o + per * d;
-  mqkv::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, H_q, H_kv, d, L_max, q_tok_stride,
-                     scale, split, n_split, part_o, part_ml, in_dtype == MQKV_BF16,
+  mqkv::DecodeArgs a{q,     k_cache, v_cache, seq_lens, o,       lse,     B,
+                     H_q,   H_kv,    d,       L_max,    q_tok_stride,     scale,
+                     split, n_slot,  part_o,  part_ml,  in_dtype == MQKV_BF16,
                      o_dtype == MQKV_BF16};
   return hip_status(mqkv::launch_decode(a, (hipStream_t)stream), "gqa_attn_decode launch");
 }

@@ -10,17 +10,20 @@
 // of tiling + softmax rescaling and the HN remark on splitting/combining the
 // softmax).
 //
-// Split kernel (bf16): one single-wave workgroup per (sequence, KV head, split,
-// block of 16 query heads of the group).  Each K/V row is read from HBM once
-// and serves all G query heads of its group through MFMA 16x16x32: S^T = K . Q^T
-// (bf16, the heads as the 16 columns) and O^T += V^T . P^T (fp16, P rounded to
-// fp16 as in the prefill kernel).  K rows are loaded straight into the MFMA
-// operand registers; V rows are staged through the wave's LDS, transposed and
-// converted to fp16.  Tiles are 32 keys; the next tile's loads are in flight
-// while the current one is finished.  Splits that start beyond seq_lens[b] exit
-// at once and free their slot; three waves fit per SIMD.
-// Combine kernel: one workgroup per (sequence, query head), one thread per
-// output element.
+// Split kernel (bf16): single-wave workgroups.  Each K/V row is read from HBM
+// once and serves all G query heads of its group through MFMA 16x16x32:
+// S^T = K . Q^T (bf16, the heads as the 16 columns) and O^T += V^T . P^T
+// (fp16, P rounded to fp16 as in the prefill kernel).  K rows are loaded
+// straight into the MFMA operand registers; V rows are staged through the
+// wave's LDS, transposed and converted to fp16.  Tiles are 32 keys; the next
+// tile's loads are in flight while the current one is finished.
+// Work assignment: for large caches the tiles of every (sequence, KV head)
+// are laid end to end and each resident workgroup streams an equal share of
+// them, crossing sequence ends, so ragged lengths stay balanced over the
+// chip; otherwise (or with an explicit split) one workgroup per fixed split.
+// Combine kernel: one wave per (sequence, query head) merges the partials.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -28,7 +31,11 @@ namespace mqkv {
 
 namespace {
 
-constexpr int kTK = 32;  // keys per tile: two 16-key MFMA blocks
+constexpr int kTK = 32;      // keys per tile: two 16-key MFMA blocks
+constexpr int kMinTiles = 4;  // balanced mode: at least this many tiles per workgroup
+constexpr int kWavesPerCU = 12;  // split-kernel workgroups resident per CU (3 per SIMD)
+constexpr int64_t kBalancedMinTiles = 16384;  // auto: balanced split from this many tiles at capacity
+constexpr int kShortSplit = 64;               // auto: keys per split below that
 
 template <int D>
 struct DecodeLds {
@@ -50,15 +57,77 @@ __device__ __forceinline__ f32x4_t mfma16_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// One single-wave workgroup (a finished wave frees its slot at once) per
-// (sequence, KV head, block of 16 query heads, split).  MFMA 16x16x32 layout:
-// A (16 x 32): lane l holds row l%16, k slot group l/16; B (32 x 16): column
-// l%16, the same k group; D (16 x 16): column l%16, rows 4*(l/16) + i.
+// Keys of sequence b that are attended (lengths beyond the cache are clamped).
+__device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b, int Lmax) {
+  return min(max(seq_lens[b], 0), Lmax);
+}
+
+// Balanced work split.  The tiles of all (sequence, KV head, query-head block)
+// segments are laid end to end, sequence-major; segment (b, g, qb) holds
+// ceil(len_b / 32) tiles.  Workgroup w streams tiles [w*tpw, (w+1)*tpw) of that
+// line, crossing segment ends, so every workgroup moves the same number of
+// bytes whatever the length mix.  Computed by one wave from seq_lens:
+// the total tile count T, and (when t >= 0) the sequence holding tile t with the
+// number of tiles before that sequence.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+struct TileLine {
+  int64_t total;
+  int b;          // sequence holding tile t (-1 if none)
+  int64_t base;   // tiles before sequence b
+};
+__device__ TileLine tile_line(const int32_t* seq_lens, int B, int Lmax, int per_seq, int64_t t) {
+  const int lane = threadIdx.x & 63;
+  TileLine r{0, -1, 0};
+  int64_t carry = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int64_t v = bb < B ? (int64_t)((seq_len(seq_lens, bb, Lmax) + kTK - 1) / kTK) * per_seq : 0;
+    int64_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const int64_t excl = carry + incl - v;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(v > 0 && excl <= t && t < carry + incl);
+    if (r.b < 0 && hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      r.b = b0 + l;
+      r.base = __shfl(excl, l, 64);
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  // every lane holds the same values: make them scalar
+  r.total = uniform64(carry);
+  r.b = __builtin_amdgcn_readfirstlane(r.b);
+  r.base = uniform64(r.base);
+  return r;
+}
+__device__ __forceinline__ int64_t balanced_tpw(int64_t total, int nwg) {
+  const int64_t t = (total + nwg - 1) / nwg;
+  return t > kMinTiles ? t : kMinTiles;
+}
+
+// One single-wave workgroup per work unit.  A unit is a run of tiles of one
+// (sequence, KV head, block of 16 query heads) segment:
+//  * aligned mode (split > 0): unit = the split-th piece of split keys of one
+//    segment; partial slot = split index;
+//  * balanced mode (split == 0): the workgroup's tiles of the balanced line,
+//    one unit per segment they touch; partial slot = workgroup - first
+//    workgroup of the segment.
+// Per unit, MFMA 16x16x32 layout: A (16 x 32): lane l holds row l%16, k slot
+// group l/16; B (32 x 16): column l%16, the same k group; D (16 x 16): column
+// l%16, rows 4*(l/16) + i.
 template <int D>
 __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_split, int n_qblk) {
+    int B, int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_slot, int n_qblk) {
   using S = DecodeLds<D>;
   constexpr int DS = D / 32;                       // k-steps of the score MFMA
   constexpr int DB = D / 16;                       // 16-row blocks of O^T
@@ -67,150 +136,204 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
   uint16_t* Vt = smem;
 
   const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
-  // splits of one (sequence, KV head) are neighbours; each XCD gets a contiguous range
-  int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int s = lid % n_split;
-  lid /= n_split;
-  const int qblk = lid % n_qblk;
-  const int bg = lid / n_qblk;
-  const int b = bg / Hkv, g = bg % Hkv;
-  const int len = min(seq_lens[b], Lmax);  // lengths beyond the cache are clamped (caller error)
-  const int kbeg = s * split;
-  if (kbeg >= len) return;
-  const int kend = min(kbeg + split, len);
-  const int nt = (kend - kbeg + kTK - 1) / kTK;
-
   const int G = Hq / Hkv;
-  const int col = qblk * 16 + l16;  // query head within the group
-  const bool hvalid = col < G;
-  const int h = g * G + (hvalid ? col : 0);
-
-  // Q^T operand: at k-step st lane (col, g4) holds d-chunk 4*st + g4 of its head
-  // (the four lanes of a row then read 64 contiguous bytes per K load)
-  u32x4_t qf[DS];
-  {
-    const uint16_t* qp = q + (int64_t)b * q_stride + (int64_t)h * D + g4 * 8;
-#pragma unroll
-    for (int st = 0; st < DS; ++st) qf[st] = hvalid ? ld16(qp + st * 32) : u32x4_t{0, 0, 0, 0};
-  }
-
   const int64_t row_stride = (int64_t)Hkv * D;
-  const uint16_t* kbase = kc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D + g4 * 8;
-  const uint16_t* vbase = vc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D;
-
-  // K goes straight into the A-operand registers (lane = key row); V is staged
-  // through LDS to be transposed.
-  u32x4_t kr[2][DS];
-  u32x4_t rv[VTASK][4];
-  auto load_tile = [&](int t) {
-    const int k0 = kbeg + t * kTK;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int gk = k0 + kb * 16 + l16;
-#pragma unroll
-      for (int st = 0; st < DS; ++st)
-        kr[kb][st] = (gk < kend) ? ld16(kbase + (int64_t)gk * row_stride + st * 32) : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < VTASK; ++j) {
-      const int ti = lane + j * 64;
-      const int a = ti / (D / 8), dg = ti % (D / 8);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int gk = k0 + a * 4 + jj;
-        rv[j][jj] = (gk < kend) ? ld16(vbase + (int64_t)gk * row_stride + dg * 8) : u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_v = [&]() {
-#pragma unroll
-    for (int j = 0; j < VTASK; ++j) {
-      const int ti = lane + j * 64;
-      const int a = ti / (D / 8), dg = ti % (D / 8);
-      const int cpos = vt_pos32(a * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u32x2_t lo, hi;
-        lo[0] = pack_f16(bf16lo(rv[j][0][e]), bf16lo(rv[j][1][e]));
-        lo[1] = pack_f16(bf16lo(rv[j][2][e]), bf16lo(rv[j][3][e]));
-        hi[0] = pack_f16(bf16hi(rv[j][0][e]), bf16hi(rv[j][1][e]));
-        hi[1] = pack_f16(bf16hi(rv[j][2][e]), bf16hi(rv[j][3][e]));
-        st8(Vt + (dg * 8 + 2 * e) * S::kVld + cpos, lo);
-        st8(Vt + (dg * 8 + 2 * e + 1) * S::kVld + cpos, hi);
-      }
-    }
-  };
-
-  f32x4_t acc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) acc[i] = f32x4_t{};
-  float m_run = -INFINITY, l_run = 0.0f;
   const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  load_tile(0);
-  for (int t = 0; t < nt; ++t) {
-    wave_lds_sync();  // the previous tile's V^T reads are done before overwriting
-    store_v();
-    wave_lds_sync();
-    const int k0 = kbeg + t * kTK;
-    f32x4_t sb[2] = {f32x4_t{}, f32x4_t{}};
-#pragma unroll
-    for (int st = 0; st < DS; ++st)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sb[kb] = mfma16_bf16(kr[kb][st], qf[st], sb[kb]);
-    if (t + 1 < nt) load_tile(t + 1);  // in flight while this tile is finished
+  // Process tiles [tb, tb + ntile) of segment (b, g, qblk) and write its partial to `slot`.
+  auto unit = [&](int b, int g, int qblk, int tb, int ntile, int slot) {
+    const int len = seq_len(seq_lens, b, Lmax);
+    const int kbeg = tb * kTK;
+    const int kend = min((tb + ntile) * kTK, len);
+    const int nt = (kend - kbeg + kTK - 1) / kTK;
+    const int col = qblk * 16 + l16;  // query head within the group
+    const bool hvalid = col < G;
+    const int h = g * G + (hvalid ? col : 0);
 
-    // lane (col, g4) holds keys kb*16 + 4*g4 + i of its query head
-    if (k0 + kTK > kend) {
-      const int rel = kend - 1 - k0 - 4 * g4;
+    // Q^T operand: at k-step st lane (col, g4) holds d-chunk 4*st + g4 of its
+    // head (the four lanes of a row then read 64 contiguous bytes per K load)
+    u32x4_t qf[DS];
+    {
+      const uint16_t* qp = q + (int64_t)b * q_stride + (int64_t)h * D + g4 * 8;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kb * 16 + i > rel) sb[kb][i] = -INFINITY;
+      for (int st = 0; st < DS; ++st) qf[st] = hvalid ? ld16(qp + st * 32) : u32x4_t{0, 0, 0, 0};
     }
-    float mx = fmaxf(fmaxf(fmaxf(sb[0][0], sb[0][1]), fmaxf(sb[0][2], sb[0][3])),
-                     fmaxf(fmaxf(sb[1][0], sb[1][1]), fmaxf(sb[1][2], sb[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mt = mx * c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.0f) != 0) {
-      // only this row's own growth moves its max (rows sharing the wave do not matter)
-      const float mn = (mt > m_run + 8.0f) ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-      m_run = mn;
-      l_run *= alpha;
+    const uint16_t* kbase = kc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D + g4 * 8;
+    const uint16_t* vbase = vc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D;
+
+    // K goes straight into the A-operand registers (lane = key row); V is staged
+    // through LDS to be transposed.  V tasks are 4 keys x 8 dimensions, with
+    // consecutive lanes on consecutive key groups so that one 8-byte LDS store
+    // covers whole V^T rows.
+    u32x4_t kr[2][DS];
+    u32x4_t rv[VTASK][4];
+    auto load_tile = [&](int t) {
+      const int k0 = kbeg + t * kTK;
 #pragma unroll
-      for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int gk = k0 + kb * 16 + l16;
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+          kr[kb][st] = (gk < kend) ? ld16(kbase + (int64_t)gk * row_stride + st * 32) : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < VTASK; ++j) {
+        const int ti = lane + j * 64;
+        const int a = ti % (kTK / 4), dg = ti / (kTK / 4);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int gk = k0 + a * 4 + jj;
+          rv[j][jj] = (gk < kend) ? ld16(vbase + (int64_t)gk * row_stride + dg * 8) : u32x4_t{0, 0, 0, 0};
+        }
+      }
+    };
+    auto store_v = [&]() {
+#pragma unroll
+      for (int j = 0; j < VTASK; ++j) {
+        const int ti = lane + j * 64;
+        const int a = ti % (kTK / 4), dg = ti / (kTK / 4);
+        const int cpos = vt_pos32(a * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u32x2_t lo, hi;
+          lo[0] = pack_f16(bf16lo(rv[j][0][e]), bf16lo(rv[j][1][e]));
+          lo[1] = pack_f16(bf16lo(rv[j][2][e]), bf16lo(rv[j][3][e]));
+          hi[0] = pack_f16(bf16hi(rv[j][0][e]), bf16hi(rv[j][1][e]));
+          hi[1] = pack_f16(bf16hi(rv[j][2][e]), bf16hi(rv[j][3][e]));
+          st8(Vt + (dg * 8 + 2 * e) * S::kVld + cpos, lo);
+          st8(Vt + (dg * 8 + 2 * e + 1) * S::kVld + cpos, hi);
+        }
+      }
+    };
+
+    f32x4_t acc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] = f32x4_t{};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    load_tile(0);
+    for (int t = 0; t < nt; ++t) {
+      wave_lds_sync();  // the previous tile's V^T reads are done before overwriting
+      store_v();
+      wave_lds_sync();
+      const int k0 = kbeg + t * kTK;
+      f32x4_t sb[2] = {f32x4_t{}, f32x4_t{}};
+#pragma unroll
+      for (int st = 0; st < DS; ++st)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sb[kb] = mfma16_bf16(kr[kb][st], qf[st], sb[kb]);
+      if (t + 1 < nt) load_tile(t + 1);  // in flight while this tile is finished
+
+      // lane (col, g4) holds keys kb*16 + 4*g4 + i of its query head
+      if (k0 + kTK > kend) {
+        const int rel = kend - 1 - k0 - 4 * g4;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kb * 16 + i > rel) sb[kb][i] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sb[0][0], sb[0][1]), fmaxf(sb[0][2], sb[0][3])),
+                       fmaxf(fmaxf(sb[1][0], sb[1][1]), fmaxf(sb[1][2], sb[1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = max_xor32(mx);
+      const float mt = mx * c;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.0f) != 0) {
+        // only this row's own growth moves its max (rows sharing the wave do not matter)
+        const float mn = (mt > m_run + 8.0f) ? mt : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        m_run = mn;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+      }
+      // P^T operand: slots 0-3 = keys 4*g4+i of block 0, slots 4-7 = the same of block 1
+      u32x4_t pf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kb = e >> 1, i = (e & 1) * 2;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[kb][i], c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[kb][i + 1], c, -m_run));
+        const uint32_t w = pack_f16(p0, p1);
+        pf[e] = w;
+        l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc[db] = mfma16_f16(ld16(Vt + (db * 16 + l16) * S::kVld + g4 * 8), pf, acc[db]);
     }
-    // P^T operand: slots 0-3 = keys 4*g4+i of block 0, slots 4-7 = the same of block 1
-    u32x4_t pf;
+
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (hvalid) {
+      const int64_t pidx = ((int64_t)b * Hq + h) * n_slot + slot;
+      float* po = part_o + pidx * D;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int kb = e >> 1, i = (e & 1) * 2;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[kb][i], c, -m_run));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[kb][i + 1], c, -m_run));
-      const uint32_t w = pack_f16(p0, p1);
-      pf[e] = w;
-      l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
+      for (int db = 0; db < DB; ++db)
+        st16(po + db * 16 + 4 * g4, u32x4_t{__float_as_uint(acc[db][0]), __float_as_uint(acc[db][1]),
+                                            __float_as_uint(acc[db][2]), __float_as_uint(acc[db][3])});
+      if (g4 == 0) {
+        part_ml[pidx * 2 + 0] = m_run;
+        part_ml[pidx * 2 + 1] = l_tot;
+      }
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      acc[db] = mfma16_f16(ld16(Vt + (db * 16 + l16) * S::kVld + g4 * 8), pf, acc[db]);
+  };
+
+  // Work assignment; a single call site keeps one copy of the unit code.
+  const int per_seq = Hkv * n_qblk;
+  int64_t t = 0, t1 = 0, tpw = 1, base = 0;
+  int b = 0;
+  bool aligned_done = false;
+  if (split > 0) {
+    // aligned mode: (sequence, KV head, query block, split), splits of one
+    // segment neighbours, each XCD a contiguous range
+    const int n_split = (Lmax + split - 1) / split;
+    int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int sidx = lid % n_split;
+    lid /= n_split;
+    const int qblk = lid % n_qblk;
+    const int bg = lid / n_qblk;
+    b = bg / Hkv;
+    if (sidx * split >= seq_len(seq_lens, b, Lmax)) return;
+    // express the split as tiles of the (b, g, qblk) segment
+    t = sidx * (split / kTK);
+    t1 = t + split / kTK;
+    base = -(int64_t)(bg % Hkv * n_qblk + qblk);  // segment index carried in base (see below)
+  } else {
+    const int64_t total = tile_line(seq_lens, B, Lmax, per_seq, -1).total;
+    tpw = balanced_tpw(total, gridDim.x);
+    t = (int64_t)blockIdx.x * tpw;
+    t1 = min(total, t + tpw);
+    if (t >= t1) return;
+    const TileLine at = tile_line(seq_lens, B, Lmax, per_seq, t);
+    b = at.b;
+    base = at.base;
   }
-
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (!hvalid) return;
-  const int64_t pidx = ((int64_t)b * Hq + h) * n_split + s;
-  float* po = part_o + pidx * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-    st16(po + db * 16 + 4 * g4, u32x4_t{__float_as_uint(acc[db][0]), __float_as_uint(acc[db][1]),
-                                        __float_as_uint(acc[db][2]), __float_as_uint(acc[db][3])});
-  if (g4 == 0) {
-    part_ml[pidx * 2 + 0] = m_run;
-    part_ml[pidx * 2 + 1] = l_tot;
+  while (t < t1 && b < B) {
+    int seg, tb, n, slot;
+    if (split > 0) {
+      if (aligned_done) break;
+      aligned_done = true;
+      seg = (int)(-base);
+      tb = (int)t;
+      n = (int)(t1 - t);
+      slot = (int)(t / (split / kTK));
+    } else {
+      const int ntb = (seq_len(seq_lens, b, Lmax) + kTK - 1) / kTK;  // tiles per segment of b
+      const int64_t local = t - base;
+      if (ntb == 0 || local >= (int64_t)ntb * per_seq) {  // past sequence b (or it is empty)
+        base += (int64_t)ntb * per_seq;
+        ++b;
+        continue;
+      }
+      seg = (int)(local / ntb);  // g * n_qblk + qblk within sequence b
+      tb = (int)(local % ntb);
+      n = (int)min((int64_t)(ntb - tb), t1 - t);
+      const int64_t seg_start = base + (int64_t)seg * ntb;
+      slot = (int)((int64_t)blockIdx.x - seg_start / tpw);
+    }
+    unit(b, seg / n_qblk, seg % n_qblk, tb, n, slot);
+    t += n;
   }
 }
 
@@ -220,7 +343,7 @@ template <int D>
 __global__ __launch_bounds__(64) void attn_decode_split_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_split) {
+    int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_slot) {
   constexpr int PER = D / 64;
   __shared__ float qs[D];
   __shared__ float ps[64];
@@ -266,7 +389,7 @@ __global__ __launch_bounds__(64) void attn_decode_split_f32_kernel(
       acc[e] = a;
     }
   }
-  const int64_t pidx = ((int64_t)b * Hq + h) * n_split + s;
+  const int64_t pidx = ((int64_t)b * Hq + h) * n_slot + s;
 #pragma unroll
   for (int e = 0; e < PER; ++e) part_o[pidx * D + e * 64 + lane] = acc[e];
   if (lane == 0) {
@@ -275,24 +398,45 @@ __global__ __launch_bounds__(64) void attn_decode_split_f32_kernel(
   }
 }
 
-// Combine the partials of every split: one wave per (sequence, query head).
-// Lanes first reduce the per-split (max, sum) statistics in parallel; then
-// each lane owns D/64 output elements and accumulates the splits' weighted
-// partial outputs with 8 loads in flight.
+// Combine the partials of every unit: one wave per (sequence, query head).
+// Lanes first reduce the per-unit (max, sum) statistics in parallel; then each
+// lane owns D/64 output elements and accumulates the units' weighted partial
+// outputs with 8 loads in flight.  The number of units of (b, h) follows from
+// the same work split the split kernel used.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     const int32_t* __restrict__ seq_lens, const float* __restrict__ part_o,
-    const float* __restrict__ part_ml, void* __restrict__ o, float* __restrict__ lse, int Hq,
-    int Lmax, int split, int n_split) {
+    const float* __restrict__ part_ml, void* __restrict__ o, float* __restrict__ lse, int B, int Hq,
+    int Hkv, int Lmax, int split, int n_slot, int n_qblk, int nwg) {
   constexpr int EPL = D / 64;  // output elements per lane
   __shared__ float wsh[64];
   const int lane = threadIdx.x;
   const int b = blockIdx.y, h = blockIdx.x;
   const int64_t bh = (int64_t)b * Hq + h;
-  const int len = min(seq_lens[b], Lmax);
-  const int n = min((len + split - 1) / split, n_split);
-  const float* ml = part_ml + bh * n_split * 2;
-  const float* po = part_o + bh * n_split * D;
+  const int len = seq_len(seq_lens, b, Lmax);
+  int n;
+  if (split > 0) {
+    n = min((len + split - 1) / split, n_slot);
+  } else {
+    const int G = Hq / Hkv, per_seq = Hkv * n_qblk;
+    const int g = h / G, qblk = (h % G) / 16;
+    const TileLine all = tile_line(seq_lens, B, Lmax, per_seq, -1);
+    const int64_t tpw = balanced_tpw(all.total, nwg);
+    const int ntb = (len + kTK - 1) / kTK;
+    int64_t base = 0;  // tiles before sequence b
+    for (int b0 = 0; b0 < b; b0 += 64) {
+      const int bb = b0 + lane;
+      int64_t v = bb < b ? (int64_t)((seq_len(seq_lens, bb, Lmax) + kTK - 1) / kTK) * per_seq : 0;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      base += v;
+    }
+    const int64_t s0 = base + (int64_t)(g * n_qblk + qblk) * ntb;
+    n = ntb > 0 ? (int)((s0 + ntb - 1) / tpw - s0 / tpw + 1) : 0;
+    n = min(n, n_slot);
+  }
+  const float* ml = part_ml + bh * n_slot * 2;
+  const float* po = part_o + bh * n_slot * D;
 
   float M = -INFINITY;
   for (int s0 = lane; s0 < n; s0 += 64) M = fmaxf(M, ml[2 * s0]);
@@ -343,43 +487,74 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
 }
 
 template <int D>
-hipError_t launch_split_bf16(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_split_bf16(const DecodeArgs& a, hipStream_t s, int& nwg) {
   const int G = a.Hq / a.Hkv;
   const int n_qblk = (G + 15) / 16;
-  const int64_t nblk = (int64_t)a.B * a.Hkv * n_qblk * a.n_split;
-  if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+  int64_t nblk;
+  if (a.split > 0) {
+    nblk = (int64_t)a.B * a.Hkv * n_qblk * ((a.Lmax + a.split - 1) / a.split);
+  } else {
+    // balanced mode: one resident wave per slot of the chip
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t tiles_max = (int64_t)a.B * a.Hkv * n_qblk * ((a.Lmax + kTK - 1) / kTK);
+    nblk = std::min((int64_t)cus * kWavesPerCU, (tiles_max + kMinTiles - 1) / kMinTiles);
+  }
+  if (nblk > 0x7fffffff || nblk < 1) return hipErrorInvalidValue;
+  nwg = (int)nblk;
   auto kern = attn_decode_split_bf16_kernel<D>;
   const size_t lds = DecodeLds<D>::kBytes;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64), lds, s, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_lens, a.part_o, a.part_ml, a.Hq,
-                     a.Hkv, a.Lmax, a.q_stride, fmaxf(a.scale * kLog2e, 1e-30f), a.split, a.n_split,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_lens, a.part_o, a.part_ml, a.B,
+                     a.Hq, a.Hkv, a.Lmax, a.q_stride, fmaxf(a.scale * kLog2e, 1e-30f), a.split, a.n_slot,
                      n_qblk);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_split_f32(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)a.n_split, (unsigned)a.Hq, (unsigned)a.B);
+  dim3 grid((unsigned)((a.Lmax + a.split - 1) / a.split), (unsigned)a.Hq, (unsigned)a.B);
   hipLaunchKernelGGL(attn_decode_split_f32_kernel<D>, grid, dim3(64), 0, s, (const float*)a.q,
                      (const float*)a.k, (const float*)a.v, a.seq_lens, a.part_o, a.part_ml, a.Hq,
-                     a.Hkv, a.Lmax, a.q_stride, a.scale * kLog2e, a.split, a.n_split);
+                     a.Hkv, a.Lmax, a.q_stride, a.scale * kLog2e, a.split, a.n_slot);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int decode_auto_split(int B, int Hq, int Hkv, int Lmax, bool bf16) {
+  // Balanced work split when the cache at capacity holds enough 32-key tiles to
+  // give every resident wave of the chip several; short splits otherwise, where
+  // the time is latency and one or two tiles per wave are best.
+  const int64_t n_qblk = (Hq / Hkv + 15) / 16;
+  const int64_t tiles = (int64_t)B * Hkv * n_qblk * ((Lmax + kTK - 1) / kTK);
+  return (bf16 && tiles >= kBalancedMinTiles) ? 0 : kShortSplit;
+}
+
+int decode_slots(int B, int Hq, int Hkv, int Lmax, int kv_split, bool bf16) {
+  const int split = kv_split > 0 ? kv_split : decode_auto_split(B, Hq, Hkv, Lmax, bf16);
+  if (split > 0) return (Lmax + split - 1) / split;
+  const int tiles = (Lmax + kTK - 1) / kTK;
+  return (tiles + kMinTiles - 1) / kMinTiles + 1;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   hipError_t e;
+  int nwg = 1;
   if (a.in_bf16)
-    e = a.d == 64 ? launch_split_bf16<64>(a, s) : launch_split_bf16<128>(a, s);
+    e = a.d == 64 ? launch_split_bf16<64>(a, s, nwg) : launch_split_bf16<128>(a, s, nwg);
   else
     e = a.d == 64 ? launch_split_f32<64>(a, s) : launch_split_f32<128>(a, s);
   if (e != hipSuccess) return e;
+  const int n_qblk = (a.Hq / a.Hkv + 15) / 16;
   const dim3 grid((unsigned)a.Hq, (unsigned)a.B);  // (query head, sequence)
 #define MQKV_COMB(DD, OB)                                                                        \
   if (a.d == DD && a.out_bf16 == OB)                                                            \
     hipLaunchKernelGGL((attn_decode_combine_kernel<DD, OB>), grid, dim3(64), 0, s, a.seq_lens,   \
-                       a.part_o, a.part_ml, a.o, a.lse, a.Hq, a.Lmax, a.split, a.n_split);
+                       a.part_o, a.part_ml, a.o, a.lse, a.B, a.Hq, a.Hkv, a.Lmax, a.split, a.n_slot,   \
+                       n_qblk, nwg);
   MQKV_COMB(64, true)
   MQKV_COMB(64, false)
   MQKV_COMB(128, true)

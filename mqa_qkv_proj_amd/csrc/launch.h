@@ -45,12 +45,18 @@ struct DecodeArgs {
   int B, Hq, Hkv, d, Lmax;
   int64_t q_stride;
   float scale;
-  int split;       // keys per split
-  int n_split;     // splits per sequence at capacity: ceil(Lmax / split)
-  float* part_o;   // [B, Hq, n_split, d]
-  float* part_ml;  // [B, Hq, n_split, 2]  (running max in log2 units, sum)
+  int split;       // keys per aligned split; 0 = balanced work split (bf16 only)
+  int n_slot;      // partial slots per (sequence, query head): decode_slots(Lmax, kv_split)
+  float* part_o;   // [B, Hq, n_slot, d]
+  float* part_ml;  // [B, Hq, n_slot, 2]  (running max in log2 units, sum)
   bool in_bf16, out_bf16;
 };
+// The library's choice for kv_split == 0 (0 = balanced work split, else keys
+// per split), and the partial slots per (sequence, query head) a call needs.
+// The workspace query has no dtype, so it sizes for the larger of the two.
+int decode_auto_split(int B, int Hq, int Hkv, int Lmax, bool bf16);
+int decode_slots(int B, int Hq, int Hkv, int Lmax, int kv_split, bool bf16);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace mqkv

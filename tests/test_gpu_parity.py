@@ -220,6 +220,34 @@ def test_decode_matches_oracle(m, B, H_q, H_kv, d, L_max, lens, split, dtype):
     assert_close(host(lse), ref_l, dtype, "decode LSE", max_abs=1e-3 if dtype == "bf16" else 1e-4)
 
 
+@pytest.mark.parametrize("B,H_q,H_kv,L_max", [(64, 16, 8, 1024), (64, 64, 2, 4096)])
+def test_decode_balanced_split_and_workspace_reuse(m, B, H_q, H_kv, L_max):
+    """Caches large enough (>= 16384 tiles of 32 keys at capacity) for the
+    library's balanced work split, where one workgroup's keys cross sequence
+    and head boundaries, with ragged lengths including 1, 31-33 and L_max.
+    Three calls share one workspace (filled with NaN bit patterns first, so a
+    stale or unwritten partial would show): every call must match the oracle."""
+    t = torch()
+    d = 128
+    say("decode balanced", B, H_q, H_kv, L_max)
+    rng = np.random.default_rng([31, B, H_q])
+    kc = W.round_bf16(W.normal(31, L_max, (B, L_max, H_kv, d)))
+    vc = W.round_bf16(W.normal(32, L_max, (B, L_max, H_kv, d)))
+    qd, kd, vd = None, dev(kc, "bf16"), dev(vc, "bf16")
+    ws = m.decode_workspace(B, H_q, H_kv, d, L_max)
+    ws.fill_(0xFF)
+    for call in range(3):
+        lens = rng.integers(1, L_max + 1, size=B).astype(np.int32)
+        lens[:6] = [1, 31, 32, 33, L_max, L_max - 1]
+        q = W.round_bf16(W.normal(33 + call, L_max, (B, H_q, d)))
+        scale = 1.0 / math.sqrt(d)
+        o, lse = m.gqa_attn_decode(dev(q, "bf16"), kd, vd, t.from_numpy(lens).cuda(), scale=scale,
+                                   return_lse=True, out_dtype=t.float32, workspace=ws)
+        ref_o, ref_l = oracle.decode(q, kc, vc, lens, scale)
+        assert_close(host(o), ref_o, "bf16", f"decode O (call {call})")
+        assert_close(host(lse), ref_l, "bf16", f"decode LSE (call {call})", max_abs=1e-3)
+
+
 def test_decode_q_as_view_of_qkv_rows(m):
     t = torch()
     B, H_q, H_kv, d, L_max = 4, 8, 2, 64, 150
