@@ -78,7 +78,7 @@ __global__ __launch_bounds__(WM* WN* KS * 64) void qkv_gemm_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < C::kBTasksPerThread; ++j) {
       const int ti = tid + j * C::kThreads;
-      const int kg = ti / (BN / 8), ng = ti % (BN / 8);
+      const int kg = ti % (BK / 4), ng = ti / (BK / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int gk = k0 + kg * 4 + r, gn = n0 + ng * 8;
@@ -98,7 +98,9 @@ __global__ __launch_bounds__(WM* WN* KS * 64) void qkv_gemm_bf16_kernel(
     for (int j = 0; j < C::kBTasksPerThread; ++j) {
       const int ti = tid + j * C::kThreads;
       if (ti < C::kBTasks) {
-        const int kg = ti / (BN / 8), ng = ti % (BN / 8);
+        // consecutive lanes take consecutive 4-row groups: one 8-byte store
+        // instruction then covers whole rows of the transposed tile
+        const int kg = ti % (BK / 4), ng = ti / (BK / 4);
         // rb[j][r].e holds W[k0+4kg+r][n0+8ng+2e .. +1]; write column n as 4 k values.
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
