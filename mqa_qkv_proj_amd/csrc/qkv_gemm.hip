@@ -238,6 +238,167 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
   }
 }
 
+// ----------------------------------------------------------------------------- copy-fed tiles
+// Workgroup tile BM x 128, k tile 64, 4 waves as 2 x 2.  Both operand tiles reach
+// LDS by LDS-DMA (buffer loads that write LDS directly, no staging registers):
+//  * x tile: BM rows of 64 k (k-contiguous) + 16 bytes of padding per row;
+//  * W tile: 64 rows of 128 n (n-contiguous, as W is stored) + 64 bytes of
+//    padding per row.  The MFMA B operand (8 consecutive k of one n per lane)
+//    is read with the transposing LDS load ds_read_b64_tr_b16: within each 16
+//    lanes, lane 4j+q reads 4 n of k-row j and lane i receives column i of the
+//    4 rows, so no VALU transposition is needed.
+// The row paddings keep both operand reads on distinct LDS banks; the lanes of
+// a copy that fall on padding point past the buffer and write nothing.  Two
+// LDS stages: the copy of k tile t+1 runs while tile t is multiplied, one
+// barrier per k tile.  Requires K % 64 == 0.
+constexpr int kCfBN = 128, kCfBK = 64, kCfThreads = 256;
+constexpr int kCfXld = kCfBK + 8;   // x tile row pitch (bf16 elements): 9 chunks of 16 B
+constexpr int kCfWld = kCfBN + 32;  // W tile row pitch: 20 chunks of 16 B
+template <int BM>
+struct CfLds {
+  static constexpr int kX = BM * kCfXld;
+  static constexpr int kW = kCfBK * kCfWld;
+  static constexpr int kStage = kX + kW;
+  static constexpr int kXCopies = kX * 2 / 1024;
+  static constexpr int kWCopies = kW * 2 / 1024;
+  static constexpr int kXcp = (kXCopies + 3) / 4;  // copies per wave
+  static constexpr int kWcp = (kWCopies + 3) / 4;
+  static constexpr size_t kBytes = 2 * (size_t)kStage * sizeof(uint16_t);
+  static_assert(kX * 2 % 1024 == 0 && kW * 2 % 1024 == 0, "tiles are whole 1 KB copies");
+};
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  const short4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+template <int BM>
+__global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, int M, int K, int N) {
+  using L = CfLds<BM>;
+  constexpr int MI = BM / 64;  // 32-row MFMA blocks per wave
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wq = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int nbn = (N + kCfBN - 1) / kCfBN, nbm = (M + BM - 1) / BM;
+  const int lid = xcd_remap(blockIdx.x, nbn * nbm);
+  const int bm = lid / nbn, bn = lid % nbn;  // the n tiles of one m row are neighbours
+  const int m0 = bm * BM, n0 = bn * kCfBN;
+  const int nk = K / kCfBK;
+
+  // ---- copy maps: slot (copy * 64 + lane) of a tile image -> global byte offset
+  constexpr uint32_t kNoCopy = 0x80000000u;
+  const uint32_t xrow = (uint32_t)K * 2, wrow = (uint32_t)N * 2;
+  uint32_t xoff[L::kXcp], woff[L::kWcp];
+#pragma unroll
+  for (int i = 0; i < L::kXcp; ++i) {
+    const int slot = (wave + 4 * i) * 64 + lane;
+    const int r = slot / 9, ch = slot % 9;
+    xoff[i] = ch < 8 ? (uint32_t)r * xrow + ch * 16 : kNoCopy;
+  }
+#pragma unroll
+  for (int i = 0; i < L::kWcp; ++i) {
+    const int slot = (wave + 4 * i) * 64 + lane;
+    const int r = slot / 20, ch = slot % 20;
+    woff[i] = ch < 16 ? (uint32_t)r * wrow + ch * 16 : kNoCopy;
+  }
+  // x rows at or past M and W rows past K lie past their buffer ends: no write.
+  const uint64_t xbytes = (uint64_t)M * K * 2, wbytes = (uint64_t)K * N * 2;
+  auto copy_tile = [&](int kt, int st) {
+    uint16_t* xs = smem + st * L::kStage;
+    uint16_t* ws = xs + L::kX;
+    const uint64_t xb = (uint64_t)m0 * K * 2 + (uint64_t)kt * kCfBK * 2;
+    const uint64_t wb = (uint64_t)kt * kCfBK * N * 2 + (uint64_t)n0 * 2;
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(reinterpret_cast<const char*>(x) + xb, (uint32_t)min(xbytes - xb, (uint64_t)0x7fffffff));
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(reinterpret_cast<const char*>(w) + wb, (uint32_t)min(wbytes - wb, (uint64_t)0x7fffffff));
+#pragma unroll
+    for (int i = 0; i < L::kXcp; ++i) {
+      const int cp = wq + 4 * i;
+      if (cp < L::kXCopies) dma16(xr, xs + cp * 512, xoff[i], 0);
+    }
+#pragma unroll
+    for (int i = 0; i < L::kWcp; ++i) {
+      const int cp = wq + 4 * i;
+      if (cp < L::kWCopies) dma16(wr, ws + cp * 512, woff[i], 0);
+    }
+  };
+
+  f32x16_t acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
+
+  // operand fragments of one 16-deep k step
+  const int bg = lane >> 4, bp = lane & 15;                   // transposing-read lane group
+  const int b_n = 16 * (bg & 1) + 4 * (bp & 3), b_k = 8 * (bg >> 1) + (bp >> 2);
+  auto frags = [&](const uint16_t* xs, const uint16_t* ws, int ks, u32x4_t (&a)[MI], u32x4_t (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a[i] = ld16(xs + (wm * (BM / 2) + i * 32 + l32) * kCfXld + ks * 16 + hf * 8);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint16_t* p = ws + (ks * 16 + b_k) * kCfWld + wn * 64 + j * 32 + b_n;
+      const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * kCfWld);
+      b[j] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
+
+  copy_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) copy_tile(kt + 1, st ^ 1);
+    const uint16_t* xs = smem + st * L::kStage;
+    const uint16_t* ws = xs + L::kX;
+    u32x4_t a[2][MI], b[2][2];
+    frags(xs, ws, 0, a[0], b[0]);
+    static_for<0, kCfBK / 16>([&](auto ks) {
+      constexpr int cur = ks & 1;
+      if constexpr (ks + 1 < kCfBK / 16) frags(xs, ws, ks + 1, a[cur ^ 1], b[cur ^ 1]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_bf16(a[cur][i], b[cur][j], acc[i][j]);
+    });
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int gn = n0 + wn * 64 + j * 32 + l32;
+    if (gn >= N) continue;
+    const float bv = bias ? bf16_to_f32(bias[gn]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int gm = m0 + wm * (BM / 2) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
+        if (gm < M) out[(int64_t)gm * N + gn] = f32_to_bf16(acc[i][j][e] + bv);
+      }
+    }
+  }
+}
+
+template <int BM>
+static hipError_t launch_gemm_cf(const void* x, const void* w, const void* bias, void* out, int M, int K,
+                                 int N, hipStream_t s) {
+  auto kern = qkv_gemm_cf_kernel<BM>;
+  const size_t lds = CfLds<BM>::kBytes;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int nblk = ((M + BM - 1) / BM) * ((N + kCfBN - 1) / kCfBN);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kCfThreads), lds, s, (const uint16_t*)x, (const uint16_t*)w,
+                     (const uint16_t*)bias, (uint16_t*)out, M, K, N);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------------------- skinny M
 // M <= 128 (decode batches, short prompts): the weight is streamed once and is
 // the whole cost, so the grid is widened by splitting the k range over
@@ -424,6 +585,14 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
                          (const float*)ws, (const uint16_t*)bias, (uint16_t*)out, m, n, p.ksplit);
     }
     return hipGetLastError();
+  }
+#ifndef MQKV_GEMM_CF
+#define MQKV_GEMM_CF 1
+#endif
+  if (MQKV_GEMM_CF && K % kCfBK == 0 && N % 8 == 0 && (uint64_t)K * N * 2 < 0x80000000ull) {
+    const int64_t t128 = ((M + 127) / 128) * ((N + kCfBN - 1) / kCfBN);
+    if (t128 >= 256) return launch_gemm_cf<128>(x, w, bias, out, m, k, n, s);
+    if (M > 128) return launch_gemm_cf<64>(x, w, bias, out, m, k, n, s);
   }
   // Pick the largest tile that still gives the chip (256 CUs) a full wave of workgroups.
   const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
