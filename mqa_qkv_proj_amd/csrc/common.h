@@ -39,6 +39,13 @@ __device__ __forceinline__ f32x16_t mfma32_f16(u32x4_t a, u32x4_t b, f32x16_t c)
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// 16x16x32: A (16 x 32): lane l holds row l%16, k slots of group l/16; B (32 x 16):
+// column l%16, the same k group; D (16 x 16): column l%16, rows 4*(l/16) + i.
+__device__ __forceinline__ f32x4_t mfma16_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // bf16 halves of a packed dword -> exact fp32.
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }

@@ -5,13 +5,19 @@
 // the diff of LlamaAttention.forward).  The split into Q/K/V is free: callers
 // address the packed rows with a token stride.
 //
-// bf16 path: bf16 MFMA 32x32x16 with fp32 accumulation, bf16 output (RNE).
-//   x tiles are k-contiguous and go to LDS unchanged.  W is n-contiguous; each
-//   thread loads a 4(k) x 8(n) block with 16-byte loads and writes it to LDS
-//   transposed (n-major, k-contiguous), so both MFMA operands are read from LDS
-//   with one 16-byte read per lane.  Tiles are double buffered in LDS with a
-//   register prefetch of the next tile.  Small M uses a split of the k range
-//   over the workgroup's waves, reduced through LDS at the end.
+// bf16 path: bf16 MFMA with fp32 accumulation, bf16 output (RNE).  Kernels,
+// chosen by shape in launch_qkv_gemm:
+//  * M <= 32, N <= 4096, K % 128 == 0: 16-column streaming kernel (no k split);
+//  * M <= 128, K % 64 == 0: 32-column streaming kernel, k split over
+//    workgroups with a fixed-order reduce kernel when the columns alone leave
+//    CUs idle;
+//  * M <= 128 otherwise: register-staged skinny kernel with the same split;
+//  * M > 128, K % 64 == 0, N % 8 == 0: LDS-DMA fed 128x128 / 64x128 tiles, the
+//    W tile kept row-major and read with transposing LDS loads;
+//  * anything else: register-prefetched tiles with W transposed into LDS by
+//    the loading threads.
+// The streaming kernels treat the weight as the whole cost (it is read once):
+// their workgroups stream W rows through an LDS ring filled by LDS-DMA.
 // fp32 path: plain LDS-tiled fp32 FMA (a correctness path for the tiny fp32 layer).
 #include "common.h"
 #include "launch.h"
@@ -267,10 +273,24 @@ struct CfLds {
   static_assert(kX * 2 % 1024 == 0 && kW * 2 % 1024 == 0, "tiles are whole 1 KB copies");
 };
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
-  const short4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)p);
-  return __builtin_bit_cast(uint2, r);
+// B operand of a 32x32x16 MFMA from a row-major W tile: two transposing reads
+// (k rows r and r+4 of this lane's group; HI_BYTES apart) that wait for
+// themselves.  Written as one asm block because the compiler treats the
+// builtin form as aliasing every LDS-DMA copy in flight and waits for all of
+// them first, which would serialize the copy pipeline; the callers order these
+// reads after the copies they need with their own vmcnt waits.
+template <int HI_BYTES>
+__device__ __forceinline__ u32x4_t lds_tr16_pair(const uint16_t* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+  u32x2_t lo, hi;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(a), "i"(HI_BYTES)
+      : "memory");
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 
 template <int BM>
@@ -342,9 +362,7 @@ __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
     for (int i = 0; i < MI; ++i) a[i] = ld16(xs + (wm * (BM / 2) + i * 32 + l32) * kCfXld + ks * 16 + hf * 8);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint16_t* p = ws + (ks * 16 + b_k) * kCfWld + wn * 64 + j * 32 + b_n;
-      const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * kCfWld);
-      b[j] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      b[j] = lds_tr16_pair<4 * kCfWld * 2>(ws + (ks * 16 + b_k) * kCfWld + wn * 64 + j * 32 + b_n);
     }
   };
 
@@ -507,7 +525,263 @@ __global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
   }
 }
 
-// Sum the k-range partials in a fixed order, add the bias, round to bf16.
+// ----------------------------------------------------------------------------- skinny M, streamed
+// M <= 128 with K % 64 == 0: a workgroup owns 32 columns of W (64 bytes of every
+// row) over a k range, and its 4 waves take the 16-row k steps of that range in
+// turn (wave w: steps w, w+4, ...).  Each wave streams on its own: a ring of D
+// LDS slots, each holding one k step's W rows (16 x 64 B) and x columns
+// (MI blocks of 32 rows x 32 B), filled by LDS-DMA D steps ahead, so about
+// 4 * D KB of W per workgroup is in flight with no register staging and no
+// barrier.  The B operand is read with ds_read_b64_tr_b16 from the row-major W
+// slot; the x slot is stored in A-fragment order, so its read is lane-linear.
+// The 4 waves' sums are added in LDS in a fixed order at the end; several k
+// ranges go through the fp32 workspace and the reduce kernel below.
+constexpr int kStBN = 32, kStThreads = 256;
+template <int MI, bool SHALLOW>
+struct StCfg {
+  // ring depth: as deep as 160 KB of LDS allows with one workgroup per CU, or
+  // a shorter ring for two (three at MI = 1) per CU
+  static constexpr int kDeep = MI == 1 ? 16 : MI == 2 ? 12 : MI == 3 ? 9 : 7;
+  static constexpr int kD = SHALLOW ? (MI == 1 ? 6 : (kDeep + 1) / 2) : kDeep;
+  static constexpr int kSlot = (1 + MI) * 512;  // bf16 elements: W rows, then x blocks
+  static constexpr size_t kBytes = (size_t)4 * kD * kSlot * sizeof(uint16_t);
+  static constexpr int kAhead = (kD - 1) * (1 + MI);  // loads issued after a step's own
+  static_assert(kAhead <= 63, "vmcnt range");
+  static_assert(kBytes >= (size_t)4 * MI * 16 * 64 * sizeof(float), "reduction fits in the ring");
+};
+
+// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int MI, bool SHALLOW>
+__global__ __launch_bounds__(kStThreads, 2) void qkv_gemm_stream_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, float* __restrict__ part, int M, int K, int N, int krange, int ksplit) {
+  using C = StCfg<MI, SHALLOW>;
+  constexpr int D = C::kD;
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int ks = lid % ksplit, cb = lid / ksplit;  // k ranges of one column block are neighbours
+  const int n0 = cb * kStBN;
+  const int kbeg = ks * krange, kend = min(K, kbeg + krange);
+  const int nst = (kend - kbeg) >> 6;  // k steps per wave
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)K * N * 2));
+  const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, xbytes);
+  // copy lane maps: W slot = 16 rows x 64 B, lane l -> row l/4, 16 B chunk l%4;
+  // x block i: slot position l holds row 32i + l%32, k half l/32 (A-fragment order);
+  // rows at or past M point past x and leave their LDS bytes untouched.
+  const uint32_t w_lane = (uint32_t)(lane >> 2) * N * 2 + (uint32_t)n0 * 2 + (lane & 3) * 16;
+  uint32_t x_lane[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = i * 32 + (lane & 31);
+    x_lane[i] = row < M ? (uint32_t)row * K * 2 + (lane >> 5) * 16 : 0x80000000u;
+  }
+  uint16_t* ring = smem + wq * D * C::kSlot;
+  auto issue = [&](int i, int slot) {  // k step i of this wave
+    const uint32_t k0 = (uint32_t)(kbeg + (i * 4 + wq) * 16);
+    uint16_t* sp = ring + slot * C::kSlot;
+    dma16(wr, sp, w_lane + k0 * (uint32_t)N * 2, 0);
+#pragma unroll
+    for (int j = 0; j < MI; ++j) dma16(xr, sp + (1 + j) * 512, x_lane[j] + k0 * 2, 0);
+  };
+  // transposing-read address of the B operand (column l%32, k rows 8*(l/32) ..)
+  const int bg = lane >> 4, bp = lane & 15;
+  const int b_off = (8 * (bg >> 1) + (bp >> 2)) * kStBN + 16 * (bg & 1) + 4 * (bp & 3);
+
+  f32x16_t acc[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) acc[i] = f32x16_t{};
+
+  static_for<0, D>([&](auto j) {
+    if (j < nst) issue(j, j);
+  });
+  for (int i0 = 0; i0 < nst; i0 += D) {
+    static_for<0, D>([&](auto j) {
+      const int i = i0 + j;
+      if (i < nst) {
+        if (i + D - 1 < nst) wait_vmcnt<C::kAhead>();
+        else wait_vmcnt<0>();
+        const uint16_t* sp = ring + j * C::kSlot;
+        const u32x4_t b = lds_tr16_pair<4 * kStBN * 2>(sp + b_off);
+#pragma unroll
+        for (int r = 0; r < MI; ++r) acc[r] = mfma32_bf16(ld16(sp + (1 + r) * 512 + lane * 8), b, acc[r]);
+        if (i + D < nst) {
+          wait_lgkm0();  // this slot's reads are done before the copy overwrites it
+          issue(i + D, j);
+        }
+      }
+    });
+  }
+  wait_vmcnt<0>();
+
+  // add the 4 waves' sums in wave order; each thread finishes MI*4 outputs
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int r = 0; r < MI; ++r)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[((wq * MI + r) * 16 + e) * 64 + lane] = acc[r][e];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < MI * 4; ++q) {
+    const int idx = q * kStThreads + tid;  // (r, e, lane) with lane fastest
+    const int ln = idx & 63, e = (idx >> 6) & 15, r = idx >> 10;
+    float v = red[idx];
+#pragma unroll
+    for (int wv = 1; wv < 4; ++wv) v += red[wv * MI * 1024 + idx];
+    const int m = r * 32 + 8 * (e >> 2) + 4 * (ln >> 5) + (e & 3), n = n0 + (ln & 31);
+    if (m < M) {
+      if (ksplit == 1) out[(int64_t)m * N + n] = f32_to_bf16(v + (bias ? bf16_to_f32(bias[n]) : 0.0f));
+      else part[((int64_t)ks * M + m) * N + n] = v;
+    }
+  }
+}
+
+template <int MI, bool SHALLOW>
+static hipError_t launch_stream(const void* x, const void* w, const void* bias, void* out, void* ws, int M,
+                                int K, int N, int krange, int ksplit, hipStream_t s) {
+  auto kern = qkv_gemm_stream_kernel<MI, SHALLOW>;
+  const size_t lds = StCfg<MI, SHALLOW>::kBytes;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((N / kStBN) * ksplit)), dim3(kStThreads), lds, s, (const uint16_t*)x,
+                     (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, (float*)ws, M, K, N, krange,
+                     ksplit);
+  return hipGetLastError();
+}
+
+template <bool SHALLOW>
+static hipError_t launch_stream_mi(int mi, const void* x, const void* w, const void* bias, void* out, void* ws,
+                                   int M, int K, int N, int krange, int ksplit, hipStream_t s) {
+  switch (mi) {
+    case 1: return launch_stream<1, SHALLOW>(x, w, bias, out, ws, M, K, N, krange, ksplit, s);
+    case 2: return launch_stream<2, SHALLOW>(x, w, bias, out, ws, M, K, N, krange, ksplit, s);
+    case 3: return launch_stream<3, SHALLOW>(x, w, bias, out, ws, M, K, N, krange, ksplit, s);
+    default: return launch_stream<4, SHALLOW>(x, w, bias, out, ws, M, K, N, krange, ksplit, s);
+  }
+}
+
+// ----------------------------------------------------------------------------- skinny M <= 32, streamed
+// M <= 32 with K % 128 == 0: the same streaming scheme on 16-column blocks
+// (MFMA 16x16x32, k steps of 32 rows).  On a narrow W this gives twice the
+// workgroups of the 32-column kernel without splitting k: no partials and no
+// second kernel.  W slot = 32 rows x 32 B; its rows are stored with index bits
+// 2 and 3 swapped so that the two 16-lane groups of a transposing read (rows r
+// and r+8) land on different LDS banks.  x block b (16 rows x 32 k) is stored
+// in A-fragment order.
+constexpr int kS16BN = 16;
+template <int MB, int D>
+__global__ __launch_bounds__(kStThreads, 2) void qkv_gemm_stream16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, int M, int K, int N) {
+  constexpr int kSlot = (1 + MB) * 512;     // bf16 elements: W rows, then x blocks
+  constexpr int kAhead = (D - 1) * (1 + MB);  // loads issued after a step's own
+  static_assert(kAhead <= 63, "vmcnt range");
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = xcd_remap(blockIdx.x, gridDim.x) * kS16BN;
+  const int nst = K >> 7;  // 32-row k steps per wave
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)K * N * 2));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+  // W copy: lane l -> slot row l/2 (k row with bits 2,3 swapped), 16 B chunk l%2
+  const int srow = lane >> 1;
+  const int krow = (srow & ~12) | ((srow & 4) << 1) | ((srow & 8) >> 1);
+  const uint32_t w_lane = (uint32_t)krow * N * 2 + (uint32_t)n0 * 2 + (lane & 1) * 16;
+  // x block b: slot position l holds row 16b + l%16, k group l/16; rows past M
+  // point past x and leave their LDS bytes untouched
+  uint32_t x_lane[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int row = b * 16 + (lane & 15);
+    x_lane[b] = row < M ? (uint32_t)row * K * 2 + (lane >> 4) * 16 : 0x80000000u;
+  }
+  uint16_t* ring = smem + wq * D * kSlot;
+  auto issue = [&](int i, int slot) {
+    const uint32_t k0 = (uint32_t)((i * 4 + wq) * 32);
+    uint16_t* sp = ring + slot * kSlot;
+    dma16(wr, sp, w_lane + k0 * (uint32_t)N * 2, 0);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) dma16(xr, sp + (1 + b) * 512, x_lane[b] + k0 * 2, 0);
+  };
+  // B operand: lane group g holds k rows 8g..8g+7 of column l%16
+  const int bg = lane >> 4, bp = lane & 15;
+  const int b_off = (16 * (bg >> 1) + 4 * (bg & 1) + (bp >> 2)) * kS16BN + 4 * (bp & 3);
+
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = f32x4_t{};
+
+  static_for<0, D>([&](auto j) {
+    if (j < nst) issue(j, j);
+  });
+  for (int i0 = 0; i0 < nst; i0 += D) {
+    static_for<0, D>([&](auto j) {
+      const int i = i0 + j;
+      if (i < nst) {
+        if (i + D - 1 < nst) wait_vmcnt<kAhead>();
+        else wait_vmcnt<0>();
+        const uint16_t* sp = ring + j * kSlot;
+        const u32x4_t bf = lds_tr16_pair<8 * kS16BN * 2>(sp + b_off);
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[b] = mfma16_bf16(ld16(sp + (1 + b) * 512 + lane * 8), bf, acc[b]);
+        if (i + D < nst) {
+          wait_lgkm0();
+          issue(i + D, j);
+        }
+      }
+    });
+  }
+  wait_vmcnt<0>();
+
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[((wq * MB + b) * 4 + e) * 64 + lane] = acc[b][e];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < MB; ++q) {
+    const int idx = q * kStThreads + tid;  // (b, e, lane) with lane fastest
+    const int ln = idx & 63, e = (idx >> 6) & 3, b = idx >> 8;
+    float v = red[idx];
+#pragma unroll
+    for (int wv = 1; wv < 4; ++wv) v += red[wv * MB * 256 + idx];
+    const int m = b * 16 + 4 * (ln >> 4) + e, n = n0 + (ln & 15);
+    if (m < M) out[(int64_t)m * N + n] = f32_to_bf16(v + (bias ? bf16_to_f32(bias[n]) : 0.0f));
+  }
+}
+
+template <int MB, int D>
+static hipError_t launch_stream16(const void* x, const void* w, const void* bias, void* out, int M, int K, int N,
+                                  hipStream_t s) {
+  auto kern = qkv_gemm_stream16_kernel<MB, D>;
+  const size_t lds = (size_t)4 * D * (1 + MB) * 512 * sizeof(uint16_t);
+  static_assert((size_t)4 * D * (1 + MB) * 512 * 2 >= (size_t)4 * MB * 4 * 64 * 4, "reduction fits");
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(N / kS16BN)), dim3(kStThreads), lds, s, (const uint16_t*)x,
+                     (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, M, K, N);
+  return hipGetLastError();
+}
+
+// Sum the k-range partials in a fixed order, add the bias, round to bf16.  The
+// loads of 8 k ranges are issued together (branch-free: buffer loads past the
+// end return zeros), so the kernel waits for one memory round trip per 8
+// ranges rather than one per range.
+constexpr int kMaxKsplit = 16;
 __global__ __launch_bounds__(256) void qkv_gemm_reduce_kernel(const float* __restrict__ part,
                                                               const uint16_t* __restrict__ bias,
                                                               uint16_t* __restrict__ out, int M, int N,
@@ -516,8 +790,16 @@ __global__ __launch_bounds__(256) void qkv_gemm_reduce_kernel(const float* __res
   const int64_t total = (int64_t)M * N;
   if (i >= total) return;
   const int n = (int)(i % N);
-  f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + i);
-  for (int k = 1; k < ksplit; ++k) s += *reinterpret_cast<const f32x4_t*>(part + (int64_t)k * total + i);
+  // loads past the last k range fall outside the buffer and read zeros
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(part, (uint32_t)(ksplit * total * 4));
+  f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < ksplit; k0 += 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = bld16(pr, (uint32_t)(((int64_t)(k0 + k) * total + i) * 4));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += __builtin_bit_cast(f32x4_t, v[k]);
+  }
   u32x2_t pk;
   const float b0 = bias ? bf16_to_f32(bias[n]) : 0.0f, b1 = bias ? bf16_to_f32(bias[n + 1]) : 0.0f;
   const float b2 = bias ? bf16_to_f32(bias[n + 2]) : 0.0f, b3 = bias ? bf16_to_f32(bias[n + 3]) : 0.0f;
@@ -544,8 +826,43 @@ static hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bia
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
   SkinnyPlan p{};
   // 32-bit buffer offsets cover W and x
-  if (M > 128 || N % kSkBN != 0 || K * N * 2 >= ((int64_t)1 << 32)) return p;
+  if (M > 128 || N % kSkBN != 0 || K * N * 2 >= ((int64_t)1 << 31) || M * K * 2 >= ((int64_t)1 << 31)) return p;
   p.nbm = (int)((M + 31) / 32);
+  // 16-column streaming kernel, no k split: used where its one workgroup per
+  // 16 columns does not exceed one per CU.  On wider W its 32-byte row pieces
+  // (a quarter of a cache line per workgroup) stream worse than the 32-column
+  // kernel with a k split plus the reduce kernel (measured at N = 5120..12288).
+  if (M <= 32 && K % 128 == 0 && N % kS16BN == 0 && N / kS16BN <= 256) {
+    p.stream16 = true;
+    p.krange = (int)K;
+    p.ksplit = 1;
+    p.ok = true;
+    return p;
+  }
+  if (K % 64 == 0) {
+    // Streaming kernel: one workgroup per 32 columns and k range.  A CU keeps
+    // only so many reads in flight, so the stream needs every CU: with one
+    // 32-row block, about three workgroups per CU (measured best on the
+    // 4096-deep decode projections); with more rows, where x is re-read per
+    // column block, split k only while the column blocks leave CUs idle.  Every
+    // extra k range costs an fp32 partial write and read and a second kernel;
+    // k ranges have at least 256 rows.
+    const int64_t ncb = N / kStBN;
+    int64_t ks = p.nbm == 1 ? (768 + ncb - 1) / ncb : ncb >= 128 ? 1 : 256 / ncb;
+    if (ks > K / 256) ks = K / 256;
+    if (ks > kMaxKsplit) ks = kMaxKsplit;
+    while (ks > 1 && ks * M * N * 4 >= ((int64_t)1 << 31)) --ks;  // partials in 32-bit offsets
+    if (ks < 1) ks = 1;
+    int64_t kr = (K + ks - 1) / ks;
+    kr = (kr + 63) / 64 * 64;
+    p.stream = true;
+    p.krange = (int)kr;
+    p.ksplit = (int)((K + kr - 1) / kr);
+    p.shallow = ncb * p.ksplit > 256;  // more workgroups than CUs: two or three per CU
+    p.ws_bytes = p.ksplit > 1 ? (size_t)p.ksplit * M * N * 4 : 0;
+    p.ok = true;
+    return p;
+  }
   const int64_t base = (N / kSkBN) * p.nbm;
   // about three workgroups per CU; each k range a multiple of the 128-deep chunk
   // and at most kSkMaxChunks chunks
@@ -553,12 +870,14 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
   const int64_t kmin = (K + kSkMaxChunks * kSkBK - 1) / (kSkMaxChunks * kSkBK);
   const int64_t kmax = (K + 255) / 256;
   if (ks > kmax) ks = kmax;
+  if (ks > kMaxKsplit) ks = kMaxKsplit;
   if (ks < kmin) ks = kmin;
   if (ks < 1) ks = 1;
   int64_t kr = (K + ks - 1) / ks;
   kr = (kr + kSkBK - 1) / kSkBK * kSkBK;
   p.krange = (int)kr;
   p.ksplit = (int)((K + kr - 1) / kr);
+  if (p.ksplit * M * N * 4 >= ((int64_t)1 << 31)) return SkinnyPlan{};  // partials in 32-bit offsets
   p.ws_bytes = p.ksplit > 1 ? (size_t)p.ksplit * M * N * 4 : 0;
   p.ok = true;
   return p;
@@ -574,7 +893,18 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
   }
   const int m = (int)M, k = (int)K, n = (int)N;
   const SkinnyPlan p = plan_skinny(M, K, N);
-  if (p.ok && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
+  if (p.ok && p.stream16)
+    return M > 16 ? launch_stream16<2, 6>(x, w, bias, out, m, k, n, s) : launch_stream16<1, 8>(x, w, bias, out, m, k, n, s);
+  if (p.ok && p.stream && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
+    hipError_t e = p.shallow ? launch_stream_mi<true>(p.nbm, x, w, bias, out, ws, m, k, n, p.krange, p.ksplit, s)
+                             : launch_stream_mi<false>(p.nbm, x, w, bias, out, ws, m, k, n, p.krange, p.ksplit, s);
+    if (e != hipSuccess || p.ksplit == 1) return e;
+    const int64_t quads = (M * N + 3) / 4;
+    hipLaunchKernelGGL(qkv_gemm_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                       (const float*)ws, (const uint16_t*)bias, (uint16_t*)out, m, n, p.ksplit);
+    return hipGetLastError();
+  }
+  if (p.ok && !p.stream && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
     const int64_t nblk = (N / kSkBN) * p.nbm * p.ksplit;
     hipLaunchKernelGGL(qkv_gemm_skinny_kernel, dim3((unsigned)nblk), dim3(kSkThreads), 0, s,
                        (const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out,
