@@ -9,11 +9,9 @@ namespace mqkv {
 struct SkinnyPlan {
   bool ok;        // the skinny path applies
   bool stream16;  // 16-column streaming kernel (M <= 32, K % 128 == 0), no k split
-  bool stream;    // streaming kernel (K % 64 == 0) rather than the general one
-  bool shallow;   // streaming kernel with the shorter copy ring (two workgroups per CU)
   int nbm;        // 32-row blocks
   int ksplit;     // k ranges
-  int krange;     // rows of W per k range (a multiple of 128, or of 64 when streaming)
+  int krange;     // rows of W per k range (a multiple of 128)
   size_t ws_bytes;  // fp32 partials needed when ksplit > 1
 };
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N);

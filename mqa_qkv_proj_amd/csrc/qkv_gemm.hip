@@ -7,17 +7,14 @@
 //
 // bf16 path: bf16 MFMA with fp32 accumulation, bf16 output (RNE).  Kernels,
 // chosen by shape in launch_qkv_gemm:
-//  * M <= 32, N <= 4096, K % 128 == 0: 16-column streaming kernel (no k split);
-//  * M <= 128, K % 64 == 0: 32-column streaming kernel, k split over
-//    workgroups with a fixed-order reduce kernel when the columns alone leave
-//    CUs idle;
-//  * M <= 128 otherwise: register-staged skinny kernel with the same split;
+//  * M <= 32, N <= 4096, K % 128 == 0: streaming kernel on 16-column blocks
+//    (W streamed through an LDS ring filled by LDS-DMA, no k split);
+//  * M <= 128 otherwise: register-staged skinny kernel, k split over
+//    workgroups with a fixed-order reduce kernel;
 //  * M > 128, K % 64 == 0, N % 8 == 0: LDS-DMA fed 128x128 / 64x128 tiles, the
 //    W tile kept row-major and read with transposing LDS loads;
 //  * anything else: register-prefetched tiles with W transposed into LDS by
 //    the loading threads.
-// The streaming kernels treat the weight as the whole cost (it is read once):
-// their workgroups stream W rows through an LDS ring filled by LDS-DMA.
 // fp32 path: plain LDS-tiled fp32 FMA (a correctness path for the tiny fp32 layer).
 #include "common.h"
 #include "launch.h"
@@ -525,31 +522,7 @@ __global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
   }
 }
 
-// ----------------------------------------------------------------------------- skinny M, streamed
-// M <= 128 with K % 64 == 0: a workgroup owns 32 columns of W (64 bytes of every
-// row) over a k range, and its 4 waves take the 16-row k steps of that range in
-// turn (wave w: steps w, w+4, ...).  Each wave streams on its own: a ring of D
-// LDS slots, each holding one k step's W rows (16 x 64 B) and x columns
-// (MI blocks of 32 rows x 32 B), filled by LDS-DMA D steps ahead, so about
-// 4 * D KB of W per workgroup is in flight with no register staging and no
-// barrier.  The B operand is read with ds_read_b64_tr_b16 from the row-major W
-// slot; the x slot is stored in A-fragment order, so its read is lane-linear.
-// The 4 waves' sums are added in LDS in a fixed order at the end; several k
-// ranges go through the fp32 workspace and the reduce kernel below.
-constexpr int kStBN = 32, kStThreads = 256;
-template <int MI, bool SHALLOW>
-struct StCfg {
-  // ring depth: as deep as 160 KB of LDS allows with one workgroup per CU, or
-  // a shorter ring for two (three at MI = 1) per CU
-  static constexpr int kDeep = MI == 1 ? 16 : MI == 2 ? 12 : MI == 3 ? 9 : 7;
-  static constexpr int kD = SHALLOW ? (MI == 1 ? 6 : (kDeep + 1) / 2) : kDeep;
-  static constexpr int kSlot = (1 + MI) * 512;  // bf16 elements: W rows, then x blocks
-  static constexpr size_t kBytes = (size_t)4 * kD * kSlot * sizeof(uint16_t);
-  static constexpr int kAhead = (kD - 1) * (1 + MI);  // loads issued after a step's own
-  static_assert(kAhead <= 63, "vmcnt range");
-  static_assert(kBytes >= (size_t)4 * MI * 16 * 64 * sizeof(float), "reduction fits in the ring");
-};
-
+// ----------------------------------------------------------------------------- LDS-DMA wait helpers
 // s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left at their maxima.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -558,130 +531,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int MI, bool SHALLOW>
-__global__ __launch_bounds__(kStThreads, 2) void qkv_gemm_stream_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, float* __restrict__ part, int M, int K, int N, int krange, int ksplit) {
-  using C = StCfg<MI, SHALLOW>;
-  constexpr int D = C::kD;
-  extern __shared__ __align__(16) uint16_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int ks = lid % ksplit, cb = lid / ksplit;  // k ranges of one column block are neighbours
-  const int n0 = cb * kStBN;
-  const int kbeg = ks * krange, kend = min(K, kbeg + krange);
-  const int nst = (kend - kbeg) >> 6;  // k steps per wave
-
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)K * N * 2));
-  const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, xbytes);
-  // copy lane maps: W slot = 16 rows x 64 B, lane l -> row l/4, 16 B chunk l%4;
-  // x block i: slot position l holds row 32i + l%32, k half l/32 (A-fragment order);
-  // rows at or past M point past x and leave their LDS bytes untouched.
-  const uint32_t w_lane = (uint32_t)(lane >> 2) * N * 2 + (uint32_t)n0 * 2 + (lane & 3) * 16;
-  uint32_t x_lane[MI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int row = i * 32 + (lane & 31);
-    x_lane[i] = row < M ? (uint32_t)row * K * 2 + (lane >> 5) * 16 : 0x80000000u;
-  }
-  uint16_t* ring = smem + wq * D * C::kSlot;
-  auto issue = [&](int i, int slot) {  // k step i of this wave
-    const uint32_t k0 = (uint32_t)(kbeg + (i * 4 + wq) * 16);
-    uint16_t* sp = ring + slot * C::kSlot;
-    dma16(wr, sp, w_lane + k0 * (uint32_t)N * 2, 0);
-#pragma unroll
-    for (int j = 0; j < MI; ++j) dma16(xr, sp + (1 + j) * 512, x_lane[j] + k0 * 2, 0);
-  };
-  // transposing-read address of the B operand (column l%32, k rows 8*(l/32) ..)
-  const int bg = lane >> 4, bp = lane & 15;
-  const int b_off = (8 * (bg >> 1) + (bp >> 2)) * kStBN + 16 * (bg & 1) + 4 * (bp & 3);
-
-  f32x16_t acc[MI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) acc[i] = f32x16_t{};
-
-  static_for<0, D>([&](auto j) {
-    if (j < nst) issue(j, j);
-  });
-  for (int i0 = 0; i0 < nst; i0 += D) {
-    static_for<0, D>([&](auto j) {
-      const int i = i0 + j;
-      if (i < nst) {
-        if (i + D - 1 < nst) wait_vmcnt<C::kAhead>();
-        else wait_vmcnt<0>();
-        const uint16_t* sp = ring + j * C::kSlot;
-        const u32x4_t b = lds_tr16_pair<4 * kStBN * 2>(sp + b_off);
-#pragma unroll
-        for (int r = 0; r < MI; ++r) acc[r] = mfma32_bf16(ld16(sp + (1 + r) * 512 + lane * 8), b, acc[r]);
-        if (i + D < nst) {
-          wait_lgkm0();  // this slot's reads are done before the copy overwrites it
-          issue(i + D, j);
-        }
-      }
-    });
-  }
-  wait_vmcnt<0>();
-
-  // add the 4 waves' sums in wave order; each thread finishes MI*4 outputs
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int r = 0; r < MI; ++r)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[((wq * MI + r) * 16 + e) * 64 + lane] = acc[r][e];
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < MI * 4; ++q) {
-    const int idx = q * kStThreads + tid;  // (r, e, lane) with lane fastest
-    const int ln = idx & 63, e = (idx >> 6) & 15, r = idx >> 10;
-    float v = red[idx];
-#pragma unroll
-    for (int wv = 1; wv < 4; ++wv) v += red[wv * MI * 1024 + idx];
-    const int m = r * 32 + 8 * (e >> 2) + 4 * (ln >> 5) + (e & 3), n = n0 + (ln & 31);
-    if (m < M) {
-      if (ksplit == 1) out[(int64_t)m * N + n] = f32_to_bf16(v + (bias ? bf16_to_f32(bias[n]) : 0.0f));
-      else part[((int64_t)ks * M + m) * N + n] = v;
-    }
-  }
-}
-
-template <int MI, bool SHALLOW>
-static hipError_t launch_stream(const void* x, const void* w, const void* bias, void* out, void* ws, int M,
-                                int K, int N, int krange, int ksplit, hipStream_t s) {
-  auto kern = qkv_gemm_stream_kernel<MI, SHALLOW>;
-  const size_t lds = StCfg<MI, SHALLOW>::kBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)((N / kStBN) * ksplit)), dim3(kStThreads), lds, s, (const uint16_t*)x,
-                     (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, (float*)ws, M, K, N, krange,
-                     ksplit);
-  return hipGetLastError();
-}
-
-template <bool SHALLOW>
-static hipError_t launch_stream_mi(int mi, const void* x, const void* w, const void* bias, void* out, void* ws,
-                                   int M, int K, int N, int krange, int ksplit, hipStream_t s) {
-  switch (mi) {
-    case 1: return launch_stream<1, SHALLOW>(x, w, bias, out, ws, M, K, N, krange, ksplit, s);
-    case 2: return launch_stream<2, SHALLOW>(x, w, bias, out, ws, M, K, N, krange, ksplit, s);
-    case 3: return launch_stream<3, SHALLOW>(x, w, bias, out, ws, M, K, N, krange, ksplit, s);
-    default: return launch_stream<4, SHALLOW>(x, w, bias, out, ws, M, K, N, krange, ksplit, s);
-  }
-}
-
 // ----------------------------------------------------------------------------- skinny M <= 32, streamed
-// M <= 32 with K % 128 == 0: the same streaming scheme on 16-column blocks
-// (MFMA 16x16x32, k steps of 32 rows).  On a narrow W this gives twice the
-// workgroups of the 32-column kernel without splitting k: no partials and no
-// second kernel.  W slot = 32 rows x 32 B; its rows are stored with index bits
-// 2 and 3 swapped so that the two 16-lane groups of a transposing read (rows r
-// and r+8) land on different LDS banks.  x block b (16 rows x 32 k) is stored
-// in A-fragment order.
-constexpr int kS16BN = 16;
+// M <= 32 with K % 128 == 0 and a narrow W: the weight is the whole cost, so a
+// workgroup owns 16 columns of W over all of K and streams them.  Its 4 waves
+// take the 32-row k steps in turn (wave w: steps w, w+4, ...), each through a
+// ring of D LDS slots of its own (one step's W rows, 32 x 32 B, and x columns,
+// MB blocks of 16 rows x 32 k) filled by LDS-DMA D steps ahead: no register
+// staging and no barrier until the 4 waves' sums are added in LDS, in wave
+// order, at the end.  MFMA 16x16x32; the B operand is read with
+// ds_read_b64_tr_b16 from the row-major W slot, whose rows are stored with
+// index bits 2 and 3 swapped so that the two 16-lane groups of a read (rows r
+// and r+8) land on different LDS banks; x is stored in A-fragment order.  With
+// one workgroup per 16 columns there is no k split: no partials and no second
+// kernel.
+constexpr int kS16BN = 16, kS16Threads = 256;
 template <int MB, int D>
-__global__ __launch_bounds__(kStThreads, 2) void qkv_gemm_stream16_kernel(
+__global__ __launch_bounds__(kS16Threads, 2) void qkv_gemm_stream16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ out, int M, int K, int N) {
   constexpr int kSlot = (1 + MB) * 512;     // bf16 elements: W rows, then x blocks
@@ -754,7 +619,7 @@ __global__ __launch_bounds__(kStThreads, 2) void qkv_gemm_stream16_kernel(
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < MB; ++q) {
-    const int idx = q * kStThreads + tid;  // (b, e, lane) with lane fastest
+    const int idx = q * kS16Threads + tid;  // (b, e, lane) with lane fastest
     const int ln = idx & 63, e = (idx >> 6) & 3, b = idx >> 8;
     float v = red[idx];
 #pragma unroll
@@ -772,7 +637,7 @@ static hipError_t launch_stream16(const void* x, const void* w, const void* bias
   static_assert((size_t)4 * D * (1 + MB) * 512 * 2 >= (size_t)4 * MB * 4 * 64 * 4, "reduction fits");
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(N / kS16BN)), dim3(kStThreads), lds, s, (const uint16_t*)x,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(N / kS16BN)), dim3(kS16Threads), lds, s, (const uint16_t*)x,
                      (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, M, K, N);
   return hipGetLastError();
 }
@@ -830,36 +695,12 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
   p.nbm = (int)((M + 31) / 32);
   // 16-column streaming kernel, no k split: used where its one workgroup per
   // 16 columns does not exceed one per CU.  On wider W its 32-byte row pieces
-  // (a quarter of a cache line per workgroup) stream worse than the 32-column
+  // (a quarter of a cache line per workgroup) stream worse than the skinny
   // kernel with a k split plus the reduce kernel (measured at N = 5120..12288).
   if (M <= 32 && K % 128 == 0 && N % kS16BN == 0 && N / kS16BN <= 256) {
     p.stream16 = true;
     p.krange = (int)K;
     p.ksplit = 1;
-    p.ok = true;
-    return p;
-  }
-  if (K % 64 == 0) {
-    // Streaming kernel: one workgroup per 32 columns and k range.  A CU keeps
-    // only so many reads in flight, so the stream needs every CU: with one
-    // 32-row block, about three workgroups per CU (measured best on the
-    // 4096-deep decode projections); with more rows, where x is re-read per
-    // column block, split k only while the column blocks leave CUs idle.  Every
-    // extra k range costs an fp32 partial write and read and a second kernel;
-    // k ranges have at least 256 rows.
-    const int64_t ncb = N / kStBN;
-    int64_t ks = p.nbm == 1 ? (768 + ncb - 1) / ncb : ncb >= 128 ? 1 : 256 / ncb;
-    if (ks > K / 256) ks = K / 256;
-    if (ks > kMaxKsplit) ks = kMaxKsplit;
-    while (ks > 1 && ks * M * N * 4 >= ((int64_t)1 << 31)) --ks;  // partials in 32-bit offsets
-    if (ks < 1) ks = 1;
-    int64_t kr = (K + ks - 1) / ks;
-    kr = (kr + 63) / 64 * 64;
-    p.stream = true;
-    p.krange = (int)kr;
-    p.ksplit = (int)((K + kr - 1) / kr);
-    p.shallow = ncb * p.ksplit > 256;  // more workgroups than CUs: two or three per CU
-    p.ws_bytes = p.ksplit > 1 ? (size_t)p.ksplit * M * N * 4 : 0;
     p.ok = true;
     return p;
   }
@@ -895,16 +736,7 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
   const SkinnyPlan p = plan_skinny(M, K, N);
   if (p.ok && p.stream16)
     return M > 16 ? launch_stream16<2, 6>(x, w, bias, out, m, k, n, s) : launch_stream16<1, 8>(x, w, bias, out, m, k, n, s);
-  if (p.ok && p.stream && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
-    hipError_t e = p.shallow ? launch_stream_mi<true>(p.nbm, x, w, bias, out, ws, m, k, n, p.krange, p.ksplit, s)
-                             : launch_stream_mi<false>(p.nbm, x, w, bias, out, ws, m, k, n, p.krange, p.ksplit, s);
-    if (e != hipSuccess || p.ksplit == 1) return e;
-    const int64_t quads = (M * N + 3) / 4;
-    hipLaunchKernelGGL(qkv_gemm_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
-                       (const float*)ws, (const uint16_t*)bias, (uint16_t*)out, m, n, p.ksplit);
-    return hipGetLastError();
-  }
-  if (p.ok && !p.stream && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
+  if (p.ok && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
     const int64_t nblk = (N / kSkBN) * p.nbm * p.ksplit;
     hipLaunchKernelGGL(qkv_gemm_skinny_kernel, dim3((unsigned)nblk), dim3(kSkThreads), 0, s,
                        (const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out,
