@@ -309,15 +309,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     static_for<0, DS>([&](auto st) { kf[st] = ld16(ks + (j * 32 + l32) * S::kKld + st * 16 + hf * 8); });
   };
   // One pipelined step.  On entry `sc` holds the scores of the current half
-  // (its row max already folded into m_run) and `kf` the K fragments of the
-  // next half.  The step turns `sc` into P, computes the next half's scores
-  // into `sc`, adds P V for the current half (V^T `vc`, keys 32jc..) and, when
-  // NEXT, reads the K fragments of the half after that (`kn`, keys 32jn..)
-  // into `kf`.  The source order is the issue order: each score MFMA is
-  // followed by one pair of softmax values and one V read, each P.V MFMA by a
-  // row-sum step and one K read, so the vector and LDS units work while the
-  // matrix cores run and every operand is in flight long before it is used.
-  // Fences keep the compiler from regrouping.
+  // and `kf` the K fragments of the next half.  The step turns `sc` into P,
+  // computes the next half's scores into `sc`, adds P V for the current half
+  // (V^T `vc`, keys 32jc..) and, when NEXT, reads the K fragments of the half
+  // after that (`kn`, keys 32jn..) into `kf`.  The source order is the issue
+  // order: each score MFMA is followed by one pair of softmax values and one V
+  // read, each P.V MFMA by a row-sum step and one K read, so the vector and LDS
+  // units work while the matrix cores run and every operand is in flight long
+  // before it is used.  Fences keep the compiler from regrouping.
+  // P is computed with the running max as it stands, while the half's row max
+  // is folded in beside it; only if some row's max grew by more than kTau
+  // (rare after the first half) is the max raised, O and l rescaled and P
+  // recomputed, before any of P is used.  So the exponentials do not wait for
+  // the max reduction.
   auto step = [&](f32x16_t& sc, u32x4_t (&kf)[DS], const uint16_t* vc, int jc, const uint16_t* kn,
                   int jn, auto next_tag, auto part0) {
     constexpr bool NEXT = decltype(next_tag)::value;
@@ -325,16 +329,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     u32x4_t pf[2];
     u32x4_t vf[2 * DB];
     f32x16_t sn = f32x16_t{};
+    float mx = sc[0];
     static_for<0, 8>([&](auto i) {
       constexpr int hb = i >> 2, e = i & 3;
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
       pf[hb][e] = pack_f16(p0, p1);
+      mx = fmaxf(fmaxf(mx, sc[hb * 8 + 2 * e]), sc[hb * 8 + 2 * e + 1]);
       if constexpr (i < DS) sn = mfma32_bf16(kf[i], qf[i], sn);
       if constexpr (i < 2 * DB)
         vf[i] = ld16(vc + ((i % DB) * 32 + l32) * S::kVld + (jc * 2 + i / DB) * 16 + hf * 8);
       __builtin_amdgcn_sched_barrier(0);
     });
+    mx = max_xor32(mx);
+    const float mt = mx * c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
+      const float mn = (mt > m_run + kTau) ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
+          pf[hb][e] = pack_f16(p0, p1);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
     static_for<0, 2 * DB>([&](auto i) {
       constexpr int hb = i / DB, db = i % DB;
@@ -382,9 +407,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     fill_begin(t + 2, st2);
     step(sc, kf, v_of(st0), 0, k_of(st1), 0, std::true_type{}, std::integral_constant<int, 0>{});
-    update_max(sc);
     step(sc, kf, v_of(st0), 1, k_of(st1), 1, std::true_type{}, std::integral_constant<int, 2 * DB>{});
-    update_max(sc);
     static_for<4 * DB, kParts>([&](auto i) { fill_part(i); });
     wait_dma();
     __syncthreads();
