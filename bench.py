@@ -1,6 +1,6 @@
 """Benchmark of the attention-layer hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--sweep]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--sweep] [--decode-loop]
 
 One step is one pass of the whole path over one batch of synthetic input, in
 the two shapes the headline metric is quoted on:
@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--sweep", action="store_true", help="also time every configuration (stderr)")
+    p.add_argument("--decode-loop", action="store_true",
+                   help="also time the 1024-step MQA decode loop, eager and as one HIP graph (stderr)")
     p.add_argument("--calib-copy", action="store_true",
                    help="run one 256 MiB device-to-device copy first (known-size reference for HBM "
                         "byte counters)")
@@ -208,6 +210,8 @@ def main():
     }
     if args.sweep:
         sweep(m, W, torch, dev, stream)
+    if args.decode_loop:
+        decode_loop(m, W, torch, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -323,6 +327,72 @@ def sweep(m, W, torch, dev, stream):
                             "gbps": round(by / us / 1e3, 1)}))
             del kc, vc
         torch.cuda.empty_cache()
+
+
+def decode_loop(m, W, torch, dev, stream):
+    """The MQA decode workload as it runs: 1024 steps of (projection with the new
+    token's K/V appended to the cache, decode, lengths + 1), the cache growing
+    from 17 to 1040 keys.  Timed eagerly and as one captured HIP graph of all
+    steps (3 kernels per step); prints per-step times to stderr."""
+    import numpy as np
+
+    wl = W.WORKLOADS["mqa_decode"]
+    steps = wl.len_hi - wl.len_lo + 1
+
+    def up(a):
+        bits = W.bf16_bits(np.ascontiguousarray(a, dtype=np.float32))
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    din = W.decode_inputs(wl)
+    kc, vc = up(din["k_cache"]), up(din["v_cache"])
+    lens0 = torch.from_numpy(W.decode_lengths(wl, 0)).to(dev)
+    lens = lens0.clone()
+    w = up(W.proj_inputs(wl)["w"])
+    xs = torch.stack([up(W.proj_inputs(wl, step=s)["x"]) for s in range(steps)])
+    qkv = torch.empty(wl.B, wl.N, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(wl.B, wl.H_q, wl.d, dtype=torch.bfloat16, device=dev)
+    ws_p = torch.empty(max(16, m.qkv_proj_workspace_bytes(wl.B, wl.hidden, wl.H_q, wl.H_kv, wl.d)),
+                       dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(m.decode_workspace_bytes(wl.B, wl.H_q, wl.H_kv, wl.d, wl.L_max), dtype=torch.uint8,
+                       device=dev)
+    scale = 1.0 / math.sqrt(wl.d)
+    q_view = qkv[:, :wl.H_q * wl.d].unflatten(-1, (wl.H_q, wl.d))
+
+    def run_all():
+        for s in range(steps):
+            m.qkv_proj_append(xs[s], w, kc, vc, lens, wl.H_q, wl.H_kv, wl.d, out=qkv, workspace=ws_p)
+            m.gqa_attn_decode(q_view, kc, vc, lens, scale=scale, workspace=ws_d, out=o)
+            lens.add_(1)
+
+    def timed(fn):
+        lens.copy_(lens0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps  # us per step
+
+    with torch.cuda.stream(stream):
+        lens.copy_(lens0)
+        run_all()  # warm-up
+        eager = min(timed(run_all) for _ in range(3))
+        out_eager = o.clone()
+        graph = torch.cuda.CUDAGraph()
+        lens.copy_(lens0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            run_all()
+        graphed = min(timed(graph.replay) for _ in range(3))
+        same = bool(torch.equal(o, out_eager))
+    kv_bytes = sum(2.0 * wl.B * (wl.len_lo + s) * wl.H_kv * wl.d * 2 for s in range(steps)) / steps
+    w_bytes = 2.0 * wl.hidden * wl.N
+    log(json.dumps({"decode_loop": wl.name, "steps": steps, "eager_us_per_step": round(eager, 2),
+                    "graph_us_per_step": round(graphed, 2), "graph_speedup": round(eager / graphed, 2),
+                    "bytes_per_step_mb": round((kv_bytes + w_bytes) / 1e6, 2),
+                    "graph_gbps": round((kv_bytes + w_bytes) / graphed / 1e3, 1),
+                    "last_step_output_equal": same}))
 
 
 if __name__ == "__main__":

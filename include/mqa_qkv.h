@@ -7,6 +7,8 @@
  *                        q/k/v projections ("Optimize LlamaAttention by fusing
  *                        QKV projections", transformers PR #40092, the diff of
  *                        LlamaAttention.forward);
+ *      qkv_proj_append   the same GEMM for a decode step, also writing the
+ *                        new token's K and V rows into the KV caches;
  *   2. the split into Q, K, V is not a call: Q, K and V are strided views of
  *      the packed qkv rows (same diff: query columns first, then key, then
  *      value; within a block the column is head*d + c).  The attention calls
@@ -82,6 +84,37 @@ size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t 
 mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv,
                      int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                      mqkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode-step projection with the KV-cache append fused into its epilogue.
+ *
+ * The GEMM of qkv_proj with M = B rows, row b being sequence b's new token.
+ * The same kernels also write the K and V column blocks of row b into the
+ * caches, at that token's position:
+ *
+ *   k_cache[b, seq_lens[b]-1, g, c] = qkv[b, H_q*d + g*d + c]
+ *   v_cache[b, seq_lens[b]-1, g, c] = qkv[b, (H_q+H_kv)*d + g*d + c]
+ *
+ * so gqa_attn_decode can follow directly with the same seq_lens: the new token
+ * is the last attended key, the cache convention of gqa_attn_decode (decode
+ * against a cache, "MHA -> GQA" blog, section 3.1).  Both copies of the values
+ * are bit-identical.  Nothing else of the caches is touched.  A row b whose
+ * seq_lens[b] lies outside [1, L_max] is projected but not appended.
+ *
+ * k_cache, v_cache [B, L_max, H_kv, d] contiguous, dtype `dtype`, 16-byte aligned
+ * seq_lens         [B] device int32: the lengths including the new token
+ * x, w_qkv, bias, qkv, workspace (qkv_proj_workspace_bytes(B, ...)) and their
+ * requirements are those of qkv_proj; additionally L_max >= 1.  B == 0 is a
+ * no-op.  The call allocates and synchronises nothing, so a whole decode step
+ * (this call, then gqa_attn_decode) can be captured and replayed as one HIP
+ * graph, the launch-overhead remedy the "custom op overhead" gist measures
+ * (its eager vs full-graph timing table).
+ */
+mqkv_status qkv_proj_append(const void* x, const void* w_qkv, const void* bias, void* qkv,
+                            void* k_cache, void* v_cache, const int32_t* seq_lens,
+                            int32_t B, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
+                            int32_t L_max, mqkv_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Grouped-query attention over a whole sequence (prefill).

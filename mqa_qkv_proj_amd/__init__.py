@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libmqa_qkv.so")
 MQKV_OK, MQKV_ERR_INVALID, MQKV_ERR_UNSUPPORTED, MQKV_ERR_HIP = 0, 1, 2, 3
 MQKV_F32, MQKV_BF16 = 0, 1
 
-EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "gqa_attn_prefill_workspace_bytes", "gqa_attn_prefill",
+EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill_workspace_bytes",
+           "gqa_attn_prefill",
            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "mqkv_status_string", "mqkv_last_error",
            "mqkv_abi_version")
 
@@ -51,6 +52,8 @@ def _load() -> ctypes.CDLL:
     lib.qkv_proj_workspace_bytes.restype = sz
     lib.qkv_proj.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, sz, vp]
     lib.qkv_proj.restype = i32
+    lib.qkv_proj_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.qkv_proj_append.restype = i32
     lib.gqa_attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.gqa_attn_prefill_workspace_bytes.restype = sz
     lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32,
@@ -166,6 +169,50 @@ def qkv_proj(x, w_qkv, H_q: int, H_kv: int, d: int, bias=None, out=None, workspa
                       out.data_ptr(), M, hidden, H_q, H_kv, d, _dtype_code(x.dtype), ws_ptr, ws_bytes,
                       _stream(x.device))
     check(st, "qkv_proj")
+    return out
+
+
+def qkv_proj_append(x, w_qkv, k_cache, v_cache, seq_lens, H_q: int, H_kv: int, d: int, bias=None, out=None,
+                    workspace=None):
+    """Decode-step projection that also appends the new token's K/V rows to the caches.
+
+    x [B, hidden] (row b = sequence b's new token), caches [B, L_max, H_kv, d]
+    contiguous, seq_lens [B] int32 on the device (lengths including the new
+    token).  Returns qkv [B, N] like qkv_proj and writes k_cache[b, seq_lens[b]-1]
+    and v_cache[b, seq_lens[b]-1] in place."""
+    torch = _torch()
+    _require_cuda(x, w_qkv, k_cache, v_cache, seq_lens, bias, out, workspace)
+    if x.dim() != 2:
+        raise ValueError("x must be [B, hidden]")
+    B, hidden = x.shape
+    N = (H_q + 2 * H_kv) * d
+    if w_qkv.shape != (hidden, N):
+        raise ValueError(f"w_qkv must be [{hidden}, {N}], got {tuple(w_qkv.shape)}")
+    if not (x.is_contiguous() and w_qkv.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("x, w_qkv and the caches must be contiguous")
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[2:] != (H_kv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError(f"caches must be [{B}, L_max, {H_kv}, {d}]")
+    if k_cache.dtype != x.dtype or v_cache.dtype != x.dtype or w_qkv.dtype != x.dtype:
+        raise ValueError("x, w_qkv and the caches must share a dtype")
+    if bias is not None and (bias.dtype != x.dtype or bias.shape != (N,)):
+        raise ValueError("bias must be [N] of x's dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    if out is None:
+        out = torch.empty(B, N, dtype=x.dtype, device=x.device)
+    elif out.shape != (B, N) or not out.is_contiguous() or out.dtype != x.dtype:
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if workspace is None:
+        need = qkv_proj_workspace_bytes(B, hidden, H_q, H_kv, d, _dtype_code(x.dtype))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.qkv_proj_append(x.data_ptr(), w_qkv.data_ptr(), bias.data_ptr() if bias is not None else None,
+                             out.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B,
+                             hidden, H_q, H_kv, d, k_cache.shape[1], _dtype_code(x.dtype), ws_ptr, ws_bytes,
+                             _stream(x.device))
+    check(st, "qkv_proj_append")
     return out
 
 

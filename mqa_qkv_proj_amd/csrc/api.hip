@@ -57,7 +57,7 @@ const char* mqkv_status_string(mqkv_status s) {
 
 const char* mqkv_last_error(void) { return g_err; }
 
-int32_t mqkv_abi_version(void) { return 102; }
+int32_t mqkv_abi_version(void) { return 103; }
 
 size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                                 mqkv_dtype dtype) {
@@ -69,10 +69,15 @@ size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t 
   return p.ok ? p.ws_bytes : 0;
 }
 
-mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, int64_t M,
-                     int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch shared by qkv_proj and qkv_proj_append.
+mqkv_status proj_common(const void* x, const void* w_qkv, const void* bias, void* qkv, int64_t M,
+                        int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream, const mqkv::KvAppend& app,
+                        const char* what) {
   if (!dtype_ok(dtype)) return fail(MQKV_ERR_INVALID, "dtype %d unknown", (int)dtype);
   mqkv_status st = check_heads(H_q, H_kv, d);
   if (st != MQKV_OK) return st;
@@ -88,10 +93,42 @@ mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* q
   if (M > 0x7fffffff || hidden > 0x7fffffff || N > 0x7fffffff)
     return fail(MQKV_ERR_UNSUPPORTED, "sizes beyond 2^31-1 are not supported");
   if (M == 0) return MQKV_OK;
-  return hip_status(mqkv::launch_qkv_gemm(x, w_qkv, bias, qkv, M, hidden, N, dtype == MQKV_BF16,
-                                          workspace, workspace ? workspace_bytes : 0,
-                                          (hipStream_t)stream),
-                    "qkv_proj launch");
+  return hip_status(mqkv::launch_qkv_gemm(x, w_qkv, bias, qkv, M, hidden, N, dtype == MQKV_BF16, workspace,
+                                          workspace ? workspace_bytes : 0, (hipStream_t)stream, app),
+                    what);
+}
+
+}  // namespace
+
+extern "C" {
+
+mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* qkv, int64_t M,
+                     int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const mqkv::KvAppend none{};
+  return proj_common(x, w_qkv, bias, qkv, M, hidden, H_q, H_kv, d, dtype, workspace, workspace_bytes, stream,
+                     none, "qkv_proj launch");
+}
+
+mqkv_status qkv_proj_append(const void* x, const void* w_qkv, const void* bias, void* qkv, void* k_cache,
+                            void* v_cache, const int32_t* seq_lens, int32_t B, int64_t hidden, int32_t H_q,
+                            int32_t H_kv, int32_t d, int32_t L_max, mqkv_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!k_cache || !v_cache || !seq_lens)
+    return fail(MQKV_ERR_INVALID, "k_cache, v_cache and seq_lens must be non-NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0)
+    return fail(MQKV_ERR_INVALID, "caches must be 16-byte aligned and seq_lens 4-byte aligned");
+  if (B < 0) return fail(MQKV_ERR_INVALID, "B=%d < 0", B);
+  if (L_max < 1) return fail(MQKV_ERR_INVALID, "L_max=%d must be >= 1", L_max);
+  const mqkv_status st = check_heads(H_q, H_kv, d);
+  if (st != MQKV_OK) return st;
+  if ((int64_t)(H_q + 2 * (int64_t)H_kv) * d > 0x7fffffff)
+    return fail(MQKV_ERR_UNSUPPORTED, "sizes beyond 2^31-1 are not supported");
+  const mqkv::KvAppend app{k_cache, v_cache, seq_lens, H_q * d, (H_q + H_kv) * d, L_max};
+  return proj_common(x, w_qkv, bias, qkv, B, hidden, H_q, H_kv, d, dtype, workspace, workspace_bytes, stream,
+                     app, "qkv_proj_append launch");
 }
 
 size_t gqa_attn_prefill_workspace_bytes(int32_t B, int32_t L_kv, int32_t H_kv, int32_t d,

@@ -16,8 +16,21 @@ struct SkinnyPlan {
 };
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N);
 
+// Optional projection epilogue: the K and V columns of row m are also written
+// to the caches [rows, L_max, H_kv, d] at token position seq_lens[m] - 1 (row m
+// is sequence m's new token).  k_cache == nullptr: no append.
+struct KvAppend {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* seq_lens;
+  int kcol;   // first K column (H_q * d)
+  int vcol;   // first V column ((H_q + H_kv) * d); H_kv * d = vcol - kcol
+  int L_max;
+};
+
 hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void* out, int64_t M,
-                           int64_t K, int64_t N, bool bf16, void* ws, size_t ws_bytes, hipStream_t s);
+                           int64_t K, int64_t N, bool bf16, void* ws, size_t ws_bytes, hipStream_t s,
+                           const KvAppend& app);
 
 struct PrefillArgs {
   const void* q;

@@ -21,6 +21,18 @@
 
 namespace mqkv {
 
+// The append epilogue for one output element (see KvAppend): a no-op unless an
+// append is requested, n is a K or V column and row m's position is valid.
+template <typename T>
+__device__ __forceinline__ void append_store(const KvAppend& a, int m, int n, T v) {
+  if (a.k_cache == nullptr || n < a.kcol) return;
+  const int len = a.seq_lens[m];
+  if (len < 1 || len > a.L_max) return;
+  const bool is_k = n < a.vcol;
+  T* cache = static_cast<T*>(is_k ? a.k_cache : a.v_cache);
+  cache[((int64_t)m * a.L_max + (len - 1)) * (a.vcol - a.kcol) + (n - (is_k ? a.kcol : a.vcol))] = v;
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int KS>
 struct GemmCfg {
   static constexpr int kWaves = WM * WN * KS;
@@ -43,7 +55,7 @@ struct GemmCfg {
 template <int BM, int BN, int BK, int WM, int WN, int KS>
 __global__ __launch_bounds__(WM* WN* KS * 64) void qkv_gemm_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int K, int N) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int K, int N, KvAppend app) {
   using C = GemmCfg<BM, BN, BK, WM, WN, KS>;
   extern __shared__ __align__(16) uint16_t smem[];
   // stage s: x tile at smem + s*kLdsTile, transposed W tile right after it
@@ -189,7 +201,11 @@ __global__ __launch_bounds__(WM* WN* KS * 64) void qkv_gemm_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int gm = m0 + wm * (BM / WM) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
-        if (gm < M) out[(int64_t)gm * N + gn] = f32_to_bf16(acc[i][j][e] + bv);
+        if (gm < M) {
+          const uint16_t r = f32_to_bf16(acc[i][j][e] + bv);
+          out[(int64_t)gm * N + gn] = r;
+          append_store(app, gm, gn, r);
+        }
       }
     }
   }
@@ -200,7 +216,7 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
                                                            const float* __restrict__ w,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ out, int M, int K,
-                                                           int N) {
+                                                           int N, KvAppend app) {
   __shared__ float As[16][64 + 1];
   __shared__ float Bs[16][64 + 4];
   const int tid = threadIdx.x;
@@ -236,7 +252,11 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int gn = n0 + tx * 4 + j;
-      if (gn < N) out[(int64_t)gm * N + gn] = acc[i][j] + (bias ? bias[gn] : 0.0f);
+      if (gn < N) {
+        const float r = acc[i][j] + (bias ? bias[gn] : 0.0f);
+        out[(int64_t)gm * N + gn] = r;
+        append_store(app, gm, gn, r);
+      }
     }
   }
 }
@@ -293,7 +313,7 @@ __device__ __forceinline__ u32x4_t lds_tr16_pair(const uint16_t* p) {
 template <int BM>
 __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int M, int K, int N) {
+    uint16_t* __restrict__ out, int M, int K, int N, KvAppend app) {
   using L = CfLds<BM>;
   constexpr int MI = BM / 64;  // 32-row MFMA blocks per wave
   extern __shared__ __align__(16) uint16_t smem[];
@@ -395,7 +415,11 @@ __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int gm = m0 + wm * (BM / 2) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
-        if (gm < M) out[(int64_t)gm * N + gn] = f32_to_bf16(acc[i][j][e] + bv);
+        if (gm < M) {
+          const uint16_t r = f32_to_bf16(acc[i][j][e] + bv);
+          out[(int64_t)gm * N + gn] = r;
+          append_store(app, gm, gn, r);
+        }
       }
     }
   }
@@ -403,14 +427,14 @@ __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
 
 template <int BM>
 static hipError_t launch_gemm_cf(const void* x, const void* w, const void* bias, void* out, int M, int K,
-                                 int N, hipStream_t s) {
+                                 int N, hipStream_t s, const KvAppend& app) {
   auto kern = qkv_gemm_cf_kernel<BM>;
   const size_t lds = CfLds<BM>::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int nblk = ((M + BM - 1) / BM) * ((N + kCfBN - 1) / kCfBN);
   hipLaunchKernelGGL(kern, dim3(nblk), dim3(kCfThreads), lds, s, (const uint16_t*)x, (const uint16_t*)w,
-                     (const uint16_t*)bias, (uint16_t*)out, M, K, N);
+                     (const uint16_t*)bias, (uint16_t*)out, M, K, N, app);
   return hipGetLastError();
 }
 
@@ -429,7 +453,7 @@ constexpr int kSkDepth = 3;      // chunks in flight ahead of the one being mult
 __global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ out, float* __restrict__ part, int M, int K, int N, int krange, int ksplit,
-    int nbm) {
+    int nbm, KvAppend app) {
   __shared__ __align__(16) uint16_t Bs[2][kSkBN * kSkLd];
   __shared__ __align__(16) float red[16 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -511,7 +535,11 @@ __global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int m = m0 + 8 * (e >> 2) + 4 * hf + (e & 3);
-      if (m < M) out[(int64_t)m * N + n] = f32_to_bf16(acc[e] + bv);
+      if (m < M) {
+        const uint16_t r = f32_to_bf16(acc[e] + bv);
+        out[(int64_t)m * N + n] = r;
+        append_store(app, m, n, r);
+      }
     }
   } else {
 #pragma unroll
@@ -548,7 +576,7 @@ constexpr int kS16BN = 16, kS16Threads = 256;
 template <int MB, int D>
 __global__ __launch_bounds__(kS16Threads, 2) void qkv_gemm_stream16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int M, int K, int N) {
+    uint16_t* __restrict__ out, int M, int K, int N, KvAppend app) {
   constexpr int kSlot = (1 + MB) * 512;     // bf16 elements: W rows, then x blocks
   constexpr int kAhead = (D - 1) * (1 + MB);  // loads issued after a step's own
   static_assert(kAhead <= 63, "vmcnt range");
@@ -625,20 +653,24 @@ __global__ __launch_bounds__(kS16Threads, 2) void qkv_gemm_stream16_kernel(
 #pragma unroll
     for (int wv = 1; wv < 4; ++wv) v += red[wv * MB * 256 + idx];
     const int m = b * 16 + 4 * (ln >> 4) + e, n = n0 + (ln & 15);
-    if (m < M) out[(int64_t)m * N + n] = f32_to_bf16(v + (bias ? bf16_to_f32(bias[n]) : 0.0f));
+    if (m < M) {
+      const uint16_t r = f32_to_bf16(v + (bias ? bf16_to_f32(bias[n]) : 0.0f));
+      out[(int64_t)m * N + n] = r;
+      append_store(app, m, n, r);
+    }
   }
 }
 
 template <int MB, int D>
 static hipError_t launch_stream16(const void* x, const void* w, const void* bias, void* out, int M, int K, int N,
-                                  hipStream_t s) {
+                                  hipStream_t s, const KvAppend& app) {
   auto kern = qkv_gemm_stream16_kernel<MB, D>;
   const size_t lds = (size_t)4 * D * (1 + MB) * 512 * sizeof(uint16_t);
   static_assert((size_t)4 * D * (1 + MB) * 512 * 2 >= (size_t)4 * MB * 4 * 64 * 4, "reduction fits");
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(N / kS16BN)), dim3(kS16Threads), lds, s, (const uint16_t*)x,
-                     (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, M, K, N);
+                     (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, M, K, N, app);
   return hipGetLastError();
 }
 
@@ -650,7 +682,7 @@ constexpr int kMaxKsplit = 16;
 __global__ __launch_bounds__(256) void qkv_gemm_reduce_kernel(const float* __restrict__ part,
                                                               const uint16_t* __restrict__ bias,
                                                               uint16_t* __restrict__ out, int M, int N,
-                                                              int ksplit) {
+                                                              int ksplit, KvAppend app) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // 4 consecutive outputs
   const int64_t total = (int64_t)M * N;
   if (i >= total) return;
@@ -671,11 +703,21 @@ __global__ __launch_bounds__(256) void qkv_gemm_reduce_kernel(const float* __res
   pk[0] = pack_bf16(s[0] + b0, s[1] + b1);
   pk[1] = pack_bf16(s[2] + b2, s[3] + b3);
   st8(out + i, pk);
+  // four consecutive columns never straddle the K/V boundaries (multiples of d)
+  if (app.k_cache != nullptr && n >= app.kcol) {
+    const int m = (int)(i / N), len = app.seq_lens[m];
+    if (len >= 1 && len <= app.L_max) {
+      const bool is_k = n < app.vcol;
+      uint16_t* cache = static_cast<uint16_t*>(is_k ? app.k_cache : app.v_cache);
+      st8(cache + ((int64_t)m * app.L_max + (len - 1)) * (app.vcol - app.kcol) + (n - (is_k ? app.kcol : app.vcol)),
+          pk);
+    }
+  }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int KS>
 static hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, void* out,
-                                   int M, int K, int N, hipStream_t s) {
+                                   int M, int K, int N, hipStream_t s, const KvAppend& app) {
   using C = GemmCfg<BM, BN, BK, WM, WN, KS>;
   const size_t lds = 2 * C::kLdsTile * sizeof(uint16_t);
   auto kern = qkv_gemm_bf16_kernel<BM, BN, BK, WM, WN, KS>;
@@ -684,7 +726,7 @@ static hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bia
   if (e != hipSuccess) return e;
   const int nblk = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3(nblk), dim3(C::kThreads), lds, s, (const uint16_t*)x,
-                     (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, M, K, N);
+                     (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, M, K, N, app);
   return hipGetLastError();
 }
 
@@ -725,26 +767,28 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
 }
 
 hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void* out, int64_t M,
-                           int64_t K, int64_t N, bool bf16, void* ws, size_t ws_bytes, hipStream_t s) {
+                           int64_t K, int64_t N, bool bf16, void* ws, size_t ws_bytes, hipStream_t s,
+                           const KvAppend& app) {
   if (!bf16) {
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     hipLaunchKernelGGL(qkv_gemm_f32_kernel, grid, dim3(256), 0, s, (const float*)x, (const float*)w,
-                       (const float*)bias, (float*)out, (int)M, (int)K, (int)N);
+                       (const float*)bias, (float*)out, (int)M, (int)K, (int)N, app);
     return hipGetLastError();
   }
   const int m = (int)M, k = (int)K, n = (int)N;
   const SkinnyPlan p = plan_skinny(M, K, N);
   if (p.ok && p.stream16)
-    return M > 16 ? launch_stream16<2, 6>(x, w, bias, out, m, k, n, s) : launch_stream16<1, 8>(x, w, bias, out, m, k, n, s);
+    return M > 16 ? launch_stream16<2, 6>(x, w, bias, out, m, k, n, s, app)
+                  : launch_stream16<1, 8>(x, w, bias, out, m, k, n, s, app);
   if (p.ok && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
     const int64_t nblk = (N / kSkBN) * p.nbm * p.ksplit;
     hipLaunchKernelGGL(qkv_gemm_skinny_kernel, dim3((unsigned)nblk), dim3(kSkThreads), 0, s,
                        (const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out,
-                       (float*)ws, m, k, n, p.krange, p.ksplit, p.nbm);
+                       (float*)ws, m, k, n, p.krange, p.ksplit, p.nbm, app);
     if (p.ksplit > 1) {
       const int64_t quads = (M * N + 3) / 4;
       hipLaunchKernelGGL(qkv_gemm_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
-                         (const float*)ws, (const uint16_t*)bias, (uint16_t*)out, m, n, p.ksplit);
+                         (const float*)ws, (const uint16_t*)bias, (uint16_t*)out, m, n, p.ksplit, app);
     }
     return hipGetLastError();
   }
@@ -753,15 +797,15 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
 #endif
   if (MQKV_GEMM_CF && K % kCfBK == 0 && N % 8 == 0 && (uint64_t)K * N * 2 < 0x80000000ull) {
     const int64_t t128 = ((M + 127) / 128) * ((N + kCfBN - 1) / kCfBN);
-    if (t128 >= 256) return launch_gemm_cf<128>(x, w, bias, out, m, k, n, s);
-    if (M > 128) return launch_gemm_cf<64>(x, w, bias, out, m, k, n, s);
+    if (t128 >= 256) return launch_gemm_cf<128>(x, w, bias, out, m, k, n, s, app);
+    if (M > 128) return launch_gemm_cf<64>(x, w, bias, out, m, k, n, s, app);
   }
   // Pick the largest tile that still gives the chip (256 CUs) a full wave of workgroups.
   const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
   const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
-  if (big >= 256) return launch_gemm_bf16<128, 128, 64, 2, 2, 1>(x, w, bias, out, m, k, n, s);
-  if (M > 32 && mid >= 128) return launch_gemm_bf16<64, 64, 64, 2, 2, 1>(x, w, bias, out, m, k, n, s);
-  return launch_gemm_bf16<32, 32, 256, 1, 1, 4>(x, w, bias, out, m, k, n, s);
+  if (big >= 256) return launch_gemm_bf16<128, 128, 64, 2, 2, 1>(x, w, bias, out, m, k, n, s, app);
+  if (M > 32 && mid >= 128) return launch_gemm_bf16<64, 64, 64, 2, 2, 1>(x, w, bias, out, m, k, n, s, app);
+  return launch_gemm_bf16<32, 32, 256, 1, 1, 4>(x, w, bias, out, m, k, n, s, app);
 }
 
 }  // namespace mqkv

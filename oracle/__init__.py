@@ -43,7 +43,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["qkv_proj", "split_qkv", "attention", "attention_rows", "decode",
-           "brute_attention", "kv_head_of"]
+           "brute_attention", "kv_head_of", "kv_append", "decode_step"]
 
 F64 = np.float64
 
@@ -177,6 +177,42 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, seq_lens: np
             O[b, h] = o[0]
             LSE[b, h] = l[0]
     return O, LSE
+
+
+def kv_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+              seq_lens: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Caches with each sequence's new token written at position seq_lens[b] - 1.
+
+    The decode convention read from the "MHA -> GQA" blog, section 3.1: the
+    token being generated attends to itself, so its key/value row is in the
+    cache, as the last of the seq_lens[b] attended keys, when decode runs.
+    k_cache, v_cache [B, L_max, H_kv, d]; k_new, v_new [B, H_kv, d]; rows whose
+    length is outside [1, L_max] are left as they are.  Returns new arrays.
+    """
+    kc = np.array(k_cache, dtype=F64, copy=True)
+    vc = np.array(v_cache, dtype=F64, copy=True)
+    for b in range(kc.shape[0]):
+        n = int(seq_lens[b])
+        if 1 <= n <= kc.shape[1]:
+            kc[b, n - 1] = k_new[b]
+            vc[b, n - 1] = v_new[b]
+    return kc, vc
+
+
+def decode_step(x: np.ndarray, w: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                seq_lens: np.ndarray, H_q: int, H_kv: int, d: int, scale: float,
+                bias: Optional[np.ndarray] = None):
+    """One whole decode step: project the new tokens, append their K/V, attend.
+
+    x [B, hidden] (one new token per sequence) -> (qkv [B, N], k_cache',
+    v_cache', O [B, H_q, d], LSE [B, H_q]): the fused projection (PR #40092
+    diff), its column split, the append above, then decode.
+    """
+    qkv = qkv_proj(x, w, bias)
+    q, k, v = split_qkv(qkv[:, None, :], H_q, H_kv, d)
+    kc, vc = kv_append(k_cache, v_cache, k[:, 0], v[:, 0], seq_lens)
+    O, LSE = decode(q[:, 0], kc, vc, seq_lens, scale)
+    return qkv, kc, vc, O, LSE
 
 
 def brute_attention(q, k, v, causal: bool, scale: float):

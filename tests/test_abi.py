@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("qkv_proj", "qkv_proj_workspace_bytes", "gqa_attn_prefill", "gqa_attn_prefill_workspace_bytes",
+    for n in ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill",
+              "gqa_attn_prefill_workspace_bytes",
               "gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
               "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version"):
         assert n in names
@@ -41,7 +42,7 @@ def test_status_strings(lib):
     assert L.mqkv_status_string(1) == b"invalid argument"
     assert L.mqkv_status_string(2) == b"unsupported configuration"
     assert L.mqkv_status_string(3) == b"HIP runtime error"
-    assert L.mqkv_abi_version() == 102
+    assert L.mqkv_abi_version() == 103
 
 
 def proj(lib, **kw):
@@ -49,6 +50,15 @@ def proj(lib, **kw):
     a.update(kw)
     return lib.lib.qkv_proj(a["x"], a["w"], a["bias"], a["out"], a["M"], a["hidden"], a["H_q"], a["H_kv"],
                             a["d"], a["dtype"], a.get("ws"), a.get("wsb", 0), None)
+
+
+def proj_append(lib, **kw):
+    a = dict(x=A, w=A, bias=None, out=A, kc=A, vc=A, lens=A, B=8, hidden=256, H_q=4, H_kv=2, d=64, Lmax=64,
+             dtype=BF16)
+    a.update(kw)
+    return lib.lib.qkv_proj_append(a["x"], a["w"], a["bias"], a["out"], a["kc"], a["vc"], a["lens"], a["B"],
+                                   a["hidden"], a["H_q"], a["H_kv"], a["d"], a["Lmax"], a["dtype"], a.get("ws"),
+                                   a.get("wsb", 0), None)
 
 
 def prefill(lib, **kw):
@@ -82,6 +92,21 @@ def test_qkv_proj_rejects(lib, kw, code):
 
 def test_qkv_proj_empty_is_noop(lib):
     assert proj(lib, M=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), INV), (dict(vc=None), INV), (dict(lens=None), INV), (dict(kc=A + 8), INV),
+    (dict(lens=A + 2), INV), (dict(B=-1), INV), (dict(Lmax=0), INV), (dict(x=None), INV),
+    (dict(H_q=3, H_kv=2), INV), (dict(d=96), UNS), (dict(hidden=260), INV), (dict(dtype=7), INV),
+    (dict(ws=A + 4, wsb=1 << 20), INV),
+])
+def test_qkv_proj_append_rejects(lib, kw, code):
+    assert proj_append(lib, **kw) == code
+    assert lib.lib.mqkv_last_error() != b""
+
+
+def test_qkv_proj_append_empty_is_noop(lib):
+    assert proj_append(lib, B=0) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -157,3 +182,7 @@ def test_python_layer_validates_without_gpu(lib):
     assert q.data_ptr() == qkv.data_ptr()
     assert k.data_ptr() == qkv.data_ptr() + 8 * 64 * 2 and v.data_ptr() == qkv.data_ptr() + 10 * 64 * 2
     assert q.stride(1) == k.stride(1) == (8 + 4) * 64
+    kc = torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # CPU tensors
+        lib.qkv_proj_append(x, torch.zeros(256, 512, dtype=torch.bfloat16), kc, kc.clone(),
+                            torch.ones(4, dtype=torch.int32), 4, 2, 64)

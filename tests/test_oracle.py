@@ -262,6 +262,41 @@ def test_decode_matches_attention_and_ignores_cache_tail():
     assert np.array_equal(O, O2) and np.array_equal(LSE, LSE2)
 
 
+def test_decode_steps_with_append_reproduce_causal_prefill_rows():
+    """Generating token by token (project, append, decode) must give, at step s,
+    row s of causal attention over the whole sequence: catches an append at the
+    wrong position or a decode that misses the new token."""
+    rng = np.random.default_rng(21)
+    B, T, hidden, H_q, H_kv, d, L_max = 2, 7, 12, 4, 2, 4, 9
+    N = (H_q + 2 * H_kv) * d
+    xs = rng.standard_normal((B, T, hidden))
+    w = rng.standard_normal((hidden, N)) / math.sqrt(hidden)
+    q_all, k_all, v_all = oracle.split_qkv(oracle.qkv_proj(xs, w), H_q, H_kv, d)
+    O_ref, L_ref = oracle.attention(q_all, k_all, v_all, True, 0.5)
+    kc = np.full((B, L_max, H_kv, d), 123.0)   # stale contents must not matter
+    vc = np.full((B, L_max, H_kv, d), -55.0)
+    for s_ in range(T):
+        lens = np.full(B, s_ + 1, dtype=np.int32)
+        qkv, kc2, vc2, O, LSE = oracle.decode_step(xs[:, s_], w, kc, vc, lens, H_q, H_kv, d, 0.5)
+        np.testing.assert_allclose(O, O_ref[:, s_], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(LSE, L_ref[:, :, s_], rtol=0, atol=1e-13)
+        # the append writes exactly one row per sequence and leaves the inputs alone
+        assert (kc2 != kc).any(axis=(2, 3)).sum() <= B and kc[0, 0, 0, 0] in (123.0, k_all[0, 0, 0, 0])
+        kc, vc = kc2, vc2
+    np.testing.assert_array_equal(kc[:, :T], k_all)
+    np.testing.assert_array_equal(vc[:, :T], v_all)
+    assert (kc[:, T:] == 123.0).all() and (vc[:, T:] == -55.0).all()
+
+
+def test_kv_append_skips_out_of_range_lengths():
+    kc, vc = np.zeros((3, 4, 1, 2)), np.zeros((3, 4, 1, 2))
+    kn, vn = np.ones((3, 1, 2)), 2 * np.ones((3, 1, 2))
+    kc2, vc2 = oracle.kv_append(kc, vc, kn, vn, np.array([0, 4, 5], dtype=np.int32))
+    assert kc2[0].sum() == 0 and kc2[2].sum() == 0            # lengths 0 and 5 > L_max: untouched
+    assert kc2[1, 3].sum() == 2 and vc2[1, 3].sum() == 4 and kc2[1, :3].sum() == 0
+    assert kc.sum() == 0                                        # inputs are not modified
+
+
 def _split_combine(q, kc, vc, lens, scale, chunk, n_split):
     """Test-local fp64 split-KV partial softmax + combine (the exact rescaling identity)."""
     B, H_q, d = q.shape
@@ -339,6 +374,7 @@ def _pins_pass(monkeypatch_ctx) -> bool:
         lambda: test_head_mapping_closed_form(),
         lambda: test_zero_keys_give_prefix_means(True),
         lambda: test_softmax_rows_sum_to_one_via_lse(),
+        lambda: test_decode_steps_with_append_reproduce_causal_prefill_rows(),
     ]
     for c in checks:
         try:
@@ -369,6 +405,18 @@ def test_planted_mistakes_are_caught(monkeypatch):
             oracle, "_softmax_rows",
             lambda S: (lambda P, l: (P, l - np.max(S, axis=-1)))(*_real_softmax(S))),
     }
+    real_append = oracle.kv_append
+
+    def append_one_late(kc, vc, kn, vn, lens):
+        # the new token written one position past its slot (where it is not attended)
+        kc2, vc2 = np.array(kc, dtype=float), np.array(vc, dtype=float)
+        for b in range(kc2.shape[0]):
+            n = int(lens[b])
+            if n < kc2.shape[1]:
+                kc2[b, n], vc2[b, n] = kn[b], vn[b]
+        return kc2, vc2
+    mutations["append_late"] = lambda: monkeypatch.setattr(oracle, "kv_append", append_one_late)
+    assert real_append is oracle.kv_append
     _real_softmax = oracle._softmax_rows
     for name, apply in mutations.items():
         monkeypatch.undo()
