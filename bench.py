@@ -319,6 +319,19 @@ def sweep(m, W, torch, dev, stream):
             by = 2.0 * (int(lens_np.sum()) * wl.H_kv * wl.d * 2 + 2 * wl.B * wl.H_q * wl.d)
             log(json.dumps({"sweep": name, "kernel": "decode", "us": round(us, 2),
                             "gbps": round(by / us / 1e3, 1), "frac": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}))
+            # the same rows in a shuffled pool of 16-key pages
+            P = 16
+            pps = wl.L_max // P
+            perm = torch.from_numpy(np.random.default_rng(wl.seed).permutation(wl.B * pps).astype(np.int32))
+            table = perm.reshape(wl.B, pps).to(dev)
+            kp = torch.empty(wl.B * pps, P, wl.H_kv, wl.d, dtype=torch.bfloat16, device=dev)
+            vp = torch.empty_like(kp)
+            kp[table.flatten().long()] = kc.reshape(wl.B * pps, P, wl.H_kv, wl.d)
+            vp[table.flatten().long()] = vc.reshape(wl.B * pps, P, wl.H_kv, wl.d)
+            us_p = timeit(lambda: m.gqa_attn_decode_paged(q, kp, vp, table, lens, workspace=ws, out=o))
+            log(json.dumps({"sweep": name, "kernel": "decode_paged16", "us": round(us_p, 2),
+                            "gbps": round(by / us_p / 1e3, 1), "frac": round(by / us_p / 1e3 / PEAK_HBM_GBS, 4)}))
+            del kp, vp
             pj = W.proj_inputs(wl)
             x, w = up(pj["x"]), up(pj["w"])
             us = timeit(lambda: m.qkv_proj(x, w, wl.H_q, wl.H_kv, wl.d))

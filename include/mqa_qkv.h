@@ -21,7 +21,8 @@
  *                        cache with per-sequence lengths ("MHA -> GQA" blog,
  *                        section 3.1), split over the keys with an exact
  *                        partial-softmax combine (FlashAttention-3 page, HN
- *                        thread: the softmax is split and recombined).
+ *                        thread: the softmax is split and recombined);
+ *      gqa_attn_decode_paged  the same over a paged KV cache.
  *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers owned by the caller; outputs are
@@ -181,6 +182,39 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
                             int64_t q_tok_stride, float scale, int32_t kv_split,
                             void* workspace, size_t workspace_bytes, mqkv_dtype in_dtype,
                             mqkv_dtype o_dtype, void* stream);
+
+/*
+ * Decode over a paged KV cache (bf16).
+ *
+ * The same operation as gqa_attn_decode, with the cache in fixed-size pages
+ * (the PagedAttention layout that the "MHA -> GQA" blog, section 3.2, names as
+ * non-contiguous storage).  Key j of sequence b is row j % page_size of page
+ * block_table[b * pages_per_seq + j / page_size]:
+ *
+ *   k(b, j, g, c) = k_pages[((page * page_size) + j % page_size) * H_kv * d + g*d + c]
+ *
+ * (v likewise).  The MFMA path is kept: each 16-key block of a page is read
+ * straight into the matrix operands, so the cache needs no gather copy.
+ *
+ * k_pages, v_pages [num_pages, page_size, H_kv, d] contiguous bf16
+ * block_table      [B, pages_per_seq] device int32 page ids.  Only the entries
+ *                  covering keys [0, seq_lens[b]) are read.  A page id outside
+ *                  [0, num_pages) is never dereferenced: its keys read as
+ *                  zero vectors.
+ * seq_lens         [B] device int32, clamped to [0, pages_per_seq * page_size]
+ * page_size        a positive multiple of 16
+ * Everything else, the workspace (gqa_attn_decode_workspace_bytes with
+ * L_max = pages_per_seq * page_size), the split and the results are those of
+ * gqa_attn_decode: a paged cache holding the same rows as a contiguous one
+ * gives bit-identical outputs.  fp32 inputs return MQKV_ERR_UNSUPPORTED.
+ */
+mqkv_status gqa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                  float* lse, int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
+                                  int32_t page_size, int32_t pages_per_seq, int32_t num_pages,
+                                  int64_t q_tok_stride, float scale, int32_t kv_split,
+                                  void* workspace, size_t workspace_bytes, mqkv_dtype in_dtype,
+                                  mqkv_dtype o_dtype, void* stream);
 
 /* Static description of a status code. */
 const char* mqkv_status_string(mqkv_status s);

@@ -26,7 +26,7 @@ MQKV_OK, MQKV_ERR_INVALID, MQKV_ERR_UNSUPPORTED, MQKV_ERR_HIP = 0, 1, 2, 3
 MQKV_F32, MQKV_BF16 = 0, 1
 
 EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill_workspace_bytes",
-           "gqa_attn_prefill",
+           "gqa_attn_prefill", "gqa_attn_decode_paged",
            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "mqkv_status_string", "mqkv_last_error",
            "mqkv_abi_version")
 
@@ -64,6 +64,9 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, i32, vp,
                                     sz, i32, i32, vp]
     lib.gqa_attn_decode.restype = i32
+    lib.gqa_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64,
+                                          f32, i32, vp, sz, i32, i32, vp]
+    lib.gqa_attn_decode_paged.restype = i32
     lib.mqkv_status_string.argtypes = [i32]
     lib.mqkv_status_string.restype = ctypes.c_char_p
     lib.mqkv_last_error.argtypes = []
@@ -318,4 +321,45 @@ def gqa_attn_decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None
                              workspace.numel() * workspace.element_size(), _dtype_code(q.dtype),
                              _dtype_code(out_dtype), _stream(q.device))
     check(st, "gqa_attn_decode")
+    return (out, lse) if return_lse else out
+
+
+def gqa_attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: Optional[float] = None,
+                          out_dtype=None, kv_split: int = 0, return_lse: bool = False, workspace=None,
+                          out=None):
+    """Decode over a paged KV cache: key j of sequence b is row j % page_size of
+    page block_table[b, j // page_size].
+
+    q [B, H_q, d] (any token stride), k_pages/v_pages [num_pages, page_size, H_kv, d]
+    contiguous bf16, block_table [B, pages_per_seq] and seq_lens [B] int32 on the
+    device.  Returns o [B, H_q, d] (and lse [B, H_q] if asked)."""
+    torch = _torch()
+    _require_cuda(q, k_pages, v_pages, block_table, seq_lens, workspace, out)
+    B, H_q, d = q.shape
+    num_pages, page_size, H_kv, _ = k_pages.shape
+    if v_pages.shape != k_pages.shape or k_pages.shape[3] != d:
+        raise ValueError("pages must be [num_pages, page_size, H_kv, d] matching q")
+    if not (k_pages.is_contiguous() and v_pages.is_contiguous() and block_table.is_contiguous()):
+        raise ValueError("pages and block_table must be contiguous")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, pages_per_seq]")
+    if q.stride(2) != 1 or (H_q > 1 and q.stride(1) != d):
+        raise ValueError("q rows must hold contiguous [H_q, d] heads")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    pages_per_seq = block_table.shape[1]
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = decode_workspace_bytes(B, H_q, H_kv, d, pages_per_seq * page_size, kv_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=out_dtype, device=q.device)
+    lse = torch.empty(B, H_q, dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.gqa_attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                   seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                   B, H_q, H_kv, d, page_size, pages_per_seq, num_pages, q.stride(0), scale,
+                                   kv_split, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _dtype_code(q.dtype), _dtype_code(out_dtype), _stream(q.device))
+    check(st, "gqa_attn_decode_paged")
     return (out, lse) if return_lse else out

@@ -57,7 +57,7 @@ const char* mqkv_status_string(mqkv_status s) {
 
 const char* mqkv_last_error(void) { return g_err; }
 
-int32_t mqkv_abi_version(void) { return 103; }
+int32_t mqkv_abi_version(void) { return 104; }
 
 size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                                 mqkv_dtype dtype) {
@@ -233,6 +233,61 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
                      split, n_slot,  part_o,  part_ml,  in_dtype == MQKV_BF16,
                      o_dtype == MQKV_BF16};
   return hip_status(mqkv::launch_decode(a, (hipStream_t)stream), "gqa_attn_decode launch");
+}
+
+mqkv_status gqa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                  int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t page_size,
+                                  int32_t pages_per_seq, int32_t num_pages, int64_t q_tok_stride, float scale,
+                                  int32_t kv_split, void* workspace, size_t workspace_bytes,
+                                  mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream) {
+  g_err[0] = 0;
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
+    return fail(MQKV_ERR_INVALID, "dtype %d/%d unknown", (int)in_dtype, (int)o_dtype);
+  mqkv_status st = check_heads(H_q, H_kv, d);
+  if (st != MQKV_OK) return st;
+  if (B < 0) return fail(MQKV_ERR_INVALID, "B=%d must be >= 0", B);
+  if (page_size < 16 || page_size % 16 != 0)
+    return fail(MQKV_ERR_INVALID, "page_size=%d must be a positive multiple of 16", page_size);
+  if (pages_per_seq < 1 || num_pages < 1)
+    return fail(MQKV_ERR_INVALID, "pages_per_seq=%d and num_pages=%d must be >= 1", pages_per_seq, num_pages);
+  if ((int64_t)pages_per_seq * page_size > 0x7fffffff)
+    return fail(MQKV_ERR_UNSUPPORTED, "pages_per_seq * page_size beyond 2^31-1");
+  const int32_t L_max = pages_per_seq * page_size;
+  if (kv_split != 0 && !split_ok(kv_split))
+    return fail(MQKV_ERR_INVALID, "kv_split=%d must be 0 or a multiple of 32 in [32, 65536]", kv_split);
+  if (!isfinite(scale) || scale < 0.0f) return fail(MQKV_ERR_INVALID, "scale must be finite and >= 0");
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o)
+    return fail(MQKV_ERR_INVALID, "q, k_pages, v_pages, block_table, seq_lens and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
+      (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned (seq_lens, block_table 4-byte)");
+  const int ea = elem_align(in_dtype);
+  if (q_tok_stride < (int64_t)H_q * d || q_tok_stride % ea != 0)
+    return fail(MQKV_ERR_INVALID, "q_tok_stride must be >= H_q*d and a multiple of %d", ea);
+  if (in_dtype != MQKV_BF16) return fail(MQKV_ERR_UNSUPPORTED, "paged caches need bf16 inputs");
+  if ((int64_t)num_pages * page_size * H_kv * d > ((int64_t)1 << 40))
+    return fail(MQKV_ERR_UNSUPPORTED, "page pool too large");
+  if (B == 0) return MQKV_OK;
+  const size_t need = gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(MQKV_ERR_INVALID, "workspace must be 16-byte aligned and >= %zu bytes (got %zu)", need,
+                workspace_bytes);
+  const int32_t n_slot = mqkv::decode_slots(B, H_q, H_kv, L_max, kv_split, true);
+  const int32_t split = kv_split > 0 ? kv_split : mqkv::decode_auto_split(B, H_q, H_kv, L_max, true);
+  const int64_t per = (int64_t)B * H_q * n_slot;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = part_o + per * d;
+  mqkv::DecodeArgs a{q,     k_pages, v_pages, seq_lens, o,       lse,     B,
+                     H_q,   H_kv,    d,       L_max,    q_tok_stride,     scale,
+                     split, n_slot,  part_o,  part_ml,  true,
+                     o_dtype == MQKV_BF16};
+  a.block_table = block_table;
+  a.page_size = page_size;
+  a.pages_per_seq = pages_per_seq;
+  a.num_pages = num_pages;
+  return hip_status(mqkv::launch_decode(a, (hipStream_t)stream), "gqa_attn_decode_paged launch");
 }
 
 }  // extern "C"

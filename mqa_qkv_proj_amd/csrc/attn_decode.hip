@@ -23,6 +23,7 @@
 // chip; otherwise (or with an explicit split) one workgroup per fixed split.
 // Combine kernel: one wave per (sequence, query head) merges the partials.
 #include <algorithm>
+#include <climits>
 
 #include "common.h"
 #include "launch.h"
@@ -123,7 +124,8 @@ template <int D>
 __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int B, int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_slot, int n_qblk) {
+    int B, int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_slot, int n_qblk,
+    const int32_t* __restrict__ block_table, int page_size, int pages_per_seq, int num_pages) {
   using S = DecodeLds<D>;
   constexpr int DS = D / 32;                       // k-steps of the score MFMA
   constexpr int DB = D / 16;                       // 16-row blocks of O^T
@@ -154,8 +156,20 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
 #pragma unroll
       for (int st = 0; st < DS; ++st) qf[st] = hvalid ? ld16(qp + st * 32) : u32x4_t{0, 0, 0, 0};
     }
-    const uint16_t* kbase = kc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D + g4 * 8;
-    const uint16_t* vbase = vc + ((int64_t)b * Lmax) * row_stride + (int64_t)g * D;
+    const uint16_t* kbase = kc + (int64_t)g * D + g4 * 8;
+    const uint16_t* vbase = vc + (int64_t)g * D;
+    // Cache row of key k = block offset + k, per 16-key block (one page holds
+    // whole 16-key blocks): the sequence's rows for a contiguous cache, the
+    // page's rows for a paged one.  A block past the keys, or on a page id
+    // outside the page pool, gets kNoRow and reads as zeros.
+    constexpr int64_t kNoRow = INT64_MIN;
+    auto block_off = [&](int ks) -> int64_t {
+      if (ks >= kend) return kNoRow;
+      if (block_table == nullptr) return (int64_t)b * Lmax;
+      const int pg = block_table[(int64_t)b * pages_per_seq + ks / page_size];
+      if (pg < 0 || pg >= num_pages) return kNoRow;
+      return (int64_t)pg * page_size + ks % page_size - ks;
+    };
 
     // K goes straight into the A-operand registers (lane = key row); V is staged
     // through LDS to be transposed.  V tasks are 4 keys x 8 dimensions, with
@@ -163,25 +177,36 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
     // covers whole V^T rows.
     u32x4_t kr[2][DS];
     u32x4_t rv[VTASK][4];
+    // block offsets of the tile that load_tile will fetch next; each call
+    // looks up the following tile's, so a paged cache's table reads are one
+    // tile ahead of the K/V loads that depend on them
+    int64_t off_next[2] = {block_off(kbeg), block_off(kbeg + 16)};
     auto load_tile = [&](int t) {
       const int k0 = kbeg + t * kTK;
+      const int64_t off[2] = {off_next[0], off_next[1]};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int gk = k0 + kb * 16 + l16;
 #pragma unroll
         for (int st = 0; st < DS; ++st)
-          kr[kb][st] = (gk < kend) ? ld16(kbase + (int64_t)gk * row_stride + st * 32) : u32x4_t{0, 0, 0, 0};
+          kr[kb][st] = (gk < kend && off[kb] != kNoRow)
+                           ? ld16(kbase + (off[kb] + gk) * row_stride + st * 32)
+                           : u32x4_t{0, 0, 0, 0};
       }
 #pragma unroll
       for (int j = 0; j < VTASK; ++j) {
         const int ti = lane + j * 64;
         const int a = ti % (kTK / 4), dg = ti / (kTK / 4);
+        const int64_t vo = off[a >> 2];  // keys 4a..4a+3 lie in 16-key block a/4
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int gk = k0 + a * 4 + jj;
-          rv[j][jj] = (gk < kend) ? ld16(vbase + (int64_t)gk * row_stride + dg * 8) : u32x4_t{0, 0, 0, 0};
+          rv[j][jj] = (gk < kend && vo != kNoRow) ? ld16(vbase + (vo + gk) * row_stride + dg * 8)
+                                                  : u32x4_t{0, 0, 0, 0};
         }
       }
+      off_next[0] = block_off(k0 + kTK);
+      off_next[1] = block_off(k0 + kTK + 16);
     };
     auto store_v = [&]() {
 #pragma unroll
@@ -505,7 +530,7 @@ hipError_t launch_split_bf16(const DecodeArgs& a, hipStream_t s, int& nwg) {
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_lens, a.part_o, a.part_ml, a.B,
                      a.Hq, a.Hkv, a.Lmax, a.q_stride, fmaxf(a.scale * kLog2e, 1e-30f), a.split, a.n_slot,
-                     n_qblk);
+                     n_qblk, a.block_table, a.page_size, a.pages_per_seq, a.num_pages);
   return hipGetLastError();
 }
 

@@ -64,6 +64,11 @@ struct DecodeArgs {
   float* part_o;   // [B, Hq, n_slot, d]
   float* part_ml;  // [B, Hq, n_slot, 2]  (running max in log2 units, sum)
   bool in_bf16, out_bf16;
+  // Paged caches (bf16 only): k/v are [num_pages, page_size, Hkv, d] pages and key j
+  // of sequence b lives in page block_table[b * pages_per_seq + j / page_size]
+  // (Lmax = pages_per_seq * page_size).  nullptr: contiguous [B, Lmax, Hkv, d].
+  const int32_t* block_table = nullptr;
+  int page_size = 0, pages_per_seq = 0, num_pages = 0;
 };
 // The library's choice for kv_split == 0 (0 = balanced work split, else keys
 // per split), and the partial slots per (sequence, query head) a call needs.

@@ -43,7 +43,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["qkv_proj", "split_qkv", "attention", "attention_rows", "decode",
-           "brute_attention", "kv_head_of", "kv_append", "decode_step"]
+           "brute_attention", "kv_head_of", "kv_append", "decode_step", "decode_paged"]
 
 F64 = np.float64
 
@@ -213,6 +213,29 @@ def decode_step(x: np.ndarray, w: np.ndarray, k_cache: np.ndarray, v_cache: np.n
     kc, vc = kv_append(k_cache, v_cache, k[:, 0], v[:, 0], seq_lens)
     O, LSE = decode(q[:, 0], kc, vc, seq_lens, scale)
     return qkv, kc, vc, O, LSE
+
+
+def decode_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
+                 seq_lens: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode over a paged cache (the PagedAttention layout the "MHA -> GQA" blog,
+    section 3.2, describes as non-contiguous KV storage).
+
+    Key j of sequence b is row j % P of page block_table[b, j // P]; a page id
+    outside the pool stands for zero rows.  The pages are gathered into the
+    contiguous cache they describe and decode runs on it.
+    k_pages, v_pages [num_pages, P, H_kv, d]; block_table [B, pages_per_seq].
+    """
+    n_pages, P = k_pages.shape[0], k_pages.shape[1]
+    B, pps = block_table.shape
+    kc = np.zeros((B, pps * P) + k_pages.shape[2:], dtype=F64)
+    vc = np.zeros_like(kc)
+    for b in range(B):
+        for i in range(pps):
+            pg = int(block_table[b, i])
+            if 0 <= pg < n_pages:
+                kc[b, i * P:(i + 1) * P] = k_pages[pg]
+                vc[b, i * P:(i + 1) * P] = v_pages[pg]
+    return decode(q, kc, vc, seq_lens, scale)
 
 
 def brute_attention(q, k, v, causal: bool, scale: float):

@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill",
               "gqa_attn_prefill_workspace_bytes",
-              "gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
+              "gqa_attn_decode", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode_paged",
               "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version"):
         assert n in names
 
@@ -42,7 +42,7 @@ def test_status_strings(lib):
     assert L.mqkv_status_string(1) == b"invalid argument"
     assert L.mqkv_status_string(2) == b"unsupported configuration"
     assert L.mqkv_status_string(3) == b"HIP runtime error"
-    assert L.mqkv_abi_version() == 103
+    assert L.mqkv_abi_version() == 104
 
 
 def proj(lib, **kw):
@@ -165,6 +165,29 @@ def test_decode_workspace_query(lib):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
+
+
+def decode_paged(lib, **kw):
+    a = dict(q=A, kp=A, vp=A, bt=A, lens=A, o=A, lse=None, B=2, H_q=8, H_kv=2, d=128, P=16, pps=8, npages=16,
+             qs=1024, scale=0.1, split=0, ws=A, wsb=1 << 20, dt=BF16, odt=BF16)
+    a.update(kw)
+    return lib.lib.gqa_attn_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["lens"], a["o"], a["lse"], a["B"],
+                                         a["H_q"], a["H_kv"], a["d"], a["P"], a["pps"], a["npages"], a["qs"],
+                                         a["scale"], a["split"], a["ws"], a["wsb"], a["dt"], a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), INV), (dict(kp=None), INV), (dict(bt=A + 2), INV), (dict(P=0), INV), (dict(P=24), INV),
+    (dict(pps=0), INV), (dict(npages=0), INV), (dict(split=48), INV), (dict(scale=-1.0), INV),
+    (dict(dt=F32, odt=F32), UNS), (dict(d=80, qs=1024), UNS), (dict(ws=None), INV), (dict(wsb=100), INV),
+    (dict(B=-1), INV), (dict(P=1 << 20, pps=1 << 12), UNS),
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert decode_paged(lib, **kw) == code
+
+
+def test_decode_paged_empty_is_noop(lib):
+    assert decode_paged(lib, B=0) == 0
 
 
 def test_decode_empty_is_noop(lib):

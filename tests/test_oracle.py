@@ -297,6 +297,35 @@ def test_kv_append_skips_out_of_range_lengths():
     assert kc.sum() == 0                                        # inputs are not modified
 
 
+@pytest.mark.parametrize("P", [1, 4, 5])
+def test_paged_decode_reduces_to_contiguous_decode(P):
+    """Pages in order (identity table) are the contiguous cache; any permutation
+    of the pages with the table permuted alike gives the same result; pages
+    outside the pool are zero rows."""
+    rng = np.random.default_rng(P)
+    B, pps, H_q, H_kv, d = 3, 4, 4, 2, 8
+    L_max = pps * P
+    kc, vc = rng.standard_normal((B, L_max, H_kv, d)), rng.standard_normal((B, L_max, H_kv, d))
+    q = rng.standard_normal((B, H_q, d))
+    lens = np.array([1, L_max // 2 + 1, L_max], dtype=np.int32)
+    O, LSE = oracle.decode(q, kc, vc, lens, 0.4)
+    kp, vp = kc.reshape(B * pps, P, H_kv, d), vc.reshape(B * pps, P, H_kv, d)
+    ident = np.arange(B * pps, dtype=np.int32).reshape(B, pps)
+    O1, L1 = oracle.decode_paged(q, kp, vp, ident, lens, 0.4)
+    assert np.array_equal(O, O1) and np.array_equal(LSE, L1)
+    perm = rng.permutation(B * pps)
+    inv = np.argsort(perm)
+    O2, L2 = oracle.decode_paged(q, kp[perm], vp[perm], inv[ident].astype(np.int32), lens, 0.4)
+    assert np.array_equal(O, O2) and np.array_equal(LSE, L2)
+    bad = ident.copy()
+    bad[2, 0] = -1
+    kz, vz = kc.copy(), vc.copy()
+    kz[2, :P] = 0.0
+    vz[2, :P] = 0.0
+    O3, _ = oracle.decode_paged(q, kp, vp, bad, lens, 0.4)
+    assert np.array_equal(O3, oracle.decode(q, kz, vz, lens, 0.4)[0])
+
+
 def _split_combine(q, kc, vc, lens, scale, chunk, n_split):
     """Test-local fp64 split-KV partial softmax + combine (the exact rescaling identity)."""
     B, H_q, d = q.shape
