@@ -340,6 +340,39 @@ def sweep(m, W, torch, dev, stream):
                             "gbps": round(by / us / 1e3, 1)}))
             del kc, vc
         torch.cuda.empty_cache()
+    varlen_batch(m, W, torch, dev, timeit)
+
+
+def varlen_batch(m, W, torch, dev, timeit):
+    """A packed batch of 8 TinyLlama-shaped prompts (H_q=32, H_kv=4, d=64, causal)
+    with seeded lengths U{128..2048}: one variable-length call against one
+    fixed-length call per prompt (same kernels, same bits)."""
+    import numpy as np
+
+    H_q, H_kv, d = 32, 4, 64
+    lens = np.random.default_rng(1007).integers(128, 2048, size=8, endpoint=True).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tot = int(cu[-1])
+    g = torch.Generator(device="cpu").manual_seed(1007)
+    q = torch.randn(tot, H_q, d, generator=g).to(torch.bfloat16).to(dev)
+    k = torch.randn(tot, H_kv, d, generator=g).to(torch.bfloat16).to(dev)
+    v = torch.randn(tot, H_kv, d, generator=g).to(torch.bfloat16).to(dev)
+    cu_d = torch.from_numpy(cu).to(dev)
+    o = torch.empty_like(q)
+    L = int(lens.max())
+    ws = torch.empty(m.prefill_workspace_bytes(len(lens), L, H_kv, d), dtype=torch.uint8, device=dev)
+    fl = sum(4.0 * H_q * d * n * (n + 1) / 2 for n in lens.tolist())
+    us_v = timeit(lambda: m.gqa_attn_prefill_varlen(q, k, v, cu_d, cu_d, L, L, causal=True, out=o, workspace=ws))
+    views = [(q[None, cu[b]:cu[b + 1]], k[None, cu[b]:cu[b + 1]], v[None, cu[b]:cu[b + 1]], o[None, cu[b]:cu[b + 1]])
+             for b in range(len(lens))]
+
+    def per_seq():
+        for qb, kb, vb, ob in views:
+            m.gqa_attn_prefill(qb, kb, vb, causal=True, out=ob, workspace=ws)
+    us_s = timeit(per_seq)
+    log(json.dumps({"sweep": "varlen_tinyllama_8", "lengths": lens.tolist(), "varlen_us": round(us_v, 2),
+                    "varlen_tflops": round(fl / us_v / 1e6, 1), "per_sequence_us": round(us_s, 2),
+                    "per_sequence_tflops": round(fl / us_s / 1e6, 1)}))
 
 
 def decode_loop(m, W, torch, dev, stream):

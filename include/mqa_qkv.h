@@ -17,6 +17,7 @@
  *                        sharing H_kv KV heads ("MHA -> GQA" blog, section 3.2;
  *                        FlashAttention-3 page, the recap of tiling with
  *                        softmax rescaling being exact);
+ *      gqa_attn_prefill_varlen  the same over a packed variable-length batch;
  *   4. gqa_attn_decode   one new query per sequence against a contiguous KV
  *                        cache with per-sequence lengths ("MHA -> GQA" blog,
  *                        section 3.1), split over the keys with an exact
@@ -148,6 +149,40 @@ mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* 
                              int32_t causal, float scale, mqkv_dtype in_dtype,
                              mqkv_dtype o_dtype, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * Prefill over a packed batch of variable-length sequences (bf16).
+ *
+ * The variable-length layout the FlashAttention-3 page lists among its further
+ * optimisations (its closing section).  Sequence b owns the packed tokens
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q and o, and
+ * [cu_seqlens_kv[b], cu_seqlens_kv[b+1]) of k and v; it is attended exactly as
+ * gqa_attn_prefill attends one sequence (same head mapping and bottom-right
+ * causal alignment per sequence):
+ *
+ *   q(t,h,c) = q[t*q_tok_stride + h*d + c]     t in [0, total_q)
+ *   k(t,g,c) = k[t*kv_tok_stride + g*d + c]    t in [0, total_kv)   (v likewise)
+ *
+ * cu_seqlens_q, cu_seqlens_kv  [B+1] device int32, non-decreasing, from 0 to
+ *                 total_q / total_kv; no sequence longer than max_L_q / max_L_kv.
+ *                 Device values are clamped to those bounds, so they never lead
+ *                 outside the buffers.
+ * o    [total_q, H_q, d] contiguous, dtype o_dtype (bf16 or fp32)
+ * lse  [H_q, total_q] fp32 natural-log normalisers, or NULL
+ * workspace: gqa_attn_prefill_workspace_bytes(B, max_L_kv, H_kv, d, MQKV_BF16) bytes
+ * A query row that sees no key (a sequence with no keys, or L_q > L_kv under
+ * the causal mask) gets O = 0 and LSE = -inf.  Each sequence's result is
+ * bit-identical to a gqa_attn_prefill call on that sequence alone.
+ * fp32 inputs return MQKV_ERR_UNSUPPORTED.  B == 0, max_L_q == 0 or
+ * total_q == 0 is a no-op; max_L_kv >= 1, total_kv >= 1.
+ */
+mqkv_status gqa_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                    int32_t B, int32_t max_L_q, int32_t max_L_kv, int32_t total_q,
+                                    int32_t total_kv, int32_t H_q, int32_t H_kv, int32_t d,
+                                    int64_t q_tok_stride, int64_t kv_tok_stride, int32_t causal,
+                                    float scale, mqkv_dtype in_dtype, mqkv_dtype o_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace gqa_attn_decode needs for these sizes: fp32

@@ -26,7 +26,7 @@ MQKV_OK, MQKV_ERR_INVALID, MQKV_ERR_UNSUPPORTED, MQKV_ERR_HIP = 0, 1, 2, 3
 MQKV_F32, MQKV_BF16 = 0, 1
 
 EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill_workspace_bytes",
-           "gqa_attn_prefill", "gqa_attn_decode_paged",
+           "gqa_attn_prefill", "gqa_attn_decode_paged", "gqa_attn_prefill_varlen",
            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "mqkv_status_string", "mqkv_last_error",
            "mqkv_abi_version")
 
@@ -59,6 +59,9 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32,
                                      f32, i32, i32, vp, sz, vp]
     lib.gqa_attn_prefill.restype = i32
+    lib.gqa_attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            i64, i64, i32, f32, i32, i32, vp, sz, vp]
+    lib.gqa_attn_prefill_varlen.restype = i32
     lib.gqa_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.gqa_attn_decode_workspace_bytes.restype = sz
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, i32, vp,
@@ -274,6 +277,54 @@ def gqa_attn_prefill(q, k, v, causal: bool = True, scale: Optional[float] = None
                               qs, ks, int(bool(causal)), scale, _dtype_code(q.dtype),
                               _dtype_code(out_dtype), ws_ptr, ws_bytes, _stream(q.device))
     check(st, "gqa_attn_prefill")
+    return (out, lse) if return_lse else out
+
+
+def gqa_attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_L_q: int, max_L_kv: int,
+                            causal: bool = True, scale: Optional[float] = None, return_lse: bool = False,
+                            out_dtype=None, out=None, workspace=None):
+    """Exact grouped-query attention over a packed batch of variable-length sequences.
+
+    q [total_q, H_q, d], k/v [total_kv, H_kv, d] (token strides may be views into
+    qkv); cu_seqlens_q / cu_seqlens_kv [B+1] int32 on the device.  Sequence b owns
+    tokens [cu[b], cu[b+1]).  Returns o [total_q, H_q, d] and, if asked,
+    lse [H_q, total_q] float32."""
+    torch = _torch()
+    _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_kv, out, workspace)
+    total_q, H_q, d = q.shape
+    total_kv, H_kv, _ = k.shape
+    if k.shape != v.shape or k.shape[2] != d:
+        raise ValueError("k and v must be [total_kv, H_kv, d] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+    for name, t, H in (("q", q, H_q), ("k", k, H_kv), ("v", v, H_kv)):
+        if t.stride(2) != 1 or (H > 1 and t.stride(1) != d):
+            raise ValueError(f"{name}: heads must be contiguous [.., H, d] rows")
+    if k.stride(0) != v.stride(0):
+        raise ValueError("k and v must share a token stride")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 [B+1] tensor")
+    if cu_seqlens_q.shape != cu_seqlens_kv.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must both be [B+1]")
+    B = cu_seqlens_q.shape[0] - 1
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(total_q, H_q, d, dtype=out_dtype, device=q.device)
+    elif out.shape != (total_q, H_q, d) or not out.is_contiguous() or out.dtype != out_dtype:
+        raise ValueError("out must be a contiguous [total_q, H_q, d] tensor of out_dtype")
+    lse = torch.empty(H_q, total_q, dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        need = prefill_workspace_bytes(max(B, 0), max_L_kv, H_kv, d, _dtype_code(q.dtype))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.gqa_attn_prefill_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None, cu_seqlens_q.data_ptr(),
+                                     cu_seqlens_kv.data_ptr(), B, max_L_q, max_L_kv, total_q, total_kv, H_q, H_kv,
+                                     d, q.stride(0), k.stride(0), int(bool(causal)), scale, _dtype_code(q.dtype),
+                                     _dtype_code(out_dtype), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(q.device))
+    check(st, "gqa_attn_prefill_varlen")
     return (out, lse) if return_lse else out
 
 

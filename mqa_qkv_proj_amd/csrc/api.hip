@@ -57,7 +57,7 @@ const char* mqkv_status_string(mqkv_status s) {
 
 const char* mqkv_last_error(void) { return g_err; }
 
-int32_t mqkv_abi_version(void) { return 104; }
+int32_t mqkv_abi_version(void) { return 105; }
 
 size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                                 mqkv_dtype dtype) {
@@ -177,6 +177,53 @@ mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* 
                       causal != 0, scale, in_dtype == MQKV_BF16, o_dtype == MQKV_BF16,
                       workspace, workspace_bytes};
   return hip_status(mqkv::launch_prefill(a, (hipStream_t)stream), "gqa_attn_prefill launch");
+}
+
+mqkv_status gqa_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B,
+                                    int32_t max_L_q, int32_t max_L_kv, int32_t total_q, int32_t total_kv,
+                                    int32_t H_q, int32_t H_kv, int32_t d, int64_t q_tok_stride,
+                                    int64_t kv_tok_stride, int32_t causal, float scale, mqkv_dtype in_dtype,
+                                    mqkv_dtype o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
+    return fail(MQKV_ERR_INVALID, "dtype %d/%d unknown", (int)in_dtype, (int)o_dtype);
+  mqkv_status st = check_heads(H_q, H_kv, d);
+  if (st != MQKV_OK) return st;
+  if (B < 0 || max_L_q < 0 || total_q < 0)
+    return fail(MQKV_ERR_INVALID, "B=%d, max_L_q=%d and total_q=%d must be >= 0", B, max_L_q, total_q);
+  if (max_L_kv < 1 || total_kv < 1)
+    return fail(MQKV_ERR_INVALID, "max_L_kv=%d and total_kv=%d must be >= 1", max_L_kv, total_kv);
+  if (causal != 0 && causal != 1) return fail(MQKV_ERR_INVALID, "causal must be 0 or 1");
+  if (!isfinite(scale) || scale < 0.0f) return fail(MQKV_ERR_INVALID, "scale must be finite and >= 0");
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_kv)
+    return fail(MQKV_ERR_INVALID, "q, k, v, o and the cu_seqlens arrays must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_kv) & 3u))
+    return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned (cu_seqlens 4-byte)");
+  const int ea = elem_align(in_dtype);
+  if (q_tok_stride < (int64_t)H_q * d || kv_tok_stride < (int64_t)H_kv * d)
+    return fail(MQKV_ERR_INVALID, "token strides must cover all heads (q >= %d, kv >= %d)", H_q * d,
+                H_kv * d);
+  if (q_tok_stride % ea != 0 || kv_tok_stride % ea != 0)
+    return fail(MQKV_ERR_INVALID, "token strides must be multiples of %d elements", ea);
+  if (in_dtype != MQKV_BF16) return fail(MQKV_ERR_UNSUPPORTED, "packed variable-length batches need bf16 inputs");
+  if ((int64_t)max_L_kv * kv_tok_stride * 2 >= ((int64_t)1 << 31))
+    return fail(MQKV_ERR_UNSUPPORTED, "one sequence's rows must span less than 2 GiB");
+  if (B == 0 || max_L_q == 0 || total_q == 0) return MQKV_OK;
+  const size_t need = mqkv::prefill_workspace_bytes(B, max_L_kv, H_kv, d, true);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(MQKV_ERR_INVALID, "workspace must be 16-byte aligned and >= %zu bytes (got %zu)", need,
+                workspace_bytes);
+  mqkv::PrefillArgs a{q,       k,     v,         o,         lse,       B,         max_L_q,
+                      max_L_kv, H_q,  H_kv,      d,         q_tok_stride, kv_tok_stride,
+                      causal != 0, scale, true, o_dtype == MQKV_BF16,
+                      workspace, workspace_bytes};
+  a.cu_q = cu_seqlens_q;
+  a.cu_kv = cu_seqlens_kv;
+  a.total_q = total_q;
+  a.total_kv = total_kv;
+  return hip_status(mqkv::launch_prefill(a, (hipStream_t)stream), "gqa_attn_prefill_varlen launch");
 }
 
 size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,

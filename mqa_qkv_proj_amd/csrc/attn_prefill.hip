@@ -82,6 +82,22 @@ struct PrefillLds {
 // keys {0-3, 8-11} first (lane half 0 of the P operand), then {4-7, 12-15}.
 __device__ __forceinline__ int vt_pos(int a) { return ((a & 1) << 3) | ((a >> 1) << 2); }
 
+// Rows and lengths of sequence b: b-major fixed lengths, or the packed
+// variable-length layout (cu_q == nullptr selects the former).  Packed offsets
+// and lengths are clamped to the buffers and to the maximum lengths the grid
+// was sized for, so no value of the device-side offsets leads outside them.
+struct SeqSpan {
+  int64_t q0, kv0;  // first row of the sequence in q / o and in k / v
+  int Lq, Lkv;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
+                                            int b, int Lq, int Lkv, int total_q, int total_kv) {
+  if (cu_q == nullptr) return SeqSpan{(int64_t)b * Lq, (int64_t)b * Lkv, Lq, Lkv};
+  const int q0 = min(max(cu_q[b], 0), total_q), q1 = min(max(cu_q[b + 1], q0), total_q);
+  const int k0 = min(max(cu_kv[b], 0), total_kv), k1 = min(max(cu_kv[b + 1], k0), total_kv);
+  return SeqSpan{q0, k0, min(q1 - q0, Lq), min(k1 - k0, Lkv)};
+}
+
 // V of one (batch, KV head, 64-key tile) written as the LDS image the prefill
 // kernel uses for P.V: V^T in fp16 (bf16 -> fp16 is exact for |v| in fp16's
 // normal range), one padded row per head dimension, keys in P-operand order.
@@ -89,7 +105,8 @@ __device__ __forceinline__ int vt_pos(int a) { return ((a & 1) << 3) | ((a >> 1)
 template <int D>
 __global__ __launch_bounds__(256) void prefill_v_image_kernel(const uint16_t* __restrict__ v,
                                                               uint16_t* __restrict__ img, int Lkv,
-                                                              int Hkv, int64_t kv_stride, int ntiles) {
+                                                              int Hkv, int64_t kv_stride, int ntiles,
+                                                              const int32_t* __restrict__ cu_kv, int total_kv) {
   using S = PrefillLds<D>;
   constexpr int VT = (kBK / 4) * (D / 8);  // tasks of 4 keys x 8 dimensions
   const int ti = threadIdx.x;
@@ -99,11 +116,13 @@ __global__ __launch_bounds__(256) void prefill_v_image_kernel(const uint16_t* __
   id /= ntiles;
   const int g = id % Hkv;
   const int b = id / Hkv;
+  const SeqSpan sp = seq_span(cu_kv, cu_kv, b, Lkv, Lkv, total_kv, total_kv);
+  if (t * kBK >= sp.Lkv) return;  // a tile no query of this sequence reads
   // consecutive lanes take consecutive key groups: one store instruction then
   // covers whole image rows
   const int kg = ti % (kBK / 4), dg = ti / (kBK / 4);
-  const uint32_t kv_bytes = (uint32_t)((int64_t)Lkv * kv_stride * 2);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(v + (int64_t)b * Lkv * kv_stride, kv_bytes);
+  const uint32_t kv_bytes = (uint32_t)((int64_t)sp.Lkv * kv_stride * 2);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(v + sp.kv0 * kv_stride, kv_bytes);
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
   u32x4_t rv[4];
 #pragma unroll
@@ -131,8 +150,9 @@ __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70);
 template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vimg,
-    void* __restrict__ o, float* __restrict__ lse, int Lq, int Lkv, int Hq, int Hkv,
-    int64_t q_stride, int64_t kv_stride, float c, int F, int n_hg, int n_qb, int ntiles) {
+    void* __restrict__ o, float* __restrict__ lse, int Lq_max, int Lkv_max, int Hq, int Hkv,
+    int64_t q_stride, int64_t kv_stride, float c, int F, int n_hg, int n_qb, int ntiles,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, int total_q, int total_kv) {
   using S = PrefillLds<D>;
   constexpr int DS = D / 16;  // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;  // 32-row blocks of O^T
@@ -159,6 +179,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   const int g = lid % Hkv;
   const int b = lid / Hkv;
   const int p0 = qb * P;
+  const SeqSpan sp = seq_span(cu_q, cu_kv, b, Lq_max, Lkv_max, total_q, total_kv);
+  if (p0 >= sp.Lq) return;  // the whole workgroup: no query rows here (packed batches only)
+  const int Lq = sp.Lq, Lkv = sp.Lkv;
   const int off = Lkv - Lq;
 
   // ---- this lane's query row (column of the S^T tile)
@@ -170,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
 
   u32x4_t qf[DS];
   {
-    const uint16_t* qp = q + ((int64_t)b * Lq + pos) * q_stride + (int64_t)h * D + hf * 8;
+    const uint16_t* qp = q + (sp.q0 + pos) * q_stride + (int64_t)h * D + hf * 8;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = valid ? ld16(qp + s * 16) : u32x4_t{0, 0, 0, 0};
   }
@@ -186,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   // buffer end too and leave stale LDS rows, which only ever meet masked keys.
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
   const uint32_t kv_bytes = (uint32_t)((int64_t)Lkv * kv_stride * 2);
-  const char* kbase = reinterpret_cast<const char*>(k + (int64_t)b * Lkv * kv_stride);
+  const char* kbase = reinterpret_cast<const char*>(k + sp.kv0 * kv_stride);
   const uint16_t* vbase = vimg + ((int64_t)b * Hkv + g) * ntiles * S::kV;
   constexpr uint32_t kNoCopy = 0x80000000u;  // beyond any buffer (spans are below 2 GiB)
   uint32_t koff[KCP];
@@ -263,7 +286,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const float mt = mx * c;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
       const float mn = (mt > m_run + kTau) ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      // a row whose max does not move keeps alpha = 1 (exp2(0) exactly), also when
+      // it has seen no key yet (m = -inf, where the difference would be NaN)
+      const float alpha = mn == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;
 #pragma unroll
@@ -271,13 +296,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     }
   };
   // P = exp2(S*c - m) rounded to fp16 (the MFMA B operand), and its row sum.
+  // A row that has seen no visible key yet (m = -inf, possible only in a packed
+  // batch with L_q > L_kv under the causal mask) gets P = 0 rather than NaN.
   auto softmax = [&](const f32x16_t& sc, u32x4_t (&pf)[2]) {
+    const float nm = m_run == -INFINITY ? 0.0f : -m_run;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, nm));
         pf[hb][e] = pack_f16(p0, p1);
       }
     // row sum of the fp16-rounded P actually multiplied into V (fp32 accumulation)
@@ -345,7 +373,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const float mt = mx * c;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
       const float mn = (mt > m_run + kTau) ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      // a row whose max does not move keeps alpha = 1 (exp2(0) exactly), also when
+      // it has seen no key yet (m = -inf, where the difference would be NaN)
+      const float alpha = mn == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;
 #pragma unroll
@@ -447,8 +477,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + xor32(l_run);
   if (!valid) return;
-  const float inv = 1.0f / l_tot;
-  const int64_t orow = (((int64_t)b * Lq + pos) * Hq + h) * D;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;  // a row that sees no key: O = 0
+  const int64_t orow = ((sp.q0 + pos) * Hq + h) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -467,8 +497,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
       }
     }
   }
-  if (lse != nullptr && hf == 0)
-    lse[((int64_t)b * Hq + h) * Lq + pos] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+  if (lse != nullptr && hf == 0) {
+    const int64_t li = cu_q != nullptr ? (int64_t)h * total_q + sp.q0 + pos : ((int64_t)b * Hq + h) * Lq + pos;
+    lse[li] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+  }
 }
 
 // ----------------------------------------------------------------------------- fp32 path
@@ -550,7 +582,7 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   if (a.ws_bytes < prefill_workspace_bytes(a.B, a.Lkv, a.Hkv, D, true)) return hipErrorInvalidValue;
   uint16_t* img = static_cast<uint16_t*>(a.ws);
   hipLaunchKernelGGL(prefill_v_image_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s,
-                     (const uint16_t*)a.v, img, a.Lkv, a.Hkv, a.kv_stride, ntiles);
+                     (const uint16_t*)a.v, img, a.Lkv, a.Hkv, a.kv_stride, ntiles, a.cu_kv, a.total_kv);
   auto kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16>;
   const size_t lds = PrefillLds<D>::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -560,7 +592,7 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const float c = fmaxf(a.scale * kLog2e, 1e-30f);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kThreads), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, img, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv,
-                     a.q_stride, a.kv_stride, c, F, n_hg, n_qb, ntiles);
+                     a.q_stride, a.kv_stride, c, F, n_hg, n_qb, ntiles, a.cu_q, a.cu_kv, a.total_q, a.total_kv);
   return hipGetLastError();
 }
 

@@ -45,6 +45,12 @@ struct PrefillArgs {
   bool in_bf16, out_bf16;
   void* ws;         // bf16 inputs: V^T tile images (prefill_workspace_bytes)
   size_t ws_bytes;
+  // Packed variable-length batch (bf16 only): sequence b owns tokens
+  // [cu_q[b], cu_q[b+1]) of q / o and [cu_kv[b], cu_kv[b+1]) of k / v; Lq and
+  // Lkv are then the maximum lengths.  nullptr: fixed lengths, b-major.
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_kv = nullptr;
+  int total_q = 0, total_kv = 0;
 };
 size_t prefill_workspace_bytes(int B, int Lkv, int Hkv, int d, bool bf16);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);

@@ -43,7 +43,8 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["qkv_proj", "split_qkv", "attention", "attention_rows", "decode",
-           "brute_attention", "kv_head_of", "kv_append", "decode_step", "decode_paged"]
+           "brute_attention", "kv_head_of", "kv_append", "decode_step", "decode_paged",
+           "attention_varlen"]
 
 F64 = np.float64
 
@@ -151,6 +152,38 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: 
                 o, l = attention_rows(q, k, v, b, h, rows, causal, scale)
                 O[b, rows, h, :] = o
                 LSE[b, h, rows] = l
+    return O, LSE
+
+
+def attention_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: np.ndarray, cu_kv: np.ndarray,
+                     causal: bool, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention over a packed batch of variable-length sequences (the variable
+    length case the FlashAttention-3 page lists among its further optimisations).
+
+    Sequence b is the packed rows [cu_q[b], cu_q[b+1]) of q [total_q, H_q, d]
+    and [cu_kv[b], cu_kv[b+1]) of k, v [total_kv, H_kv, d]; each is attended on
+    its own as attention() attends one sequence (bottom-right causal alignment).
+    A query row that sees no key has no softmax: it is given O = 0 and
+    LSE = -inf.  Returns O [total_q, H_q, d], LSE [H_q, total_q].
+    """
+    total_q, H_q, d = q.shape
+    O = np.zeros((total_q, H_q, d), dtype=F64)
+    LSE = np.full((H_q, total_q), -np.inf, dtype=F64)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_kv[b]), int(cu_kv[b + 1])
+        Lq, Lkv = q1 - q0, k1 - k0
+        if Lq == 0 or Lkv == 0:
+            continue
+        qb, kb, vb = q[None, q0:q1], k[None, k0:k1], v[None, k0:k1]
+        # rows that see at least one key: all of them unless causal with L_q > L_kv
+        first = max(0, Lq - Lkv) if causal else 0
+        rows = np.arange(first, Lq)
+        for h in range(H_q):
+            # a row's visible keys depend only on its offset from the end, so
+            # dropping the blind leading rows keeps the alignment
+            o, l = attention_rows(qb[:, first:], kb, vb, 0, h, rows - first, causal, scale)
+            O[q0 + first:q1, h] = o
+            LSE[h, q0 + first:q1] = l
     return O, LSE
 
 

@@ -25,6 +25,7 @@ def test_header_declares_the_boundary():
     for n in ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill",
               "gqa_attn_prefill_workspace_bytes",
               "gqa_attn_decode", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode_paged",
+              "gqa_attn_prefill_varlen",
               "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version"):
         assert n in names
 
@@ -42,7 +43,7 @@ def test_status_strings(lib):
     assert L.mqkv_status_string(1) == b"invalid argument"
     assert L.mqkv_status_string(2) == b"unsupported configuration"
     assert L.mqkv_status_string(3) == b"HIP runtime error"
-    assert L.mqkv_abi_version() == 104
+    assert L.mqkv_abi_version() == 105
 
 
 def proj(lib, **kw):
@@ -119,6 +120,32 @@ def test_qkv_proj_append_empty_is_noop(lib):
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(lib, **kw) == code
+
+
+def prefill_varlen(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=None, cuq=A, cuk=A, B=3, mq=64, mk=64, tq=100, tk=100, H_q=4, H_kv=2, d=64,
+             qs=512, ks=512, causal=1, scale=0.125, dt=BF16, odt=BF16, ws=A, wsb=1 << 20)
+    a.update(kw)
+    return lib.lib.gqa_attn_prefill_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cuq"], a["cuk"], a["B"],
+                                           a["mq"], a["mk"], a["tq"], a["tk"], a["H_q"], a["H_kv"], a["d"], a["qs"],
+                                           a["ks"], a["causal"], a["scale"], a["dt"], a["odt"], a["ws"], a["wsb"],
+                                           None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cuq=None), INV), (dict(cuk=A + 2), INV), (dict(q=None), INV), (dict(mk=0), INV), (dict(tk=0), INV),
+    (dict(B=-1), INV), (dict(mq=-1), INV), (dict(causal=3), INV), (dict(scale=float("nan")), INV),
+    (dict(qs=100), INV), (dict(dt=F32, odt=F32), UNS), (dict(d=96), UNS), (dict(ws=None), INV),
+    (dict(wsb=1000), INV), (dict(H_q=4, H_kv=3), INV),
+])
+def test_prefill_varlen_rejects(lib, kw, code):
+    assert prefill_varlen(lib, **kw) == code
+
+
+def test_prefill_varlen_empty_is_noop(lib):
+    assert prefill_varlen(lib, B=0) == 0
+    assert prefill_varlen(lib, mq=0) == 0
+    assert prefill_varlen(lib, tq=0) == 0
 
 
 def test_prefill_empty_is_noop(lib):

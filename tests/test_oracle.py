@@ -326,6 +326,36 @@ def test_paged_decode_reduces_to_contiguous_decode(P):
     assert np.array_equal(O3, oracle.decode(q, kz, vz, lens, 0.4)[0])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_attention_reduces_to_batched_and_brute_force(causal):
+    """Equal lengths packed = the batched attention; ragged lengths = brute force
+    per sequence; blind rows (no key, or L_q > L_kv under causal) give 0 / -inf."""
+    rng = np.random.default_rng(31 + causal)
+    B, L, H_q, H_kv, d = 3, 6, 4, 2, 4
+    q, k, v = rng.standard_normal((B, L, H_q, d)), rng.standard_normal((B, L, H_kv, d)), rng.standard_normal((B, L, H_kv, d))
+    cu = np.arange(0, (B + 1) * L, L, dtype=np.int32)
+    O, LSE = oracle.attention_varlen(q.reshape(B * L, H_q, d), k.reshape(B * L, H_kv, d), v.reshape(B * L, H_kv, d),
+                                     cu, cu, causal, 0.7)
+    Ob, Lb = oracle.attention(q, k, v, causal, 0.7)
+    assert np.array_equal(O, Ob.reshape(B * L, H_q, d)) and np.array_equal(LSE, Lb.transpose(1, 0, 2).reshape(H_q, B * L))
+    # ragged: lengths (L_q, L_kv) = (3, 5), (1, 1), (0, 2), (2, 0), (4, 2)
+    lq, lk = [3, 1, 0, 2, 4], [5, 1, 2, 0, 2]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32), np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    qp, kp, vp = rng.standard_normal((cq[-1], H_q, d)), rng.standard_normal((ck[-1], H_kv, d)), rng.standard_normal((ck[-1], H_kv, d))
+    O, LSE = oracle.attention_varlen(qp, kp, vp, cq, ck, causal, 0.7)
+    for b in range(len(lq)):
+        for i in range(lq[b]):
+            t = cq[b] + i
+            vis = lk[b] if not causal else min(lk[b], i + lk[b] - lq[b] + 1)
+            if vis <= 0:
+                assert (O[t] == 0).all() and (LSE[:, t] == -np.inf).all()
+                continue
+            ob, lb = oracle.brute_attention(_tolist(qp[None, t:t + 1]), _tolist(kp[None, ck[b]:ck[b] + vis]),
+                                            _tolist(vp[None, ck[b]:ck[b] + vis]), False, 0.7)
+            np.testing.assert_allclose(O[t], np.array(ob)[0, 0], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(LSE[:, t], np.array(lb)[0, :, 0], rtol=0, atol=1e-12)
+
+
 def _split_combine(q, kc, vc, lens, scale, chunk, n_split):
     """Test-local fp64 split-KV partial softmax + combine (the exact rescaling identity)."""
     B, H_q, d = q.shape
