@@ -19,7 +19,11 @@ Readings where the page is silent (listed in the design notes):
     Sylvester Hadamard matrix;
   * scales are plain fp32 factors: one per query row (max |q'| / 448)
     and one per 64-key tile of each KV head (max |k'| over the tile / 448), so
-    that S = scale * (q8 . k8) * s_q * s_k.
+    that S = scale * (q8 . k8) * s_q * s_k;
+  * the quantisation decision is taken in fp32 (the page fixes no precision
+    for it): the mapped values rounded to fp32, s = fp32(max / 448) and the
+    code of the correctly rounded fp32 quotient x / s.  The map and the
+    attention around it stay in fp64.
 
 Each function follows these steps in that order; the pins are in
 tests/test_oracle.py.
@@ -61,27 +65,35 @@ def e4m3(x: np.ndarray) -> np.ndarray:
     return t.numpy()
 
 
+def _quantize(x: np.ndarray, amax: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """e4m3 codes of x / s with s = amax / 448 (1 where amax = 0), both the scale
+    and the quotient rounded to fp32; amax broadcasts against x."""
+    x32 = np.asarray(x, dtype=F64).astype(np.float32)
+    a32 = np.asarray(amax, dtype=F64).astype(np.float32)
+    s32 = np.where(a32 > 0, a32 / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    return e4m3((x32 / s32).astype(F64)), s32.astype(F64)
+
+
 def quantize_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Per-row (last axis) scale max|x| / 448 (1 for an all-zero row) and e4m3(x / s)."""
-    x = np.asarray(x, dtype=F64)
-    s = np.max(np.abs(x), axis=-1) / E4M3_MAX
-    s = np.where(s > 0, s, 1.0)
-    return e4m3(x / s[..., None]), s
+    x32 = np.asarray(x, dtype=F64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    q, s = _quantize(x32, amax[..., None])
+    return q, s[..., 0]
 
 
 def quantize_key_tiles(k: np.ndarray, tile: int = KEY_TILE) -> Tuple[np.ndarray, np.ndarray]:
     """k [B, L, H, d]: one scale per (batch, head, tile of `tile` keys), max over the tile."""
-    k = np.asarray(k, dtype=F64)
-    B, L, H, d = k.shape
+    k32 = np.asarray(k, dtype=F64).astype(np.float32)
+    B, L, H, d = k32.shape
     nt = -(-L // tile)
-    k8 = np.empty_like(k)
+    k8 = np.empty(k32.shape, dtype=F64)
     s = np.empty((B, H, nt), dtype=F64)
     for t in range(nt):
-        blk = k[:, t * tile:(t + 1) * tile]                       # [B, <=tile, H, d]
-        st = np.max(np.abs(blk), axis=(1, 3)) / E4M3_MAX            # [B, H]
-        st = np.where(st > 0, st, 1.0)
-        s[:, :, t] = st
-        k8[:, t * tile:(t + 1) * tile] = e4m3(blk / st[:, None, :, None])
+        blk = k32[:, t * tile:(t + 1) * tile]                     # [B, <=tile, H, d]
+        amax = np.max(np.abs(blk), axis=(1, 3))                     # [B, H]
+        k8[:, t * tile:(t + 1) * tile], st = _quantize(blk, amax[:, None, :, None])
+        s[:, :, t] = st[:, 0, :, 0]
     return k8, s
 
 
@@ -112,3 +124,27 @@ def attention_fp8(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, sca
             O[b, :, h] = P @ vv[b, :, g]
             LSE[b, h] = lse
     return O, LSE
+
+
+def attention_fp8_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, b: int, h: int, rows: np.ndarray,
+                       causal: bool, scale: float, signs: Optional[np.ndarray] = None, tile: int = KEY_TILE):
+    """attention_fp8 for selected query rows of one (batch, head): the same
+    steps, restricted to those rows and to the one KV head they read (whose K
+    tile scales still span every key).  Returns O [len(rows), d], LSE [len(rows)]."""
+    H_q, H_kv = q.shape[2], k.shape[2]
+    L_q, L_kv = q.shape[1], k.shape[1]
+    g = h // (H_q // H_kv)
+    rows = np.asarray(rows, dtype=np.int64)
+    qr = np.asarray(q[b, rows, h], dtype=F64)
+    kg = np.asarray(k[b:b + 1, :, g:g + 1], dtype=F64)               # [1, L_kv, 1, d]
+    qi = incoherent(qr, signs) if signs is not None else qr
+    ki = incoherent(kg, signs) if signs is not None else kg
+    q8, sq = quantize_rows(qi)
+    k8, sk = quantize_key_tiles(ki, tile)
+    key_scale = np.repeat(sk[0, 0], tile)[:L_kv]
+    S = scale * (q8 @ k8[0, :, 0].T) * sq[:, None] * key_scale[None, :]
+    if causal:
+        lim = rows + (L_kv - L_q)
+        S = np.where(np.arange(L_kv)[None, :] <= lim[:, None], S, -np.inf)
+    P, lse = _softmax_rows(S)
+    return P @ np.asarray(v[b, :, g], dtype=F64), lse

@@ -571,3 +571,34 @@ def test_incoherent_processing_lowers_the_error_on_outliers():
         e_plain += np.linalg.norm(fp8.attention_fp8(q, k, v, False, scale)[0] - O)
         e_inc += np.linalg.norm(fp8.attention_fp8(q, k, v, False, scale, signs)[0] - O)
     assert e_inc * 1.1 < e_plain, (e_plain, e_inc)
+
+
+def test_fp8_sampled_rows_equal_the_full_oracle():
+    """attention_fp8_rows (used at full sizes) gives the rows of attention_fp8."""
+    from oracle import fp8
+    rng = np.random.default_rng(17)
+    B, L_q, L_kv, H_q, H_kv, d = 2, 70, 150, 6, 2, 128
+    q = rng.standard_normal((B, L_q, H_q, d))
+    k = rng.standard_normal((B, L_kv, H_kv, d))
+    v = rng.standard_normal((B, L_kv, H_kv, d))
+    signs = rng.choice([-1.0, 1.0], size=d)
+    rows = np.array([0, 5, 63, 64, 69])
+    for causal in (False, True):
+        O, LSE = fp8.attention_fp8(q, k, v, causal, 0.09, signs)
+        for b, h in ((0, 0), (1, 5), (1, 2)):
+            Or, Lr = fp8.attention_fp8_rows(q, k, v, b, h, rows, causal, 0.09, signs)
+            np.testing.assert_allclose(Or, O[b, rows, h], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(Lr, LSE[b, h, rows], rtol=0, atol=1e-12)
+
+
+def test_fp8_row_quantisation_ties_and_saturation():
+    """A row whose max is 3.5 has the exact scale 3.5 / 448 = 2^-7, so x / s is
+    exact and the e4m3 rounding shows: 232 and 248 are ties (to the even codes
+    224 and 256), 250 rounds up to 256, the max maps to 448 exactly."""
+    from oracle import fp8
+    x = np.array([[3.5, 232 / 128, 248 / 128, 250 / 128, -232 / 128, 0.0]])
+    q8, s = fp8.quantize_rows(x)
+    assert s[0] == 2.0 ** -7
+    np.testing.assert_array_equal(q8[0], [448, 224, 256, 256, -224, 0])
+    z8, zs = fp8.quantize_rows(np.zeros((1, 8)))
+    assert zs[0] == 1.0 and not z8.any()

@@ -25,7 +25,7 @@ import numpy as np
 __all__ = [
     "bf16_bits", "bf16_to_f32", "round_bf16", "normal", "WORKLOADS", "Workload",
     "proj_inputs", "prefill_inputs", "decode_inputs", "decode_step_q",
-    "outlier_channels",
+    "outlier_channels", "random_signs", "outlier_entries",
 ]
 
 # ----------------------------------------------------------------------------- bf16 encoding
@@ -77,6 +77,22 @@ def outlier_channels(seed: int, tag: int, n_channels: int, frac: float = 0.001) 
     k = max(1, int(round(frac * n_channels)))
     rng = np.random.default_rng([seed, tag, 999_999])
     return np.sort(rng.choice(n_channels, size=k, replace=False))
+
+
+def random_signs(seed: int, tag: int, n: int) -> np.ndarray:
+    """n independent fair +-1 draws (fp32), seeded: the random signs of the
+    incoherent map, drawn here and passed to both sides as an input."""
+    rng = np.random.default_rng([seed, tag, 777_777])
+    return np.where(rng.random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+
+
+def outlier_entries(a: np.ndarray, seed: int, tag: int, frac: float = 0.001, mult: float = 10.0) -> np.ndarray:
+    """A copy of `a` with a seeded fraction `frac` of its entries (not whole
+    channels) multiplied by `mult`: the outlier recipe of the FP8 error test."""
+    rng = np.random.default_rng([seed, tag, 888_888])
+    out = np.array(a, dtype=np.float32, copy=True)
+    out[rng.random(out.shape) < frac] *= np.float32(mult)
+    return out
 
 
 # ----------------------------------------------------------------------------- workloads
