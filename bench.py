@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 COPY_BYTES = 256 << 20      # calibration copy: reads and writes this many bytes
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_long_kv4_causal_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "mqa_qkv_proj_amd", "csrc", "attn_prefill.hip")
@@ -296,6 +297,19 @@ def sweep(m, W, torch, dev, stream):
             fl = prefill_flops(wl.B, wl.H_q, wl.d, wl.L, wl.L, wl.causal)
             log(json.dumps({"sweep": name, "kernel": "prefill", "us": round(us, 2),
                             "tflops": round(fl / us / 1e6, 2), "frac": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}))
+            if wl.d == 128:
+                # FP8 scores after the random-sign Hadamard map (pre-passes included);
+                # half the FLOPs (Q K^T) on the fp8 matrix cores, half (P V) on fp16 ones
+                signs = torch.from_numpy(W.random_signs(wl.seed, 6, wl.d)).to(dev)
+                ws8 = torch.empty(m.prefill_fp8_workspace_bytes(wl.B, wl.L, wl.L, wl.H_q, wl.H_kv, wl.d),
+                                  dtype=torch.uint8, device=dev)
+                us8 = timeit(lambda: m.gqa_attn_prefill_fp8(q, k, v, signs=signs, causal=wl.causal, out=o,
+                                                            workspace=ws8))
+                mixed_peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+                log(json.dumps({"sweep": name, "kernel": "prefill_fp8", "us": round(us8, 2),
+                                "tflops": round(fl / us8 / 1e6, 2), "speedup_vs_bf16": round(us / us8, 3),
+                                "frac_of_mixed_peak": round(fl / us8 / 1e6 / mixed_peak, 4)}))
+                del ws8
             if wl.hidden:
                 pj = W.proj_inputs(wl)
                 x, w = up(pj["x"]), up(pj["w"])

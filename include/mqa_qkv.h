@@ -18,6 +18,9 @@
  *                        FlashAttention-3 page, the recap of tiling with
  *                        softmax rescaling being exact);
  *      gqa_attn_prefill_varlen  the same over a packed variable-length batch;
+ *      gqa_attn_prefill_fp8     the same with the scores computed from e4m3
+ *                        Q and K after an incoherent (random-sign Hadamard)
+ *                        map (FlashAttention-3 page, FP8 section);
  *   4. gqa_attn_decode   one new query per sequence against a contiguous KV
  *                        cache with per-sequence lengths ("MHA -> GQA" blog,
  *                        section 3.1), split over the keys with an exact
@@ -183,6 +186,44 @@ mqkv_status gqa_attn_prefill_varlen(const void* q, const void* k, const void* v,
                                     int64_t q_tok_stride, int64_t kv_tok_stride, int32_t causal,
                                     float scale, mqkv_dtype in_dtype, mqkv_dtype o_dtype,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Prefill with FP8 scores and incoherent processing (bf16 inputs, d = 128).
+ *
+ * The FlashAttention-3 page, FP8 section: outlier features of Q and K inflate
+ * the e4m3 quantisation error; multiplying both by one random orthogonal
+ * matrix (a Hadamard transform with random signs) leaves Q K^T unchanged and
+ * spreads the outliers before the cast.  The call computes
+ *
+ *   q' = q . diag(signs) . H / sqrt(d),  k' likewise  (H: Sylvester Hadamard;
+ *        signs == NULL: q' = q, k' = k, plain FP8 attention)
+ *   q8 = e4m3(q' / s_q)   one fp32 scale per query row: s_q = max|q'| / 448
+ *   k8 = e4m3(k' / s_k)   one fp32 scale per 64-key tile of each KV head:
+ *                         s_k = max |k'| over the tile / 448
+ *   S  = scale * (q8 . k8) * s_q * s_k   on the fp8 matrix cores, fp32 sums
+ *   O  = softmax(S) V     V and P as in gqa_attn_prefill (V unquantised)
+ *
+ * e4m3 is the OCP e4m3fn encoding (max 448, no infinities), rounded to nearest
+ * even after saturating to +-448.  Layout, GQA mapping, causal alignment, o,
+ * lse, strides and alignment are those of gqa_attn_prefill with
+ * in_dtype = MQKV_BF16.
+ * signs  [d] device fp32 (the random signs, +-1), or NULL; 4-byte aligned.
+ *        Other values are used as given (a diagonal scaling then makes the map
+ *        non-orthogonal and changes the result).
+ * workspace: gqa_attn_prefill_fp8_workspace_bytes(B, L_q, L_kv, H_q, H_kv, d)
+ *   bytes, 16-byte aligned: the V tiles of gqa_attn_prefill, the e4m3 K tiles
+ *   with their scales, and the e4m3 Q rows with theirs; dead after the call.
+ * d != 128 returns MQKV_ERR_UNSUPPORTED (the workspace size is then 0).
+ */
+size_t gqa_attn_prefill_fp8_workspace_bytes(int32_t B, int32_t L_q, int32_t L_kv, int32_t H_q,
+                                            int32_t H_kv, int32_t d);
+
+mqkv_status gqa_attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const float* signs, int32_t B, int32_t L_q, int32_t L_kv,
+                                 int32_t H_q, int32_t H_kv, int32_t d, int64_t q_tok_stride,
+                                 int64_t kv_tok_stride, int32_t causal, float scale,
+                                 mqkv_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /*
  * Bytes of device workspace gqa_attn_decode needs for these sizes: fp32

@@ -10,6 +10,8 @@ Functions mirror the C ABI:
     qkv_proj(x, w_qkv, bias=None, H_q, H_kv, d)     -> qkv [..., (H_q+2H_kv)*d]
     split_qkv(qkv, H_q, H_kv, d)                     -> (q, k, v) strided views, no copy
     gqa_attn_prefill(q, k, v, causal, scale, ...)    -> o [B, L_q, H_q, d] (, lse)
+    gqa_attn_prefill_varlen(q, k, v, cu_q, cu_kv, ...) -> o [total_q, H_q, d] (, lse)
+    gqa_attn_prefill_fp8(q, k, v, signs, ...)        -> o [B, L_q, H_q, d] (, lse), e4m3 scores
     gqa_attn_decode(q, k_cache, v_cache, seq_lens, ...) -> o [B, H_q, d] (, lse)
 """
 from __future__ import annotations
@@ -27,6 +29,7 @@ MQKV_F32, MQKV_BF16 = 0, 1
 
 EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill_workspace_bytes",
            "gqa_attn_prefill", "gqa_attn_decode_paged", "gqa_attn_prefill_varlen",
+           "gqa_attn_prefill_fp8_workspace_bytes", "gqa_attn_prefill_fp8",
            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "mqkv_status_string", "mqkv_last_error",
            "mqkv_abi_version")
 
@@ -62,6 +65,11 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                             i64, i64, i32, f32, i32, i32, vp, sz, vp]
     lib.gqa_attn_prefill_varlen.restype = i32
+    lib.gqa_attn_prefill_fp8_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.gqa_attn_prefill_fp8_workspace_bytes.restype = sz
+    lib.gqa_attn_prefill_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32,
+                                         f32, i32, vp, sz, vp]
+    lib.gqa_attn_prefill_fp8.restype = i32
     lib.gqa_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.gqa_attn_decode_workspace_bytes.restype = sz
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, i32, vp,
@@ -325,6 +333,52 @@ def gqa_attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_L_q: int, 
                                      _dtype_code(out_dtype), workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(), _stream(q.device))
     check(st, "gqa_attn_prefill_varlen")
+    return (out, lse) if return_lse else out
+
+
+def prefill_fp8_workspace_bytes(B: int, L_q: int, L_kv: int, H_q: int, H_kv: int, d: int) -> int:
+    return int(lib.gqa_attn_prefill_fp8_workspace_bytes(B, L_q, L_kv, H_q, H_kv, d))
+
+
+def gqa_attn_prefill_fp8(q, k, v, signs=None, causal: bool = True, scale: Optional[float] = None,
+                         return_lse: bool = False, out_dtype=None, out=None, workspace=None):
+    """Grouped-query attention with e4m3 scores after the incoherent map.
+
+    q [B, L_q, H_q, d], k/v [B, L_kv, H_kv, d] bf16 (d = 128; token strides may be
+    views into qkv); signs: float32 [d] device tensor of random +-1 (the
+    Hadamard transform's signs), or None for plain FP8 scores.  Returns
+    o [B, L_q, H_q, d] (out_dtype, default bf16) and, if asked, lse [B, H_q, L_q]."""
+    torch = _torch()
+    _require_cuda(q, k, v, signs, out, workspace)
+    B, L_q, H_q, d = q.shape
+    _, L_kv, H_kv, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, L_kv, H_kv, d] matching q")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise ValueError("q, k and v must be bfloat16")
+    if signs is not None and (signs.dtype != torch.float32 or tuple(signs.shape) != (d,)
+                              or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous float32 [d] tensor")
+    qs = _tok_stride(q, L_q, H_q, d, "q")
+    ks = _tok_stride(k, L_kv, H_kv, d, "k")
+    if _tok_stride(v, L_kv, H_kv, d, "v") != ks:
+        raise ValueError("k and v must share a token stride")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, L_q, H_q, d, dtype=out_dtype, device=q.device)
+    elif out.shape != (B, L_q, H_q, d) or not out.is_contiguous() or out.dtype != out_dtype:
+        raise ValueError("out must be a contiguous [B, L_q, H_q, d] tensor of out_dtype")
+    lse = torch.empty(B, H_q, L_q, dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        need = prefill_fp8_workspace_bytes(B, L_q, L_kv, H_q, H_kv, d)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.gqa_attn_prefill_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None,
+                                  signs.data_ptr() if signs is not None else None, B, L_q, L_kv, H_q, H_kv, d,
+                                  qs, ks, int(bool(causal)), scale, _dtype_code(out_dtype), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(q.device))
+    check(st, "gqa_attn_prefill_fp8")
     return (out, lse) if return_lse else out
 
 

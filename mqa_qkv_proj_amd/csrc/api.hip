@@ -57,7 +57,7 @@ const char* mqkv_status_string(mqkv_status s) {
 
 const char* mqkv_last_error(void) { return g_err; }
 
-int32_t mqkv_abi_version(void) { return 105; }
+int32_t mqkv_abi_version(void) { return 106; }
 
 size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                                 mqkv_dtype dtype) {
@@ -224,6 +224,53 @@ mqkv_status gqa_attn_prefill_varlen(const void* q, const void* k, const void* v,
   a.total_q = total_q;
   a.total_kv = total_kv;
   return hip_status(mqkv::launch_prefill(a, (hipStream_t)stream), "gqa_attn_prefill_varlen launch");
+}
+
+size_t gqa_attn_prefill_fp8_workspace_bytes(int32_t B, int32_t L_q, int32_t L_kv, int32_t H_q, int32_t H_kv,
+                                            int32_t d) {
+  if (B < 1 || L_q < 1 || L_kv < 1 || H_q < 1 || H_kv < 1 || d != 128) return 0;
+  return mqkv::prefill_fp8_workspace_bytes(B, L_q, L_kv, H_q, H_kv, d);
+}
+
+mqkv_status gqa_attn_prefill_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const float* signs, int32_t B, int32_t L_q, int32_t L_kv, int32_t H_q,
+                                 int32_t H_kv, int32_t d, int64_t q_tok_stride, int64_t kv_tok_stride,
+                                 int32_t causal, float scale, mqkv_dtype o_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!dtype_ok(o_dtype)) return fail(MQKV_ERR_INVALID, "dtype %d unknown", (int)o_dtype);
+  mqkv_status st = check_heads(H_q, H_kv, d);
+  if (st != MQKV_OK) return st;
+  if (d != 128) return fail(MQKV_ERR_UNSUPPORTED, "FP8 prefill supports d=128 only (got %d)", d);
+  if (B < 0 || L_q < 0) return fail(MQKV_ERR_INVALID, "B=%d and L_q=%d must be >= 0", B, L_q);
+  if (L_kv < 1) return fail(MQKV_ERR_INVALID, "L_kv=%d must be >= 1", L_kv);
+  if (causal != 0 && causal != 1) return fail(MQKV_ERR_INVALID, "causal must be 0 or 1");
+  if (causal && L_q > L_kv)
+    return fail(MQKV_ERR_INVALID, "causal attention needs L_q (%d) <= L_kv (%d)", L_q, L_kv);
+  if (!isfinite(scale) || scale < 0.0f) return fail(MQKV_ERR_INVALID, "scale must be finite and >= 0");
+  if (!q || !k || !v || !o) return fail(MQKV_ERR_INVALID, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)) ||
+      (reinterpret_cast<uintptr_t>(signs) & 3u))
+    return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned (signs 4-byte)");
+  if (q_tok_stride < (int64_t)H_q * d || kv_tok_stride < (int64_t)H_kv * d)
+    return fail(MQKV_ERR_INVALID, "token strides must cover all heads (q >= %d, kv >= %d)", H_q * d,
+                H_kv * d);
+  if (q_tok_stride % 8 != 0 || kv_tok_stride % 8 != 0)
+    return fail(MQKV_ERR_INVALID, "token strides must be multiples of 8 elements");
+  if ((int64_t)L_kv * kv_tok_stride * 2 >= ((int64_t)1 << 31) || (int64_t)L_q * q_tok_stride * 2 >= ((int64_t)1 << 31))
+    return fail(MQKV_ERR_UNSUPPORTED, "one sequence's rows must span less than 2 GiB");
+  if (B == 0 || L_q == 0) return MQKV_OK;
+  const size_t need = mqkv::prefill_fp8_workspace_bytes(B, L_q, L_kv, H_q, H_kv, d);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(MQKV_ERR_INVALID, "workspace must be 16-byte aligned and >= %zu bytes (got %zu)", need,
+                workspace_bytes);
+  mqkv::PrefillArgs a{q,      k,     v,         o,         lse,       B,         L_q,
+                      L_kv,   H_q,   H_kv,      d,         q_tok_stride, kv_tok_stride,
+                      causal != 0, scale, true, o_dtype == MQKV_BF16,
+                      workspace, workspace_bytes};
+  a.fp8 = true;
+  a.signs = signs;
+  return hip_status(mqkv::launch_prefill(a, (hipStream_t)stream), "gqa_attn_prefill_fp8 launch");
 }
 
 size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,

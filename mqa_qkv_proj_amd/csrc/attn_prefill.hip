@@ -64,9 +64,11 @@ constexpr float kTau = 8.0f;        // lazy-rescale threshold (log2 units)
 // MFMA operand reads of 16 consecutive rows on distinct banks.  LDS-DMA copies
 // 1 KB per instruction (64 lanes x 16 bytes, lane-linear), so each image is a
 // whole number of copies.
-template <int D>
+template <int D, bool F8 = false>
 struct PrefillLds {
-  static constexpr int kKld = D + 8;    // K row pitch (bf16 elements)
+  // K row pitch in 16-bit units: bf16 rows of D + 8 elements, or (F8) e4m3 rows
+  // of D + 16 bytes whose padding also carries the tile's quantisation scale
+  static constexpr int kKld = F8 ? (D + 16) / 2 : D + 8;
   static constexpr int kVld = kBK + 8;  // V^T row pitch (fp16 elements)
   static constexpr int kK = kBK * kKld;
   static constexpr int kV = D * kVld;
@@ -143,18 +145,163 @@ __global__ __launch_bounds__(256) void prefill_v_image_kernel(const uint16_t* __
   }
 }
 
+// ---- FP8 (e4m3) pre-passes: the incoherent map on Q and K, then quantisation
+// ("FlashAttention-3" page, FP8 section: a random orthogonal matrix, here a
+// Hadamard transform with random signs, spreads outlier features before the
+// cast).  One wave per row of D values, E = D/64 per lane at d = E*lane + e.
+
+// x <- x . diag(signs) . H / sqrt(D), the fast Walsh-Hadamard transform: stage s
+// pairs elements i and i ^ 2^s, inside a lane while 2^s < E, across lanes after.
+template <int D>
+__device__ __forceinline__ void incoherent_row(float (&x)[D / 64], const float* __restrict__ signs, int lane) {
+  constexpr int E = D / 64;
+  if (signs == nullptr) return;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] *= signs[E * lane + e];
+#pragma unroll
+  for (int st = 1; st < D; st <<= 1) {
+    if (st < E) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((e & st) == 0) {
+          const float a = x[e], b2 = x[e + st];
+          x[e] = a + b2;
+          x[e + st] = a - b2;
+        }
+    } else {
+      const int lm = st / E;  // partner lane distance
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float y = __shfl_xor(x[e], lm, 64);
+        x[e] = (lane & lm) ? y - x[e] : x[e] + y;
+      }
+    }
+  }
+  const float nrm = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] *= nrm;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// e4m3 bytes of x / s (a correctly rounded fp32 division, so the rounding
+// decision is a function of the fp32 values alone), saturated to +-448 (the
+// conversion itself gives NaN past the range), rounded to nearest even;
+// returned in the low E bytes.
+template <int E>
+__device__ __forceinline__ uint32_t e4m3_pack(const float (&x)[E], float s) {
+  const float a = fminf(fmaxf(x[0] / s, -448.0f), 448.0f);
+  const float b = E > 1 ? fminf(fmaxf(x[E > 1 ? 1 : 0] / s, -448.0f), 448.0f) : 0.0f;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & (E > 1 ? 0xffffu : 0xffu);
+}
+
+// Q rows [B*L_q*H_q rows of D] -> e4m3 rows q8 [same rows, D bytes] and the
+// per-row scales max|q'| / 448 (1 for an all-zero row).
+template <int D>
+__global__ __launch_bounds__(256) void prefill_fp8_q_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
+                                                            const float* __restrict__ signs,
+                                                            uint8_t* __restrict__ q8, float* __restrict__ q8s,
+                                                            int64_t rows, int Hq) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int h = (int)(row % Hq);
+  const int64_t tok = row / Hq;
+  const uint16_t* src = q + tok * q_stride + (int64_t)h * D + E * lane;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = bf16_to_f32(src[e]);
+  incoherent_row<D>(x, signs, lane);
+  float am = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(x[e]));
+  am = wave_max(am);
+  const float s = am > 0.0f ? am / 448.0f : 1.0f;
+  const uint32_t v = e4m3_pack<E>(x, s);
+  uint8_t* dst = q8 + row * D + E * lane;
+  if constexpr (E == 2)
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
+  else
+    *dst = (uint8_t)v;
+  if (lane == 0) q8s[row] = s;
+}
+
+// K of one (batch, KV head, 64-key tile) -> the fp8 LDS image the attention
+// kernel copies: 64 rows of D e4m3 bytes + 16 bytes of padding, one scale
+// (max |k'| over the tile / 448) stored in row 0's padding.  Keys at or past
+// L_kv are zero rows.  Four waves, 16 rows each.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_fp8_k_kernel(const uint16_t* __restrict__ k, int Lkv, int Hkv,
+                                                            int64_t kv_stride, const float* __restrict__ signs,
+                                                            uint8_t* __restrict__ k8img, int ntiles) {
+  constexpr int E = D / 64, kPitch = D + 16, kRowsPerWave = kBK / 4;
+  __shared__ float wmax[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int id = blockIdx.x;
+  const int t = id % ntiles;
+  id /= ntiles;
+  const int g = id % Hkv;
+  const int b = id / Hkv;
+  float x[kRowsPerWave][E];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int key = t * kBK + wave * kRowsPerWave + i;
+    if (key < Lkv) {
+      const uint16_t* src = k + ((int64_t)b * Lkv + key) * kv_stride + (int64_t)g * D + E * lane;
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[i][e] = bf16_to_f32(src[e]);
+      incoherent_row<D>(x[i], signs, lane);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[i][e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(x[i][e]));
+  }
+  am = wave_max(am);
+  if (lane == 0) wmax[wave] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = am > 0.0f ? am / 448.0f : 1.0f;
+  uint8_t* img = k8img + (((int64_t)b * Hkv + g) * ntiles + t) * (kBK * kPitch);
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = wave * kRowsPerWave + i;
+    const uint32_t v = e4m3_pack<E>(x[i], s);
+    uint8_t* dst = img + r * kPitch + E * lane;
+    if constexpr (E == 2)
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
+    else
+      *dst = (uint8_t)v;
+  }
+  if (wave == 0)  // the padding of row `lane`: the scale in row 0's, zeros elsewhere
+    st16(img + lane * kPitch + D, u32x4_t{lane == 0 ? __float_as_uint(s) : 0u, 0u, 0u, 0u});
+}
+
 // s_waitcnt vmcnt(0) with the other counters left alone: the LDS-DMA copies a
 // wave issued have landed.
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int D, bool CAUSAL, bool OUT_BF16>
+// F8: Q and K arrive as e4m3 (Q rows q8 [rows, D] with per-row scales q8s; K as
+// per-tile LDS images k8img with the tile scale in row 0's padding) and the
+// scores run on the fp8 MFMA 32x32x64; P and V are as in the bf16 path.
+template <int D, bool CAUSAL, bool OUT_BF16, bool F8 = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vimg,
     void* __restrict__ o, float* __restrict__ lse, int Lq_max, int Lkv_max, int Hq, int Hkv,
     int64_t q_stride, int64_t kv_stride, float c, int F, int n_hg, int n_qb, int ntiles,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, int total_q, int total_kv) {
-  using S = PrefillLds<D>;
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, int total_q, int total_kv,
+    const uint8_t* __restrict__ q8, const float* __restrict__ q8s, const uint8_t* __restrict__ k8img) {
+  using S = PrefillLds<D, F8>;
   constexpr int DS = D / 16;  // MFMA k-steps over the head dimension
+  constexpr int KS8 = D / 64;  // fp8 MFMA k-steps (64 bytes each)
+  constexpr int KF = F8 ? 2 * KS8 : DS;  // 16-byte operand fragments per row of a half
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   // Tile copies are issued by the first kFillWaves waves only: the hardware
   // favours the older wave of the two that share a SIMD, so those waves run
@@ -191,8 +338,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   const bool valid = pos < Lq;
   const int lim = CAUSAL ? min(pos + off, Lkv - 1) : Lkv - 1;  // last visible key
 
-  u32x4_t qf[DS];
-  {
+  u32x4_t qf[KF];
+  float crow = c;  // score scale of this lane's row (F8: times the row's quantisation scale)
+  if constexpr (F8) {
+    // B operand of the fp8 MFMA: column = this query row, bytes 64 s + 32 hf ..
+    const int64_t qrow = (sp.q0 + pos) * Hq + h;
+    const uint8_t* qp = q8 + qrow * D + hf * 32;
+#pragma unroll
+    for (int s = 0; s < KF; ++s) qf[s] = valid ? ld16(qp + (s >> 1) * 64 + (s & 1) * 16) : u32x4_t{0, 0, 0, 0};
+    crow = valid ? c * q8s[qrow] : c;
+  } else {
     const uint16_t* qp = q + (sp.q0 + pos) * q_stride + (int64_t)h * D + hf * 8;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = valid ? ld16(qp + s * 16) : u32x4_t{0, 0, 0, 0};
@@ -217,8 +372,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   for (int i = 0; i < KCP; ++i) {
     const int slot = (wave + i * kFillWaves) * 64 + lane;
     const int row = slot / S::kKChunks, ch = slot % S::kKChunks;
-    koff[i] = ch < D / 8 ? (uint32_t)row * row_bytes + (uint32_t)(g * D * 2) + ch * 16 : kNoCopy;
+    koff[i] = F8 ? (uint32_t)lane * 16
+                 : ch < D / 8 ? (uint32_t)row * row_bytes + (uint32_t)(g * D * 2) + ch * 16 : kNoCopy;
   }
+  const uint8_t* k8base = F8 ? k8img + ((int64_t)b * Hkv + g) * ntiles * (S::kK * 2) : nullptr;
   // A tile copy is split into numbered parts (K copies, then V copies) so that
   // the pipelined steps can issue them one at a time between MFMAs.
   constexpr int kParts = KCP + VCP;
@@ -230,15 +387,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     fill_on = wq < kFillWaves && t < nt;
     ks_dst = smem + st * S::kStage;
     vs_dst = ks_dst + S::kK;
-    const uint32_t k0b = (uint32_t)(t * kBK) * row_bytes;
-    krs = make_rsrc(kbase + k0b, kv_bytes - k0b);
+    if constexpr (F8) {
+      krs = make_rsrc(k8base + (int64_t)t * (S::kK * 2), S::kK * 2);
+    } else {
+      const uint32_t k0b = (uint32_t)(t * kBK) * row_bytes;
+      krs = make_rsrc(kbase + k0b, kv_bytes - k0b);
+    }
     vrs = make_rsrc(vbase + (int64_t)t * S::kV, S::kV * 2);
   };
   auto fill_part = [&](auto part) {
     constexpr int i = part;
     if constexpr (i < KCP) {
       const int cp = wq + i * kFillWaves;
-      if (fill_on && cp < S::kKCopies) dma16(krs, ks_dst + cp * 512, koff[i], 0);
+      if (fill_on && cp < S::kKCopies) dma16(krs, ks_dst + cp * 512, koff[i], F8 ? cp * 1024 : 0);
     } else if constexpr (i < kParts) {
       const int cp = wq + (i - KCP) * kFillWaves;
       if (fill_on && cp < S::kVCopies) dma16(vrs, vs_dst + cp * 512, (uint32_t)lane * 16, cp * 1024);
@@ -257,13 +418,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
 
   auto k_of = [&](int st) -> const uint16_t* { return smem + st * S::kStage; };
   auto v_of = [&](int st) -> const uint16_t* { return smem + st * S::kStage + S::kK; };
+  // Scale of the scores of the tile in stage st (F8: the tile's K scale rides
+  // in row 0's padding, bytes D..D+3).
+  float cc = crow;
+  auto tile_c = [&](int st) -> float {
+    if constexpr (F8) return crow * *reinterpret_cast<const float*>(k_of(st) + D / 2);
+    return crow;
+  };
+  // 16-byte fragment f of the MFMA A operand (key row r of a K stage):
+  // bf16: k-step f; F8: bytes 64 (f/2) + 32 hf + 16 (f%2).
+  auto kfrag = [&](const uint16_t* ks, int r, int f) -> u32x4_t {
+    if constexpr (F8)
+      return ld16(reinterpret_cast<const char*>(ks) + r * S::kKld * 2 + (f >> 1) * 64 + hf * 32 + (f & 1) * 16);
+    return ld16(ks + r * S::kKld + f * 16 + hf * 8);
+  };
+  // score MFMA over fragments [f, f + 1] (F8) or fragment f (bf16)
+  auto smfma = [&](const u32x4_t* kfr, int f, f32x16_t acc_s) -> f32x16_t {
+    if constexpr (F8) return mfma32_f8(kfr[f], kfr[f + 1], qf[f], qf[f + 1], acc_s);
+    return mfma32_bf16(kfr[f], qf[f], acc_s);
+  };
 
   // S^T for the 32 keys [32j, 32j + 32) of the tile held in K rows `ks`.
   auto qk = [&](const uint16_t* ks, int j) {
     f32x16_t sc = f32x16_t{};
+    u32x4_t kr[KF];
 #pragma unroll
-    for (int st = 0; st < DS; ++st)
-      sc = mfma32_bf16(ld16(ks + (j * 32 + l32) * S::kKld + st * 16 + hf * 8), qf[st], sc);
+    for (int f = 0; f < KF; ++f) kr[f] = kfrag(ks, j * 32 + l32, f);
+#pragma unroll
+    for (int f = 0; f < KF; f += F8 ? 2 : 1) sc = smfma(kr, f, sc);
     return sc;
   };
   // Element i of a half starting at key kbase is key kbase + 8(i/4) + 4hf + (i%4);
@@ -283,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[i]), sc[i + 1]);
     mx = fmaxf(mx, sc[15]);
     mx = max_xor32(mx);
-    const float mt = mx * c;
+    const float mt = mx * cc;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
       const float mn = (mt > m_run + kTau) ? mt : m_run;
       // a row whose max does not move keeps alpha = 1 (exp2(0) exactly), also when
@@ -304,8 +486,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, nm));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, nm));
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], cc, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], cc, nm));
         pf[hb][e] = pack_f16(p0, p1);
       }
     // row sum of the fp16-rounded P actually multiplied into V (fp32 accumulation)
@@ -333,8 +515,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     }
   };
   // K fragments (MFMA A operand) of the 32 keys [32j, 32j + 32) of a tile.
-  auto load_kf = [&](u32x4_t (&kf)[DS], const uint16_t* ks, int j) {
-    static_for<0, DS>([&](auto st) { kf[st] = ld16(ks + (j * 32 + l32) * S::kKld + st * 16 + hf * 8); });
+  auto load_kf = [&](u32x4_t (&kf)[KF], const uint16_t* ks, int j) {
+    static_for<0, KF>([&](auto f) { kf[f] = kfrag(ks, j * 32 + l32, f); });
   };
   // One pipelined step.  On entry `sc` holds the scores of the current half
   // and `kf` the K fragments of the next half.  The step turns `sc` into P,
@@ -350,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   // (rare after the first half) is the max raised, O and l rescaled and P
   // recomputed, before any of P is used.  So the exponentials do not wait for
   // the max reduction.
-  auto step = [&](f32x16_t& sc, u32x4_t (&kf)[DS], const uint16_t* vc, int jc, const uint16_t* kn,
+  auto step = [&](f32x16_t& sc, u32x4_t (&kf)[KF], const uint16_t* vc, int jc, const uint16_t* kn,
                   int jn, auto next_tag, auto part0) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr int PART0 = part0;
@@ -360,17 +542,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     float mx = sc[0];
     static_for<0, 8>([&](auto i) {
       constexpr int hb = i >> 2, e = i & 3;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], cc, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], cc, -m_run));
       pf[hb][e] = pack_f16(p0, p1);
       mx = fmaxf(fmaxf(mx, sc[hb * 8 + 2 * e]), sc[hb * 8 + 2 * e + 1]);
-      if constexpr (i < DS) sn = mfma32_bf16(kf[i], qf[i], sn);
+      if constexpr (F8) {
+        if constexpr (i % (8 / KS8) == 0) sn = smfma(kf, 2 * (i / (8 / KS8)), sn);
+      } else if constexpr (i < DS) {
+        sn = smfma(kf, i, sn);
+      }
       if constexpr (i < 2 * DB)
         vf[i] = ld16(vc + ((i % DB) * 32 + l32) * S::kVld + (jc * 2 + i / DB) * 16 + hf * 8);
       __builtin_amdgcn_sched_barrier(0);
     });
     mx = max_xor32(mx);
-    const float mt = mx * c;
+    const float mt = mx * cc;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
       const float mn = (mt > m_run + kTau) ? mt : m_run;
       // a row whose max does not move keeps alpha = 1 (exp2(0) exactly), also when
@@ -384,8 +570,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], c, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], c, -m_run));
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], cc, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], cc, -m_run));
           pf[hb][e] = pack_f16(p0, p1);
         }
     }
@@ -398,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
         const uint32_t w = pf[hb][(int)e];
         l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
       });
-      if constexpr (NEXT && i < DS) kf[i] = ld16(kn + (jn * 32 + l32) * S::kKld + i * 16 + hf * 8);
+      if constexpr (NEXT && i < KF) kf[i] = kfrag(kn, jn * 32 + l32, i);
       if constexpr (PART0 >= 0) fill_part(std::integral_constant<int, PART0 + i>{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -426,8 +612,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   int t = 0, st0 = 0;
   f32x16_t sc = f32x16_t{};
   u32x4_t pf[2];
-  u32x4_t kf[DS];
+  u32x4_t kf[KF];
   if (t_mask > 0) {
+    cc = tile_c(0);
     sc = qk(k_of(0), 0);
     update_max(sc);
     load_kf(kf, k_of(0), 1);
@@ -436,6 +623,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const int st1 = st0 == 2 ? 0 : st0 + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     fill_begin(t + 2, st2);
+    cc = tile_c(st0);
     step(sc, kf, v_of(st0), 0, k_of(st1), 0, std::true_type{}, std::integral_constant<int, 0>{});
     step(sc, kf, v_of(st0), 1, k_of(st1), 1, std::true_type{}, std::integral_constant<int, 2 * DB>{});
     static_for<4 * DB, kParts>([&](auto i) { fill_part(i); });
@@ -447,6 +635,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const int st1 = st0 == 2 ? 0 : st0 + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     if (t + 2 < nt) fill(t + 2, st2);
+    cc = tile_c(st0);
     step(sc, kf, v_of(st0), 0, k_of(st1), 0, std::false_type{}, std::integral_constant<int, -1>{});
     update_max(sc);
     drain(sc, v_of(st0), 1);
@@ -461,6 +650,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const int st1 = st0 == 2 ? 0 : st0 + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     if (t + 2 < nt) fill(t + 2, st2);
+    cc = tile_c(st0);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       sc = qk(k_of(st0), j);
@@ -592,7 +782,61 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const float c = fmaxf(a.scale * kLog2e, 1e-30f);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kThreads), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, img, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv,
-                     a.q_stride, a.kv_stride, c, F, n_hg, n_qb, ntiles, a.cu_q, a.cu_kv, a.total_q, a.total_kv);
+                     a.q_stride, a.kv_stride, c, F, n_hg, n_qb, ntiles, a.cu_q, a.cu_kv, a.total_q, a.total_kv,
+                     nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+// Workspace of an FP8 call: V images, K e4m3 tile images, Q e4m3 rows, Q scales.
+struct Fp8Ws {
+  size_t v, k8, q8, q8s, total;
+};
+inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+inline Fp8Ws fp8_ws(int B, int Lq, int Lkv, int Hq, int Hkv, int d) {
+  const int64_t ntiles = (Lkv + kBK - 1) / kBK;
+  Fp8Ws w{};
+  w.v = round256(prefill_workspace_bytes(B, Lkv, Hkv, d, true));
+  w.k8 = round256((size_t)B * Hkv * ntiles * kBK * (d + 16));
+  w.q8 = round256((size_t)B * Lq * Hq * d);
+  w.q8s = round256((size_t)B * Lq * Hq * 4);
+  w.total = w.v + w.k8 + w.q8 + w.q8s;
+  return w;
+}
+
+template <int D, bool CAUSAL, bool OUT_BF16>
+hipError_t launch_fp8(const PrefillArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  int F = 1;
+  while (F < 32 && (G % (2 * F)) == 0) F *= 2;
+  const int P = kRows / F;
+  const int n_hg = G / F;
+  const int n_qb = (a.Lq + P - 1) / P;
+  const int ntiles = (a.Lkv + kBK - 1) / kBK;
+  const int64_t nblk = (int64_t)a.B * a.Hkv * n_hg * n_qb;
+  const int64_t nimg = (int64_t)a.B * a.Hkv * ntiles;
+  const int64_t qrows = (int64_t)a.B * a.Lq * a.Hq;
+  if (nblk > 0x7fffffff || nimg > 0x7fffffff || (qrows + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
+  const Fp8Ws w = fp8_ws(a.B, a.Lq, a.Lkv, a.Hq, a.Hkv, D);
+  if (a.ws_bytes < w.total) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(a.ws);
+  uint16_t* img = reinterpret_cast<uint16_t*>(base);
+  uint8_t* k8 = reinterpret_cast<uint8_t*>(base + w.v);
+  uint8_t* q8 = reinterpret_cast<uint8_t*>(base + w.v + w.k8);
+  float* q8s = reinterpret_cast<float*>(base + w.v + w.k8 + w.q8);
+  hipLaunchKernelGGL(prefill_v_image_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s,
+                     (const uint16_t*)a.v, img, a.Lkv, a.Hkv, a.kv_stride, ntiles, nullptr, 0);
+  hipLaunchKernelGGL(prefill_fp8_k_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s, (const uint16_t*)a.k, a.Lkv,
+                     a.Hkv, a.kv_stride, a.signs, k8, ntiles);
+  hipLaunchKernelGGL(prefill_fp8_q_kernel<D>, dim3((unsigned)((qrows + 3) / 4)), dim3(256), 0, s,
+                     (const uint16_t*)a.q, a.q_stride, a.signs, q8, q8s, qrows, a.Hq);
+  auto kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, true>;
+  const size_t lds = PrefillLds<D, true>::kBytes;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const float c = fmaxf(a.scale * kLog2e, 1e-30f);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kThreads), lds, s, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, img, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv, a.q_stride, a.kv_stride, c, F,
+                     n_hg, n_qb, ntiles, nullptr, nullptr, 0, 0, q8, q8s, k8);
   return hipGetLastError();
 }
 
@@ -614,8 +858,18 @@ size_t prefill_workspace_bytes(int B, int Lkv, int Hkv, int d, bool bf16) {
   return (size_t)((int64_t)B * Hkv * ntiles * per * 2);
 }
 
+size_t prefill_fp8_workspace_bytes(int B, int Lq, int Lkv, int Hq, int Hkv, int d) {
+  if (B <= 0 || Lq <= 0 || Lkv <= 0 || Hq <= 0 || Hkv <= 0 || d != 128) return 0;
+  return fp8_ws(B, Lq, Lkv, Hq, Hkv, d).total;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (!a.in_bf16) return a.d == 64 ? launch_f32<64>(a, s) : launch_f32<128>(a, s);
+  if (a.fp8) {
+    if (a.d != 128 || a.cu_q != nullptr) return hipErrorInvalidValue;
+    if (a.causal) return a.out_bf16 ? launch_fp8<128, true, true>(a, s) : launch_fp8<128, true, false>(a, s);
+    return a.out_bf16 ? launch_fp8<128, false, true>(a, s) : launch_fp8<128, false, false>(a, s);
+  }
 #define MQKV_PF(D, C, O) \
   if (a.d == D && a.causal == C && a.out_bf16 == O) return launch_bf16<D, C, O>(a, s);
   MQKV_PF(64, true, true)

@@ -46,6 +46,15 @@ __device__ __forceinline__ f32x4_t mfma16_bf16(u32x4_t a, u32x4_t b, f32x4_t c) 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// 32x32x64 e4m3 x e4m3 -> fp32 (OCP fp8): the same row / column placement as
+// 32x32x16, with 32 bytes of k per lane given as two 16-byte fragments.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16_t mfma32_f8(u32x4_t a0, u32x4_t a1, u32x4_t b0, u32x4_t b1, f32x16_t c) {
+  const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // bf16 halves of a packed dword -> exact fp32.
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }

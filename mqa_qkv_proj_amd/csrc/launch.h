@@ -51,7 +51,13 @@ struct PrefillArgs {
   const int32_t* cu_q = nullptr;
   const int32_t* cu_kv = nullptr;
   int total_q = 0, total_kv = 0;
+  // FP8 scores (bf16 inputs, d = 128): Q and K quantised to e4m3 after the
+  // incoherent map with these signs (nullptr: no map); workspace per
+  // prefill_fp8_workspace_bytes.
+  bool fp8 = false;
+  const float* signs = nullptr;
 };
+size_t prefill_fp8_workspace_bytes(int B, int Lq, int Lkv, int Hq, int Hkv, int d);
 size_t prefill_workspace_bytes(int B, int Lkv, int Hkv, int d, bool bf16);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 

@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     for n in ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill",
               "gqa_attn_prefill_workspace_bytes",
               "gqa_attn_decode", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode_paged",
-              "gqa_attn_prefill_varlen",
+              "gqa_attn_prefill_varlen", "gqa_attn_prefill_fp8", "gqa_attn_prefill_fp8_workspace_bytes",
               "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version"):
         assert n in names
 
@@ -43,7 +43,7 @@ def test_status_strings(lib):
     assert L.mqkv_status_string(1) == b"invalid argument"
     assert L.mqkv_status_string(2) == b"unsupported configuration"
     assert L.mqkv_status_string(3) == b"HIP runtime error"
-    assert L.mqkv_abi_version() == 105
+    assert L.mqkv_abi_version() == 106
 
 
 def proj(lib, **kw):
@@ -236,3 +236,44 @@ def test_python_layer_validates_without_gpu(lib):
     with pytest.raises(ValueError):  # CPU tensors
         lib.qkv_proj_append(x, torch.zeros(256, 512, dtype=torch.bfloat16), kc, kc.clone(),
                             torch.ones(4, dtype=torch.int32), 4, 2, 64)
+
+
+def prefill_fp8(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=None, signs=A, B=1, Lq=16, Lkv=16, H_q=4, H_kv=2, d=128, qs=512, ks=256,
+             causal=1, scale=0.125, odt=BF16, ws=A, wsb=1 << 20)
+    a.update(kw)
+    return lib.lib.gqa_attn_prefill_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["signs"], a["B"], a["Lq"],
+                                        a["Lkv"], a["H_q"], a["H_kv"], a["d"], a["qs"], a["ks"], a["causal"],
+                                        a["scale"], a["odt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(signs=A + 2), INV), (dict(o=A + 8), INV), (dict(Lkv=0), INV),
+    (dict(causal=1, Lq=17, Lkv=16), INV), (dict(causal=2), INV), (dict(scale=float("nan")), INV),
+    (dict(scale=-1.0), INV), (dict(qs=500), INV), (dict(qs=516), INV), (dict(ks=200), INV),
+    (dict(H_q=4, H_kv=3), INV), (dict(d=64, qs=256, ks=128), UNS), (dict(d=96), UNS), (dict(odt=5), INV),
+    (dict(B=-1), INV), (dict(ws=None), INV), (dict(ws=A + 8), INV), (dict(wsb=1000), INV),
+])
+def test_prefill_fp8_rejects(lib, kw, code):
+    assert prefill_fp8(lib, **kw) == code
+    assert lib.lib.mqkv_last_error() != b""
+
+
+def test_prefill_fp8_empty_is_noop(lib):
+    assert prefill_fp8(lib, B=0) == 0
+    assert prefill_fp8(lib, Lq=0) == 0
+    assert prefill_fp8(lib, signs=None, B=0) == 0
+
+
+def test_prefill_fp8_workspace_query(lib):
+    f = lib.prefill_fp8_workspace_bytes
+    r = lambda n: (n + 255) // 256 * 256
+    B, Lq, Lkv, H_q, H_kv, d = 2, 100, 130, 8, 2, 128
+    nt = 3
+    v_img = B * H_kv * nt * d * 72 * 2         # the fp16 V^T tiles of the bf16 prefill
+    k8 = B * H_kv * nt * 64 * (d + 16)          # e4m3 K tiles, 16 padding bytes per row
+    q8 = B * Lq * H_q * d                       # e4m3 Q rows
+    qs = B * Lq * H_q * 4                       # fp32 Q scales
+    assert f(B, Lq, Lkv, H_q, H_kv, d) == r(v_img) + r(k8) + r(q8) + r(qs)
+    assert f(B, Lq, Lkv, H_q, H_kv, 64) == 0    # d = 128 only
+    assert f(0, Lq, Lkv, H_q, H_kv, d) == 0
