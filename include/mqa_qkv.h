@@ -207,12 +207,13 @@ mqkv_status gqa_attn_prefill_varlen(const void* q, const void* k, const void* v,
  * even after saturating to +-448.  Layout, GQA mapping, causal alignment, o,
  * lse, strides and alignment are those of gqa_attn_prefill with
  * in_dtype = MQKV_BF16.
- * signs  [d] device fp32 (the random signs, +-1), or NULL; 4-byte aligned.
+ * signs  [d] device fp32 (the random signs, +-1), or NULL; 16-byte aligned.
  *        Other values are used as given (a diagonal scaling then makes the map
  *        non-orthogonal and changes the result).
  * workspace: gqa_attn_prefill_fp8_workspace_bytes(B, L_q, L_kv, H_q, H_kv, d)
- *   bytes, 16-byte aligned: the V tiles of gqa_attn_prefill, the e4m3 K tiles
- *   with their scales, and the e4m3 Q rows with theirs; dead after the call.
+ *   bytes, 16-byte aligned: the V tiles of gqa_attn_prefill and the e4m3 K
+ *   tiles with their scales, both written by one pre-pass over K and V; Q is
+ *   mapped and quantised inside the attention kernel.  Dead after the call.
  * d != 128 returns MQKV_ERR_UNSUPPORTED (the workspace size is then 0).
  */
 size_t gqa_attn_prefill_fp8_workspace_bytes(int32_t B, int32_t L_q, int32_t L_kv, int32_t H_q,

@@ -250,8 +250,8 @@ mqkv_status gqa_attn_prefill_fp8(const void* q, const void* k, const void* v, vo
   if (!isfinite(scale) || scale < 0.0f) return fail(MQKV_ERR_INVALID, "scale must be finite and >= 0");
   if (!q || !k || !v || !o) return fail(MQKV_ERR_INVALID, "q, k, v and o must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)) ||
-      (reinterpret_cast<uintptr_t>(signs) & 3u))
-    return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned (signs 4-byte)");
+      (signs && !aligned16(signs)))
+    return fail(MQKV_ERR_INVALID, "data pointers must be 16-byte aligned");
   if (q_tok_stride < (int64_t)H_q * d || kv_tok_stride < (int64_t)H_kv * d)
     return fail(MQKV_ERR_INVALID, "token strides must cover all heads (q >= %d, kv >= %d)", H_q * d,
                 H_kv * d);

@@ -105,21 +105,10 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* __restrict__ cu_q, co
 // normal range), one padded row per head dimension, keys in P-operand order.
 // Keys at or past L_kv are zeros, so every image is a full tile.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_v_image_kernel(const uint16_t* __restrict__ v,
-                                                              uint16_t* __restrict__ img, int Lkv,
-                                                              int Hkv, int64_t kv_stride, int ntiles,
-                                                              const int32_t* __restrict__ cu_kv, int total_kv) {
+__device__ __forceinline__ void v_image_tile(const uint16_t* __restrict__ v, uint16_t* __restrict__ img, int Hkv,
+                                             int64_t kv_stride, int ntiles, int b, int g, int t, const SeqSpan& sp,
+                                             int ti) {
   using S = PrefillLds<D>;
-  constexpr int VT = (kBK / 4) * (D / 8);  // tasks of 4 keys x 8 dimensions
-  const int ti = threadIdx.x;
-  if (ti >= VT) return;
-  int id = blockIdx.x;
-  const int t = id % ntiles;
-  id /= ntiles;
-  const int g = id % Hkv;
-  const int b = id / Hkv;
-  const SeqSpan sp = seq_span(cu_kv, cu_kv, b, Lkv, Lkv, total_kv, total_kv);
-  if (t * kBK >= sp.Lkv) return;  // a tile no query of this sequence reads
   // consecutive lanes take consecutive key groups: one store instruction then
   // covers whole image rows
   const int kg = ti % (kBK / 4), dg = ti / (kBK / 4);
@@ -145,41 +134,42 @@ __global__ __launch_bounds__(256) void prefill_v_image_kernel(const uint16_t* __
   }
 }
 
-// ---- FP8 (e4m3) pre-passes: the incoherent map on Q and K, then quantisation
-// ("FlashAttention-3" page, FP8 section: a random orthogonal matrix, here a
-// Hadamard transform with random signs, spreads outlier features before the
-// cast).  One wave per row of D values, E = D/64 per lane at d = E*lane + e.
-
-// x <- x . diag(signs) . H / sqrt(D), the fast Walsh-Hadamard transform: stage s
-// pairs elements i and i ^ 2^s, inside a lane while 2^s < E, across lanes after.
 template <int D>
-__device__ __forceinline__ void incoherent_row(float (&x)[D / 64], const float* __restrict__ signs, int lane) {
-  constexpr int E = D / 64;
-  if (signs == nullptr) return;
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] *= signs[E * lane + e];
-#pragma unroll
-  for (int st = 1; st < D; st <<= 1) {
-    if (st < E) {
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if ((e & st) == 0) {
-          const float a = x[e], b2 = x[e + st];
-          x[e] = a + b2;
-          x[e + st] = a - b2;
-        }
-    } else {
-      const int lm = st / E;  // partner lane distance
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float y = __shfl_xor(x[e], lm, 64);
-        x[e] = (lane & lm) ? y - x[e] : x[e] + y;
-      }
-    }
-  }
-  const float nrm = 1.0f / __builtin_sqrtf((float)D);
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] *= nrm;
+__global__ __launch_bounds__(256) void prefill_v_image_kernel(const uint16_t* __restrict__ v,
+                                                              uint16_t* __restrict__ img, int Lkv,
+                                                              int Hkv, int64_t kv_stride, int ntiles,
+                                                              const int32_t* __restrict__ cu_kv, int total_kv) {
+  constexpr int VT = (kBK / 4) * (D / 8);  // tasks of 4 keys x 8 dimensions
+  const int ti = threadIdx.x;
+  if (ti >= VT) return;
+  int id = blockIdx.x;
+  const int t = id % ntiles;
+  id /= ntiles;
+  const int g = id % Hkv;
+  const int b = id / Hkv;
+  const SeqSpan sp = seq_span(cu_kv, cu_kv, b, Lkv, Lkv, total_kv, total_kv);
+  if (t * kBK >= sp.Lkv) return;  // a tile no query of this sequence reads
+  v_image_tile<D>(v, img, Hkv, kv_stride, ntiles, b, g, t, sp, ti);
+}
+
+// ---- FP8 (e4m3) quantisation with incoherent processing ("FlashAttention-3"
+// page, FP8 section): a random orthogonal matrix, here a Hadamard transform
+// with random signs, spreads outlier features of Q and K before the cast.
+// The transform is the fast Walsh-Hadamard butterfly: stage `st` pairs
+// elements i and i ^ st (a + b to the lower index, a - b to the upper); the
+// stages commute, so each layout below runs them in whatever order its
+// element-to-lane mapping makes cheapest.
+
+__device__ __forceinline__ void bfly(float& lo, float& hi) {
+  const float a = lo, b = hi;
+  lo = a + b;
+  hi = a - b;
+}
+// The butterfly with the partner element held by lane ^ lm (`upper`: this lane
+// holds the upper index).
+__device__ __forceinline__ float bfly_x(float x, int lm, bool upper) {
+  const float y = __shfl_xor(x, lm, 64);
+  return upper ? y - x : x + y;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -188,82 +178,165 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// e4m3 bytes of x / s (a correctly rounded fp32 division, so the rounding
-// decision is a function of the fp32 values alone), saturated to +-448 (the
-// conversion itself gives NaN past the range), rounded to nearest even;
-// returned in the low E bytes.
-template <int E>
-__device__ __forceinline__ uint32_t e4m3_pack(const float (&x)[E], float s) {
-  const float a = fminf(fmaxf(x[0] / s, -448.0f), 448.0f);
-  const float b = E > 1 ? fminf(fmaxf(x[E > 1 ? 1 : 0] / s, -448.0f), 448.0f) : 0.0f;
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & (E > 1 ? 0xffffu : 0xffu);
+// Code of x / s (a correctly rounded fp32 division, so the rounding decision
+// is a function of the fp32 values alone) after saturating to +-448 (the
+// conversion gives NaN past the range); round to nearest even.  Four values
+// to one dword, first value in the low byte.
+__device__ __forceinline__ uint32_t e4m3x4(float x0, float x1, float x2, float x3, float s) {
+  auto sat = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat(x0 / s), sat(x1 / s), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(x2 / s), sat(x3 / s), lo, true);
 }
 
-// Q rows [B*L_q*H_q rows of D] -> e4m3 rows q8 [same rows, D bytes] and the
-// per-row scales max|q'| / 448 (1 for an all-zero row).
+// One Q row (D = 128) inside the attention kernel, where the lane pair
+// (l, l ^ 32) owns the row: the lane with half hf holds the elements
+// 64a + 32hf + j (a < D/64, j < 32), exactly the bytes of the fp8 MFMA B
+// operand it supplies.  Loads the bf16 row, applies the map (signs != nullptr),
+// and returns the fragments qf[2a + c] = bytes 64a + 32hf + 16c.. and the
+// row's scale max |q'| / 448 (1 for an all-zero or absent row).
 template <int D>
-__global__ __launch_bounds__(256) void prefill_fp8_q_kernel(const uint16_t* __restrict__ q, int64_t q_stride,
-                                                            const float* __restrict__ signs,
-                                                            uint8_t* __restrict__ q8, float* __restrict__ q8s,
-                                                            int64_t rows, int Hq) {
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int h = (int)(row % Hq);
-  const int64_t tok = row / Hq;
-  const uint16_t* src = q + tok * q_stride + (int64_t)h * D + E * lane;
-  float x[E];
+__device__ __forceinline__ float q_row_fp8(const uint16_t* __restrict__ qp, bool valid,
+                                           const float* __restrict__ signs, int hf, u32x4_t (&qf)[D / 32]) {
+  constexpr int A = D / 64;
+  float x[A][32];
 #pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = bf16_to_f32(src[e]);
-  incoherent_row<D>(x, signs, lane);
+  for (int a = 0; a < A; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4_t w = valid ? ld16(qp + 64 * a + 32 * hf + 8 * c) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[a][8 * c + 2 * e] = bf16lo(w[e]);
+        x[a][8 * c + 2 * e + 1] = bf16hi(w[e]);
+      }
+    }
+  if (signs != nullptr) {
+#pragma unroll
+    for (int a = 0; a < A; ++a)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const u32x4_t sg = ld16(signs + 64 * a + 32 * hf + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[a][4 * c + e] *= __uint_as_float(sg[e]);
+      }
+#pragma unroll
+    for (int st = 1; st < 32; st <<= 1)  // index bits 0..4: inside the lane
+#pragma unroll
+      for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          if ((j & st) == 0) bfly(x[a][j], x[a][j + st]);
+#pragma unroll
+    for (int a = 0; a < A; ++a)  // index bit 5: across the lane pair
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[a][j] = bfly_x(x[a][j], 32, hf != 0);
+#pragma unroll
+    for (int sa = 1; sa < A; sa <<= 1)  // index bits 6..: across the a blocks
+#pragma unroll
+      for (int a = 0; a < A; ++a)
+        if ((a & sa) == 0)
+#pragma unroll
+          for (int j = 0; j < 32; ++j) bfly(x[a][j], x[a + sa][j]);
+    const float nrm = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+    for (int a = 0; a < A; ++a)
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[a][j] *= nrm;
+  }
   float am = 0.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(x[e]));
-  am = wave_max(am);
+  for (int a = 0; a < A; ++a)
+#pragma unroll
+    for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(x[a][j]));
+  am = fmaxf(am, __shfl_xor(am, 32, 64));
   const float s = am > 0.0f ? am / 448.0f : 1.0f;
-  const uint32_t v = e4m3_pack<E>(x, s);
-  uint8_t* dst = q8 + row * D + E * lane;
-  if constexpr (E == 2)
-    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
-  else
-    *dst = (uint8_t)v;
-  if (lane == 0) q8s[row] = s;
+#pragma unroll
+  for (int a = 0; a < A; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int j = 16 * c + 4 * w;
+        qf[2 * a + c][w] = e4m3x4(x[a][j], x[a][j + 1], x[a][j + 2], x[a][j + 3], s);
+      }
+  return s;
 }
 
-// K of one (batch, KV head, 64-key tile) -> the fp8 LDS image the attention
-// kernel copies: 64 rows of D e4m3 bytes + 16 bytes of padding, one scale
-// (max |k'| over the tile / 448) stored in row 0's padding.  Keys at or past
-// L_kv are zero rows.  Four waves, 16 rows each.
+// K and V of one (batch, KV head, 64-key tile) of an FP8 call, one pass over
+// both: V as the fp16 image of the bf16 path, K as the e4m3 LDS image the
+// attention kernel copies: 64 rows of D code bytes + 16 bytes of padding, with
+// the tile's scale (max |k'| over the tile / 448) in row 0's padding.  Keys at
+// or past L_kv are zero rows.  A K row is held by 16 lanes, 8 elements each
+// (element 8(l % 16) + e); a wave covers 4 rows per 16-byte load and takes 16
+// rows in 4 loads, all in flight together.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_fp8_k_kernel(const uint16_t* __restrict__ k, int Lkv, int Hkv,
-                                                            int64_t kv_stride, const float* __restrict__ signs,
-                                                            uint8_t* __restrict__ k8img, int ntiles) {
-  constexpr int E = D / 64, kPitch = D + 16, kRowsPerWave = kBK / 4;
+__global__ __launch_bounds__(256) void prefill_fp8_kv_kernel(const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v, int Lkv, int Hkv,
+                                                             int64_t kv_stride, const float* __restrict__ signs,
+                                                             uint8_t* __restrict__ k8img, uint16_t* __restrict__ vimg,
+                                                             int ntiles) {
+  static_assert(D == 128, "16 lanes of 8 elements per K row");
+  constexpr int kPitch = D + 16, kPass = 4;
   __shared__ float wmax[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15;  // element block 8 li .. 8 li + 7 of a row
   int id = blockIdx.x;
   const int t = id % ntiles;
   id /= ntiles;
   const int g = id % Hkv;
   const int b = id / Hkv;
-  float x[kRowsPerWave][E];
+  const SeqSpan sp{(int64_t)b * Lkv, (int64_t)b * Lkv, Lkv, Lkv};
+  const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(k + sp.kv0 * kv_stride, (uint32_t)((int64_t)Lkv * kv_stride * 2));  // rows >= L_kv read 0
+  u32x4_t raw[kPass];
+#pragma unroll
+  for (int p = 0; p < kPass; ++p) {
+    const int r = wave * 16 + p * 4 + (lane >> 4);
+    raw[p] = bld16(rs, (uint32_t)(t * kBK + r) * row_bytes + (uint32_t)(g * D * 2) + li * 16);
+  }
+  v_image_tile<D>(v, vimg, Hkv, kv_stride, ntiles, b, g, t, sp, tid);
+  float x[kPass][8];
+#pragma unroll
+  for (int p = 0; p < kPass; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[p][2 * e] = bf16lo(raw[p][e]);
+      x[p][2 * e + 1] = bf16hi(raw[p][e]);
+    }
+  if (signs != nullptr) {
+    const u32x4_t s0 = ld16(signs + 8 * li), s1 = ld16(signs + 8 * li + 4);
+#pragma unroll
+    for (int p = 0; p < kPass; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[p][e] *= __uint_as_float(s0[e]);
+        x[p][4 + e] *= __uint_as_float(s1[e]);
+      }
+#pragma unroll
+    for (int st = 1; st < 8; st <<= 1)  // index bits 0..2: inside the lane
+#pragma unroll
+      for (int p = 0; p < kPass; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((e & st) == 0) bfly(x[p][e], x[p][e + st]);
+#pragma unroll
+    for (int lm = 1; lm < 16; lm <<= 1)  // index bits 3..6: across the 16 lanes of the row
+#pragma unroll
+      for (int p = 0; p < kPass; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[p][e] = bfly_x(x[p][e], lm, (li & lm) != 0);
+    const float nrm = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+    for (int p = 0; p < kPass; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[p][e] *= nrm;
+  }
   float am = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int key = t * kBK + wave * kRowsPerWave + i;
-    if (key < Lkv) {
-      const uint16_t* src = k + ((int64_t)b * Lkv + key) * kv_stride + (int64_t)g * D + E * lane;
+  for (int p = 0; p < kPass; ++p)
 #pragma unroll
-      for (int e = 0; e < E; ++e) x[i][e] = bf16_to_f32(src[e]);
-      incoherent_row<D>(x[i], signs, lane);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[i][e] = 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) am = fmaxf(am, fabsf(x[i][e]));
-  }
+    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[p][e]));
   am = wave_max(am);
   if (lane == 0) wmax[wave] = am;
   __syncthreads();
@@ -271,14 +344,10 @@ __global__ __launch_bounds__(256) void prefill_fp8_k_kernel(const uint16_t* __re
   const float s = am > 0.0f ? am / 448.0f : 1.0f;
   uint8_t* img = k8img + (((int64_t)b * Hkv + g) * ntiles + t) * (kBK * kPitch);
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int r = wave * kRowsPerWave + i;
-    const uint32_t v = e4m3_pack<E>(x[i], s);
-    uint8_t* dst = img + r * kPitch + E * lane;
-    if constexpr (E == 2)
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
-    else
-      *dst = (uint8_t)v;
+  for (int p = 0; p < kPass; ++p) {
+    const int r = wave * 16 + p * 4 + (lane >> 4);
+    st8(img + r * kPitch + li * 8, u32x2_t{e4m3x4(x[p][0], x[p][1], x[p][2], x[p][3], s),
+                                           e4m3x4(x[p][4], x[p][5], x[p][6], x[p][7], s)});
   }
   if (wave == 0)  // the padding of row `lane`: the scale in row 0's, zeros elsewhere
     st16(img + lane * kPitch + D, u32x4_t{lane == 0 ? __float_as_uint(s) : 0u, 0u, 0u, 0u});
@@ -288,16 +357,17 @@ __global__ __launch_bounds__(256) void prefill_fp8_k_kernel(const uint16_t* __re
 // wave issued have landed.
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// F8: Q and K arrive as e4m3 (Q rows q8 [rows, D] with per-row scales q8s; K as
-// per-tile LDS images k8img with the tile scale in row 0's padding) and the
-// scores run on the fp8 MFMA 32x32x64; P and V are as in the bf16 path.
+// F8: each lane pair quantises its Q row to e4m3 in the prologue (after the
+// map with `signs`), K arrives as per-tile e4m3 LDS images k8img with the tile
+// scale in row 0's padding, and the scores run on the fp8 MFMA 32x32x64; P and
+// V are as in the bf16 path.
 template <int D, bool CAUSAL, bool OUT_BF16, bool F8 = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vimg,
     void* __restrict__ o, float* __restrict__ lse, int Lq_max, int Lkv_max, int Hq, int Hkv,
     int64_t q_stride, int64_t kv_stride, float c, int F, int n_hg, int n_qb, int ntiles,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, int total_q, int total_kv,
-    const uint8_t* __restrict__ q8, const float* __restrict__ q8s, const uint8_t* __restrict__ k8img) {
+    const float* __restrict__ signs, const uint8_t* __restrict__ k8img) {
   using S = PrefillLds<D, F8>;
   constexpr int DS = D / 16;  // MFMA k-steps over the head dimension
   constexpr int KS8 = D / 64;  // fp8 MFMA k-steps (64 bytes each)
@@ -342,11 +412,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   float crow = c;  // score scale of this lane's row (F8: times the row's quantisation scale)
   if constexpr (F8) {
     // B operand of the fp8 MFMA: column = this query row, bytes 64 s + 32 hf ..
-    const int64_t qrow = (sp.q0 + pos) * Hq + h;
-    const uint8_t* qp = q8 + qrow * D + hf * 32;
-#pragma unroll
-    for (int s = 0; s < KF; ++s) qf[s] = valid ? ld16(qp + (s >> 1) * 64 + (s & 1) * 16) : u32x4_t{0, 0, 0, 0};
-    crow = valid ? c * q8s[qrow] : c;
+    crow = c * q_row_fp8<D>(q + (sp.q0 + pos) * q_stride + (int64_t)h * D, valid, signs, hf, qf);
   } else {
     const uint16_t* qp = q + (sp.q0 + pos) * q_stride + (int64_t)h * D + hf * 8;
 #pragma unroll
@@ -783,23 +849,21 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kThreads), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, img, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv,
                      a.q_stride, a.kv_stride, c, F, n_hg, n_qb, ntiles, a.cu_q, a.cu_kv, a.total_q, a.total_kv,
-                     nullptr, nullptr, nullptr);
+                     nullptr, nullptr);
   return hipGetLastError();
 }
 
-// Workspace of an FP8 call: V images, K e4m3 tile images, Q e4m3 rows, Q scales.
+// Workspace of an FP8 call: the V images, then the K e4m3 tile images.
 struct Fp8Ws {
-  size_t v, k8, q8, q8s, total;
+  size_t v, k8, total;
 };
 inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
-inline Fp8Ws fp8_ws(int B, int Lq, int Lkv, int Hq, int Hkv, int d) {
+inline Fp8Ws fp8_ws(int B, int Lkv, int Hkv, int d) {
   const int64_t ntiles = (Lkv + kBK - 1) / kBK;
   Fp8Ws w{};
   w.v = round256(prefill_workspace_bytes(B, Lkv, Hkv, d, true));
   w.k8 = round256((size_t)B * Hkv * ntiles * kBK * (d + 16));
-  w.q8 = round256((size_t)B * Lq * Hq * d);
-  w.q8s = round256((size_t)B * Lq * Hq * 4);
-  w.total = w.v + w.k8 + w.q8 + w.q8s;
+  w.total = w.v + w.k8;
   return w;
 }
 
@@ -814,21 +878,14 @@ hipError_t launch_fp8(const PrefillArgs& a, hipStream_t s) {
   const int ntiles = (a.Lkv + kBK - 1) / kBK;
   const int64_t nblk = (int64_t)a.B * a.Hkv * n_hg * n_qb;
   const int64_t nimg = (int64_t)a.B * a.Hkv * ntiles;
-  const int64_t qrows = (int64_t)a.B * a.Lq * a.Hq;
-  if (nblk > 0x7fffffff || nimg > 0x7fffffff || (qrows + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
-  const Fp8Ws w = fp8_ws(a.B, a.Lq, a.Lkv, a.Hq, a.Hkv, D);
+  if (nblk > 0x7fffffff || nimg > 0x7fffffff) return hipErrorInvalidValue;
+  const Fp8Ws w = fp8_ws(a.B, a.Lkv, a.Hkv, D);
   if (a.ws_bytes < w.total) return hipErrorInvalidValue;
   char* base = static_cast<char*>(a.ws);
   uint16_t* img = reinterpret_cast<uint16_t*>(base);
   uint8_t* k8 = reinterpret_cast<uint8_t*>(base + w.v);
-  uint8_t* q8 = reinterpret_cast<uint8_t*>(base + w.v + w.k8);
-  float* q8s = reinterpret_cast<float*>(base + w.v + w.k8 + w.q8);
-  hipLaunchKernelGGL(prefill_v_image_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s,
-                     (const uint16_t*)a.v, img, a.Lkv, a.Hkv, a.kv_stride, ntiles, nullptr, 0);
-  hipLaunchKernelGGL(prefill_fp8_k_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s, (const uint16_t*)a.k, a.Lkv,
-                     a.Hkv, a.kv_stride, a.signs, k8, ntiles);
-  hipLaunchKernelGGL(prefill_fp8_q_kernel<D>, dim3((unsigned)((qrows + 3) / 4)), dim3(256), 0, s,
-                     (const uint16_t*)a.q, a.q_stride, a.signs, q8, q8s, qrows, a.Hq);
+  hipLaunchKernelGGL(prefill_fp8_kv_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, a.Lkv, a.Hkv, a.kv_stride, a.signs, k8, img, ntiles);
   auto kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, true>;
   const size_t lds = PrefillLds<D, true>::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -836,7 +893,7 @@ hipError_t launch_fp8(const PrefillArgs& a, hipStream_t s) {
   const float c = fmaxf(a.scale * kLog2e, 1e-30f);
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kThreads), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, img, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv, a.q_stride, a.kv_stride, c, F,
-                     n_hg, n_qb, ntiles, nullptr, nullptr, 0, 0, q8, q8s, k8);
+                     n_hg, n_qb, ntiles, nullptr, nullptr, 0, 0, a.signs, k8);
   return hipGetLastError();
 }
 
@@ -860,7 +917,7 @@ size_t prefill_workspace_bytes(int B, int Lkv, int Hkv, int d, bool bf16) {
 
 size_t prefill_fp8_workspace_bytes(int B, int Lq, int Lkv, int Hq, int Hkv, int d) {
   if (B <= 0 || Lq <= 0 || Lkv <= 0 || Hq <= 0 || Hkv <= 0 || d != 128) return 0;
-  return fp8_ws(B, Lq, Lkv, Hq, Hkv, d).total;
+  return fp8_ws(B, Lkv, Hkv, d).total;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {

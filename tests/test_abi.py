@@ -248,7 +248,8 @@ def prefill_fp8(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(q=None), INV), (dict(signs=A + 2), INV), (dict(o=A + 8), INV), (dict(Lkv=0), INV),
+    (dict(q=None), INV), (dict(signs=A + 2), INV), (dict(signs=A + 4), INV), (dict(o=A + 8), INV),
+    (dict(Lkv=0), INV),
     (dict(causal=1, Lq=17, Lkv=16), INV), (dict(causal=2), INV), (dict(scale=float("nan")), INV),
     (dict(scale=-1.0), INV), (dict(qs=500), INV), (dict(qs=516), INV), (dict(ks=200), INV),
     (dict(H_q=4, H_kv=3), INV), (dict(d=64, qs=256, ks=128), UNS), (dict(d=96), UNS), (dict(odt=5), INV),
@@ -272,8 +273,6 @@ def test_prefill_fp8_workspace_query(lib):
     nt = 3
     v_img = B * H_kv * nt * d * 72 * 2         # the fp16 V^T tiles of the bf16 prefill
     k8 = B * H_kv * nt * 64 * (d + 16)          # e4m3 K tiles, 16 padding bytes per row
-    q8 = B * Lq * H_q * d                       # e4m3 Q rows
-    qs = B * Lq * H_q * 4                       # fp32 Q scales
-    assert f(B, Lq, Lkv, H_q, H_kv, d) == r(v_img) + r(k8) + r(q8) + r(qs)
+    assert f(B, Lq, Lkv, H_q, H_kv, d) == r(v_img) + r(k8)
     assert f(B, Lq, Lkv, H_q, H_kv, 64) == 0    # d = 128 only
     assert f(0, Lq, Lkv, H_q, H_kv, d) == 0
