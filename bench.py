@@ -165,6 +165,23 @@ def main():
     def avg_ms(a, b):
         return sum(x.elapsed_time(y) for x, y in zip(ev[a], ev[b])) / len(ev[a])
 
+    # Side measurement outside the timed steps: the same prefill with FP8 scores after
+    # the random-sign Hadamard map (gqa_attn_prefill_fp8), for comparison only.
+    signs = torch.from_numpy(W.random_signs(wp.seed, 6, wp.d)).to(dev)
+    ws_f8 = torch.empty(m.prefill_fp8_workspace_bytes(wp.B, wp.L, wp.L, wp.H_q, wp.H_kv, wp.d), dtype=torch.uint8,
+                        device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            m.gqa_attn_prefill_fp8(Qp, Kp, Vp, signs=signs, causal=True, scale=scale_p, out=Op, workspace=ws_f8)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(10):
+            m.gqa_attn_prefill_fp8(Qp, Kp, Vp, signs=signs, causal=True, scale=scale_p, out=Op, workspace=ws_f8)
+        f1.record(stream)
+        f1.synchronize()
+    ms_f8 = f0.elapsed_time(f1) / 10
+    del ws_f8
+
     ms_prefill = avg_ms("p0", "p1")
     ms_gemm = avg_ms("g0", "g1")
     ms_decode = avg_ms("g1", "d1")
@@ -203,6 +220,9 @@ def main():
                    "us": round(ms_decode * 1e3, 2), "mbytes": round(by_decode / 1e6, 2)},
         "qkv_proj": {"tflops": round(gemm_tf, 2), "gbps": round(gemm_gbs, 1),
                      "frac_hbm": round(gemm_gbs / PEAK_HBM_GBS, 4), "us": round(ms_gemm * 1e3, 2)},
+        "prefill_fp8": {"tflops": round(fl_prefill / (ms_f8 * 1e-3) / 1e12, 2), "us": round(ms_f8 * 1e3, 1),
+                        "speedup_vs_bf16": round(ms_prefill / ms_f8, 3),
+                        "note": "same workload, e4m3 Q/K scores after the random-sign Hadamard map; not in value"},
         "roofline": {"bound": "mfma", "achieved": round(pre_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),

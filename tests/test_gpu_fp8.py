@@ -133,3 +133,41 @@ def test_fp8_full_size_sampled_rows(m):
     for b, h in ((0, 5), (1, 31)):
         ref, _ = ofp8.attention_fp8_rows(qh, kh, vh, b, h, rows, True, 1.0 / math.sqrt(d), signs)
         assert_close(got[b, rows, h], ref, "bf16", f"fp8 full-size rows b={b} h={h}")
+
+
+def test_fp8_scale_zero_gives_prefix_means(m):
+    """scale = 0: every visible score is 0 whatever the FP8 codes, so each row's
+    output is the mean of V over its visible keys (causal: a prefix mean)."""
+    import torch
+    B, L, H_q, H_kv, d = 1, 200, 4, 2, 128
+    say("prefill fp8 scale 0", B, L, H_q, H_kv)
+    q = W.round_bf16(W.normal(501, 1, (B, L, H_q, d)))
+    k = W.round_bf16(W.normal(501, 2, (B, L, H_kv, d)))
+    v = W.round_bf16(W.normal(501, 3, (B, L, H_kv, d)))
+    o = m.gqa_attn_prefill_fp8(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"),
+                               signs=dev(W.random_signs(501, 6, d), "f32"), causal=True, scale=0.0,
+                               out_dtype=torch.float32)
+    prefix = np.cumsum(v.astype(np.float64), axis=1) / np.arange(1, L + 1)[None, :, None, None]
+    ref = np.repeat(prefix, H_q // H_kv, axis=2)
+    assert_close(host(o), ref, "bf16", "fp8 scale 0 = prefix means")
+
+
+def test_fp8_zero_rows_and_tiles(m):
+    """All-zero Q rows and an all-zero 64-key K tile take the unit scale (no
+    division by zero) and match the oracle."""
+    import torch
+    B, L, H_q, H_kv, d = 1, 256, 8, 2, 128
+    say("prefill fp8 zero rows/tiles", B, L, H_q, H_kv)
+    q = W.round_bf16(W.normal(502, 1, (B, L, H_q, d)))
+    k = W.round_bf16(W.normal(502, 2, (B, L, H_kv, d)))
+    v = W.round_bf16(W.normal(502, 3, (B, L, H_kv, d)))
+    q[:, 10:20] = 0.0
+    q[:, :, 3] = 0.0
+    k[:, 64:128] = 0.0
+    signs = W.random_signs(502, 6, d)
+    for causal in (True, False):
+        o, lse = m.gqa_attn_prefill_fp8(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), signs=dev(signs, "f32"),
+                                        causal=causal, return_lse=True, out_dtype=torch.float32)
+        ref, ref_lse = ofp8.attention_fp8(q, k, v, causal, 1.0 / math.sqrt(d), signs)
+        assert_close(host(o), ref, "bf16", f"fp8 zero rows/tiles causal={causal}")
+        assert_close(host(lse), ref_lse, "bf16", "fp8 zero rows/tiles LSE", max_abs=1e-3, rel_l2=1e-4)
