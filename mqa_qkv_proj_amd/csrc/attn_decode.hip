@@ -420,17 +420,18 @@ __global__ __launch_bounds__(64) void attn_decode_split_f32_kernel(
 }
 
 // Combine the partials of every unit: one wave per (sequence, query head).
-// Lanes first reduce the per-unit (max, sum) statistics in parallel; then each
-// lane owns D/64 output elements and accumulates the units' weighted partial
-// outputs with 8 loads in flight.  The number of units of (b, h) follows from
-// the same work split the split kernel used.
+// The number of units of (b, h) follows from the same work split the split
+// kernel used (one pass over seq_lens).  Then, 16 units at a time, every lane
+// loads one unit's (max, sum) and its D/64 elements of all 16 units' partial
+// outputs at once, so the statistics and the outputs cost one round trip
+// together; the weights are applied once the wave's maximum is known.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     const int32_t* __restrict__ seq_lens, const float* __restrict__ part_o,
     const float* __restrict__ part_ml, void* __restrict__ o, float* __restrict__ lse, int B, int Hq,
     int Hkv, int Lmax, int split, int n_slot, int n_qblk, int nwg) {
   constexpr int EPL = D / 64;  // output elements per lane
-  __shared__ float wsh[64];
+  constexpr int U = 16;        // units per round
   const int lane = threadIdx.x;
   const int b = blockIdx.y, h = blockIdx.x;
   const int64_t bh = (int64_t)b * Hq + h;
@@ -441,17 +442,22 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
   } else {
     const int G = Hq / Hkv, per_seq = Hkv * n_qblk;
     const int g = h / G, qblk = (h % G) / 16;
-    const TileLine all = tile_line(seq_lens, B, Lmax, per_seq, -1);
-    const int64_t tpw = balanced_tpw(all.total, nwg);
-    const int ntb = (len + kTK - 1) / kTK;
-    int64_t base = 0;  // tiles before sequence b
-    for (int b0 = 0; b0 < b; b0 += 64) {
+    // tiles of all sequences (the line's total) and before sequence b, in one scan
+    int64_t carry = 0, base = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
       const int bb = b0 + lane;
-      int64_t v = bb < b ? (int64_t)((seq_len(seq_lens, bb, Lmax) + kTK - 1) / kTK) * per_seq : 0;
+      const int64_t v = bb < B ? (int64_t)((seq_len(seq_lens, bb, Lmax) + kTK - 1) / kTK) * per_seq : 0;
+      int64_t incl = v;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-      base += v;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      if (b >= b0 && b < b0 + 64) base = carry + __shfl(incl - v, b - b0, 64);
+      carry += __shfl(incl, 63, 64);
     }
+    const int64_t tpw = balanced_tpw(carry, nwg);
+    const int ntb = (len + kTK - 1) / kTK;
     const int64_t s0 = base + (int64_t)(g * n_qblk + qblk) * ntb;
     n = ntb > 0 ? (int)((s0 + ntb - 1) / tpw - s0 / tpw + 1) : 0;
     n = min(n, n_slot);
@@ -459,41 +465,41 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
   const float* ml = part_ml + bh * n_slot * 2;
   const float* po = part_o + bh * n_slot * D;
 
-  float M = -INFINITY;
-  for (int s0 = lane; s0 < n; s0 += 64) M = fmaxf(M, ml[2 * s0]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float M = -INFINITY, L = 0.0f;  // running max (log2 units) and sum over the rounds so far
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  float L = 0.0f;
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    const int sl = c0 + lane;
-    const float w = (sl < n) ? __builtin_amdgcn_exp2f(ml[2 * sl] - M) : 0.0f;
-    float lw = (sl < n) ? w * ml[2 * sl + 1] : 0.0f;
+  for (int c0 = 0; c0 < n; c0 += U) {
+    const int cnt = min(U, n - c0);
+    // this lane's unit statistics (lanes >= cnt: none) and every unit's outputs
+    const int sl = c0 + (lane < cnt ? lane : 0);
+    const float m_l = lane < cnt ? ml[2 * sl] : -INFINITY;
+    const float l_l = lane < cnt ? ml[2 * sl + 1] : 0.0f;
+    float v[U][EPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[u][e] = u < cnt ? po[(int64_t)(c0 + u) * D + e * 64 + lane] : 0.0f;
+    float mr = m_l;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mr = fmaxf(mr, __shfl_xor(mr, off, 64));
+    const float Mn = fmaxf(M, mr);
+    // rescale what the earlier rounds accumulated (no earlier round: factor 1)
+    const float a = M == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+    const float w = lane < cnt ? __builtin_amdgcn_exp2f(m_l - Mn) : 0.0f;
+    float lw = w * l_l;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off, 64);
-    L += lw;
-    wsh[lane] = w;
-    __syncthreads();
-    const int cnt = min(64, n - c0);
-    int s = 0;
-    for (; s + 8 <= cnt; s += 8) {
-      float v[8][EPL];
+    L = L * a + lw;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+    for (int e = 0; e < EPL; ++e) acc[e] *= a;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) v[u][e] = po[(int64_t)(c0 + s + u) * D + e * 64 + lane];
+    for (int u = 0; u < U; ++u) {
+      const float wu = __shfl(w, u, 64);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(wsh[s + u], v[u][e], acc[e]);
+      for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(wu, v[u][e], acc[e]);
     }
-    for (; s < cnt; ++s)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        acc[e] = __builtin_fmaf(wsh[s], po[(int64_t)(c0 + s) * D + e * 64 + lane], acc[e]);
-    __syncthreads();
+    M = Mn;
   }
   const float inv = 1.0f / L;
 #pragma unroll
