@@ -37,7 +37,21 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 COPY_BYTES = 256 << 20      # calibration copy: reads and writes this many bytes
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_long_kv4_causal_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "mqa_qkv_proj_amd", "csrc", "attn_prefill.hip")
+# what the prefill kernels' machine code depends on: their source, the shared
+# device helpers and the build flags
+KERNEL_SRCS = [os.path.join(ROOT, "mqa_qkv_proj_amd", "csrc", "attn_prefill.hip"),
+               os.path.join(ROOT, "mqa_qkv_proj_amd", "csrc", "common.h"),
+               os.path.join(ROOT, "mqa_qkv_proj_amd", "build.py")]
+
+
+def kernel_digest():
+    """SHA-256 over the files the prefill kernels are built from, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -240,13 +254,11 @@ def main():
 
 def measured_traffic():
     """HBM bytes per prefill launch from the committed counter summary, or None when
-    the kernel source changed since the counters were taken."""
-    import hashlib
+    the kernels' source or build flags changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        with open(KERNEL_SRC, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        digest = kernel_digest()
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != digest:
