@@ -276,3 +276,17 @@ def test_prefill_fp8_workspace_query(lib):
     assert f(B, Lq, Lkv, H_q, H_kv, d) == r(v_img) + r(k8)
     assert f(B, Lq, Lkv, H_q, H_kv, 64) == 0    # d = 128 only
     assert f(0, Lq, Lkv, H_q, H_kv, d) == 0
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback: importing the binding where the library is not built raises
+    ImportError naming the build command (checked on a copy of the package)."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "mqa_qkv_proj_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "mqa_qkv_proj_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import mqa_qkv_proj_amd"], cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "build.py" in r.stderr
