@@ -317,6 +317,28 @@ def sweep(m, W, torch, dev, stream):
             e.synchronize()
         return s.elapsed_time(e) / n * 1e3  # us
 
+    # cold-cache timing for the streaming kernels: before each call, read a
+    # 512 MB buffer (clean lines, so nothing is written back) outside the events,
+    # which evicts the 256 MB Infinity Cache
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timeit_cold(fn, n=20):
+        ts = []
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            for _ in range(n):
+                torch.sum(flush, dim=0, out=flush_out)
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record(stream)
+                fn()
+                e.record(stream)
+                e.synchronize()
+                ts.append(s.elapsed_time(e) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2]  # median, us
+
     for name, wl in W.WORKLOADS.items():
         if wl.dtype != "bf16":
             continue
@@ -362,9 +384,12 @@ def sweep(m, W, torch, dev, stream):
             ws = torch.empty(m.decode_workspace_bytes(wl.B, wl.H_q, wl.H_kv, wl.d, wl.L_max), dtype=torch.uint8,
                              device=dev)
             us = timeit(lambda: m.gqa_attn_decode(q, kc, vc, lens, workspace=ws, out=o))
+            us_c = timeit_cold(lambda: m.gqa_attn_decode(q, kc, vc, lens, workspace=ws, out=o))
             by = 2.0 * (int(lens_np.sum()) * wl.H_kv * wl.d * 2 + 2 * wl.B * wl.H_q * wl.d)
             log(json.dumps({"sweep": name, "kernel": "decode", "us": round(us, 2),
-                            "gbps": round(by / us / 1e3, 1), "frac": round(by / us / 1e3 / PEAK_HBM_GBS, 4)}))
+                            "gbps": round(by / us / 1e3, 1), "frac": round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                            "us_cold": round(us_c, 2), "gbps_cold": round(by / us_c / 1e3, 1),
+                            "frac_cold": round(by / us_c / 1e3 / PEAK_HBM_GBS, 4)}))
             # the same rows in a shuffled pool of 16-key pages
             P = 16
             pps = wl.L_max // P
@@ -375,15 +400,19 @@ def sweep(m, W, torch, dev, stream):
             kp[table.flatten().long()] = kc.reshape(wl.B * pps, P, wl.H_kv, wl.d)
             vp[table.flatten().long()] = vc.reshape(wl.B * pps, P, wl.H_kv, wl.d)
             us_p = timeit(lambda: m.gqa_attn_decode_paged(q, kp, vp, table, lens, workspace=ws, out=o))
+            us_pc = timeit_cold(lambda: m.gqa_attn_decode_paged(q, kp, vp, table, lens, workspace=ws, out=o))
             log(json.dumps({"sweep": name, "kernel": "decode_paged16", "us": round(us_p, 2),
-                            "gbps": round(by / us_p / 1e3, 1), "frac": round(by / us_p / 1e3 / PEAK_HBM_GBS, 4)}))
+                            "gbps": round(by / us_p / 1e3, 1), "frac": round(by / us_p / 1e3 / PEAK_HBM_GBS, 4),
+                            "us_cold": round(us_pc, 2), "gbps_cold": round(by / us_pc / 1e3, 1)}))
             del kp, vp
             pj = W.proj_inputs(wl)
             x, w = up(pj["x"]), up(pj["w"])
             us = timeit(lambda: m.qkv_proj(x, w, wl.H_q, wl.H_kv, wl.d))
+            us_c = timeit_cold(lambda: m.qkv_proj(x, w, wl.H_q, wl.H_kv, wl.d))
             by = 2.0 * (wl.hidden * wl.N + x.shape[0] * (wl.hidden + wl.N))
             log(json.dumps({"sweep": name, "kernel": "qkv_proj", "us": round(us, 2),
-                            "gbps": round(by / us / 1e3, 1)}))
+                            "gbps": round(by / us / 1e3, 1), "us_cold": round(us_c, 2),
+                            "gbps_cold": round(by / us_c / 1e3, 1)}))
             del kc, vc
         torch.cuda.empty_cache()
     varlen_batch(m, W, torch, dev, timeit)

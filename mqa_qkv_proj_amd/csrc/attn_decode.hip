@@ -54,6 +54,19 @@ __device__ __forceinline__ f32x4_t mfma16_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// A K/V cache row is read once per call.  When the caches are large (STREAM),
+// rows are loaded with the non-temporal hint so the stream does not allocate in
+// the caches: it then neither evicts data that is reused (a projection weight
+// that fits the Infinity Cache) nor has to write back, while it streams, the
+// dirty lines earlier kernels left there.  Small caches (a few MB, which stay
+// resident from one decode step to the next) use ordinary loads.
+constexpr int64_t kStreamBytes = (int64_t)64 << 20;  // K + V capacity from which STREAM is used
+template <bool STREAM>
+__device__ __forceinline__ u32x4_t ld16_kv(const void* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return ld16(p);
+}
+
 // Keys of sequence b that are attended (lengths beyond the cache are clamped).
 __device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b, int Lmax) {
   return min(max(seq_lens[b], 0), Lmax);
@@ -120,7 +133,7 @@ __device__ __forceinline__ int64_t balanced_tpw(int64_t total, int nwg) {
 // Per unit, MFMA 16x16x32 layout: A (16 x 32): lane l holds row l%16, k slot
 // group l/16; B (32 x 16): column l%16, the same k group; D (16 x 16): column
 // l%16, rows 4*(l/16) + i.
-template <int D>
+template <int D, bool STREAM>
 __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_ml,
@@ -190,7 +203,7 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
 #pragma unroll
         for (int st = 0; st < DS; ++st)
           kr[kb][st] = (gk < kend && off[kb] != kNoRow)
-                           ? ld16(kbase + (off[kb] + gk) * row_stride + st * 32)
+                           ? ld16_kv<STREAM>(kbase + (off[kb] + gk) * row_stride + st * 32)
                            : u32x4_t{0, 0, 0, 0};
       }
 #pragma unroll
@@ -201,7 +214,7 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int gk = k0 + a * 4 + jj;
-          rv[j][jj] = (gk < kend && vo != kNoRow) ? ld16(vbase + (vo + gk) * row_stride + dg * 8)
+          rv[j][jj] = (gk < kend && vo != kNoRow) ? ld16_kv<STREAM>(vbase + (vo + gk) * row_stride + dg * 8)
                                                   : u32x4_t{0, 0, 0, 0};
         }
       }
@@ -531,7 +544,8 @@ hipError_t launch_split_bf16(const DecodeArgs& a, hipStream_t s, int& nwg) {
   }
   if (nblk > 0x7fffffff || nblk < 1) return hipErrorInvalidValue;
   nwg = (int)nblk;
-  auto kern = attn_decode_split_bf16_kernel<D>;
+  const bool stream = (int64_t)a.B * a.Lmax * a.Hkv * D * 4 >= kStreamBytes;
+  auto kern = stream ? attn_decode_split_bf16_kernel<D, true> : attn_decode_split_bf16_kernel<D, false>;
   const size_t lds = DecodeLds<D>::kBytes;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_lens, a.part_o, a.part_ml, a.B,
