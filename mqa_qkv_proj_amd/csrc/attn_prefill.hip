@@ -589,33 +589,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   // computes the next half's scores into `sc`, adds P V for the current half
   // (V^T `vc`, keys 32jc..) and, when NEXT, reads the K fragments of the half
   // after that (`kn`, keys 32jn..) into `kf`.  The source order is the issue
-  // order: each score MFMA is followed by one pair of softmax values and one V
-  // read, each P.V MFMA by a row-sum step and one K read, so the vector and LDS
-  // units work while the matrix cores run and every operand is in flight long
+  // order: each score MFMA is followed by one V read and exponentials, each
+  // P.V MFMA by a row-sum step and one K read, so the vector and LDS units
+  // work while the matrix cores run and every operand is in flight long
   // before it is used.  Fences keep the compiler from regrouping.
+  // bf16 scores (SPREAD) split a half's exponentials between two steps: those
+  // of its first 16 keys are computed under the previous step's P.V MFMAs
+  // (carried in `pl`, their max in `ml`, with the half's score scale `cn`),
+  // the rest under its own score MFMAs, which spreads the vector work evenly
+  // under the matrix work (measured 1-3% faster).  The fp8 score MFMAs come
+  // two per step, too few to carry that; there every exponential of the half
+  // follows the score MFMAs.
   // P is computed with the running max as it stands, while the half's row max
   // is folded in beside it; only if some row's max grew by more than kTau
   // (rare after the first half) is the max raised, O and l rescaled and P
   // recomputed, before any of P is used.  So the exponentials do not wait for
-  // the max reduction.
-  auto step = [&](f32x16_t& sc, u32x4_t (&kf)[KF], const uint16_t* vc, int jc, const uint16_t* kn,
-                  int jn, auto next_tag, auto part0) {
+  // the max reduction, and every one of them uses the running max that holds
+  // when the half's P is consumed.
+  auto step = [&](f32x16_t& sc, u32x4_t& pl, float& ml, u32x4_t (&kf)[KF], const uint16_t* vc, int jc,
+                  const uint16_t* kn, int jn, float cn, auto next_tag, auto part0) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr int PART0 = part0;
+    constexpr bool SPREAD = !F8;
     u32x4_t pf[2];
     u32x4_t vf[2 * DB];
     f32x16_t sn = f32x16_t{};
-    float mx = sc[0];
+    float mx = SPREAD ? ml : sc[0];
+    if constexpr (SPREAD) pf[0] = pl;
     static_for<0, 8>([&](auto i) {
-      constexpr int hb = i >> 2, e = i & 3;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], cc, -m_run));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], cc, -m_run));
-      pf[hb][e] = pack_f16(p0, p1);
-      mx = fmaxf(fmaxf(mx, sc[hb * 8 + 2 * e]), sc[hb * 8 + 2 * e + 1]);
+      if constexpr (!SPREAD) {  // all 16 pairs of the current half, one per slot
+        constexpr int hb = i >> 2, e = i & 3;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e], cc, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hb * 8 + 2 * e + 1], cc, -m_run));
+        pf[hb][e] = pack_f16(p0, p1);
+        mx = fmaxf(fmaxf(mx, sc[hb * 8 + 2 * e]), sc[hb * 8 + 2 * e + 1]);
+      }
       if constexpr (F8) {
         if constexpr (i % (8 / KS8) == 0) sn = smfma(kf, 2 * (i / (8 / KS8)), sn);
       } else if constexpr (i < DS) {
         sn = smfma(kf, i, sn);
+      }
+      if constexpr (SPREAD && i % 2 == 1) {  // keys 16.. of the current half: one pair every other slot
+        constexpr int e = i / 2;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 + 2 * e], cc, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 + 2 * e + 1], cc, -m_run));
+        pf[1][e] = pack_f16(p0, p1);
+        // keep the exponentials here: the compiler would otherwise sink them past
+        // the max check into its no-rescale branch, away from the MFMAs
+        asm volatile("" ::"v"(pf[1][e]));
+        mx = fmaxf(fmaxf(mx, sc[8 + 2 * e]), sc[8 + 2 * e + 1]);
       }
       if constexpr (i < 2 * DB)
         vf[i] = ld16(vc + ((i % DB) * 32 + l32) * S::kVld + (jc * 2 + i / DB) * 16 + hf * 8);
@@ -643,6 +665,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    if constexpr (SPREAD) ml = -INFINITY;
     static_for<0, 2 * DB>([&](auto i) {
       constexpr int hb = i / DB, db = i % DB;
       acc[db] = mfma32_f16(vf[i], pf[hb], acc[db]);
@@ -652,9 +675,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
       });
       if constexpr (NEXT && i < KF) kf[i] = kfrag(kn, jn * 32 + l32, i);
       if constexpr (PART0 >= 0) fill_part(std::integral_constant<int, PART0 + i>{});
+      // keys 0..15 of the next half, spread over the P.V MFMAs
+      if constexpr (SPREAD) static_for<i * 4 / (2 * DB), (i + 1) * 4 / (2 * DB)>([&](auto e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sn[2 * e], cn, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sn[2 * e + 1], cn, -m_run));
+        pl[(int)e] = pack_f16(p0, p1);
+        ml = fmaxf(fmaxf(ml, sn[2 * e]), sn[2 * e + 1]);
+      });
       __builtin_amdgcn_sched_barrier(0);
     });
     sc = sn;
+  };
+  // The P of keys 0..15 of the half held in `s` (and their max), as the
+  // SPREAD step carries it from one step to the next.
+  auto first_p = [&](const f32x16_t& s, u32x4_t& plq, float& mlq) {
+    mlq = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e], cc, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * e + 1], cc, -m_run));
+      plq[e] = pack_f16(p0, p1);
+      mlq = fmaxf(fmaxf(mlq, s[2 * e]), s[2 * e + 1]);
+    }
   };
   // Last step of the pipeline: P V for the current half only.
   auto drain = [&](const f32x16_t& sc, const uint16_t* vc, int jc) {
@@ -679,10 +721,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   f32x16_t sc = f32x16_t{};
   u32x4_t pf[2];
   u32x4_t kf[KF];
+  u32x4_t pl = u32x4_t{0, 0, 0, 0};  // the step's carried P of keys 0..15 of the current half
+  float ml = -INFINITY;
   if (t_mask > 0) {
     cc = tile_c(0);
     sc = qk(k_of(0), 0);
     update_max(sc);
+    if constexpr (!F8) first_p(sc, pl, ml);
     load_kf(kf, k_of(0), 1);
   }
   for (; t + 1 < t_mask; ++t) {
@@ -690,8 +735,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     fill_begin(t + 2, st2);
     cc = tile_c(st0);
-    step(sc, kf, v_of(st0), 0, k_of(st1), 0, std::true_type{}, std::integral_constant<int, 0>{});
-    step(sc, kf, v_of(st0), 1, k_of(st1), 1, std::true_type{}, std::integral_constant<int, 2 * DB>{});
+    // the second step computes the scores of tile t + 1 (stage st1), under that tile's scale
+    step(sc, pl, ml, kf, v_of(st0), 0, k_of(st1), 0, cc, std::true_type{}, std::integral_constant<int, 0>{});
+    step(sc, pl, ml, kf, v_of(st0), 1, k_of(st1), 1, tile_c(st1), std::true_type{},
+         std::integral_constant<int, 2 * DB>{});
     static_for<4 * DB, kParts>([&](auto i) { fill_part(i); });
     wait_dma();
     __syncthreads();
@@ -702,7 +749,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     if (t + 2 < nt) fill(t + 2, st2);
     cc = tile_c(st0);
-    step(sc, kf, v_of(st0), 0, k_of(st1), 0, std::false_type{}, std::integral_constant<int, -1>{});
+    step(sc, pl, ml, kf, v_of(st0), 0, k_of(st1), 0, cc, std::false_type{}, std::integral_constant<int, -1>{});
     update_max(sc);
     drain(sc, v_of(st0), 1);
     wait_dma();
