@@ -593,13 +593,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
   // P.V MFMA by a row-sum step and one K read, so the vector and LDS units
   // work while the matrix cores run and every operand is in flight long
   // before it is used.  Fences keep the compiler from regrouping.
-  // bf16 scores (SPREAD) split a half's exponentials between two steps: those
-  // of its first 16 keys are computed under the previous step's P.V MFMAs
-  // (carried in `pl`, their max in `ml`, with the half's score scale `cn`),
-  // the rest under its own score MFMAs, which spreads the vector work evenly
-  // under the matrix work (measured 1-3% faster).  The fp8 score MFMAs come
-  // two per step, too few to carry that; there every exponential of the half
-  // follows the score MFMAs.
+  // With bf16 scores and d = 128 (SPREAD) a half's exponentials are split
+  // between two steps: those of its first 16 keys are computed under the
+  // previous step's P.V MFMAs (carried in `pl`, their max in `ml`, with the
+  // half's score scale `cn`), the rest under its own score MFMAs, which
+  // spreads the vector work evenly under the matrix work (measured 1-3%
+  // faster).  Otherwise every exponential of the half follows the score
+  // MFMAs: with fp8 scores (two MFMAs per step) the split measured 8% slower,
+  // with d = 64 (half the MFMAs per step) 6% slower.
   // P is computed with the running max as it stands, while the half's row max
   // is folded in beside it; only if some row's max grew by more than kTau
   // (rare after the first half) is the max raised, O and l rescaled and P
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
                   const uint16_t* kn, int jn, float cn, auto next_tag, auto part0) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr int PART0 = part0;
-    constexpr bool SPREAD = !F8;
+    constexpr bool SPREAD = !F8 && D == 128;
     u32x4_t pf[2];
     u32x4_t vf[2 * DB];
     f32x16_t sn = f32x16_t{};
@@ -727,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_bf16_kernel(
     cc = tile_c(0);
     sc = qk(k_of(0), 0);
     update_max(sc);
-    if constexpr (!F8) first_p(sc, pl, ml);
+    if constexpr (!F8 && D == 128) first_p(sc, pl, ml);
     load_kf(kf, k_of(0), 1);
   }
   for (; t + 1 < t_mask; ++t) {
