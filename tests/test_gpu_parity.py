@@ -177,6 +177,32 @@ def test_prefill_workspace_reuse(m):
         m.gqa_attn_prefill(q, k, v, workspace=small)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_d64_workgroup_sizes_give_the_same_bits(m, causal):
+    """d=64 grids under two 8-wave workgroups per CU run 4-wave workgroups.
+    A batch of 8 sequences (an 8-wave grid of 8 x 4 x 64 = 2048 blocks) and
+    each sequence on its own (256 blocks: 4-wave workgroups) give the same bits,
+    since each row's arithmetic does not depend on the workgroup shape; the
+    batch is also checked against the oracle on sampled rows."""
+    t = torch()
+    B, L, H_q, H_kv, d = 8, 2048, 32, 4, 64
+    say("prefill d=64 workgroup sizes", causal)
+    g = t.Generator().manual_seed(77)
+    q = t.randn(B, L, H_q, d, generator=g).to(t.bfloat16).cuda()
+    k = t.randn(B, L, H_kv, d, generator=g).to(t.bfloat16).cuda()
+    v = t.randn(B, L, H_kv, d, generator=g).to(t.bfloat16).cuda()
+    o, lse = m.gqa_attn_prefill(q, k, v, causal=causal, return_lse=True, out_dtype=t.float32)
+    for b in (0, 3, 7):
+        ob, lb = m.gqa_attn_prefill(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal=causal, return_lse=True,
+                                    out_dtype=t.float32)
+        assert t.equal(o[b:b + 1], ob), f"sequence {b}: O differs between workgroup shapes"
+        assert t.equal(lse[b:b + 1], lb), f"sequence {b}: LSE differs between workgroup shapes"
+    rows = np.array([0, 1, 63, 64, 1000, 2047])
+    for b, h in ((0, 0), (7, 31)):
+        ref, _ = oracle.attention_rows(host(q), host(k), host(v), b, h, rows, causal, 1.0 / math.sqrt(d))
+        assert_close(host(o[b, rows, h]), ref, "bf16", f"sampled rows b={b} h={h}")
+
+
 def test_prefill_on_qkv_views_equals_contiguous_copies(m):
     """The split is zero-copy: strided views of qkv give the same bits as packed copies."""
     t = torch()
