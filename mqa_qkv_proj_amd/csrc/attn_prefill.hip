@@ -908,8 +908,9 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   uint16_t* img = static_cast<uint16_t*>(a.ws);
   hipLaunchKernelGGL(prefill_v_image_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s,
                      (const uint16_t*)a.v, img, a.Lkv, a.Hkv, a.kv_stride, ntiles, a.cu_kv, a.total_kv);
-  auto kern = nw == 4 ? attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, 4>
-                      : attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, kWaves>;
+  auto kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, kWaves>;
+  if constexpr (D == 64)
+    if (nw == 4) kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, 4>;
   const size_t lds = PrefillLds<D>::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
