@@ -448,6 +448,23 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
   const int lane = threadIdx.x;
   const int b = blockIdx.y, h = blockIdx.x;
   const int64_t bh = (int64_t)b * Hq + h;
+  const float* ml = part_ml + bh * n_slot * 2;
+  const float* po = part_o + bh * n_slot * D;
+  // The first round's statistics and outputs are loaded before the number of
+  // units is known, so those loads overlap the pass over seq_lens.  Slots
+  // below n_slot lie inside the workspace; the values of slots past the unit
+  // count (stale or never written) are replaced below, never used.
+  const int pre = min(U, n_slot);
+  float m_pre = -INFINITY, l_pre = 0.0f, v_pre[U][EPL] = {};
+  if (pre > 0) {
+    const int sl = lane < pre ? lane : 0;
+    m_pre = ml[2 * sl];
+    l_pre = ml[2 * sl + 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v_pre[u][e] = u < pre ? po[(int64_t)u * D + e * 64 + lane] : 0.0f;
+  }
   const int len = seq_len(seq_lens, b, Lmax);
   int n;
   if (split > 0) {
@@ -475,8 +492,6 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     n = ntb > 0 ? (int)((s0 + ntb - 1) / tpw - s0 / tpw + 1) : 0;
     n = min(n, n_slot);
   }
-  const float* ml = part_ml + bh * n_slot * 2;
-  const float* po = part_o + bh * n_slot * D;
 
   float M = -INFINITY, L = 0.0f;  // running max (log2 units) and sum over the rounds so far
   float acc[EPL];
@@ -485,14 +500,23 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
   for (int c0 = 0; c0 < n; c0 += U) {
     const int cnt = min(U, n - c0);
     // this lane's unit statistics (lanes >= cnt: none) and every unit's outputs
-    const int sl = c0 + (lane < cnt ? lane : 0);
-    const float m_l = lane < cnt ? ml[2 * sl] : -INFINITY;
-    const float l_l = lane < cnt ? ml[2 * sl + 1] : 0.0f;
-    float v[U][EPL];
+    float m_l, l_l, v[U][EPL];
+    if (c0 == 0) {
+      m_l = lane < cnt ? m_pre : -INFINITY;
+      l_l = lane < cnt ? l_pre : 0.0f;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) v[u][e] = u < cnt ? po[(int64_t)(c0 + u) * D + e * 64 + lane] : 0.0f;
+        for (int e = 0; e < EPL; ++e) v[u][e] = u < cnt ? v_pre[u][e] : 0.0f;
+    } else {
+      const int sl = c0 + (lane < cnt ? lane : 0);
+      m_l = lane < cnt ? ml[2 * sl] : -INFINITY;
+      l_l = lane < cnt ? ml[2 * sl + 1] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[u][e] = u < cnt ? po[(int64_t)(c0 + u) * D + e * 64 + lane] : 0.0f;
+    }
     float mr = m_l;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mr = fmaxf(mr, __shfl_xor(mr, off, 64));
