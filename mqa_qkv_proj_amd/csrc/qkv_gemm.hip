@@ -273,7 +273,9 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
 // The row paddings keep both operand reads on distinct LDS banks; the lanes of
 // a copy that fall on padding point past the buffer and write nothing.  Two
 // LDS stages: the copy of k tile t+1 runs while tile t is multiplied, one
-// barrier per k tile.  Requires K % 64 == 0.
+// barrier per k tile.  All operand reads of a 16-deep k step are issued
+// together and waited for once, a step ahead of their MFMAs.  Requires
+// K % 64 == 0.
 constexpr int kCfBN = 128, kCfBK = 64, kCfThreads = 256;
 constexpr int kCfXld = kCfBK + 8;   // x tile row pitch (bf16 elements): 9 chunks of 16 B
 constexpr int kCfWld = kCfBN + 32;  // W tile row pitch: 20 chunks of 16 B
@@ -308,6 +310,45 @@ __device__ __forceinline__ u32x4_t lds_tr16_pair(const uint16_t* p) {
       : "v"(a), "i"(HI_BYTES)
       : "memory");
   return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// All operand fragments of one 16-deep k step: the MI x rows (A) and the two
+// transposed W pairs (B), read in one asm block that waits for itself once,
+// so a k step costs one LDS round trip rather than one per B pair.
+template <int MI, int HI_BYTES>
+__device__ __forceinline__ void lds_step_frags(const uint16_t* pa0, const uint16_t* pa1, const uint16_t* pb0,
+                                               const uint16_t* pb1, u32x4_t (&a)[MI], u32x4_t (&b)[2]) {
+  auto addr = [](const uint16_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+  };
+  u32x2_t l0, h0, l1, h1;
+  if constexpr (MI == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b64_tr_b16 %2, %8\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %4, %9\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%10\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
+        : "v"(addr(pa0)), "v"(addr(pa1)), "v"(addr(pb0)), "v"(addr(pb1)), "i"(HI_BYTES)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b64_tr_b16 %1, %6\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "ds_read_b64_tr_b16 %4, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
+        : "v"(addr(pa0)), "v"(addr(pb0)), "v"(addr(pb1)), "i"(HI_BYTES)
+        : "memory");
+    (void)pa1;
+  }
+  b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
+  b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
 }
 
 template <int BM>
@@ -375,12 +416,9 @@ __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
   const int bg = lane >> 4, bp = lane & 15;                   // transposing-read lane group
   const int b_n = 16 * (bg & 1) + 4 * (bp & 3), b_k = 8 * (bg >> 1) + (bp >> 2);
   auto frags = [&](const uint16_t* xs, const uint16_t* ws, int ks, u32x4_t (&a)[MI], u32x4_t (&b)[2]) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i) a[i] = ld16(xs + (wm * (BM / 2) + i * 32 + l32) * kCfXld + ks * 16 + hf * 8);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      b[j] = lds_tr16_pair<4 * kCfWld * 2>(ws + (ks * 16 + b_k) * kCfWld + wn * 64 + j * 32 + b_n);
-    }
+    const uint16_t* pa = xs + (wm * (BM / 2) + l32) * kCfXld + ks * 16 + hf * 8;
+    const uint16_t* pb = ws + (ks * 16 + b_k) * kCfWld + wn * 64 + b_n;
+    lds_step_frags<MI, 4 * kCfWld * 2>(pa, pa + 32 * kCfXld, pb, pb + 32, a, b);
   };
 
   copy_tile(0, 0);
