@@ -32,9 +32,9 @@
 //    copied in, with one barrier per 64-key tile.
 //  * Tiles reach LDS by LDS-DMA (buffer loads that write LDS directly): no
 //    staging registers and no LDS store instructions.  K rows keep 16 bytes of
-//    padding per row (the pad lanes of a copy point past the buffer and write
-//    nothing) so that the operand reads of 16 consecutive rows hit distinct
-//    banks; the V^T images carry the same padding.  The copies are issued by
+//    padding per row (the pad lanes of a copy point past the buffer, so they
+//    fetch nothing and land only on padding) so that the operand reads of 16
+//    consecutive rows hit distinct banks; the V^T images carry the same padding.  The copies are issued by
 //    the four older waves, between the MFMAs of the pipelined steps.
 //  * Causal: tiles beyond the block's diagonal are never visited, only tiles
 //    that cross a row's limit are masked (a separate, unpipelined loop), and
@@ -426,9 +426,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
   const int nt = (kv_end + kBK - 1) / kBK;
 
   // ---- tile copies (LDS-DMA, no registers): K straight from the K rows, with
-  // the lanes that fall on row padding pointed past the buffer so they write
-  // nothing; V from its prepared image.  Rows at or past L_kv are past the
-  // buffer end too and leave stale LDS rows, which only ever meet masked keys.
+  // the lanes that fall on row padding pointed past the buffer, so they fetch
+  // nothing and land only on padding bytes, which are never read; V from its
+  // prepared image.  Rows at or past L_kv are past the buffer end too: their
+  // LDS rows (zeros or stale) only ever meet masked keys.
   const uint32_t row_bytes = (uint32_t)(kv_stride * 2);
   const uint32_t kv_bytes = (uint32_t)((int64_t)Lkv * kv_stride * 2);
   const char* kbase = reinterpret_cast<const char*>(k + sp.kv0 * kv_stride);

@@ -271,7 +271,8 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
 //    lanes, lane 4j+q reads 4 n of k-row j and lane i receives column i of the
 //    4 rows, so no VALU transposition is needed.
 // The row paddings keep both operand reads on distinct LDS banks; the lanes of
-// a copy that fall on padding point past the buffer and write nothing.  Two
+// a copy that fall on padding point past the buffer, so they fetch nothing and
+// land only on padding bytes, which are never read.  Two
 // LDS stages: the copy of k tile t+1 runs while tile t is multiplied, one
 // barrier per k tile.  All operand reads of a 16-deep k step are issued
 // together and waited for once, a step ahead of their MFMAs.  Requires
@@ -385,7 +386,8 @@ __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
     const int r = slot / 20, ch = slot % 20;
     woff[i] = ch < 16 ? (uint32_t)r * wrow + ch * 16 : kNoCopy;
   }
-  // x rows at or past M and W rows past K lie past their buffer ends: no write.
+  // x rows at or past M and W rows past K lie past their buffer ends: they
+  // fetch nothing, and their LDS rows only feed outputs that are not stored.
   const uint64_t xbytes = (uint64_t)M * K * 2, wbytes = (uint64_t)K * N * 2;
   auto copy_tile = [&](int kt, int st) {
     uint16_t* xs = smem + st * L::kStage;
