@@ -32,17 +32,26 @@
  *   - All data pointers are DEVICE pointers owned by the caller; outputs are
  *     fully overwritten (never accumulated), in the style of an op that
  *     mutates a caller-allocated `out` ("custom op overhead" gist).
- *   - The library never allocates device memory, never synchronises and keeps
- *     no mutable global state; calls are asynchronous on `stream`
- *     (a hipStream_t; NULL = the default stream) and reentrant.
+ *   - The library never allocates device memory and never synchronises;
+ *     calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and reentrant; every scratch buffer is the caller's.
  *   - Arguments are validated on the host before any HIP call.  A rejected
  *     call launches nothing and returns MQKV_ERR_INVALID (malformed) or
  *     MQKV_ERR_UNSUPPORTED (well-formed but not implemented); a failed launch
  *     returns MQKV_ERR_HIP.  mqkv_last_error() gives the thread-local detail.
- *   - Device-side data (seq_lens values) is trusted: values outside
- *     [1, L_max] are undefined behaviour.
+ *   - Device-side lengths are clamped to their buffers (decode: seq_lens to
+ *     [0, L_max]), so no device value leads outside them.
  *   - dtypes: MQKV_BF16 (bf16 storage, fp32 accumulation, round-to-nearest-
  *     even outputs) or MQKV_F32 (fp32 throughout).
+ *   - bf16 attention multiplies P by V on fp16 matrix cores; each tile of V
+ *     (64 keys in prefill, 32 in decode) is converted as V * 2^-s with a
+ *     power-of-two exponent s of its own (s = 0 when the tile lies inside
+ *     fp16's range) and the accumulator follows with exact power-of-two
+ *     rescales, so every finite bf16 V, however large or small, gives a finite
+ *     result.  Values at least 2^-29 of their tile's largest |v| convert
+ *     exactly; smaller ones are rounded with an absolute error of at most
+ *     max(2^-39 * that largest |v|, 2^-25) (a prefill tile's largest |v|
+ *     includes keys a causal row does not see).
  *   - Alignment: every data pointer 16-byte aligned; element strides multiples
  *     of 8 (bf16) or 4 (fp32) elements.
  */
@@ -240,8 +249,9 @@ size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int
  *
  *   q(b,h,c)       = q[b*q_tok_stride + h*d + c]          (e.g. a view of qkv rows)
  *   k_cache, v_cache [B, L_max, H_kv, d] contiguous
- *   seq_lens [B] device int32, each in [1, L_max]: sequence b attends to keys
- *   [0, seq_lens[b]) (the new token's K/V are already in the cache)
+ *   seq_lens [B] device int32, clamped to [0, L_max]: sequence b attends to
+ *   keys [0, seq_lens[b]) (the new token's K/V are already in the cache).  A
+ *   sequence with no keys gets O = 0 and LSE = -inf
  *   o   [B, H_q, d] contiguous (o_dtype), lse [B, H_q] fp32 or NULL
  *
  * The keys of every (sequence, KV head) are cut into work units: splits of
@@ -278,7 +288,8 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
  *                  covering keys [0, seq_lens[b]) are read.  A page id outside
  *                  [0, num_pages) is never dereferenced: its keys read as
  *                  zero vectors.
- * seq_lens         [B] device int32, clamped to [0, pages_per_seq * page_size]
+ * seq_lens         [B] device int32, clamped to [0, pages_per_seq * page_size];
+ *                  a sequence with no keys gets O = 0 and LSE = -inf
  * page_size        a positive multiple of 16
  * Everything else, the workspace (gqa_attn_decode_workspace_bytes with
  * L_max = pages_per_seq * page_size), the split and the results are those of

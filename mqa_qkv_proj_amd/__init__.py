@@ -30,8 +30,8 @@ MQKV_F32, MQKV_BF16 = 0, 1
 EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill_workspace_bytes",
            "gqa_attn_prefill", "gqa_attn_decode_paged", "gqa_attn_prefill_varlen",
            "gqa_attn_prefill_fp8_workspace_bytes", "gqa_attn_prefill_fp8",
-           "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "mqkv_status_string", "mqkv_last_error",
-           "mqkv_abi_version")
+           "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "mqkv_status_string",
+           "mqkv_last_error", "mqkv_abi_version")
 
 
 class MqkvError(RuntimeError):
@@ -382,6 +382,26 @@ def gqa_attn_prefill_fp8(q, k, v, signs=None, causal: bool = True, scale: Option
     return (out, lse) if return_lse else out
 
 
+def _check_decode_operands(torch, q, caches, seq_lens, out, out_dtype, B: int, H_q: int, d: int):
+    """Host checks shared by the decode calls; returns the output dtype.
+
+    The kernels take their element type from q alone, so caches of another
+    dtype, a non-contiguous seq_lens or an `out` of the wrong shape, layout or
+    dtype would make them read or write outside those buffers."""
+    if q.stride(2) != 1 or (H_q > 1 and q.stride(1) != d):
+        raise ValueError("q rows must hold contiguous [H_q, d] heads")
+    if any(c.dtype != q.dtype for c in caches):
+        raise ValueError(f"the caches must have q's dtype ({q.dtype})")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"out_dtype must be bfloat16 or float32, got {out_dtype}")
+    if out is not None and (tuple(out.shape) != (B, H_q, d) or not out.is_contiguous() or out.dtype != out_dtype):
+        raise ValueError(f"out must be a contiguous [{B}, {H_q}, {d}] tensor of {out_dtype}")
+    return out_dtype
+
+
 def decode_workspace_bytes(B: int, H_q: int, H_kv: int, d: int, L_max: int, kv_split: int = 0) -> int:
     return int(lib.gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split))
 
@@ -401,18 +421,14 @@ def gqa_attn_decode(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None
     [B, L_max, H_kv, d] contiguous, seq_lens [B] int32 on the device.
     Returns o [B, H_q, d] (and lse [B, H_q] if asked)."""
     torch = _torch()
-    _require_cuda(q, k_cache, v_cache, seq_lens, workspace, out)
     B, H_q, d = q.shape
     _, L_max, H_kv, _ = k_cache.shape
     if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != d:
         raise ValueError("caches must be [B, L_max, H_kv, d] matching q")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise ValueError("caches must be contiguous")
-    if q.stride(2) != 1 or (H_q > 1 and q.stride(1) != d):
-        raise ValueError("q rows must hold contiguous [H_q, d] heads")
-    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
-        raise ValueError("seq_lens must be int32 [B]")
-    out_dtype = q.dtype if out_dtype is None else out_dtype
+    out_dtype = _check_decode_operands(torch, q, (k_cache, v_cache), seq_lens, out, out_dtype, B, H_q, d)
+    _require_cuda(q, k_cache, v_cache, seq_lens, workspace, out)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split)
     if workspace is None:
@@ -439,7 +455,6 @@ def gqa_attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: Opt
     contiguous bf16, block_table [B, pages_per_seq] and seq_lens [B] int32 on the
     device.  Returns o [B, H_q, d] (and lse [B, H_q] if asked)."""
     torch = _torch()
-    _require_cuda(q, k_pages, v_pages, block_table, seq_lens, workspace, out)
     B, H_q, d = q.shape
     num_pages, page_size, H_kv, _ = k_pages.shape
     if v_pages.shape != k_pages.shape or k_pages.shape[3] != d:
@@ -448,12 +463,9 @@ def gqa_attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: Opt
         raise ValueError("pages and block_table must be contiguous")
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be int32 [B, pages_per_seq]")
-    if q.stride(2) != 1 or (H_q > 1 and q.stride(1) != d):
-        raise ValueError("q rows must hold contiguous [H_q, d] heads")
-    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
-        raise ValueError("seq_lens must be int32 [B]")
+    out_dtype = _check_decode_operands(torch, q, (k_pages, v_pages), seq_lens, out, out_dtype, B, H_q, d)
+    _require_cuda(q, k_pages, v_pages, block_table, seq_lens, workspace, out)
     pages_per_seq = block_table.shape[1]
-    out_dtype = q.dtype if out_dtype is None else out_dtype
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = decode_workspace_bytes(B, H_q, H_kv, d, pages_per_seq * page_size, kv_split)
     if workspace is None:

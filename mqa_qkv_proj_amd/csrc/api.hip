@@ -273,23 +273,15 @@ mqkv_status gqa_attn_prefill_fp8(const void* q, const void* k, const void* v, vo
   return hip_status(mqkv::launch_prefill(a, (hipStream_t)stream), "gqa_attn_prefill_fp8 launch");
 }
 
-size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
-                                       int32_t L_max, int32_t kv_split) {
-  if (B < 0 || L_max < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
-    return 0;
-  if (kv_split != 0 && !split_ok(kv_split)) return 0;
-  const int slots = std::max(mqkv::decode_slots(B, H_q, H_kv, L_max, kv_split, true),
-                             mqkv::decode_slots(B, H_q, H_kv, L_max, kv_split, false));
-  const int64_t per = (int64_t)B * H_q * slots;
-  return (size_t)(per * d * 4 + per * 2 * 4 + 256);  // outputs, then (max, sum) pairs
-}
+}  // extern "C"
 
-mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* seq_lens, void* o, float* lse, int32_t B, int32_t H_q,
-                            int32_t H_kv, int32_t d, int32_t L_max, int64_t q_tok_stride,
-                            float scale, int32_t kv_split, void* workspace, size_t workspace_bytes,
-                            mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream) {
-  g_err[0] = 0;
+namespace {
+
+// Host validation of a decode call.
+mqkv_status decode_check(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                         void* o, float* lse, int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t L_max,
+                         int64_t q_tok_stride, float scale, int32_t kv_split, mqkv_dtype in_dtype,
+                         mqkv_dtype o_dtype) {
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
     return fail(MQKV_ERR_INVALID, "dtype %d/%d unknown", (int)in_dtype, (int)o_dtype);
   mqkv_status st = check_heads(H_q, H_kv, d);
@@ -311,11 +303,22 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
     return fail(MQKV_ERR_UNSUPPORTED, "fp32 inputs need an fp32 output");
   if ((int64_t)B * L_max * H_kv * d > ((int64_t)1 << 40))
     return fail(MQKV_ERR_UNSUPPORTED, "cache too large");
-  if (B == 0) return MQKV_OK;
-  const size_t need = gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace))
-    return fail(MQKV_ERR_INVALID, "workspace must be 16-byte aligned and >= %zu bytes (got %zu)", need,
-                workspace_bytes);
+  return MQKV_OK;
+}
+
+// Workspace bytes one call of this dtype uses: partial outputs, then the
+// (max, sum, V exponent, -) quads of every slot.
+size_t decode_need(int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t L_max, int32_t kv_split, bool bf16) {
+  const int slots = mqkv::decode_slots(B, H_q, H_kv, L_max, kv_split, bf16);
+  const int64_t per = (int64_t)B * H_q * slots;
+  return (size_t)(per * d * 4 + per * 4 * 4 + 256);
+}
+
+// Launch of a validated decode call on a workspace of at least decode_need bytes.
+mqkv_status decode_launch(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                          void* o, float* lse, int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t L_max,
+                          int64_t q_tok_stride, float scale, int32_t kv_split, void* workspace,
+                          mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream) {
   const bool bf16 = in_dtype == MQKV_BF16;
   const int32_t n_slot = mqkv::decode_slots(B, H_q, H_kv, L_max, kv_split, bf16);
   const int32_t split = kv_split > 0 ? kv_split : mqkv::decode_auto_split(B, H_q, H_kv, L_max, bf16);
@@ -324,9 +327,39 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
   float* part_ml = part_o + per * d;
   mqkv::DecodeArgs a{q,     k_cache, v_cache, seq_lens, o,       lse,     B,
                      H_q,   H_kv,    d,       L_max,    q_tok_stride,     scale,
-                     split, n_slot,  part_o,  part_ml,  in_dtype == MQKV_BF16,
-                     o_dtype == MQKV_BF16};
+                     split, n_slot,  part_o,  part_ml,  bf16,    o_dtype == MQKV_BF16};
   return hip_status(mqkv::launch_decode(a, (hipStream_t)stream), "gqa_attn_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
+                                       int32_t L_max, int32_t kv_split) {
+  if (B < 0 || L_max < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
+    return 0;
+  if (kv_split != 0 && !split_ok(kv_split)) return 0;
+  // the query has no dtype: size for the larger of the two
+  return std::max(decode_need(B, H_q, H_kv, d, L_max, kv_split, true),
+                  decode_need(B, H_q, H_kv, d, L_max, kv_split, false));
+}
+
+mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, void* o, float* lse, int32_t B, int32_t H_q,
+                            int32_t H_kv, int32_t d, int32_t L_max, int64_t q_tok_stride,
+                            float scale, int32_t kv_split, void* workspace, size_t workspace_bytes,
+                            mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream) {
+  g_err[0] = 0;
+  mqkv_status st = decode_check(q, k_cache, v_cache, seq_lens, o, lse, B, H_q, H_kv, d, L_max, q_tok_stride,
+                                scale, kv_split, in_dtype, o_dtype);
+  if (st != MQKV_OK || B == 0) return st;
+  const size_t need = gqa_attn_decode_workspace_bytes(B, H_q, H_kv, d, L_max, kv_split);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(MQKV_ERR_INVALID, "workspace must be 16-byte aligned and >= %zu bytes (got %zu)", need,
+                workspace_bytes);
+  return decode_launch(q, k_cache, v_cache, seq_lens, o, lse, B, H_q, H_kv, d, L_max, q_tok_stride, scale,
+                       kv_split, workspace, in_dtype, o_dtype, stream);
 }
 
 mqkv_status gqa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -221,7 +221,20 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
       off_next[0] = block_off(k0 + kTK);
       off_next[1] = block_off(k0 + kTK + 16);
     };
-    auto store_v = [&]() {
+    // V^T of the tile in fp16 as V * 2^-s, s = the tile's exponent (returned,
+    // wave-uniform); s = 0 for values inside fp16's range
+    auto store_v = [&]() -> int {
+      uint32_t em = 0;
+#pragma unroll
+      for (int j = 0; j < VTASK; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) em = max(em, bf16x2_expmax(rv[j][jj][e]));
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) em = max(em, (uint32_t)__shfl_xor((int)em, o, 64));
+      const int sv = __builtin_amdgcn_readfirstlane(v_tile_exp(em));
+      auto cv = [&](float x) { return __builtin_amdgcn_ldexpf(x, -sv); };
 #pragma unroll
       for (int j = 0; j < VTASK; ++j) {
         const int ti = lane + j * 64;
@@ -230,25 +243,34 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           u32x2_t lo, hi;
-          lo[0] = pack_f16(bf16lo(rv[j][0][e]), bf16lo(rv[j][1][e]));
-          lo[1] = pack_f16(bf16lo(rv[j][2][e]), bf16lo(rv[j][3][e]));
-          hi[0] = pack_f16(bf16hi(rv[j][0][e]), bf16hi(rv[j][1][e]));
-          hi[1] = pack_f16(bf16hi(rv[j][2][e]), bf16hi(rv[j][3][e]));
+          lo[0] = pack_f16(cv(bf16lo(rv[j][0][e])), cv(bf16lo(rv[j][1][e])));
+          lo[1] = pack_f16(cv(bf16lo(rv[j][2][e])), cv(bf16lo(rv[j][3][e])));
+          hi[0] = pack_f16(cv(bf16hi(rv[j][0][e])), cv(bf16hi(rv[j][1][e])));
+          hi[1] = pack_f16(cv(bf16hi(rv[j][2][e])), cv(bf16hi(rv[j][3][e])));
           st8(Vt + (dg * 8 + 2 * e) * S::kVld + cpos, lo);
           st8(Vt + (dg * 8 + 2 * e + 1) * S::kVld + cpos, hi);
         }
       }
+      return sv;
     };
 
     f32x4_t acc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) acc[i] = f32x4_t{};
     float m_run = -INFINITY, l_run = 0.0f;
+    int sig = 0;  // acc holds O * 2^-sig: the exponent of the V tiles accumulated so far
 
     load_tile(0);
     for (int t = 0; t < nt; ++t) {
       wave_lds_sync();  // the previous tile's V^T reads are done before overwriting
-      store_v();
+      const int sv = store_v();
+      if (sv != sig) {  // exact power-of-two rescale to this tile's V exponent
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_amdgcn_ldexpf(acc[i][e], sig - sv);
+        sig = sv;
+      }
       wave_lds_sync();
       const int k0 = kbeg + t * kTK;
       f32x4_t sb[2] = {f32x4_t{}, f32x4_t{}};
@@ -306,10 +328,8 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
       for (int db = 0; db < DB; ++db)
         st16(po + db * 16 + 4 * g4, u32x4_t{__float_as_uint(acc[db][0]), __float_as_uint(acc[db][1]),
                                             __float_as_uint(acc[db][2]), __float_as_uint(acc[db][3])});
-      if (g4 == 0) {
-        part_ml[pidx * 2 + 0] = m_run;
-        part_ml[pidx * 2 + 1] = l_tot;
-      }
+      if (g4 == 0)
+        st16(part_ml + pidx * 4, u32x4_t{__float_as_uint(m_run), __float_as_uint(l_tot), (uint32_t)sig, 0u});
     }
   };
 
@@ -426,18 +446,19 @@ __global__ __launch_bounds__(64) void attn_decode_split_f32_kernel(
   const int64_t pidx = ((int64_t)b * Hq + h) * n_slot + s;
 #pragma unroll
   for (int e = 0; e < PER; ++e) part_o[pidx * D + e * 64 + lane] = acc[e];
-  if (lane == 0) {
-    part_ml[pidx * 2 + 0] = m;
-    part_ml[pidx * 2 + 1] = l;
-  }
+  if (lane == 0) st16(part_ml + pidx * 4, u32x4_t{__float_as_uint(m), __float_as_uint(l), 0u, 0u});
 }
 
 // Combine the partials of every unit: one wave per (sequence, query head).
 // The number of units of (b, h) follows from the same work split the split
 // kernel used (one pass over seq_lens).  Then, 16 units at a time, every lane
-// loads one unit's (max, sum) and its D/64 elements of all 16 units' partial
-// outputs at once, so the statistics and the outputs cost one round trip
-// together; the weights are applied once the wave's maximum is known.
+// loads one unit's (max, sum, V exponent) and its D/64 elements of all 16
+// units' partial outputs at once, so the statistics and the outputs cost one
+// round trip together; the weights are applied once the wave's maximum is
+// known.  A unit's partial output is stored at the scale 2^-s of its V
+// exponent s; the sum is kept at the largest exponent seen, with exact
+// power-of-two rescaling (all exponents 0 for V inside fp16's range).
+// A sequence with no keys has no units: O = 0, LSE = -inf.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     const int32_t* __restrict__ seq_lens, const float* __restrict__ part_o,
@@ -448,7 +469,7 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
   const int lane = threadIdx.x;
   const int b = blockIdx.y, h = blockIdx.x;
   const int64_t bh = (int64_t)b * Hq + h;
-  const float* ml = part_ml + bh * n_slot * 2;
+  const float* ml = part_ml + bh * n_slot * 4;
   const float* po = part_o + bh * n_slot * D;
   // The first round's statistics and outputs are loaded before the number of
   // units is known, so those loads overlap the pass over seq_lens.  Slots
@@ -456,10 +477,13 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
   // count (stale or never written) are replaced below, never used.
   const int pre = min(U, n_slot);
   float m_pre = -INFINITY, l_pre = 0.0f, v_pre[U][EPL] = {};
+  int s_pre = 0;
   if (pre > 0) {
     const int sl = lane < pre ? lane : 0;
-    m_pre = ml[2 * sl];
-    l_pre = ml[2 * sl + 1];
+    const u32x4_t st = ld16(ml + 4 * sl);
+    m_pre = __uint_as_float(st[0]);
+    l_pre = __uint_as_float(st[1]);
+    s_pre = (int)st[2];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -493,7 +517,9 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     n = min(n, n_slot);
   }
 
+  constexpr int kNoUnit = -(1 << 20);  // V exponent of a lane without a unit (below any real one)
   float M = -INFINITY, L = 0.0f;  // running max (log2 units) and sum over the rounds so far
+  int Sx = INT_MIN;               // largest V exponent so far: acc holds O * L * 2^-Sx
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
@@ -501,51 +527,66 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     const int cnt = min(U, n - c0);
     // this lane's unit statistics (lanes >= cnt: none) and every unit's outputs
     float m_l, l_l, v[U][EPL];
+    int s_l;
     if (c0 == 0) {
       m_l = lane < cnt ? m_pre : -INFINITY;
       l_l = lane < cnt ? l_pre : 0.0f;
+      s_l = lane < cnt ? s_pre : kNoUnit;
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) v[u][e] = u < cnt ? v_pre[u][e] : 0.0f;
     } else {
       const int sl = c0 + (lane < cnt ? lane : 0);
-      m_l = lane < cnt ? ml[2 * sl] : -INFINITY;
-      l_l = lane < cnt ? ml[2 * sl + 1] : 0.0f;
+      const u32x4_t st = ld16(ml + 4 * sl);
+      m_l = lane < cnt ? __uint_as_float(st[0]) : -INFINITY;
+      l_l = lane < cnt ? __uint_as_float(st[1]) : 0.0f;
+      s_l = lane < cnt ? (int)st[2] : kNoUnit;
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) v[u][e] = u < cnt ? po[(int64_t)(c0 + u) * D + e * 64 + lane] : 0.0f;
     }
     float mr = m_l;
+    int sr = s_l;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mr = fmaxf(mr, __shfl_xor(mr, off, 64));
+    for (int off = 32; off > 0; off >>= 1) {
+      mr = fmaxf(mr, __shfl_xor(mr, off, 64));
+      sr = max(sr, __shfl_xor(sr, off, 64));
+    }
     const float Mn = fmaxf(M, mr);
+    const int Sn = max(Sx, sr);
     // rescale what the earlier rounds accumulated (no earlier round: factor 1)
     const float a = M == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+    const int ash = Sx == INT_MIN ? 0 : Sx - Sn;
     const float w = lane < cnt ? __builtin_amdgcn_exp2f(m_l - Mn) : 0.0f;
+    // weight of the unit's output: w * 2^(s - Sn), exactly w when s = Sn
+    const float wo = lane < cnt ? __builtin_amdgcn_ldexpf(w, s_l - Sn) : 0.0f;
     float lw = w * l_l;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off, 64);
     L = L * a + lw;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= a;
+    for (int e = 0; e < EPL; ++e) acc[e] = __builtin_amdgcn_ldexpf(acc[e] * a, ash);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wu = __shfl(w, u, 64);
+      const float wu = __shfl(wo, u, 64);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(wu, v[u][e], acc[e]);
     }
     M = Mn;
+    Sx = Sn;
   }
-  const float inv = 1.0f / L;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no keys: O = 0
+  const int osh = Sx == INT_MIN ? 0 : Sx;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const int64_t oi = bh * D + e * 64 + lane;
+    const float r = __builtin_amdgcn_ldexpf(acc[e] * inv, osh);
     if constexpr (OUT_BF16)
-      static_cast<uint16_t*>(o)[oi] = f32_to_bf16(acc[e] * inv);
+      static_cast<uint16_t*>(o)[oi] = f32_to_bf16(r);
     else
-      static_cast<float*>(o)[oi] = acc[e] * inv;
+      static_cast<float*>(o)[oi] = r;
   }
   if (lse != nullptr && lane == 0) lse[bh] = (M + __builtin_log2f(L)) * kLn2;
 }

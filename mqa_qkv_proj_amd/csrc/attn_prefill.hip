@@ -22,8 +22,10 @@
 //  * P is rounded to fp16 and O^T += V^T . P^T runs as an fp16 MFMA.  fp16 P
 //    carries 3 more mantissa bits than bf16, which keeps the error of
 //    outlier-heavy rows inside the bf16 tolerance.  A small pre-pass writes V
-//    once as fp16 V^T tile images (exact for |v| in fp16's normal range), in
-//    the key order the P operand holds, into caller-provided workspace.
+//    once as fp16 V^T tile images, in the key order the P operand holds, into
+//    caller-provided workspace.  Each image carries a power-of-two exponent
+//    (0 for values inside fp16's range) so the conversion is exact for every
+//    finite bf16 V; the accumulator follows it with exact rescales.
 //  * Software pipeline over 32-key halves: the softmax of one half runs on the
 //    vector unit while the matrix cores compute the next half's scores and
 //    this half's P.V; the operands of each MFMA are read from LDS one slot
@@ -102,14 +104,20 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* __restrict__ cu_q, co
 }
 
 // V of one (batch, KV head, 64-key tile) written as the LDS image the prefill
-// kernel uses for P.V: V^T in fp16 (bf16 -> fp16 is exact for |v| in fp16's
-// normal range), one padded row per head dimension, keys in P-operand order.
-// Keys at or past L_kv are zeros, so every image is a full tile.
+// kernel uses for P.V: V^T in fp16, one padded row per head dimension, keys in
+// P-operand order.  The tile is stored as V * 2^-s with its power-of-two
+// exponent s (v_tile_exp: 0 unless the tile lies beyond fp16's range or is
+// entirely tiny), so the conversion is exact for every finite bf16 tile; s
+// rides in row 0's padding (int32 at element kBK).  Keys at or past L_kv are
+// zeros, so every image is a full tile.  Called by all (kBK/4)*(D/8) threads of
+// the workgroup, task ti each (a workgroup barrier inside); `red` is LDS for
+// one int per wave.
 template <int D>
 __device__ __forceinline__ void v_image_tile(const uint16_t* __restrict__ v, uint16_t* __restrict__ img, int Hkv,
                                              int64_t kv_stride, int ntiles, int b, int g, int t, const SeqSpan& sp,
-                                             int ti) {
+                                             int ti, uint32_t* red) {
   using S = PrefillLds<D>;
+  constexpr int NW = (kBK / 4) * (D / 8) / 64;  // waves taking part
   // consecutive lanes take consecutive key groups: one store instruction then
   // covers whole image rows
   const int kg = ti % (kBK / 4), dg = ti / (kBK / 4);
@@ -120,37 +128,50 @@ __device__ __forceinline__ void v_image_tile(const uint16_t* __restrict__ v, uin
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj)
     rv[jj] = bld16(rs, (uint32_t)(t * kBK + kg * 4 + jj) * row_bytes + (uint32_t)(g * D * 2) + dg * 16);
+  // the tile's largest exponent field: per lane, per wave, then over the waves
+  uint32_t em = 0;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) em = max(em, bf16x2_expmax(rv[jj][e]));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) em = max(em, (uint32_t)__shfl_xor((int)em, o, 64));
+  if ((ti & 63) == 0) red[ti >> 6] = em;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) em = max(em, red[w]);
+  const int sv = v_tile_exp(em);
+  auto cv = [&](float x) { return __builtin_amdgcn_ldexpf(x, -sv); };
   uint16_t* out = img + (((int64_t)b * Hkv + g) * ntiles + t) * S::kV;
   const int col = (kg >> 2) * 16 + vt_pos(kg & 3);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     // rv[jj][e] = V[key jj][d = 8dg+2e, 8dg+2e+1] (bf16 pair)
     u32x2_t lo, hi;
-    lo[0] = pack_f16(bf16lo(rv[0][e]), bf16lo(rv[1][e]));
-    lo[1] = pack_f16(bf16lo(rv[2][e]), bf16lo(rv[3][e]));
-    hi[0] = pack_f16(bf16hi(rv[0][e]), bf16hi(rv[1][e]));
-    hi[1] = pack_f16(bf16hi(rv[2][e]), bf16hi(rv[3][e]));
+    lo[0] = pack_f16(cv(bf16lo(rv[0][e])), cv(bf16lo(rv[1][e])));
+    lo[1] = pack_f16(cv(bf16lo(rv[2][e])), cv(bf16lo(rv[3][e])));
+    hi[0] = pack_f16(cv(bf16hi(rv[0][e])), cv(bf16hi(rv[1][e])));
+    hi[1] = pack_f16(cv(bf16hi(rv[2][e])), cv(bf16hi(rv[3][e])));
     st8(out + (dg * 8 + 2 * e) * S::kVld + col, lo);
     st8(out + (dg * 8 + 2 * e + 1) * S::kVld + col, hi);
   }
+  if (ti == 0) *reinterpret_cast<int32_t*>(out + kBK) = sv;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_v_image_kernel(const uint16_t* __restrict__ v,
-                                                              uint16_t* __restrict__ img, int Lkv,
-                                                              int Hkv, int64_t kv_stride, int ntiles,
-                                                              const int32_t* __restrict__ cu_kv, int total_kv) {
-  constexpr int VT = (kBK / 4) * (D / 8);  // tasks of 4 keys x 8 dimensions
-  const int ti = threadIdx.x;
-  if (ti >= VT) return;
+__global__ __launch_bounds__((kBK / 4) * (D / 8)) void prefill_v_image_kernel(
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ img, int Lkv, int Hkv, int64_t kv_stride, int ntiles,
+    const int32_t* __restrict__ cu_kv, int total_kv) {
+  __shared__ uint32_t red[4];
+  const int ti = threadIdx.x;  // one task of 4 keys x 8 dimensions per thread
   int id = blockIdx.x;
   const int t = id % ntiles;
   id /= ntiles;
   const int g = id % Hkv;
   const int b = id / Hkv;
   const SeqSpan sp = seq_span(cu_kv, cu_kv, b, Lkv, Lkv, total_kv, total_kv);
-  if (t * kBK >= sp.Lkv) return;  // a tile no query of this sequence reads
-  v_image_tile<D>(v, img, Hkv, kv_stride, ntiles, b, g, t, sp, ti);
+  if (t * kBK >= sp.Lkv) return;  // a tile no query of this sequence reads (the whole workgroup)
+  v_image_tile<D>(v, img, Hkv, kv_stride, ntiles, b, g, t, sp, ti, red);
 }
 
 // ---- FP8 (e4m3) quantisation with incoherent processing ("FlashAttention-3"
@@ -279,6 +300,7 @@ __global__ __launch_bounds__(256) void prefill_fp8_kv_kernel(const uint16_t* __r
   static_assert(D == 128, "16 lanes of 8 elements per K row");
   constexpr int kPitch = D + 16, kPass = 4;
   __shared__ float wmax[4];
+  __shared__ uint32_t vred[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15;  // element block 8 li .. 8 li + 7 of a row
   int id = blockIdx.x;
@@ -296,7 +318,7 @@ __global__ __launch_bounds__(256) void prefill_fp8_kv_kernel(const uint16_t* __r
     const int r = wave * 16 + p * 4 + (lane >> 4);
     raw[p] = bld16(rs, (uint32_t)(t * kBK + r) * row_bytes + (uint32_t)(g * D * 2) + li * 16);
   }
-  v_image_tile<D>(v, vimg, Hkv, kv_stride, ntiles, b, g, t, sp, tid);
+  v_image_tile<D>(v, vimg, Hkv, kv_stride, ntiles, b, g, t, sp, tid, vred);
   float x[kPass][8];
 #pragma unroll
   for (int p = 0; p < kPass; ++p)
@@ -486,6 +508,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
 
   auto k_of = [&](int st) -> const uint16_t* { return smem + st * S::kStage; };
   auto v_of = [&](int st) -> const uint16_t* { return smem + st * S::kStage + S::kK; };
+  // The V tile in stage st is V * 2^-s with its exponent s in row 0's padding
+  // (0 unless the tile lies outside fp16's range).  acc holds O * l * 2^-sig;
+  // before a tile's P.V it is brought to that tile's exponent by an exact
+  // power-of-two rescale.
+  auto v_exp_of = [&](int st) -> int { return *reinterpret_cast<const int32_t*>(v_of(st) + kBK); };
+  int sig = 0;
+  auto v_rescale = [&](int sv_any) {
+    const int sv = __builtin_amdgcn_readfirstlane(sv_any);
+    if (sv != sig) {
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = __builtin_amdgcn_ldexpf(acc[i][e], sig - sv);
+      sig = sv;
+    }
+  };
   // Scale of the scores of the tile in stage st (F8: the tile's K scale rides
   // in row 0's padding, bytes D..D+3).
   float cc = crow;
@@ -726,6 +764,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
   u32x4_t kf[KF];
   u32x4_t pl = u32x4_t{0, 0, 0, 0};  // the step's carried P of keys 0..15 of the current half
   float ml = -INFINITY;
+  int sv_cur = v_exp_of(0);  // V exponent of tile t (read one tile ahead)
   if (t_mask > 0) {
     cc = tile_c(0);
     sc = qk(k_of(0), 0);
@@ -738,6 +777,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     fill_begin(t + 2, st2);
     cc = tile_c(st0);
+    v_rescale(sv_cur);
+    sv_cur = v_exp_of(st1);  // tile t + 1 is complete in LDS
     // the second step computes the scores of tile t + 1 (stage st1), under that tile's scale
     step(sc, pl, ml, kf, v_of(st0), 0, k_of(st1), 0, cc, std::true_type{}, std::integral_constant<int, 0>{});
     step(sc, pl, ml, kf, v_of(st0), 1, k_of(st1), 1, tile_c(st1), std::true_type{},
@@ -752,6 +793,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     if (t + 2 < nt) fill(t + 2, st2);
     cc = tile_c(st0);
+    v_rescale(sv_cur);
     step(sc, pl, ml, kf, v_of(st0), 0, k_of(st1), 0, cc, std::false_type{}, std::integral_constant<int, -1>{});
     update_max(sc);
     drain(sc, v_of(st0), 1);
@@ -767,6 +809,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
     const int st2 = st1 == 2 ? 0 : st1 + 1;
     if (t + 2 < nt) fill(t + 2, st2);
     cc = tile_c(st0);
+    v_rescale(v_exp_of(st0));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       sc = qk(k_of(st0), j);
@@ -790,8 +833,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d0 = db * 32 + 8 * g4 + 4 * hf;
-      const float v0 = acc[db][4 * g4 + 0] * inv, v1 = acc[db][4 * g4 + 1] * inv;
-      const float v2 = acc[db][4 * g4 + 2] * inv, v3 = acc[db][4 * g4 + 3] * inv;
+      // O = acc / l * 2^sig (exactly acc / l when sig = 0)
+      auto ov = [&](float a) { return __builtin_amdgcn_ldexpf(a * inv, sig); };
+      const float v0 = ov(acc[db][4 * g4 + 0]), v1 = ov(acc[db][4 * g4 + 1]);
+      const float v2 = ov(acc[db][4 * g4 + 2]), v3 = ov(acc[db][4 * g4 + 3]);
       if constexpr (OUT_BF16) {
         u32x2_t pk;
         pk[0] = pack_bf16(v0, v1);
@@ -907,7 +952,7 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   if (nblk > 0x7fffffff || nimg > 0x7fffffff) return hipErrorInvalidValue;
   if (a.ws_bytes < prefill_workspace_bytes(a.B, a.Lkv, a.Hkv, D, true)) return hipErrorInvalidValue;
   uint16_t* img = static_cast<uint16_t*>(a.ws);
-  hipLaunchKernelGGL(prefill_v_image_kernel<D>, dim3((unsigned)nimg), dim3(256), 0, s,
+  hipLaunchKernelGGL(prefill_v_image_kernel<D>, dim3((unsigned)nimg), dim3((kBK / 4) * (D / 8)), 0, s,
                      (const uint16_t*)a.v, img, a.Lkv, a.Hkv, a.kv_stride, ntiles, a.cu_kv, a.total_kv);
   auto kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, kWaves>;
   if constexpr (D == 64)

@@ -84,6 +84,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
   return (uint16_t)(__builtin_bit_cast(uint32_t, r) & 0xffffu);
 }
 
+// Power-of-two exponent s of a tile of V (bf16) for the fp16 P.V products: the
+// tile is converted to fp16 as V * 2^-s.  bf16 values with an unbiased exponent in [-17, 15] convert to fp16
+// exactly, so a tile whose largest |v| lies in [2^-10, 2^16) keeps s = 0; a tile
+// beyond fp16's range (or entirely tiny) takes s = e - 14, which puts its
+// largest |v| in [2^14, 2^15).  `em` is the largest exponent field (bits 7..14
+// of the bf16 pattern, shifted down) of the tile; 0 = only zeros/subnormals.
+__device__ __forceinline__ int v_tile_exp(uint32_t em) {
+  const int e = (int)em - 127;
+  return (em != 0 && (e > 15 || e < -10)) ? e - 14 : 0;
+}
+// largest bf16 exponent field of the two halves of a packed pair
+__device__ __forceinline__ uint32_t bf16x2_expmax(uint32_t u) {
+  return max((u >> 7) & 0xffu, u >> 23 & 0xffu);
+}
+
 // Exchange with the lane 32 positions away (the other k-half of an MFMA tile).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -74,7 +74,7 @@ struct DecodeArgs {
   int split;       // keys per aligned split; 0 = balanced work split (bf16 only)
   int n_slot;      // partial slots per (sequence, query head): decode_slots(Lmax, kv_split)
   float* part_o;   // [B, Hq, n_slot, d]
-  float* part_ml;  // [B, Hq, n_slot, 2]  (running max in log2 units, sum)
+  float* part_ml;  // [B, Hq, n_slot, 4]  (running max in log2 units, sum, V exponent as int32, unused)
   bool in_bf16, out_bf16;
   // Paged caches (bf16 only): k/v are [num_pages, page_size, Hkv, d] pages and key j
   // of sequence b lives in page block_table[b * pages_per_seq + j / page_size]

@@ -193,15 +193,19 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, seq_lens: np
 
     The per-token decode of the "MHA -> GQA" blog, section 3.1 (batched
     matrix-vector attention with per-request lengths).  q [B, H_q, d], caches
-    [B, L_max, H_kv, d], seq_lens [B] -> O [B, H_q, d], LSE [B, H_q].
+    [B, L_max, H_kv, d], seq_lens [B] in [0, L_max] -> O [B, H_q, d], LSE [B, H_q].
+    A sequence with no keys (seq_lens[b] = 0) has no softmax: like a query row
+    that sees no key in attention_varlen, it is given O = 0 and LSE = -inf.
     """
     B, H_q, d = q.shape
-    O = np.empty((B, H_q, d), dtype=F64)
-    LSE = np.empty((B, H_q), dtype=F64)
+    O = np.zeros((B, H_q, d), dtype=F64)
+    LSE = np.full((B, H_q), -np.inf, dtype=F64)
     for b in range(B):
         n = int(seq_lens[b])
-        if not 1 <= n <= k_cache.shape[1]:
+        if not 0 <= n <= k_cache.shape[1]:
             raise ValueError("seq_lens out of range")
+        if n == 0:
+            continue
         kb = k_cache[b:b + 1, :n]
         vb = v_cache[b:b + 1, :n]
         qb = q[b:b + 1, None]                              # [1, 1, H_q, d]

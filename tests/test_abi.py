@@ -178,7 +178,7 @@ def test_decode_workspace_query(lib):
     f = lib.decode_workspace_bytes
     n = f(32, 32, 8, 128, 4096, 0)
     assert n > 32 * 32 * 128 * 4
-    assert f(32, 32, 8, 128, 4096, 64) == 32 * 32 * 64 * (128 * 4 + 8) + 256
+    assert f(32, 32, 8, 128, 4096, 64) == 32 * 32 * 64 * (128 * 4 + 16) + 256
     assert f(2, 8, 3, 128, 100, 0) == 0       # H_q % H_kv
     assert f(2, 8, 2, 128, 100, 100) == 0     # split not a multiple of 32
     assert f(2, 8, 2, 96, 100, 0) == 0        # d
@@ -192,6 +192,7 @@ def test_decode_workspace_query(lib):
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
+
 
 
 def decode_paged(lib, **kw):
@@ -237,6 +238,43 @@ def test_python_layer_validates_without_gpu(lib):
         lib.qkv_proj_append(x, torch.zeros(256, 512, dtype=torch.bfloat16), kc, kc.clone(),
                             torch.ones(4, dtype=torch.int32), 4, 2, 64)
 
+
+
+def test_decode_bindings_validate_operands(lib):
+    """The decode kernels take their element type from q and address `out`,
+    the caches and seq_lens as contiguous buffers, so a mismatch would read or
+    write outside them.  The bindings reject each case before any device call
+    (checked here with host tensors: the checks run before the device check)."""
+    import torch
+    B, H_q, H_kv, d, L = 2, 8, 2, 64, 32
+    q = torch.zeros(B, H_q, d, dtype=torch.bfloat16)
+    kc = torch.zeros(B, L, H_kv, d, dtype=torch.bfloat16)
+    lens = torch.ones(B, dtype=torch.int32)
+    kp = torch.zeros(4, 16, H_kv, d, dtype=torch.bfloat16)
+    bt = torch.zeros(B, 2, dtype=torch.int32)
+
+    def both(match, **kw):
+        a = dict(q=q, k=kc, v=kc, lens=lens, out=None, out_dtype=None)
+        a.update(kw)
+        with pytest.raises(ValueError, match=match):
+            lib.gqa_attn_decode(a["q"], a["k"], a["v"], a["lens"], out=a["out"], out_dtype=a["out_dtype"])
+        pk = kp if a["k"] is kc else kp.to(a["k"].dtype)
+        with pytest.raises(ValueError, match=match):
+            lib.gqa_attn_decode_paged(a["q"], pk, kp if a["v"] is kc else kp.to(a["v"].dtype), bt, a["lens"],
+                                      out=a["out"], out_dtype=a["out_dtype"])
+
+    both("dtype", k=kc.float(), v=kc.float())                     # caches wider than q
+    both("dtype", q=q.float())                                    # fp32 q over bf16 caches
+    both("seq_lens", lens=torch.ones(2 * B, dtype=torch.int32)[::2])  # not contiguous
+    both("seq_lens", lens=lens.long())
+    both("out", out=torch.zeros(B, H_q, d, dtype=torch.float32))  # out of q's dtype, none asked
+    both("out", out=torch.zeros(B, H_q, d + 8, dtype=torch.bfloat16))
+    both("out", out=torch.zeros(B, d, H_q, dtype=torch.bfloat16).transpose(1, 2))
+    both("out", out=torch.zeros(B, H_q, d, dtype=torch.bfloat16), out_dtype=torch.float32)
+    both("out_dtype", out_dtype=torch.float16)
+    # well-formed host tensors get as far as the device check
+    with pytest.raises(ValueError, match="HIP device"):
+        lib.gqa_attn_decode(q, kc, kc, lens, out=torch.zeros(B, H_q, d, dtype=torch.bfloat16))
 
 def prefill_fp8(lib, **kw):
     a = dict(q=A, k=A, v=A, o=A, lse=None, signs=A, B=1, Lq=16, Lkv=16, H_q=4, H_kv=2, d=128, qs=512, ks=256,

@@ -149,6 +149,17 @@ def test_long_context_prefill_sampled(m, name):
     ma, rl16 = errors(got16, ref)
     say(f"{name} O bf16 output: max-abs {ma:.3e} (bf16 half-ulp at |O|~60 is 0.125), rel-L2 {rl16:.3e}")
     assert rl16 <= 5e-3
+    # every row of two (batch, head) pairs: the first head of the first
+    # sequence and the last head of the last (the other KV group)
+    for b, h in ((0, 0), (wl.B - 1, wl.H_q - 1)):
+        ro, rl = [], []
+        for r0 in range(0, wl.L, 1024):
+            o_blk, l_blk = oracle.attention_rows(pin["q"], pin["k"], pin["v"], b, h, np.arange(r0, r0 + 1024),
+                                                 wl.causal, scale)
+            ro.append(o_blk); rl.append(l_blk)
+        assert_close(o32h[b, :, h], np.concatenate(ro), "bf16", f"{name} O, all {wl.L} rows of b={b} h={h}")
+        assert_close(lseh[b, h], np.concatenate(rl), "bf16", f"{name} LSE, all rows of b={b} h={h}",
+                     max_abs=2e-3, rel_l2=1e-4)
 
 
 # ----------------------------------------------------------------------------- invariants

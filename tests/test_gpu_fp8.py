@@ -114,9 +114,9 @@ def test_fp8_incoherent_processing_cuts_the_error_on_gpu(m):
 
 
 def test_fp8_full_size_sampled_rows(m):
-    """The long-context prefill shape (B=2, L=4096, H_q=32, H_kv=4, causal) in the
-    launch configuration the benchmark times; rows of two heads checked against
-    the oracle, which computes those rows only."""
+    """A wide-group shape (B=2, L=4096, H_q=32, H_kv=4, causal: G = 8, so the
+    8-head workgroups); rows of two heads checked against the oracle, which
+    computes those rows only."""
     import torch
     B, L, H_q, H_kv, d = 2, 4096, 32, 4, 128
     say("prefill fp8 full size", B, L, H_q, H_kv)
@@ -134,6 +134,26 @@ def test_fp8_full_size_sampled_rows(m):
         ref, _ = ofp8.attention_fp8_rows(qh, kh, vh, b, h, rows, True, 1.0 / math.sqrt(d), signs)
         assert_close(got[b, rows, h], ref, "bf16", f"fp8 full-size rows b={b} h={h}")
 
+
+
+def test_fp8_long_context_bench_shape(m):
+    """The long-context GQA prefill exactly as the benchmark times its FP8
+    variant: B=2, L=8192, H_q=16, H_kv=4, d=128, causal, the workload's own
+    inputs (0.1% of feature channels x20) and random signs; sampled rows of
+    two (batch, head) pairs in different KV groups against the oracle."""
+    import torch
+    wl = W.WORKLOADS["long_kv4_causal"]
+    say("prefill fp8 at the benchmark shape", wl.name)
+    pin = W.prefill_inputs(wl)
+    signs = W.random_signs(wl.seed, 6, wl.d)
+    q, k, v = (dev(pin[n], "bf16") for n in ("q", "k", "v"))
+    o = m.gqa_attn_prefill_fp8(q, k, v, signs=dev(signs, "f32"), causal=True, out_dtype=torch.float32)
+    got = host(o)
+    rows = np.array([0, 1, 63, 64, 65, 511, 1000, 4095, 4096, 6000, 8127, 8128, 8191])
+    for b, h in ((0, 3), (1, 12)):
+        ref, _ = ofp8.attention_fp8_rows(pin["q"], pin["k"], pin["v"], b, h, rows, True,
+                                         1.0 / math.sqrt(wl.d), signs)
+        assert_close(got[b, rows, h], ref, "bf16", f"fp8 bench-shape rows b={b} h={h}")
 
 def test_fp8_scale_zero_gives_prefix_means(m):
     """scale = 0: every visible score is 0 whatever the FP8 codes, so each row's

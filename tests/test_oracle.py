@@ -262,6 +262,43 @@ def test_decode_matches_attention_and_ignores_cache_tail():
     assert np.array_equal(O, O2) and np.array_equal(LSE, LSE2)
 
 
+
+def test_decode_empty_sequence_reading():
+    """A sequence with no keys has no softmax; the reading shared with the
+    variable-length oracle's blind rows gives O = 0, LSE = -inf, and leaves the
+    other sequences of the batch unchanged."""
+    rng = np.random.default_rng(12)
+    B, L_max, H_q, H_kv, d = 3, 10, 4, 2, 8
+    kc, vc = rng.standard_normal((B, L_max, H_kv, d)), rng.standard_normal((B, L_max, H_kv, d))
+    q = rng.standard_normal((B, H_q, d))
+    lens = np.array([4, 0, 10], dtype=np.int32)
+    O, LSE = oracle.decode(q, kc, vc, lens, 0.3)
+    assert np.array_equal(O[1], np.zeros((H_q, d))) and np.all(LSE[1] == -np.inf)
+    keep = np.array([0, 2])
+    O2, LSE2 = oracle.decode(q[keep], kc[keep], vc[keep], lens[keep], 0.3)
+    assert np.array_equal(O[keep], O2) and np.array_equal(LSE[keep], LSE2)
+    # the same query as a one-row packed sequence with no keys
+    cu_q, cu_kv = np.array([0, 1]), np.array([0, 0])
+    Ov, Lv = oracle.attention_varlen(q[1:2], kc[1, :1], vc[1, :1], cu_q, cu_kv, False, 0.3)
+    assert np.array_equal(Ov[0], O[1]) and np.array_equal(Lv[:, 0], LSE[1])
+    with pytest.raises(ValueError):
+        oracle.decode(q, kc, vc, np.array([4, -1, 10], dtype=np.int32), 0.3)
+
+
+def test_output_is_linear_in_v():
+    """O = P V is linear in V: scaling V by a power of two scales O by exactly
+    that power (fp64, no overflow), and P, hence LSE, does not depend on V.
+    The kernels must keep this for V beyond the 16-bit operand range."""
+    rng = np.random.default_rng(13)
+    q, k, v = (rng.standard_normal((1, 9, 4, 8)), rng.standard_normal((1, 9, 2, 8)),
+               rng.standard_normal((1, 9, 2, 8)))
+    O, LSE = oracle.attention(q, k, v, True, 0.35)
+    for e in (-60, 20, 100):
+        Oe, LSEe = oracle.attention(q, k, v * 2.0 ** e, True, 0.35)
+        assert np.array_equal(Oe, O * 2.0 ** e) and np.array_equal(LSEe, LSE)
+    Ob, _ = oracle.brute_attention(_tolist(q), _tolist(k), _tolist(v * 2.0 ** 20), True, 0.35)
+    np.testing.assert_allclose(np.array(Ob) / 2.0 ** 20, O, rtol=0, atol=1e-12)
+
 def test_decode_steps_with_append_reproduce_causal_prefill_rows():
     """Generating token by token (project, append, decode) must give, at step s,
     row s of causal attention over the whole sequence: catches an append at the
