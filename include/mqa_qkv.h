@@ -34,7 +34,8 @@
  *     mutates a caller-allocated `out` ("custom op overhead" gist).
  *   - The library never allocates device memory and never synchronises;
  *     calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- *     stream) and reentrant; every scratch buffer is the caller's.
+ *     stream) and reentrant.  The one exception to "caller-owned scratch" is
+ *     gqa_attn_decode_noalloc, which uses a static per-GPU buffer.
  *   - Arguments are validated on the host before any HIP call.  A rejected
  *     call launches nothing and returns MQKV_ERR_INVALID (malformed) or
  *     MQKV_ERR_UNSUPPORTED (well-formed but not implemented); a failed launch
@@ -269,6 +270,30 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
                             int64_t q_tok_stride, float scale, int32_t kv_split,
                             void* workspace, size_t workspace_bytes, mqkv_dtype in_dtype,
                             mqkv_dtype o_dtype, void* stream);
+
+/*
+ * gqa_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).
+ *
+ * Arguments, results and errors are those of gqa_attn_decode.  The split
+ * partials go to a static device buffer of MQKV_DECODE_NOALLOC_SCRATCH_BYTES
+ * per GPU, held until the process ends; the call allocates and frees nothing.
+ * Sizes whose partials need more than that (gqa_attn_decode's workspace for
+ * this dtype) return MQKV_ERR_UNSUPPORTED, with nothing launched.  The buffer
+ * needs no initial contents.  Every call on one GPU uses the same buffer:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.  The first call on a device looks up the
+ * buffer's device address (the library's only mutable host state, guarded by
+ * a lock).
+ */
+#define MQKV_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+mqkv_status gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* seq_lens, void* o, float* lse, int32_t B,
+                                    int32_t H_q, int32_t H_kv, int32_t d, int32_t L_max,
+                                    int64_t q_tok_stride, float scale, int32_t kv_split,
+                                    mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream);
 
 /*
  * Decode over a paged KV cache (bf16).

@@ -30,8 +30,10 @@ MQKV_F32, MQKV_BF16 = 0, 1
 EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill_workspace_bytes",
            "gqa_attn_prefill", "gqa_attn_decode_paged", "gqa_attn_prefill_varlen",
            "gqa_attn_prefill_fp8_workspace_bytes", "gqa_attn_prefill_fp8",
-           "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "mqkv_status_string",
+           "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "gqa_attn_decode_noalloc", "mqkv_status_string",
            "mqkv_last_error", "mqkv_abi_version")
+
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20  # MQKV_DECODE_NOALLOC_SCRATCH_BYTES
 
 
 class MqkvError(RuntimeError):
@@ -75,6 +77,9 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, i32, vp,
                                     sz, i32, i32, vp]
     lib.gqa_attn_decode.restype = i32
+    lib.gqa_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, f32, i32, i32,
+                                            i32, vp]
+    lib.gqa_attn_decode_noalloc.restype = i32
     lib.gqa_attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64,
                                           f32, i32, vp, sz, i32, i32, vp]
     lib.gqa_attn_decode_paged.restype = i32

@@ -1,6 +1,7 @@
 // C ABI of the library: host-side validation and dispatch to the gfx950 kernels.
 // Every check runs before any HIP call, so a rejected call touches no device.
 #include <algorithm>
+#include <mutex>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -57,7 +58,7 @@ const char* mqkv_status_string(mqkv_status s) {
 
 const char* mqkv_last_error(void) { return g_err; }
 
-int32_t mqkv_abi_version(void) { return 106; }
+int32_t mqkv_abi_version(void) { return 107; }
 
 size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                                 mqkv_dtype dtype) {
@@ -277,7 +278,7 @@ mqkv_status gqa_attn_prefill_fp8(const void* q, const void* k, const void* v, vo
 
 namespace {
 
-// Host validation of a decode call.
+// Host validation of a decode call (gqa_attn_decode, gqa_attn_decode_noalloc).
 mqkv_status decode_check(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                          void* o, float* lse, int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t L_max,
                          int64_t q_tok_stride, float scale, int32_t kv_split, mqkv_dtype in_dtype,
@@ -331,6 +332,33 @@ mqkv_status decode_launch(const void* q, const void* k_cache, const void* v_cach
   return hip_status(mqkv::launch_decode(a, (hipStream_t)stream), "gqa_attn_decode launch");
 }
 
+// Scratch of gqa_attn_decode_noalloc: a static device array (each GPU the
+// library runs on holds its own copy until the process ends).  In host code
+// `scratch` names a host-side stand-in, not device memory: host code uses only
+// the device address hipGetSymbolAddress returns for it, looked up once per
+// device with that device current and kept per device.
+static __device__ __align__(256) unsigned char scratch[MQKV_DECODE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+mqkv_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "gqa_attn_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MQKV_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "gqa_attn_decode_noalloc: hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MQKV_ERR_HIP, "gqa_attn_decode_noalloc: no device address for the scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MQKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,6 +388,26 @@ mqkv_status gqa_attn_decode(const void* q, const void* k_cache, const void* v_ca
                 workspace_bytes);
   return decode_launch(q, k_cache, v_cache, seq_lens, o, lse, B, H_q, H_kv, d, L_max, q_tok_stride, scale,
                        kv_split, workspace, in_dtype, o_dtype, stream);
+}
+
+mqkv_status gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* seq_lens, void* o, float* lse, int32_t B, int32_t H_q,
+                                    int32_t H_kv, int32_t d, int32_t L_max, int64_t q_tok_stride, float scale,
+                                    int32_t kv_split, mqkv_dtype in_dtype, mqkv_dtype o_dtype, void* stream) {
+  g_err[0] = 0;
+  mqkv_status st = decode_check(q, k_cache, v_cache, seq_lens, o, lse, B, H_q, H_kv, d, L_max, q_tok_stride,
+                                scale, kv_split, in_dtype, o_dtype);
+  if (st != MQKV_OK || B == 0) return st;
+  const size_t need = decode_need(B, H_q, H_kv, d, L_max, kv_split, in_dtype == MQKV_BF16);
+  if (need > (size_t)MQKV_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(MQKV_ERR_UNSUPPORTED,
+                "gqa_attn_decode_noalloc: these sizes need %zu bytes of scratch, beyond its %u-byte static buffer "
+                "(use gqa_attn_decode with a workspace)", need, (unsigned)MQKV_DECODE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != MQKV_OK) return st;
+  return decode_launch(q, k_cache, v_cache, seq_lens, o, lse, B, H_q, H_kv, d, L_max, q_tok_stride, scale,
+                       kv_split, ws, in_dtype, o_dtype, stream);
 }
 
 mqkv_status gqa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -43,7 +43,7 @@ def test_status_strings(lib):
     assert L.mqkv_status_string(1) == b"invalid argument"
     assert L.mqkv_status_string(2) == b"unsupported configuration"
     assert L.mqkv_status_string(3) == b"HIP runtime error"
-    assert L.mqkv_abi_version() == 106
+    assert L.mqkv_abi_version() == 107
 
 
 def proj(lib, **kw):
@@ -194,6 +194,38 @@ def test_decode_rejects(lib, kw, code):
     assert decode(lib, **kw) == code
 
 
+
+def decode_noalloc(lib, **kw):
+    a = dict(q=A, k=A, v=A, lens=A, o=A, lse=None, B=2, H_q=8, H_kv=2, d=128, Lmax=100, qs=1024, scale=0.1,
+             split=0, dt=BF16, odt=BF16)
+    a.update(kw)
+    return lib.lib.gqa_attn_decode_noalloc(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["H_q"],
+                                           a["H_kv"], a["d"], a["Lmax"], a["qs"], a["scale"], a["split"], a["dt"],
+                                           a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=None), INV), (dict(lens=A + 2), INV), (dict(split=48), INV), (dict(Lmax=0), INV),
+    (dict(qs=512), INV), (dict(scale=float("nan")), INV), (dict(d=80, qs=1024), UNS),
+    (dict(dt=F32, odt=BF16), UNS), (dict(H_q=8, H_kv=3), INV), (dict(o=A + 8), INV),
+    # partials beyond the static scratch: rejected before any device call
+    (dict(B=64, H_q=64, H_kv=8, Lmax=1 << 16, qs=8192), UNS),
+    (dict(B=512, H_q=32, H_kv=8, Lmax=4096, qs=4096, split=32), UNS),
+])
+def test_decode_noalloc_rejects(lib, kw, code):
+    assert decode_noalloc(lib, **kw) == code
+    assert lib.lib.mqkv_last_error() != b""
+
+
+def test_decode_noalloc_limit_covers_the_decode_workloads(lib):
+    """The static scratch holds the MQA decode workload's partials in either
+    dtype (the Llama-2-7B shapes are run on the GPU); the rejection message
+    names the limit."""
+    f = lib.decode_workspace_bytes
+    assert f(8, 16, 1, 128, 1040) <= lib.DECODE_NOALLOC_SCRATCH_BYTES     # MQA decode
+    assert decode_noalloc(lib, B=0) == 0
+    assert decode_noalloc(lib, B=64, H_q=64, H_kv=8, Lmax=1 << 16, qs=8192) == UNS
+    assert str(lib.DECODE_NOALLOC_SCRATCH_BYTES).encode() in lib.lib.mqkv_last_error()
 
 def decode_paged(lib, **kw):
     a = dict(q=A, kp=A, vp=A, bt=A, lens=A, o=A, lse=None, B=2, H_q=8, H_kv=2, d=128, P=16, pps=8, npages=16,
