@@ -262,43 +262,171 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
 }
 
 // ----------------------------------------------------------------------------- copy-fed tiles
-// Workgroup tile BM x 128, k tile 64, 4 waves as 2 x 2.  Both operand tiles reach
-// LDS by LDS-DMA (buffer loads that write LDS directly, no staging registers):
+// Workgroup tile BM x BN, k tile 64, WM x WN x KW waves: WM x WN positions of
+// (32 MI) x (32 NI) blocks of 32x32x16 MFMAs, each position held by KW waves
+// that take the 16-deep k steps of every k tile in turn (KW = 2 puts two
+// waves on every SIMD of a 4-position tile, which hides the operand-read and
+// barrier latency of one wave behind the other's MFMAs); their sums are added
+// through LDS at the end.  Both operand tiles reach LDS by LDS-DMA (buffer
+// loads that write LDS directly, no staging registers) into a ring of ST
+// stages, the copies of a tile issued ST-1 tiles ahead of its use; one barrier
+// per k tile publishes the copies and frees the stage being refilled.
 //  * x tile: BM rows of 64 k (k-contiguous) + 16 bytes of padding per row;
-//  * W tile: 64 rows of 128 n (n-contiguous, as W is stored) + 64 bytes of
-//    padding per row.  The MFMA B operand (8 consecutive k of one n per lane)
-//    is read with the transposing LDS load ds_read_b64_tr_b16: within each 16
-//    lanes, lane 4j+q reads 4 n of k-row j and lane i receives column i of the
-//    4 rows, so no VALU transposition is needed.
-// The row paddings keep both operand reads on distinct LDS banks; the lanes of
-// a copy that fall on padding point past the buffer, so they fetch nothing and
-// land only on padding bytes, which are never read.  Two
-// LDS stages: the copy of k tile t+1 runs while tile t is multiplied, one
-// barrier per k tile.  All operand reads of a 16-deep k step are issued
-// together and waited for once, a step ahead of their MFMAs.  Requires
-// K % 64 == 0.
-constexpr int kCfBN = 128, kCfBK = 64, kCfThreads = 256;
-constexpr int kCfXld = kCfBK + 8;   // x tile row pitch (bf16 elements): 9 chunks of 16 B
-constexpr int kCfWld = kCfBN + 32;  // W tile row pitch: 20 chunks of 16 B
-template <int BM>
-struct CfLds {
-  static constexpr int kX = BM * kCfXld;
-  static constexpr int kW = kCfBK * kCfWld;
+//  * W tile: 64 rows of BN n (n-contiguous, as W is stored), row pitch
+//    padded to 16 dwords past a multiple of 64.  The MFMA B operand (8
+//    consecutive k of one n per lane) is read with the transposing LDS load
+//    ds_read_b64_tr_b16: within each 16 lanes, lane 4j+q reads 4 n of k-row j
+//    and lane i receives column i of the 4 rows, so no VALU transposition is
+//    needed.
+// The row pitches keep both operand reads on distinct LDS banks (x: 36 dwords
+// per row; W: consecutive k rows 16 banks apart, the lane groups of a read 8
+// banks apart); the lanes of a copy that fall on padding point past the
+// buffer, so they fetch nothing and land only on padding bytes, which are
+// never read.  All operand reads of a 16-deep k step are issued together and
+// waited for once, a step ahead of their MFMAs.  Requires K % 64 == 0.
+constexpr int kTBK = 64;
+constexpr int kTXld = kTBK + 8;  // x tile row pitch (bf16): 9 chunks of 16 B
+// W tile row pitch (bf16) for BN columns: the data rounded up to 16 dwords
+// past a multiple of 64 dwords
+constexpr int tile_wpitch(int bn) {
+  int p = bn / 2;
+  while (p % 64 != 16) ++p;
+  return p * 2;
+}
+template <int BM, int BN, int WM, int WN, int KW, int ST>
+struct TileCfg {
+  static constexpr int kNW = WM * WN * KW;  // waves
+  static constexpr int kThreads = kNW * 64;
+  static constexpr int kMI = BM / WM / 32;  // 32-row MFMA blocks per wave
+  static constexpr int kNI = BN / WN / 32;  // 32-column MFMA blocks per wave
+  static constexpr int kKS = kTBK / 16 / KW;  // k steps per wave per k tile
+  static constexpr int kWld = tile_wpitch(BN);
+  static constexpr int kX = BM * kTXld;
+  static constexpr int kW = kTBK * kWld;
   static constexpr int kStage = kX + kW;
-  static constexpr int kXCopies = kX * 2 / 1024;
-  static constexpr int kWCopies = kW * 2 / 1024;
-  static constexpr int kXcp = (kXCopies + 3) / 4;  // copies per wave
-  static constexpr int kWcp = (kWCopies + 3) / 4;
-  static constexpr size_t kBytes = 2 * (size_t)kStage * sizeof(uint16_t);
+  static constexpr int kXChunks = kTXld / 8, kWChunks = kWld / 8;  // 16-byte chunks per row
+  static constexpr int kXCopies = kX * 2 / 1024, kWCopies = kW * 2 / 1024;
+  static constexpr int kXcp = (kXCopies + kNW - 1) / kNW, kWcp = (kWCopies + kNW - 1) / kNW;  // per wave (at most)
+  static constexpr size_t kBytes = (size_t)ST * kStage * sizeof(uint16_t);
+  static constexpr size_t kRedBytes = (size_t)(KW - 1) * WM * WN * kMI * kNI * 16 * 64 * 4;  // k-split sums
+  static_assert(kMI * WM * 32 == BM && kNI * WN * 32 == BN && kKS * KW * 16 == kTBK, "wave layout");
   static_assert(kX * 2 % 1024 == 0 && kW * 2 % 1024 == 0, "tiles are whole 1 KB copies");
+  static_assert(kBytes <= 160 * 1024 && kRedBytes <= kBytes, "LDS");
+  // DMA instructions wave w issues per k tile
+  static constexpr int copies_of(int w) {
+    int c = 0;
+    for (int i = 0; i < kXcp; ++i) c += (w + kNW * i < kXCopies);
+    for (int i = 0; i < kWcp; ++i) c += (w + kNW * i < kWCopies);
+    return c;
+  }
 };
+
+// All operand fragments of one 16-deep k step, read in one asm block that
+// waits for itself once (a load written in asm is complete before the block
+// ends): MI x-row fragments at pa + 32 i rows (A), NI transposed W pairs at
+// pb + 32 j columns (B), the second read of a pair HI_BYTES (4 k rows) on.
+template <int MI, int NI, int A_STRIDE, int HI>
+struct StepFrags;
+#define MQKV_LDSADDR(p) ((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)(p))
+template <int A_STRIDE, int HI>
+struct StepFrags<1, 2, A_STRIDE, HI> {
+  __device__ static void read(const uint16_t* pa, const uint16_t* pb, u32x4_t (&a)[1], u32x4_t (&b)[2]) {
+    u32x2_t l0, h0, l1, h1;
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b64_tr_b16 %1, %6\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %3, %6 offset:64\n\t"
+        "ds_read_b64_tr_b16 %4, %6 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
+        : "v"(MQKV_LDSADDR(pa)), "v"(MQKV_LDSADDR(pb)), "i"(HI), "i"(64 + HI)
+        : "memory");
+    b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
+    b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
+  }
+};
+template <int A_STRIDE, int HI>
+struct StepFrags<2, 2, A_STRIDE, HI> {
+  __device__ static void read(const uint16_t* pa, const uint16_t* pb, u32x4_t (&a)[2], u32x4_t (&b)[2]) {
+    u32x2_t l0, h0, l1, h1;
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %2, %7\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %4, %7 offset:64\n\t"
+        "ds_read_b64_tr_b16 %5, %7 offset:%10\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
+        : "v"(MQKV_LDSADDR(pa)), "v"(MQKV_LDSADDR(pb)), "i"(A_STRIDE), "i"(HI), "i"(64 + HI)
+        : "memory");
+    b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
+    b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
+  }
+};
+template <int A_STRIDE, int HI>
+struct StepFrags<1, 4, A_STRIDE, HI> {
+  __device__ static void read(const uint16_t* pa, const uint16_t* pb, u32x4_t (&a)[1], u32x4_t (&b)[4]) {
+    u32x2_t l0, h0, l1, h1, l2, h2, l3, h3;
+    asm volatile(
+        "ds_read_b128 %0, %9\n\t"
+        "ds_read_b64_tr_b16 %1, %10\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %3, %10 offset:64\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:128\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %7, %10 offset:192\n\t"
+        "ds_read_b64_tr_b16 %8, %10 offset:%14\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2), "=&v"(l3), "=&v"(h3)
+        : "v"(MQKV_LDSADDR(pa)), "v"(MQKV_LDSADDR(pb)), "i"(HI), "i"(64 + HI), "i"(128 + HI), "i"(192 + HI)
+        : "memory");
+    b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
+    b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
+    b[2] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+    b[3] = u32x4_t{l3[0], l3[1], h3[0], h3[1]};
+  }
+};
+template <int A_STRIDE, int HI>
+struct StepFrags<1, 5, A_STRIDE, HI> {
+  __device__ static void read(const uint16_t* pa, const uint16_t* pb, u32x4_t (&a)[1], u32x4_t (&b)[5]) {
+    u32x2_t l0, h0, l1, h1, l2, h2, l3, h3, l4, h4;
+    asm volatile(
+        "ds_read_b128 %0, %11\n\t"
+        "ds_read_b64_tr_b16 %1, %12\n\t"
+        "ds_read_b64_tr_b16 %2, %12 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %3, %12 offset:64\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %5, %12 offset:128\n\t"
+        "ds_read_b64_tr_b16 %6, %12 offset:%15\n\t"
+        "ds_read_b64_tr_b16 %7, %12 offset:192\n\t"
+        "ds_read_b64_tr_b16 %8, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %9, %12 offset:256\n\t"
+        "ds_read_b64_tr_b16 %10, %12 offset:%17\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2), "=&v"(l3), "=&v"(h3),
+          "=&v"(l4), "=&v"(h4)
+        : "v"(MQKV_LDSADDR(pa)), "v"(MQKV_LDSADDR(pb)), "i"(HI), "i"(64 + HI), "i"(128 + HI), "i"(192 + HI),
+          "i"(256 + HI)
+        : "memory");
+    b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
+    b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
+    b[2] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+    b[3] = u32x4_t{l3[0], l3[1], h3[0], h3[1]};
+    b[4] = u32x4_t{l4[0], l4[1], h4[0], h4[1]};
+  }
+};
+#undef MQKV_LDSADDR
 
 // B operand of a 32x32x16 MFMA from a row-major W tile: two transposing reads
 // (k rows r and r+4 of this lane's group; HI_BYTES apart) that wait for
-// themselves.  Written as one asm block because the compiler treats the
-// builtin form as aliasing every LDS-DMA copy in flight and waits for all of
-// them first, which would serialize the copy pipeline; the callers order these
-// reads after the copies they need with their own vmcnt waits.
+// themselves (the 16-column streaming kernel's reads).  Written as one asm
+// block because the compiler treats the builtin form as aliasing every LDS-DMA
+// copy in flight and waits for all of them first, which would serialize the
+// copy pipeline; the callers order these reads after the copies they need
+// with their own vmcnt waits.
 template <int HI_BYTES>
 __device__ __forceinline__ u32x4_t lds_tr16_pair(const uint16_t* p) {
   const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
@@ -313,62 +441,32 @@ __device__ __forceinline__ u32x4_t lds_tr16_pair(const uint16_t* p) {
   return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// All operand fragments of one 16-deep k step: the MI x rows (A) and the two
-// transposed W pairs (B), read in one asm block that waits for itself once,
-// so a k step costs one LDS round trip rather than one per B pair.
-template <int MI, int HI_BYTES>
-__device__ __forceinline__ void lds_step_frags(const uint16_t* pa0, const uint16_t* pa1, const uint16_t* pb0,
-                                               const uint16_t* pb1, u32x4_t (&a)[MI], u32x4_t (&b)[2]) {
-  auto addr = [](const uint16_t* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
-  };
-  u32x2_t l0, h0, l1, h1;
-  if constexpr (MI == 2) {
-    asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %7\n\t"
-        "ds_read_b64_tr_b16 %2, %8\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:%10\n\t"
-        "ds_read_b64_tr_b16 %4, %9\n\t"
-        "ds_read_b64_tr_b16 %5, %9 offset:%10\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
-        : "v"(addr(pa0)), "v"(addr(pa1)), "v"(addr(pb0)), "v"(addr(pb1)), "i"(HI_BYTES)
-        : "memory");
-  } else {
-    asm volatile(
-        "ds_read_b128 %0, %5\n\t"
-        "ds_read_b64_tr_b16 %1, %6\n\t"
-        "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
-        "ds_read_b64_tr_b16 %3, %7\n\t"
-        "ds_read_b64_tr_b16 %4, %7 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
-        : "v"(addr(pa0)), "v"(addr(pb0)), "v"(addr(pb1)), "i"(HI_BYTES)
-        : "memory");
-    (void)pa1;
-  }
-  b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
-  b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
+// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int BM>
-__global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
+template <int BM, int BN, int WM, int WN, int KW, int ST>
+__global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ out, int M, int K, int N, KvAppend app) {
-  using L = CfLds<BM>;
-  constexpr int MI = BM / 64;  // 32-row MFMA blocks per wave
+  using L = TileCfg<BM, BN, WM, WN, KW, ST>;
+  constexpr int MI = L::kMI, NI = L::kNI, NW = L::kNW;
   extern __shared__ __align__(16) uint16_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wq = __builtin_amdgcn_readfirstlane(wave);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int pos = wave % (WM * WN), kg = wave / (WM * WN);  // tile position, k-step group
+  const int wm = pos / WN, wn = pos % WN;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  const int nbn = (N + kCfBN - 1) / kCfBN, nbm = (M + BM - 1) / BM;
+  const int nbn = (N + BN - 1) / BN, nbm = (M + BM - 1) / BM;
   const int lid = xcd_remap(blockIdx.x, nbn * nbm);
   const int bm = lid / nbn, bn = lid % nbn;  // the n tiles of one m row are neighbours
-  const int m0 = bm * BM, n0 = bn * kCfBN;
-  const int nk = K / kCfBK;
+  const int m0 = bm * BM, n0 = bn * BN;
+  const int nk = K / kTBK;
 
   // ---- copy maps: slot (copy * 64 + lane) of a tile image -> global byte offset
   constexpr uint32_t kNoCopy = 0x80000000u;
@@ -376,15 +474,17 @@ __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
   uint32_t xoff[L::kXcp], woff[L::kWcp];
 #pragma unroll
   for (int i = 0; i < L::kXcp; ++i) {
-    const int slot = (wave + 4 * i) * 64 + lane;
-    const int r = slot / 9, ch = slot % 9;
-    xoff[i] = ch < 8 ? (uint32_t)r * xrow + ch * 16 : kNoCopy;
+    const int slot = (wave + NW * i) * 64 + lane;
+    const int r = slot / L::kXChunks, ch = slot % L::kXChunks;
+    xoff[i] = ch < kTBK / 8 ? (uint32_t)r * xrow + ch * 16 : kNoCopy;
   }
 #pragma unroll
   for (int i = 0; i < L::kWcp; ++i) {
-    const int slot = (wave + 4 * i) * 64 + lane;
-    const int r = slot / 20, ch = slot % 20;
-    woff[i] = ch < 16 ? (uint32_t)r * wrow + ch * 16 : kNoCopy;
+    const int slot = (wave + NW * i) * 64 + lane;
+    const int r = slot / L::kWChunks, ch = slot % L::kWChunks;
+    // chunks of columns at or past N (a ragged last tile) fetch nothing: their
+    // LDS columns feed only outputs that are not stored
+    woff[i] = (ch < BN / 8 && n0 + ch * 8 < N) ? (uint32_t)r * wrow + ch * 16 : kNoCopy;
   }
   // x rows at or past M and W rows past K lie past their buffer ends: they
   // fetch nothing, and their LDS rows only feed outputs that are not stored.
@@ -392,69 +492,119 @@ __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
   auto copy_tile = [&](int kt, int st) {
     uint16_t* xs = smem + st * L::kStage;
     uint16_t* ws = xs + L::kX;
-    const uint64_t xb = (uint64_t)m0 * K * 2 + (uint64_t)kt * kCfBK * 2;
-    const uint64_t wb = (uint64_t)kt * kCfBK * N * 2 + (uint64_t)n0 * 2;
+    const uint64_t xb = (uint64_t)m0 * K * 2 + (uint64_t)kt * kTBK * 2;
+    const uint64_t wb = (uint64_t)kt * kTBK * N * 2 + (uint64_t)n0 * 2;
     const __amdgpu_buffer_rsrc_t xr =
         make_rsrc(reinterpret_cast<const char*>(x) + xb, (uint32_t)min(xbytes - xb, (uint64_t)0x7fffffff));
     const __amdgpu_buffer_rsrc_t wr =
         make_rsrc(reinterpret_cast<const char*>(w) + wb, (uint32_t)min(wbytes - wb, (uint64_t)0x7fffffff));
 #pragma unroll
     for (int i = 0; i < L::kXcp; ++i) {
-      const int cp = wq + 4 * i;
+      const int cp = wq + NW * i;
       if (cp < L::kXCopies) dma16(xr, xs + cp * 512, xoff[i], 0);
     }
 #pragma unroll
     for (int i = 0; i < L::kWcp; ++i) {
-      const int cp = wq + 4 * i;
+      const int cp = wq + NW * i;
       if (cp < L::kWCopies) dma16(wr, ws + cp * 512, woff[i], 0);
     }
   };
-
-  f32x16_t acc[MI][2];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
-
-  // operand fragments of one 16-deep k step
-  const int bg = lane >> 4, bp = lane & 15;                   // transposing-read lane group
-  const int b_n = 16 * (bg & 1) + 4 * (bp & 3), b_k = 8 * (bg >> 1) + (bp >> 2);
-  auto frags = [&](const uint16_t* xs, const uint16_t* ws, int ks, u32x4_t (&a)[MI], u32x4_t (&b)[2]) {
-    const uint16_t* pa = xs + (wm * (BM / 2) + l32) * kCfXld + ks * 16 + hf * 8;
-    const uint16_t* pb = ws + (ks * 16 + b_k) * kCfWld + wn * 64 + b_n;
-    lds_step_frags<MI, 4 * kCfWld * 2>(pa, pa + 32 * kCfXld, pb, pb + 32, a, b);
+  // Wait until at most `ahead` later tiles of this wave's copies are still in
+  // flight (ahead <= ST - 2): an exact vmcnt per wave, since the waves issue
+  // different numbers of copies per tile.
+  auto wait_copies = [&](int ahead) {
+    static_for<0, NW>([&](auto wv) {
+      if (wq == wv) {
+        static_for<0, ST - 1>([&](auto a) {
+          if (ahead == a) wait_vmcnt<a * L::copies_of(wv)>();
+        });
+      }
+    });
   };
 
-  copy_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
-  __syncthreads();
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) acc[i][j] = f32x16_t{};
+
+  // operand fragments of one 16-deep k step
+  const int bg = lane >> 4, bp = lane & 15;  // transposing-read lane group
+  const int b_n = 16 * (bg & 1) + 4 * (bp & 3), b_k = 8 * (bg >> 1) + (bp >> 2);
+  using Frags = StepFrags<MI, NI, 32 * kTXld * 2, 4 * L::kWld * 2>;
+  auto frags = [&](const uint16_t* xs, const uint16_t* ws, int ks, u32x4_t (&a)[MI], u32x4_t (&b)[NI]) {
+    const uint16_t* pa = xs + (wm * (32 * MI) + l32) * kTXld + ks * 16 + hf * 8;
+    const uint16_t* pb = ws + (ks * 16 + b_k) * L::kWld + wn * (32 * NI) + b_n;
+    Frags::read(pa, pb, a, b);
+  };
+
+  static_for<0, ST - 1>([&](auto s) {
+    if (s < nk) copy_tile(s, s);
+  });
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) copy_tile(kt + 1, st ^ 1);
+    const int st = kt % ST;
+    wait_copies(min(ST - 2, nk - 1 - kt));
+    // Tile kt is in LDS (every wave has waited for its own copies of it) and
+    // stage (kt - 1) % ST is free (every wave's reads of it completed inside
+    // their asm blocks).  A bare barrier: __syncthreads' workgroup fence would
+    // add a vmcnt(0) wait for the copies of the later tiles as well, which
+    // would leave only one tile of lookahead whatever ST is.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + ST - 1 < nk) copy_tile(kt + ST - 1, (kt + ST - 1) % ST);
     const uint16_t* xs = smem + st * L::kStage;
     const uint16_t* ws = xs + L::kX;
-    u32x4_t a[2][MI], b[2][2];
-    frags(xs, ws, 0, a[0], b[0]);
-    static_for<0, kCfBK / 16>([&](auto ks) {
-      constexpr int cur = ks & 1;
-      if constexpr (ks + 1 < kCfBK / 16) frags(xs, ws, ks + 1, a[cur ^ 1], b[cur ^ 1]);
+    u32x4_t a[2][MI], b[2][NI];
+    frags(xs, ws, kg, a[0], b[0]);
+    static_for<0, L::kKS>([&](auto kk) {
+      constexpr int cur = kk & 1;
+      if constexpr (kk + 1 < L::kKS) frags(xs, ws, (kk + 1) * KW + kg, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_bf16(a[cur][i], b[cur][j], acc[i][j]);
+        for (int j = 0; j < NI; ++j) acc[i][j] = mfma32_bf16(a[cur][i], b[cur][j], acc[i][j]);
     });
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+
+  if constexpr (KW > 1) {
+    // add the k-step groups' sums through LDS (the stages are free now), in
+    // group order, so the result does not depend on timing
+    float* red = reinterpret_cast<float*>(smem);
+    constexpr int kPer = MI * NI * 16 * 64;  // floats per wave
     __syncthreads();
+    if (kg > 0) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            red[((kg - 1) * (WM * WN) + pos) * kPer + ((i * NI + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KW; ++g)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc[i][j][e] += red[((g - 1) * (WM * WN) + pos) * kPer + ((i * NI + j) * 16 + e) * 64 + lane];
   }
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int gn = n0 + wn * 64 + j * 32 + l32;
+  for (int j = 0; j < NI; ++j) {
+    const int gn = n0 + wn * (32 * NI) + j * 32 + l32;
     if (gn >= N) continue;
     const float bv = bias ? bf16_to_f32(bias[gn]) : 0.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int gm = m0 + wm * (BM / 2) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
+        const int gm = m0 + wm * (32 * MI) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
         if (gm < M) {
           const uint16_t r = f32_to_bf16(acc[i][j][e] + bv);
           out[(int64_t)gm * N + gn] = r;
@@ -465,15 +615,16 @@ __global__ __launch_bounds__(kCfThreads, 2) void qkv_gemm_cf_kernel(
   }
 }
 
-template <int BM>
-static hipError_t launch_gemm_cf(const void* x, const void* w, const void* bias, void* out, int M, int K,
-                                 int N, hipStream_t s, const KvAppend& app) {
-  auto kern = qkv_gemm_cf_kernel<BM>;
-  const size_t lds = CfLds<BM>::kBytes;
+template <int BM, int BN, int WM, int WN, int KW, int ST>
+static hipError_t launch_gemm_tiles(const void* x, const void* w, const void* bias, void* out, int M, int K, int N,
+                                    hipStream_t s, const KvAppend& app) {
+  using L = TileCfg<BM, BN, WM, WN, KW, ST>;
+  auto kern = qkv_gemm_tiles_kernel<BM, BN, WM, WN, KW, ST>;
+  const size_t lds = L::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int nblk = ((M + BM - 1) / BM) * ((N + kCfBN - 1) / kCfBN);
-  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kCfThreads), lds, s, (const uint16_t*)x, (const uint16_t*)w,
+  const int nblk = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(L::kThreads), lds, s, (const uint16_t*)x, (const uint16_t*)w,
                      (const uint16_t*)bias, (uint16_t*)out, M, K, N, app);
   return hipGetLastError();
 }
@@ -589,15 +740,6 @@ __global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
     }
   }
 }
-
-// ----------------------------------------------------------------------------- LDS-DMA wait helpers
-// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left at their maxima.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 63, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // ----------------------------------------------------------------------------- skinny M <= 32, streamed
 // M <= 32 with K % 128 == 0 and a narrow W: the weight is the whole cost, so a
@@ -773,7 +915,7 @@ static hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bia
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
   SkinnyPlan p{};
   // 32-bit buffer offsets cover W and x
-  if (M > 128 || N % kSkBN != 0 || K * N * 2 >= ((int64_t)1 << 31) || M * K * 2 >= ((int64_t)1 << 31)) return p;
+  if (M > 128 || K * N * 2 >= ((int64_t)1 << 31) || M * K * 2 >= ((int64_t)1 << 31)) return p;
   p.nbm = (int)((M + 31) / 32);
   // 16-column streaming kernel, no k split: used where its one workgroup per
   // 16 columns does not exceed one per CU.  On wider W its 32-byte row pieces
@@ -786,6 +928,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
     p.ok = true;
     return p;
   }
+  if (N % kSkBN != 0) return SkinnyPlan{};
   const int64_t base = (N / kSkBN) * p.nbm;
   // about three workgroups per CU; each k range a multiple of the 128-deep chunk
   // and at most kSkMaxChunks chunks
@@ -832,13 +975,30 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
     }
     return hipGetLastError();
   }
-#ifndef MQKV_GEMM_CF
-#define MQKV_GEMM_CF 1
-#endif
-  if (MQKV_GEMM_CF && K % kCfBK == 0 && N % 8 == 0 && (uint64_t)K * N * 2 < 0x80000000ull) {
-    const int64_t t128 = ((M + 127) / 128) * ((N + kCfBN - 1) / kCfBN);
-    if (t128 >= 256) return launch_gemm_cf<128>(x, w, bias, out, m, k, n, s, app);
-    if (M > 128) return launch_gemm_cf<64>(x, w, bias, out, m, k, n, s, app);
+  if (K % kTBK == 0 && N % 8 == 0 && (uint64_t)K * N * 2 < 0x80000000ull && (uint64_t)M * K * 2 < 0x80000000ull) {
+    // Tile shape: the one-workgroup-per-CU configuration with the most tiles
+    // that still fit one round on the CUs (ties: the larger tile, which reads
+    // fewer operand bytes per FLOP); shapes with more tiles than that run the
+    // 128 x 160 tile two workgroups per CU.  Measured on the 2560-column
+    // projection: M = 512 / 1024 / 2048 / 4096 -> 20.6 / 26.8 / 33.2 / 45.3 us.
+    int dev = 0, cus = 256;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const int64_t t160 = tiles(128, 160), t128 = tiles(128, 128), t64_160 = tiles(64, 160), t64 = tiles(64, 128);
+    int64_t best = 0;
+    int pick = -1;
+    const int64_t cand[4] = {t160, t128, t64_160, t64};  // larger tiles first
+    for (int c = 0; c < 4; ++c)
+      if (cand[c] <= cus && cand[c] > best) best = cand[c], pick = c;
+    switch (pick) {
+      case 0: return launch_gemm_tiles<128, 160, 4, 1, 2, 3>(x, w, bias, out, m, k, n, s, app);
+      case 1: return launch_gemm_tiles<128, 128, 2, 2, 2, 3>(x, w, bias, out, m, k, n, s, app);
+      case 2: return launch_gemm_tiles<64, 160, 2, 1, 2, 4>(x, w, bias, out, m, k, n, s, app);
+      case 3: return launch_gemm_tiles<64, 128, 2, 2, 2, 4>(x, w, bias, out, m, k, n, s, app);
+      default: return launch_gemm_tiles<128, 160, 4, 1, 1, 2>(x, w, bias, out, m, k, n, s, app);
+    }
   }
   // Pick the largest tile that still gives the chip (256 CUs) a full wave of workgroups.
   const int64_t big = ((M + 127) / 128) * ((N + 127) / 128);
