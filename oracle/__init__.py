@@ -31,6 +31,10 @@ Readings where the pages are silent (all listed in the design notes):
     position L_kv - L_q + i and sees keys j <= that position.
   * decode: the new token is already in the cache; sequence b attends to
     keys [0, seq_lens[b]).
+  * rotary position embedding: the RoFormer rotation of consecutive pairs
+    (2i, 2i+1) of every Q and K head by the angle p * theta_i, the angle
+    rounded to fp32 (rope_angles); a decode token's position is
+    seq_lens[b] - 1, the slot its key is appended to.
 
 Parity pins for every function live in tests/test_oracle.py (brute force,
 closed forms, invariants, a library-routine reduction); none is unpinned.
@@ -44,7 +48,7 @@ import numpy as np
 
 __all__ = ["qkv_proj", "split_qkv", "attention", "attention_rows", "decode",
            "brute_attention", "kv_head_of", "kv_append", "decode_step", "decode_paged",
-           "attention_varlen"]
+           "attention_varlen", "rope_angles", "rope", "qkv_proj_rope", "append_positions"]
 
 F64 = np.float64
 
@@ -236,16 +240,87 @@ def kv_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new
     return kc, vc
 
 
+def rope_angles(positions: np.ndarray, inv_freq: np.ndarray) -> np.ndarray:
+    """Rotation angles angle[..., i] = p * theta_i for positions [...] and theta [d/2].
+
+    The pages name the rotary embedding without fixing its arithmetic (the
+    "custom op overhead" gist applies a positional step to q and k right after
+    the split; the FlashAttention-3 news page, FP8 section, calls rotary a
+    memory-bound step ahead of attention).  Reading: the position and theta are
+    fp32 values and the angle is their fp32 product (one IEEE rounding, as an
+    fp32 position table times an fp32 frequency table gives); sine and cosine
+    are then taken of that fp32 angle exactly (in float64 here).
+    """
+    p = np.asarray(positions).astype(np.float32)            # exact for |p| < 2^24
+    th = np.asarray(inv_freq, dtype=np.float32)
+    return (p[..., None] * th).astype(F64)                   # float32 product, then widened
+
+
+def rope(t: np.ndarray, positions: np.ndarray, inv_freq: np.ndarray) -> np.ndarray:
+    """Rotary position embedding of head vectors t [..., H, d] at positions [...].
+
+    Reading of the rotation (the pages give none): RoFormer's definition, in
+    which the head dimension is a sum of d/2 planes, plane i spanned by
+    components (2i, 2i+1), each turned counter-clockwise by angle p * theta_i:
+
+        y[2i]   = t[2i] cos a - t[2i+1] sin a
+        y[2i+1] = t[2i] sin a + t[2i+1] cos a,   a = rope_angles(p, theta)[i]
+
+    The "MHA -> GQA" blog's conversion section treats the rotary embedding as
+    acting on such 2-dimensional subspaces of the Q and K heads.  Returns a new
+    float64 array.
+    """
+    t = np.asarray(t, dtype=F64)
+    d = t.shape[-1]
+    if d % 2 != 0 or np.asarray(inv_freq).shape != (d // 2,):
+        raise ValueError("d must be even and inv_freq of length d/2")
+    a = rope_angles(positions, inv_freq)[..., None, :]      # [..., 1 (heads), d/2]
+    c, s = np.cos(a), np.sin(a)
+    x0, x1 = t[..., 0::2], t[..., 1::2]
+    y = np.empty_like(t)
+    y[..., 0::2] = x0 * c - x1 * s
+    y[..., 1::2] = x0 * s + x1 * c
+    return y
+
+
+def qkv_proj_rope(x: np.ndarray, w: np.ndarray, positions: np.ndarray, inv_freq: np.ndarray,
+                  H_q: int, H_kv: int, d: int, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """The fused projection (PR #40092 diff) with the rotary embedding applied to
+    its Q and K heads after the bias, V untouched: the order of the "custom op
+    overhead" gist's forward (projection, split, positional step on q and k).
+
+    x [M, hidden], positions [M] -> qkv [M, N] float64.
+    """
+    qkv = qkv_proj(x, w, bias)
+    q, k, _ = split_qkv(qkv, H_q, H_kv, d)
+    out = qkv.copy()
+    qo, ko, _ = split_qkv(out, H_q, H_kv, d)
+    qo[...] = rope(q, positions, inv_freq)
+    ko[...] = rope(k, positions, inv_freq)
+    return out
+
+
+def append_positions(seq_lens: np.ndarray, L_max: int) -> np.ndarray:
+    """Position of each decode row's new token: the cache slot seq_lens[b] - 1 it
+    is appended to (kv_append), clamped to [0, L_max - 1] for the rows that are
+    not appended."""
+    return np.clip(np.asarray(seq_lens, dtype=np.int64) - 1, 0, L_max - 1)
+
+
 def decode_step(x: np.ndarray, w: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                 seq_lens: np.ndarray, H_q: int, H_kv: int, d: int, scale: float,
-                bias: Optional[np.ndarray] = None):
+                bias: Optional[np.ndarray] = None, inv_freq: Optional[np.ndarray] = None):
     """One whole decode step: project the new tokens, append their K/V, attend.
 
     x [B, hidden] (one new token per sequence) -> (qkv [B, N], k_cache',
     v_cache', O [B, H_q, d], LSE [B, H_q]): the fused projection (PR #40092
-    diff), its column split, the append above, then decode.
+    diff), its column split, the append above, then decode.  With inv_freq,
+    Q and K are rotated at the new token's position (append_positions) first.
     """
-    qkv = qkv_proj(x, w, bias)
+    if inv_freq is None:
+        qkv = qkv_proj(x, w, bias)
+    else:
+        qkv = qkv_proj_rope(x, w, append_positions(seq_lens, k_cache.shape[1]), inv_freq, H_q, H_kv, d, bias)
     q, k, v = split_qkv(qkv[:, None, :], H_q, H_kv, d)
     kc, vc = kv_append(k_cache, v_cache, k[:, 0], v[:, 0], seq_lens)
     O, LSE = decode(q[:, 0], kc, vc, seq_lens, scale)

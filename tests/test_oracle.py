@@ -325,6 +325,146 @@ def test_decode_steps_with_append_reproduce_causal_prefill_rows():
     assert (kc[:, T:] == 123.0).all() and (vc[:, T:] == -55.0).all()
 
 
+# ----------------------------------------------------------------------------- rotary embedding
+
+def _pow2_freqs(n, rng):
+    """theta_i = 2^-j: with small integer positions every angle p*theta is exact
+    in fp32, so the rotation angles are known without rounding."""
+    return (2.0 ** -rng.integers(0, 6, size=n)).astype(np.float32)
+
+
+def test_rope_position_zero_is_identity():
+    rng = np.random.default_rng(31)
+    t = rng.standard_normal((5, 3, 8))
+    th = rng.uniform(0.0, 2.0, 4).astype(np.float32)
+    assert np.array_equal(oracle.rope(t, np.zeros(5, np.int32), th), t)
+    # and a zero frequency table is the identity at every position
+    assert np.array_equal(oracle.rope(t, np.arange(5) * 977, np.zeros(4, np.float32)), t)
+
+
+def test_rope_is_the_complex_rotation():
+    """Plane i as the complex number t[2i] + 1j t[2i+1], multiplied by
+    exp(1j * p * theta_i): an independent form of RoFormer's rotation."""
+    rng = np.random.default_rng(32)
+    t = rng.standard_normal((6, 4, 16))
+    pos = rng.integers(-40, 300, size=6)
+    th = _pow2_freqs(8, rng)
+    z = (t[..., 0::2] + 1j * t[..., 1::2]) * np.exp(1j * pos[:, None, None] * th.astype(np.float64))
+    y = oracle.rope(t, pos, th)
+    np.testing.assert_allclose(y[..., 0::2], z.real, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y[..., 1::2], z.imag, rtol=0, atol=1e-13)
+
+
+def test_rope_sign_and_plane_of_each_frequency():
+    """Unit vector e_{2i} at angle a turns to (cos a, sin a) in plane i and
+    e_{2i+1} to (-sin a, cos a), with a = p * theta_i of its own plane i; no
+    other component moves (catches a clockwise turn, the half-split pairing
+    (c, c + d/2) and a frequency taken by component instead of by plane)."""
+    d = 8
+    th = np.array([1.0, 0.5, 0.25, 0.125], np.float32)
+    p = 3
+    for i in range(d // 2):
+        a = p * float(th[i])
+        for comp, want in ((2 * i, (math.cos(a), math.sin(a))), (2 * i + 1, (-math.sin(a), math.cos(a)))):
+            e = np.zeros((1, 1, d))
+            e[0, 0, comp] = 1.0
+            y = oracle.rope(e, np.array([p]), th)[0, 0]
+            expect = np.zeros(d)
+            expect[2 * i], expect[2 * i + 1] = want
+            np.testing.assert_allclose(y, expect, rtol=0, atol=1e-15)
+
+
+def test_rope_preserves_norms_of_every_plane():
+    rng = np.random.default_rng(33)
+    t = rng.standard_normal((7, 2, 64)) * 3
+    y = oracle.rope(t, rng.integers(0, 100000, 7), W.rope_inv_freq(64))
+    n_in = t[..., 0::2] ** 2 + t[..., 1::2] ** 2
+    n_out = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    np.testing.assert_allclose(n_out, n_in, rtol=1e-13, atol=0)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    """<R(m) q, R(n) k> = <q, R(n - m) k> = <R(m + s) q, R(n + s) k> for exact angles."""
+    rng = np.random.default_rng(34)
+    d = 16
+    th = _pow2_freqs(d // 2, rng)
+    q, k = rng.standard_normal((1, 1, d)), rng.standard_normal((1, 1, d))
+    for m, n, sh in ((0, 5, 7), (9, 2, 30), (40, 40, -13), (3, 100, 61)):
+        base = np.dot(oracle.rope(q, [m], th).ravel(), oracle.rope(k, [n], th).ravel())
+        rel = np.dot(q.ravel(), oracle.rope(k, [n - m], th).ravel())
+        shifted = np.dot(oracle.rope(q, [m + sh], th).ravel(), oracle.rope(k, [n + sh], th).ravel())
+        assert abs(base - rel) < 1e-12 and abs(base - shifted) < 1e-12
+
+
+def test_rope_composes_and_inverts():
+    rng = np.random.default_rng(35)
+    th = _pow2_freqs(4, rng)
+    t = rng.standard_normal((3, 2, 8))
+    a, b = np.array([3, 11, 50]), np.array([-7, 4, 9])
+    np.testing.assert_allclose(oracle.rope(oracle.rope(t, a, th), b, th), oracle.rope(t, a + b, th),
+                               rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.rope(oracle.rope(t, a, th), -a, th), t, rtol=0, atol=1e-13)
+
+
+def test_rope_angle_is_the_fp32_product():
+    """The angle reading: fp32 position times fp32 theta, rounded once to fp32."""
+    th = np.array([0.1, 1.0 / 3.0], np.float32)
+    a = oracle.rope_angles(np.array([12345, 7]), th)
+    for r, p in enumerate((12345, 7)):
+        for i in range(2):
+            assert a[r, i] == float(np.float32(np.float32(p) * th[i]))
+    assert a[0, 0] != 12345 * float(th[0])          # the rounding is visible at this position
+
+
+def test_qkv_proj_rope_rotates_q_and_k_heads_only():
+    rng = np.random.default_rng(36)
+    M, hidden, H_q, H_kv, d = 5, 12, 4, 2, 8
+    N = (H_q + 2 * H_kv) * d
+    x, w, bias = rng.standard_normal((M, hidden)), rng.standard_normal((hidden, N)), rng.standard_normal(N)
+    pos = rng.integers(0, 50, M)
+    th = _pow2_freqs(d // 2, rng)
+    out = oracle.qkv_proj_rope(x, w, pos, th, H_q, H_kv, d, bias)
+    plain = x @ w + bias
+    np.testing.assert_array_equal(out[:, (H_q + H_kv) * d:], plain[:, (H_q + H_kv) * d:])
+    # every Q and K head: the complex rotation of the biased projection
+    for c0 in range(0, (H_q + H_kv) * d, d):
+        blk = plain[:, c0:c0 + d]
+        z = (blk[:, 0::2] + 1j * blk[:, 1::2]) * np.exp(1j * pos[:, None] * th.astype(np.float64))
+        np.testing.assert_allclose(out[:, c0:c0 + d:2], z.real, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(out[:, c0 + 1:c0 + d:2], z.imag, rtol=0, atol=1e-12)
+
+
+def test_rope_decode_steps_reproduce_causal_prefill_rows():
+    """With the rotary embedding, generating token by token (the token at step s
+    rotated at position s = seq_len - 1) gives row s of causal attention over
+    the whole sequence rotated at positions 0..T-1: pins the decode position."""
+    rng = np.random.default_rng(37)
+    B, T, hidden, H_q, H_kv, d, L_max = 2, 6, 12, 4, 2, 8, 8
+    N = (H_q + 2 * H_kv) * d
+    xs = rng.standard_normal((B, T, hidden))
+    w = rng.standard_normal((hidden, N)) / math.sqrt(hidden)
+    th = W.rope_inv_freq(d, base=7.0)
+    pos = W.prefill_positions(B, T)
+    qkv = oracle.qkv_proj_rope(xs.reshape(B * T, hidden), w, pos, th, H_q, H_kv, d).reshape(B, T, N)
+    q_all, k_all, v_all = oracle.split_qkv(qkv, H_q, H_kv, d)
+    O_ref, L_ref = oracle.attention(q_all, k_all, v_all, True, 0.5)
+    kc = np.full((B, L_max, H_kv, d), 7.0)
+    vc = np.full((B, L_max, H_kv, d), -3.0)
+    for s_ in range(T):
+        lens = np.full(B, s_ + 1, dtype=np.int32)
+        _, kc, vc, O, LSE = oracle.decode_step(xs[:, s_], w, kc, vc, lens, H_q, H_kv, d, 0.5, inv_freq=th)
+        np.testing.assert_allclose(O, O_ref[:, s_], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(LSE, L_ref[:, :, s_], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(kc[:, :T], k_all, rtol=0, atol=1e-14)
+    # rotation matters here: without it the cached keys differ
+    k_plain = oracle.split_qkv(oracle.qkv_proj(xs, w), H_q, H_kv, d)[1]
+    assert np.abs(k_plain[:, 1:] - k_all[:, 1:]).max() > 1e-2
+
+
+def test_append_positions_reading():
+    np.testing.assert_array_equal(oracle.append_positions(np.array([1, 5, 0, 9, -3]), 8), [0, 4, 0, 7, 0])
+
+
 def test_kv_append_skips_out_of_range_lengths():
     kc, vc = np.zeros((3, 4, 1, 2)), np.zeros((3, 4, 1, 2))
     kn, vn = np.ones((3, 1, 2)), 2 * np.ones((3, 1, 2))
@@ -639,3 +779,58 @@ def test_fp8_row_quantisation_ties_and_saturation():
     np.testing.assert_array_equal(q8[0], [448, 224, 256, 256, -224, 0])
     z8, zs = fp8.quantize_rows(np.zeros((1, 8)))
     assert zs[0] == 1.0 and not z8.any()
+
+
+def _rope_pins_pass() -> bool:
+    checks = [test_rope_position_zero_is_identity, test_rope_is_the_complex_rotation,
+              test_rope_sign_and_plane_of_each_frequency, test_rope_preserves_norms_of_every_plane,
+              test_rope_scores_depend_on_relative_position_only, test_qkv_proj_rope_rotates_q_and_k_heads_only,
+              test_rope_decode_steps_reproduce_causal_prefill_rows]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def test_planted_rope_mistakes_are_caught(monkeypatch):
+    assert _rope_pins_pass()
+    real_rope, real_angles, real_pos = oracle.rope, oracle.rope_angles, oracle.append_positions
+
+    def clockwise(t, p, th):
+        return real_rope(t, -np.asarray(p), th)
+
+    def half_split(t, p, th):
+        # pairs (c, c + d/2) instead of (2i, 2i+1)
+        t = np.asarray(t, dtype=float)
+        d = t.shape[-1]
+        perm = np.empty(d, dtype=int)
+        perm[0::2], perm[1::2] = np.arange(d // 2), np.arange(d // 2) + d // 2
+        y = np.empty_like(t)
+        y[..., perm] = real_rope(t[..., perm], p, th)
+        return y
+
+    def freq_by_component(p, th):
+        # theta indexed by component 2i instead of by plane i (wraps at d/2)
+        th = np.asarray(th)
+        return real_angles(p, th[(2 * np.arange(len(th))) % len(th)])
+
+    mutations = {
+        "clockwise": lambda: monkeypatch.setattr(oracle, "rope", clockwise),
+        "half_split": lambda: monkeypatch.setattr(oracle, "rope", half_split),
+        "freq_by_component": lambda: monkeypatch.setattr(oracle, "rope_angles", freq_by_component),
+        "decode_position_is_length": lambda: monkeypatch.setattr(
+            oracle, "append_positions", lambda lens, L: np.clip(np.asarray(lens), 0, L - 1)),
+        "no_rotation_of_k": lambda: monkeypatch.setattr(
+            oracle, "qkv_proj_rope",
+            lambda x, w, p, th, Hq, Hkv, d, bias=None: (lambda o: (o.__setitem__(
+                (slice(None), slice(0, Hq * d)),
+                real_rope(o[:, :Hq * d].reshape(len(o), Hq, d), p, th).reshape(len(o), Hq * d)), o)[1])(
+                oracle.qkv_proj(x, w, bias))),
+    }
+    assert real_pos is oracle.append_positions
+    for name, apply in mutations.items():
+        monkeypatch.undo()
+        apply()
+        assert not _rope_pins_pass(), f"planted mistake {name} not caught"

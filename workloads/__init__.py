@@ -223,6 +223,19 @@ def decode_step_q(wl: Workload, step: int, batch: Optional[range] = None) -> np.
     return _encode(q, wl.dtype)
 
 
+def rope_inv_freq(d: int, base: float = 10000.0) -> np.ndarray:
+    """Rotary frequencies theta_i = base^(-2i/d), i < d/2, as fp32: the usual
+    table of LLaMA-family models (TinyLlama and Llama-2 use base 10000).  An
+    input of the projection, like its weight."""
+    i = np.arange(d // 2, dtype=np.float64)
+    return (base ** (-2.0 * i / d)).astype(np.float32)
+
+
+def prefill_positions(B: int, L: int) -> np.ndarray:
+    """Row positions of a [B*L]-row prefill batch: 0..L-1 for each sequence."""
+    return np.tile(np.arange(L, dtype=np.int32), B)
+
+
 def small(dtype: str, seed: int, B: int, L_q: int, L_kv: int, H_q: int, H_kv: int, d: int,
           std: float = 1.0) -> Dict[str, np.ndarray]:
     """Small random Q/K/V for parity cases that span several tiles and a ragged tail."""
