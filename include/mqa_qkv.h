@@ -9,6 +9,8 @@
  *                        LlamaAttention.forward);
  *      qkv_proj_append   the same GEMM for a decode step, also writing the
  *                        new token's K and V rows into the KV caches;
+ *      qkv_proj_rope, qkv_proj_append_rope  the same with the rotary
+ *                        position embedding of Q and K in the epilogue;
  *   2. the split into Q, K, V is not a call: Q, K and V are strided views of
  *      the packed qkv rows (same diff: query columns first, then key, then
  *      value; within a block the column is head*d + c).  The attention calls
@@ -130,6 +132,53 @@ mqkv_status qkv_proj_append(const void* x, const void* w_qkv, const void* bias, 
                             int32_t B, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                             int32_t L_max, mqkv_dtype dtype, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * qkv_proj with the rotary position embedding of the Q and K heads fused into
+ * its epilogue (the positional step the "custom op overhead" gist's forward
+ * applies to q and k right after the split; the FlashAttention-3 news page,
+ * FP8 section, counts rotary among the memory-bound steps ahead of attention
+ * that are best fused).  The pages do not define the rotation; this is
+ * RoFormer's: for row m at position p = positions[m], plane i of every Q and
+ * K head, its components (2i, 2i+1) at columns c0 + 2i and c0 + 2i + 1 of a
+ * head starting at column c0, turns counter-clockwise by
+ *
+ *   a = fp32(fp32(p) * inv_freq[i])              (one fp32 rounding)
+ *   y[2i]   = x[2i] cos a - x[2i+1] sin a
+ *   y[2i+1] = x[2i] sin a + x[2i+1] cos a
+ *
+ * where x is the projection with its bias, in fp32 before the output rounding.
+ * V columns are as in qkv_proj.  sin and cos are evaluated on the device to a
+ * few fp32 ulps for |a| < 2^22.  Checkpoints that pair components (c, c + d/2)
+ * instead use this call after permuting each Q and K head's columns of W (and
+ * bias) so that c -> 2c and c + d/2 -> 2c + 1; attention scores are unchanged
+ * by such a permutation of Q and K alike.
+ *
+ * positions [M] device int32 (any values; converted to fp32 exactly for
+ *           |p| < 2^24), 4-byte aligned
+ * inv_freq  [d/2] device fp32 rotation frequencies theta_i (usually
+ *           base^(-2i/d)), 4-byte aligned
+ * Other arguments, requirements and errors are those of qkv_proj;
+ * MQKV_ERR_INVALID if positions or inv_freq is NULL or misaligned.
+ */
+mqkv_status qkv_proj_rope(const void* x, const void* w_qkv, const void* bias, void* qkv,
+                          const int32_t* positions, const float* inv_freq, int64_t M, int64_t hidden,
+                          int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * qkv_proj_append with the rotary embedding of qkv_proj_rope: row b is rotated
+ * at the position of its own cache slot, p = seq_lens[b] - 1 (clamped to
+ * [0, L_max - 1] for rows that are not appended), so a decode step reproduces
+ * the prefill row at that position.  The appended K is the rotated K (the same
+ * bits as qkv's K columns); V is not rotated.  Arguments as qkv_proj_append,
+ * plus inv_freq as in qkv_proj_rope (MQKV_ERR_INVALID if NULL or misaligned).
+ */
+mqkv_status qkv_proj_append_rope(const void* x, const void* w_qkv, const void* bias, void* qkv,
+                                 void* k_cache, void* v_cache, const int32_t* seq_lens,
+                                 const float* inv_freq, int32_t B, int64_t hidden, int32_t H_q,
+                                 int32_t H_kv, int32_t d, int32_t L_max, mqkv_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Grouped-query attention over a whole sequence (prefill).

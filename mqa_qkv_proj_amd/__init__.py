@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libmqa_qkv.so")
 MQKV_OK, MQKV_ERR_INVALID, MQKV_ERR_UNSUPPORTED, MQKV_ERR_HIP = 0, 1, 2, 3
 MQKV_F32, MQKV_BF16 = 0, 1
 
-EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill_workspace_bytes",
+EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "qkv_proj_rope", "qkv_proj_append_rope",
+           "gqa_attn_prefill_workspace_bytes",
            "gqa_attn_prefill", "gqa_attn_decode_paged", "gqa_attn_prefill_varlen",
            "gqa_attn_prefill_fp8_workspace_bytes", "gqa_attn_prefill_fp8",
            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "gqa_attn_decode_noalloc", "mqkv_status_string",
@@ -59,6 +60,11 @@ def _load() -> ctypes.CDLL:
     lib.qkv_proj.restype = i32
     lib.qkv_proj_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.qkv_proj_append.restype = i32
+    lib.qkv_proj_rope.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, sz, vp]
+    lib.qkv_proj_rope.restype = i32
+    lib.qkv_proj_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, vp,
+                                         sz, vp]
+    lib.qkv_proj_append_rope.restype = i32
     lib.gqa_attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.gqa_attn_prefill_workspace_bytes.restype = sz
     lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32,
@@ -157,14 +163,8 @@ def qkv_proj_workspace_bytes(M: int, hidden: int, H_q: int, H_kv: int, d: int, d
     return int(lib.qkv_proj_workspace_bytes(M, hidden, H_q, H_kv, d, dtype_code))
 
 
-def qkv_proj(x, w_qkv, H_q: int, H_kv: int, d: int, bias=None, out=None, workspace=None):
-    """Fused projection qkv = x . W_qkv (+ bias): one GEMM for Q, K and V.
-
-    x [..., hidden] (contiguous), w_qkv [hidden, N] row-major, N = (H_q + 2*H_kv)*d.
-    Returns qkv [..., N] (or writes `out`).  `workspace` (uint8 device tensor) is
-    allocated when the call can use one and none is given."""
-    torch = _torch()
-    _require_cuda(x, w_qkv, bias, out, workspace)
+def _proj_operands(torch, x, w_qkv, H_q, H_kv, d, bias, out, workspace):
+    """Checks shared by the projection calls; returns (M, hidden, out, ws_ptr, ws_bytes)."""
     hidden = x.shape[-1]
     N = (H_q + 2 * H_kv) * d
     if w_qkv.shape != (hidden, N):
@@ -184,10 +184,75 @@ def qkv_proj(x, w_qkv, H_q: int, H_kv: int, d: int, bias=None, out=None, workspa
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return M, hidden, out, ws_ptr, ws_bytes
+
+
+def _check_inv_freq(torch, inv_freq, d):
+    if inv_freq.dtype != torch.float32 or inv_freq.shape != (d // 2,) or not inv_freq.is_contiguous():
+        raise ValueError(f"inv_freq must be a contiguous float32 [{d // 2}] tensor")
+
+
+def qkv_proj(x, w_qkv, H_q: int, H_kv: int, d: int, bias=None, out=None, workspace=None):
+    """Fused projection qkv = x . W_qkv (+ bias): one GEMM for Q, K and V.
+
+    x [..., hidden] (contiguous), w_qkv [hidden, N] row-major, N = (H_q + 2*H_kv)*d.
+    Returns qkv [..., N] (or writes `out`).  `workspace` (uint8 device tensor) is
+    allocated when the call can use one and none is given."""
+    torch = _torch()
+    _require_cuda(x, w_qkv, bias, out, workspace)
+    M, hidden, out, ws_ptr, ws_bytes = _proj_operands(torch, x, w_qkv, H_q, H_kv, d, bias, out, workspace)
     st = lib.qkv_proj(x.data_ptr(), w_qkv.data_ptr(), bias.data_ptr() if bias is not None else None,
                       out.data_ptr(), M, hidden, H_q, H_kv, d, _dtype_code(x.dtype), ws_ptr, ws_bytes,
                       _stream(x.device))
     check(st, "qkv_proj")
+    return out
+
+
+def qkv_proj_rope(x, w_qkv, positions, inv_freq, H_q: int, H_kv: int, d: int, bias=None, out=None,
+                  workspace=None):
+    """qkv_proj with the rotary embedding of every Q and K head in the epilogue.
+
+    positions: int32 [M] device tensor (one per row of x), inv_freq: float32
+    [d/2] device tensor; plane i = components (2i, 2i+1) of a head turns by
+    fp32(position * inv_freq[i]).  V is not rotated."""
+    torch = _torch()
+    _require_cuda(x, w_qkv, positions, inv_freq, bias, out, workspace)
+    M, hidden, out, ws_ptr, ws_bytes = _proj_operands(torch, x, w_qkv, H_q, H_kv, d, bias, out, workspace)
+    if positions.dtype != torch.int32 or positions.numel() != M or not positions.is_contiguous():
+        raise ValueError(f"positions must be a contiguous int32 tensor of {M} elements")
+    _check_inv_freq(torch, inv_freq, d)
+    st = lib.qkv_proj_rope(x.data_ptr(), w_qkv.data_ptr(), bias.data_ptr() if bias is not None else None,
+                           out.data_ptr(), positions.data_ptr(), inv_freq.data_ptr(), M, hidden, H_q, H_kv, d,
+                           _dtype_code(x.dtype), ws_ptr, ws_bytes, _stream(x.device))
+    check(st, "qkv_proj_rope")
+    return out
+
+
+def _append_call(fn_name, x, w_qkv, k_cache, v_cache, seq_lens, inv_freq, H_q, H_kv, d, bias, out, workspace):
+    torch = _torch()
+    _require_cuda(x, w_qkv, k_cache, v_cache, seq_lens, inv_freq, bias, out, workspace)
+    if x.dim() != 2:
+        raise ValueError("x must be [B, hidden]")
+    B = x.shape[0]
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("the caches must be contiguous")
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[2:] != (H_kv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError(f"caches must be [{B}, L_max, {H_kv}, {d}]")
+    if k_cache.dtype != x.dtype or v_cache.dtype != x.dtype:
+        raise ValueError("x, w_qkv and the caches must share a dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    if inv_freq is not None:
+        _check_inv_freq(torch, inv_freq, d)
+    _, hidden, out, ws_ptr, ws_bytes = _proj_operands(torch, x, w_qkv, H_q, H_kv, d, bias, out, workspace)
+    head = (x.data_ptr(), w_qkv.data_ptr(), bias.data_ptr() if bias is not None else None, out.data_ptr(),
+            k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr())
+    tail = (B, hidden, H_q, H_kv, d, k_cache.shape[1], _dtype_code(x.dtype), ws_ptr, ws_bytes, _stream(x.device))
+    if inv_freq is None:
+        st = lib.qkv_proj_append(*head, *tail)
+    else:
+        st = lib.qkv_proj_append_rope(*head, inv_freq.data_ptr(), *tail)
+    check(st, fn_name)
     return out
 
 
@@ -199,40 +264,16 @@ def qkv_proj_append(x, w_qkv, k_cache, v_cache, seq_lens, H_q: int, H_kv: int, d
     contiguous, seq_lens [B] int32 on the device (lengths including the new
     token).  Returns qkv [B, N] like qkv_proj and writes k_cache[b, seq_lens[b]-1]
     and v_cache[b, seq_lens[b]-1] in place."""
-    torch = _torch()
-    _require_cuda(x, w_qkv, k_cache, v_cache, seq_lens, bias, out, workspace)
-    if x.dim() != 2:
-        raise ValueError("x must be [B, hidden]")
-    B, hidden = x.shape
-    N = (H_q + 2 * H_kv) * d
-    if w_qkv.shape != (hidden, N):
-        raise ValueError(f"w_qkv must be [{hidden}, {N}], got {tuple(w_qkv.shape)}")
-    if not (x.is_contiguous() and w_qkv.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()):
-        raise ValueError("x, w_qkv and the caches must be contiguous")
-    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[2:] != (H_kv, d) or v_cache.shape != k_cache.shape:
-        raise ValueError(f"caches must be [{B}, L_max, {H_kv}, {d}]")
-    if k_cache.dtype != x.dtype or v_cache.dtype != x.dtype or w_qkv.dtype != x.dtype:
-        raise ValueError("x, w_qkv and the caches must share a dtype")
-    if bias is not None and (bias.dtype != x.dtype or bias.shape != (N,)):
-        raise ValueError("bias must be [N] of x's dtype")
-    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_contiguous():
-        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
-    if out is None:
-        out = torch.empty(B, N, dtype=x.dtype, device=x.device)
-    elif out.shape != (B, N) or not out.is_contiguous() or out.dtype != x.dtype:
-        raise ValueError("out has the wrong shape, dtype or layout")
-    if workspace is None:
-        need = qkv_proj_workspace_bytes(B, hidden, H_q, H_kv, d, _dtype_code(x.dtype))
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.qkv_proj_append(x.data_ptr(), w_qkv.data_ptr(), bias.data_ptr() if bias is not None else None,
-                             out.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B,
-                             hidden, H_q, H_kv, d, k_cache.shape[1], _dtype_code(x.dtype), ws_ptr, ws_bytes,
-                             _stream(x.device))
-    check(st, "qkv_proj_append")
-    return out
+    return _append_call("qkv_proj_append", x, w_qkv, k_cache, v_cache, seq_lens, None, H_q, H_kv, d, bias, out,
+                        workspace)
+
+
+def qkv_proj_append_rope(x, w_qkv, k_cache, v_cache, seq_lens, inv_freq, H_q: int, H_kv: int, d: int, bias=None,
+                         out=None, workspace=None):
+    """qkv_proj_append with Q and K rotated at each row's cache slot seq_lens[b] - 1
+    (the rotation of qkv_proj_rope); the appended K is the rotated one."""
+    return _append_call("qkv_proj_append_rope", x, w_qkv, k_cache, v_cache, seq_lens, inv_freq, H_q, H_kv, d, bias,
+                        out, workspace)
 
 
 def split_qkv(qkv, H_q: int, H_kv: int, d: int):

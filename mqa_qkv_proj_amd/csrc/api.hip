@@ -58,7 +58,7 @@ const char* mqkv_status_string(mqkv_status s) {
 
 const char* mqkv_last_error(void) { return g_err; }
 
-int32_t mqkv_abi_version(void) { return 107; }
+int32_t mqkv_abi_version(void) { return 108; }
 
 size_t qkv_proj_workspace_bytes(int64_t M, int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d,
                                 mqkv_dtype dtype) {
@@ -77,7 +77,7 @@ namespace {
 // Validation and dispatch shared by qkv_proj and qkv_proj_append.
 mqkv_status proj_common(const void* x, const void* w_qkv, const void* bias, void* qkv, int64_t M,
                         int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype,
-                        void* workspace, size_t workspace_bytes, void* stream, const mqkv::KvAppend& app,
+                        void* workspace, size_t workspace_bytes, void* stream, const mqkv::ProjEpilogue& app,
                         const char* what) {
   if (!dtype_ok(dtype)) return fail(MQKV_ERR_INVALID, "dtype %d unknown", (int)dtype);
   mqkv_status st = check_heads(H_q, H_kv, d);
@@ -107,16 +107,43 @@ mqkv_status qkv_proj(const void* x, const void* w_qkv, const void* bias, void* q
                      int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype,
                      void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  const mqkv::KvAppend none{};
+  const mqkv::ProjEpilogue none{};
   return proj_common(x, w_qkv, bias, qkv, M, hidden, H_q, H_kv, d, dtype, workspace, workspace_bytes, stream,
                      none, "qkv_proj launch");
 }
 
-mqkv_status qkv_proj_append(const void* x, const void* w_qkv, const void* bias, void* qkv, void* k_cache,
-                            void* v_cache, const int32_t* seq_lens, int32_t B, int64_t hidden, int32_t H_q,
-                            int32_t H_kv, int32_t d, int32_t L_max, mqkv_dtype dtype, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+mqkv_status qkv_proj_rope(const void* x, const void* w_qkv, const void* bias, void* qkv,
+                          const int32_t* positions, const float* inv_freq, int64_t M, int64_t hidden,
+                          int32_t H_q, int32_t H_kv, int32_t d, mqkv_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
+  if (!positions || !inv_freq) return fail(MQKV_ERR_INVALID, "positions and inv_freq must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(positions) & 3u) != 0 || (reinterpret_cast<uintptr_t>(inv_freq) & 3u) != 0)
+    return fail(MQKV_ERR_INVALID, "positions and inv_freq must be 4-byte aligned");
+  const mqkv_status st = check_heads(H_q, H_kv, d);
+  if (st != MQKV_OK) return st;
+  if ((int64_t)(H_q + 2 * (int64_t)H_kv) * d > 0x7fffffff)
+    return fail(MQKV_ERR_UNSUPPORTED, "sizes beyond 2^31-1 are not supported");
+  mqkv::ProjEpilogue ep{};
+  ep.kcol = H_q * d;
+  ep.vcol = (H_q + H_kv) * d;
+  ep.inv_freq = inv_freq;
+  ep.pos = positions;
+  ep.rope_d = d;
+  return proj_common(x, w_qkv, bias, qkv, M, hidden, H_q, H_kv, d, dtype, workspace, workspace_bytes, stream,
+                     ep, "qkv_proj_rope launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch shared by qkv_proj_append and qkv_proj_append_rope.
+mqkv_status append_common(const void* x, const void* w_qkv, const void* bias, void* qkv, void* k_cache,
+                          void* v_cache, const int32_t* seq_lens, const float* inv_freq, int32_t B,
+                          int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, int32_t L_max,
+                          mqkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                          const char* what) {
   if (!k_cache || !v_cache || !seq_lens)
     return fail(MQKV_ERR_INVALID, "k_cache, v_cache and seq_lens must be non-NULL");
   if (!aligned16(k_cache) || !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0)
@@ -127,9 +154,43 @@ mqkv_status qkv_proj_append(const void* x, const void* w_qkv, const void* bias, 
   if (st != MQKV_OK) return st;
   if ((int64_t)(H_q + 2 * (int64_t)H_kv) * d > 0x7fffffff)
     return fail(MQKV_ERR_UNSUPPORTED, "sizes beyond 2^31-1 are not supported");
-  const mqkv::KvAppend app{k_cache, v_cache, seq_lens, H_q * d, (H_q + H_kv) * d, L_max};
+  mqkv::ProjEpilogue ep{};
+  ep.k_cache = k_cache;
+  ep.v_cache = v_cache;
+  ep.seq_lens = seq_lens;
+  ep.kcol = H_q * d;
+  ep.vcol = (H_q + H_kv) * d;
+  ep.L_max = L_max;
+  ep.inv_freq = inv_freq;  // nullptr: no rotation
+  ep.pos = nullptr;        // rotation at seq_lens[b] - 1
+  ep.rope_d = d;
   return proj_common(x, w_qkv, bias, qkv, B, hidden, H_q, H_kv, d, dtype, workspace, workspace_bytes, stream,
-                     app, "qkv_proj_append launch");
+                     ep, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+mqkv_status qkv_proj_append(const void* x, const void* w_qkv, const void* bias, void* qkv, void* k_cache,
+                            void* v_cache, const int32_t* seq_lens, int32_t B, int64_t hidden, int32_t H_q,
+                            int32_t H_kv, int32_t d, int32_t L_max, mqkv_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  return append_common(x, w_qkv, bias, qkv, k_cache, v_cache, seq_lens, nullptr, B, hidden, H_q, H_kv, d, L_max,
+                       dtype, workspace, workspace_bytes, stream, "qkv_proj_append launch");
+}
+
+mqkv_status qkv_proj_append_rope(const void* x, const void* w_qkv, const void* bias, void* qkv, void* k_cache,
+                                 void* v_cache, const int32_t* seq_lens, const float* inv_freq, int32_t B,
+                                 int64_t hidden, int32_t H_q, int32_t H_kv, int32_t d, int32_t L_max,
+                                 mqkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!inv_freq) return fail(MQKV_ERR_INVALID, "inv_freq must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(inv_freq) & 3u) != 0)
+    return fail(MQKV_ERR_INVALID, "inv_freq must be 4-byte aligned");
+  return append_common(x, w_qkv, bias, qkv, k_cache, v_cache, seq_lens, inv_freq, B, hidden, H_q, H_kv, d, L_max,
+                       dtype, workspace, workspace_bytes, stream, "qkv_proj_append_rope launch");
 }
 
 size_t gqa_attn_prefill_workspace_bytes(int32_t B, int32_t L_kv, int32_t H_kv, int32_t d,

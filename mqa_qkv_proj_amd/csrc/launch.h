@@ -16,21 +16,31 @@ struct SkinnyPlan {
 };
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N);
 
-// Optional projection epilogue: the K and V columns of row m are also written
-// to the caches [rows, L_max, H_kv, d] at token position seq_lens[m] - 1 (row m
-// is sequence m's new token).  k_cache == nullptr: no append.
-struct KvAppend {
+// Optional projection epilogue work, applied to each output element in fp32
+// before its rounding:
+//  * rotary embedding (inv_freq != nullptr): the columns n < vcol (Q and K
+//    heads) are turned in planes (2i, 2i+1) of each head by the angle
+//    fp32(position(m) * inv_freq[i]), i = (n mod d) / 2, the bias added first;
+//    position(m) = pos[m], or with pos == nullptr seq_lens[m] - 1 clamped to
+//    [0, L_max - 1] (the decode row's own cache slot);
+//  * KV-cache append (k_cache != nullptr): the K and V columns of row m are
+//    also written to the caches [rows, L_max, H_kv, d] at token position
+//    seq_lens[m] - 1 (row m is sequence m's new token).
+struct ProjEpilogue {
   void* k_cache;
   void* v_cache;
   const int32_t* seq_lens;
   int kcol;   // first K column (H_q * d)
   int vcol;   // first V column ((H_q + H_kv) * d); H_kv * d = vcol - kcol
   int L_max;
+  const float* inv_freq;  // [d / 2]
+  const int32_t* pos;     // [M] or nullptr
+  int rope_d;             // head dimension d (64 or 128)
 };
 
 hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void* out, int64_t M,
                            int64_t K, int64_t N, bool bf16, void* ws, size_t ws_bytes, hipStream_t s,
-                           const KvAppend& app);
+                           const ProjEpilogue& app);
 
 struct PrefillArgs {
   const void* q;

@@ -11,26 +11,85 @@
 //    (W streamed through an LDS ring filled by LDS-DMA, no k split);
 //  * M <= 128 otherwise: register-staged skinny kernel, k split over
 //    workgroups with a fixed-order reduce kernel;
-//  * M > 128, K % 64 == 0, N % 8 == 0: LDS-DMA fed 128x128 / 64x128 tiles, the
-//    W tile kept row-major and read with transposing LDS loads;
+//  * M > 128, K % 64 == 0, N % 8 == 0: LDS-DMA fed tiles (128 or 64 rows, 128
+//    or 160 columns, picked so the tiles fill the CUs), the W tile kept
+//    row-major and read with transposing LDS loads;
 //  * anything else: register-prefetched tiles with W transposed into LDS by
 //    the loading threads.
 // fp32 path: plain LDS-tiled fp32 FMA (a correctness path for the tiny fp32 layer).
+//
+// Every kernel's epilogue can also rotate the Q and K heads (rotary position
+// embedding, see ProjEpilogue) before the output is rounded, and append the
+// new token's K and V rows to the KV caches.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
 namespace mqkv {
 
-// The append epilogue for one output element (see KvAppend): a no-op unless an
+// The append epilogue for one output element (see ProjEpilogue): a no-op unless an
 // append is requested, n is a K or V column and row m's position is valid.
 template <typename T>
-__device__ __forceinline__ void append_store(const KvAppend& a, int m, int n, T v) {
+__device__ __forceinline__ void append_store(const ProjEpilogue& a, int m, int n, T v) {
   if (a.k_cache == nullptr || n < a.kcol) return;
   const int len = a.seq_lens[m];
   if (len < 1 || len > a.L_max) return;
   const bool is_k = n < a.vcol;
   T* cache = static_cast<T*>(is_k ? a.k_cache : a.v_cache);
   cache[((int64_t)m * a.L_max + (len - 1)) * (a.vcol - a.kcol) + (n - (is_k ? a.kcol : a.vcol))] = v;
+}
+
+// ----------------------------------------------------------------------------- rotary embedding
+// sin and cos of a (radians).  Cody and Waite's argument reduction: a = k pi/2
+// + r with k the integer nearest a 2/pi and r = a - k P1 - k P2, pi/2 = P1 + P2
+// split into its fp32 value and the fp32 remainder; each product is exact
+// inside its FMA, so r carries an error near one ulp of r plus k times the
+// 2.6e-15 left of pi/2 (1e-8 at |a| = 2^22).  On |r| <= pi/4 the Taylor series
+// of sin to r^9 and of cos to r^10 are within 3e-9; k mod 4 picks and signs them.
+__device__ __forceinline__ void rope_sincos(float a, float& s, float& c) {
+  const float k = __builtin_rintf(a * 0.636619772367581343f);
+  float r = __builtin_fmaf(-k, 1.57079637050628662109375f, a);
+  r = __builtin_fmaf(-k, -4.37113900018624283e-8f, r);
+  const float r2 = r * r;
+  float ps = __builtin_fmaf(r2, 2.75573192239858907e-6f, -1.98412698412698413e-4f);
+  ps = __builtin_fmaf(r2, ps, 8.33333333333333333e-3f);
+  ps = __builtin_fmaf(r2, ps, -1.66666666666666667e-1f);
+  ps = __builtin_fmaf(r2 * r, ps, r);
+  float pc = __builtin_fmaf(r2, -2.75573192239858907e-7f, 2.48015873015873016e-5f);
+  pc = __builtin_fmaf(r2, pc, -1.38888888888888889e-3f);
+  pc = __builtin_fmaf(r2, pc, 4.16666666666666667e-2f);
+  pc = __builtin_fmaf(r2, pc, -0.5f);
+  pc = __builtin_fmaf(r2, pc, 1.0f);
+  const int q = (int)k;
+  const float sq = (q & 1) ? pc : ps, cq = (q & 1) ? ps : pc;
+  s = (q & 2) ? -sq : sq;
+  c = ((q + 1) & 2) ? -cq : cq;
+}
+
+// The value held by the neighbouring lane (lane ^ 1).  In every output layout
+// here a lane's partner column n ^ 1 is held by that lane, for the same rows.
+// Both lanes of a pair must be active.
+__device__ __forceinline__ float pair_partner(float v) {
+  // DPP quad_perm [1, 0, 3, 2]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ int rope_position(const ProjEpilogue& e, int m) {
+  if (e.pos) return e.pos[m];
+  return min(max(e.seq_lens[m] - 1, 0), e.L_max - 1);
+}
+
+// Column n (a Q or K column) of a row at position p: v is its value, w the
+// value of the other column of its plane (n ^ 1), th the plane's frequency.
+__device__ __forceinline__ float rope_turn(float v, float w, int n, int p, float th) {
+  float sn, cs;
+  rope_sincos((float)p * th, sn, cs);
+  return __builtin_fmaf(w, (n & 1) ? sn : -sn, v * cs);
+}
+
+__device__ __forceinline__ float rope_freq(const ProjEpilogue& e, int n) {
+  return e.inv_freq[(n & (e.rope_d - 1)) >> 1];
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int KS>
@@ -55,7 +114,7 @@ struct GemmCfg {
 template <int BM, int BN, int BK, int WM, int WN, int KS>
 __global__ __launch_bounds__(WM* WN* KS * 64) void qkv_gemm_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int K, int N, KvAppend app) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int M, int K, int N, ProjEpilogue app) {
   using C = GemmCfg<BM, BN, BK, WM, WN, KS>;
   extern __shared__ __align__(16) uint16_t smem[];
   // stage s: x tile at smem + s*kLdsTile, transposed W tile right after it
@@ -194,15 +253,22 @@ __global__ __launch_bounds__(WM* WN* KS * 64) void qkv_gemm_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < C::kNI; ++j) {
     const int gn = n0 + wn * (BN / WN) + j * 32 + l32;
-    if (gn >= N) continue;
+    if (gn >= N) continue;  // N is even: both columns of a plane are in or out
     const float bv = bias ? bf16_to_f32(bias[gn]) : 0.0f;
+    const bool rot = app.inv_freq != nullptr && gn < app.vcol;  // uniform over 32 columns
+    const float th = rot ? rope_freq(app, gn) : 0.0f;
 #pragma unroll
     for (int i = 0; i < C::kMI; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int gm = m0 + wm * (BM / WM) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
+        float v = acc[i][j][e] + bv;
+        if (rot) {
+          const float w = pair_partner(v);
+          if (gm < M) v = rope_turn(v, w, gn, rope_position(app, gm), th);
+        }
         if (gm < M) {
-          const uint16_t r = f32_to_bf16(acc[i][j][e] + bv);
+          const uint16_t r = f32_to_bf16(v);
           out[(int64_t)gm * N + gn] = r;
           append_store(app, gm, gn, r);
         }
@@ -216,7 +282,7 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
                                                            const float* __restrict__ w,
                                                            const float* __restrict__ bias,
                                                            float* __restrict__ out, int M, int K,
-                                                           int N, KvAppend app) {
+                                                           int N, ProjEpilogue app) {
   __shared__ float As[16][64 + 1];
   __shared__ float Bs[16][64 + 4];
   const int tid = threadIdx.x;
@@ -245,17 +311,29 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
     }
     __syncthreads();
   }
+  const int gn0 = n0 + tx * 4;  // 4 columns: two whole planes, all on one side of vcol
+  const bool rot = app.inv_freq != nullptr && gn0 < app.vcol;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int gm = m0 + ty * 4 + i;
     if (gm >= M) continue;
+    float r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = gn0 + j < N ? acc[i][j] + (bias ? bias[gn0 + j] : 0.0f) : 0.0f;
+    if (rot) {
+      const int p = rope_position(app, gm);
+      float t[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[j] = rope_turn(r[j], r[j ^ 1], gn0 + j, p, rope_freq(app, gn0 + j));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = t[j];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + tx * 4 + j;
+      const int gn = gn0 + j;
       if (gn < N) {
-        const float r = acc[i][j] + (bias ? bias[gn] : 0.0f);
-        out[(int64_t)gm * N + gn] = r;
-        append_store(app, gm, gn, r);
+        out[(int64_t)gm * N + gn] = r[j];
+        append_store(app, gm, gn, r[j]);
       }
     }
   }
@@ -283,7 +361,8 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
 // banks apart); the lanes of a copy that fall on padding point past the
 // buffer, so they fetch nothing and land only on padding bytes, which are
 // never read.  All operand reads of a 16-deep k step are issued together and
-// waited for once, a step ahead of their MFMAs.  Requires K % 64 == 0.
+// waited for once, a step ahead of their MFMAs.  The epilogue stages the sums
+// in LDS and writes 16-byte row pieces (TileEpi).  Requires K % 64 == 0.
 constexpr int kTBK = 64;
 constexpr int kTXld = kTBK + 8;  // x tile row pitch (bf16): 9 chunks of 16 B
 // W tile row pitch (bf16) for BN columns: the data rounded up to 16 dwords
@@ -308,10 +387,9 @@ struct TileCfg {
   static constexpr int kXCopies = kX * 2 / 1024, kWCopies = kW * 2 / 1024;
   static constexpr int kXcp = (kXCopies + kNW - 1) / kNW, kWcp = (kWCopies + kNW - 1) / kNW;  // per wave (at most)
   static constexpr size_t kBytes = (size_t)ST * kStage * sizeof(uint16_t);
-  static constexpr size_t kRedBytes = (size_t)(KW - 1) * WM * WN * kMI * kNI * 16 * 64 * 4;  // k-split sums
   static_assert(kMI * WM * 32 == BM && kNI * WN * 32 == BN && kKS * KW * 16 == kTBK, "wave layout");
   static_assert(kX * 2 % 1024 == 0 && kW * 2 % 1024 == 0, "tiles are whole 1 KB copies");
-  static_assert(kBytes <= 160 * 1024 && kRedBytes <= kBytes, "LDS");
+  static_assert(kBytes <= 160 * 1024, "LDS");
   // DMA instructions wave w issues per k tile
   static constexpr int copies_of(int w) {
     int c = 0;
@@ -449,10 +527,62 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// cos and sin of the rotation angle of every (row, plane) of a BM-row tile:
+// (cos, sin) of row r, plane i at tab[r * pitch + i], P = d / 2 planes;
+// rows past M take position 0.  Thread t fills planes 4g .. 4g + 3, g = t mod
+// (P / 4), of rows t / (P / 4) + k * THREADS / (P / 4).  Its positions and
+// frequencies are loaded by prefetch() before the main loop, so that their
+// latency hides under it; fill() evaluates the angles with the arithmetic of
+// rope_turn, so every kernel rotates alike.
+template <int BM, int THREADS>
+struct RopeTable {
+  static constexpr int kMaxRows = BM * 16 / THREADS;  // rows per thread at P = 64
+  static_assert(kMaxRows >= 1 && BM * 8 % THREADS == 0, "table split");
+  int pos[kMaxRows];
+  float th[4];
+  __device__ __forceinline__ void prefetch(const ProjEpilogue& app, int m0, int M, int tid) {
+    const int groups = app.rope_d >> 3, rows = BM * groups / THREADS;  // groups = P / 4
+    const int g = tid % groups, q = tid / groups;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) th[c] = app.inv_freq[4 * g + c];
+#pragma unroll
+    for (int k = 0; k < kMaxRows; ++k) {
+      const int m = m0 + q + k * (THREADS / groups);
+      pos[k] = (k < rows && m < M) ? rope_position(app, m) : 0;
+    }
+  }
+  __device__ __forceinline__ void fill(const ProjEpilogue& app, float2* tab, int pitch, int tid) const {
+    const int P = app.rope_d >> 1, groups = P >> 2, rows = BM * groups / THREADS;
+    const int g = tid % groups, q = tid / groups;
+#pragma unroll
+    for (int k = 0; k < kMaxRows; ++k) {
+      if (k >= rows) break;
+      float2 cs[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rope_sincos((float)pos[k] * th[c], cs[c].y, cs[c].x);
+      float2* dst = tab + (q + k * (THREADS / groups)) * pitch + 4 * g;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[c] = cs[c];
+    }
+  }
+};
+
+// LDS of the tile epilogue: fp32 staging rows of BN + 8 floats (rows 4 apart
+// fall 32 banks apart), then the rotation table (BM rows of d/2 + 2 float2),
+// then the bias of the tile's columns (BN bf16).
+template <int BM, int BN>
+struct TileEpi {
+  static constexpr int kPitch = BN + 8;
+  static constexpr size_t kStageBytes = (size_t)BM * kPitch * 4;
+  static size_t bytes(bool rope, int d, bool bias) {
+    return kStageBytes + (rope ? (size_t)BM * (d / 2 + 2) * 8 : 0) + (bias ? (size_t)BN * 2 : 0);
+  }
+};
+
 template <int BM, int BN, int WM, int WN, int KW, int ST>
 __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int M, int K, int N, KvAppend app) {
+    uint16_t* __restrict__ out, int M, int K, int N, ProjEpilogue app) {
   using L = TileCfg<BM, BN, WM, WN, KW, ST>;
   constexpr int MI = L::kMI, NI = L::kNI, NW = L::kNW;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -467,6 +597,10 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
   const int bm = lid / nbn, bn = lid % nbn;  // the n tiles of one m row are neighbours
   const int m0 = bm * BM, n0 = bn * BN;
   const int nk = K / kTBK;
+  // rotary embedding: this thread's positions and frequencies, loaded now
+  const bool rope = app.inv_freq != nullptr && n0 < app.vcol;  // uniform over the workgroup
+  RopeTable<BM, L::kThreads> rtab;
+  if (rope) rtab.prefetch(app, m0, M, tid);
 
   // ---- copy maps: slot (copy * 64 + lane) of a tile image -> global byte offset
   constexpr uint32_t kNoCopy = 0x80000000u;
@@ -567,49 +701,80 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
     });
   }
 
-  if constexpr (KW > 1) {
-    // add the k-step groups' sums through LDS (the stages are free now), in
-    // group order, so the result does not depend on timing
-    float* red = reinterpret_cast<float*>(smem);
-    constexpr int kPer = MI * NI * 16 * 64;  // floats per wave
-    __syncthreads();
-    if (kg > 0) {
+  // ---- epilogue.  The tile's sums are staged in LDS as fp32 rows (the stages
+  // are free now): k-step group 0 writes its sums, groups 1.. add theirs in
+  // group order (a fixed order, so the result does not depend on timing).
+  // Every thread then takes 8-column row pieces: bias, rotation, rounding to
+  // bf16, one 16-byte store (and the cache append).  A piece holds 4 whole
+  // planes of one head, so the rotation needs nothing from other threads.
+  using E = TileEpi<BM, BN>;
+  float* stg = reinterpret_cast<float*>(smem);
+  float2* tab = reinterpret_cast<float2*>(reinterpret_cast<char*>(smem) + E::kStageBytes);
+  const int tpitch = (app.rope_d >> 1) + 2;  // float2 per table row: 16-byte aligned rows
+  uint16_t* bstg = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(smem) + E::kStageBytes +
+                                               (rope ? (size_t)BM * tpitch * 8 : 0));
+  auto stage = [&](bool add) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            red[((kg - 1) * (WM * WN) + pos) * kPer + ((i * NI + j) * 16 + e) * 64 + lane] = acc[i][j][e];
-    }
-    __syncthreads();
-    if (kg > 0) return;
-#pragma unroll
-    for (int g = 1; g < KW; ++g)
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            acc[i][j][e] += red[((g - 1) * (WM * WN) + pos) * kPer + ((i * NI + j) * 16 + e) * 64 + lane];
-  }
-
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int gn = n0 + wn * (32 * NI) + j * 32 + l32;
-    if (gn >= N) continue;
-    const float bv = bias ? bf16_to_f32(bias[gn]) : 0.0f;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int gm = m0 + wm * (32 * MI) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
-        if (gm < M) {
-          const uint16_t r = f32_to_bf16(acc[i][j][e] + bv);
-          out[(int64_t)gm * N + gn] = r;
-          append_store(app, gm, gn, r);
+        for (int e = 0; e < 16; ++e) {
+          float& d = stg[(wm * (32 * MI) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4)) * E::kPitch + wn * (32 * NI) +
+                         j * 32 + l32];
+          d = add ? d + acc[i][j][e] : acc[i][j][e];
         }
+  };
+  __syncthreads();  // every wave is done with the stages
+  if (kg == 0) stage(false);
+  if (rope) rtab.fill(app, tab, tpitch, tid);
+  if (bias && tid < BN / 8 && n0 + tid * 8 < N) st16(bstg + tid * 8, ld16(bias + n0 + tid * 8));
+#pragma unroll
+  for (int g = 1; g < KW; ++g) {
+    __syncthreads();
+    if (kg == g) stage(true);
+  }
+  __syncthreads();
+
+  constexpr int kPieces = BM * BN / 8, kPerRow = BN / 8;
+  static_assert(kPieces % L::kThreads == 0, "pieces per thread");
+#pragma unroll
+  for (int k = 0; k < kPieces / L::kThreads; ++k) {
+    const int c = tid + k * L::kThreads, r = c / kPerRow, cg = c % kPerRow;
+    const int gm = m0 + r, gn = n0 + cg * 8;
+    if (gm >= M || gn >= N) continue;  // N % 8 == 0: a piece is wholly in or out
+    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8);
+    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8 + 4);
+    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (bias) {
+      const u32x4_t bb = ld16(bstg + cg * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] += __builtin_bit_cast(float, bb[q] << 16);
+        v[2 * q + 1] += __builtin_bit_cast(float, bb[q] & 0xffff0000u);
+      }
+    }
+    if (rope && gn < app.vcol) {
+      const float2* t = tab + r * tpitch + ((gn & (app.rope_d - 1)) >> 1);
+      const f32x4_t c01 = *reinterpret_cast<const f32x4_t*>(t), c23 = *reinterpret_cast<const f32x4_t*>(t + 2);
+      const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};  // (cos, sin) x 4
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x0 = v[2 * q], x1 = v[2 * q + 1], cq = cs[2 * q], sq = cs[2 * q + 1];
+        v[2 * q] = __builtin_fmaf(x1, -sq, x0 * cq);      // rope_turn of the even column
+        v[2 * q + 1] = __builtin_fmaf(x0, sq, x1 * cq);   // and of the odd one
+      }
+    }
+    const u32x4_t pk = u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
+                               pack_bf16(v[6], v[7])};
+    st16(out + (int64_t)gm * N + gn, pk);
+    if (app.k_cache != nullptr && gn >= app.kcol) {  // a piece never straddles the K/V boundaries
+      const int len = app.seq_lens[gm];
+      if (len >= 1 && len <= app.L_max) {
+        const bool is_k = gn < app.vcol;
+        uint16_t* cache = static_cast<uint16_t*>(is_k ? app.k_cache : app.v_cache);
+        st16(cache + ((int64_t)gm * app.L_max + (len - 1)) * (app.vcol - app.kcol) + (gn - (is_k ? app.kcol : app.vcol)),
+             pk);
       }
     }
   }
@@ -617,10 +782,10 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
 
 template <int BM, int BN, int WM, int WN, int KW, int ST>
 static hipError_t launch_gemm_tiles(const void* x, const void* w, const void* bias, void* out, int M, int K, int N,
-                                    hipStream_t s, const KvAppend& app) {
+                                    hipStream_t s, const ProjEpilogue& app) {
   using L = TileCfg<BM, BN, WM, WN, KW, ST>;
   auto kern = qkv_gemm_tiles_kernel<BM, BN, WM, WN, KW, ST>;
-  const size_t lds = L::kBytes;
+  const size_t lds = std::max(L::kBytes, TileEpi<BM, BN>::bytes(app.inv_freq != nullptr, app.rope_d, bias != nullptr));
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int nblk = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -644,7 +809,7 @@ constexpr int kSkDepth = 3;      // chunks in flight ahead of the one being mult
 __global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ out, float* __restrict__ part, int M, int K, int N, int krange, int ksplit,
-    int nbm, KvAppend app) {
+    int nbm, ProjEpilogue app) {
   __shared__ __align__(16) uint16_t Bs[2][kSkBN * kSkLd];
   __shared__ __align__(16) float red[16 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -723,11 +888,18 @@ __global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
   const int n = n0 + l32;
   if (ksplit == 1) {
     const float bv = bias ? bf16_to_f32(bias[n]) : 0.0f;
+    const bool rot = app.inv_freq != nullptr && n0 < app.vcol;  // 32 columns, one side of vcol
+    const float th = rot ? rope_freq(app, n) : 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int m = m0 + 8 * (e >> 2) + 4 * hf + (e & 3);
+      float v = acc[e] + bv;
+      if (rot) {
+        const float w = pair_partner(v);
+        if (m < M) v = rope_turn(v, w, n, rope_position(app, m), th);
+      }
       if (m < M) {
-        const uint16_t r = f32_to_bf16(acc[e] + bv);
+        const uint16_t r = f32_to_bf16(v);
         out[(int64_t)m * N + n] = r;
         append_store(app, m, n, r);
       }
@@ -758,7 +930,7 @@ constexpr int kS16BN = 16, kS16Threads = 256;
 template <int MB, int D>
 __global__ __launch_bounds__(kS16Threads, 2) void qkv_gemm_stream16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int M, int K, int N, KvAppend app) {
+    uint16_t* __restrict__ out, int M, int K, int N, ProjEpilogue app) {
   constexpr int kSlot = (1 + MB) * 512;     // bf16 elements: W rows, then x blocks
   constexpr int kAhead = (D - 1) * (1 + MB);  // loads issued after a step's own
   static_assert(kAhead <= 63, "vmcnt range");
@@ -835,8 +1007,13 @@ __global__ __launch_bounds__(kS16Threads, 2) void qkv_gemm_stream16_kernel(
 #pragma unroll
     for (int wv = 1; wv < 4; ++wv) v += red[wv * MB * 256 + idx];
     const int m = b * 16 + 4 * (ln >> 4) + e, n = n0 + (ln & 15);
+    v += bias ? bf16_to_f32(bias[n]) : 0.0f;
+    if (app.inv_freq != nullptr && n0 < app.vcol) {  // 16 columns, one side of vcol
+      const float w = pair_partner(v);                // thread tid ^ 1 holds column n ^ 1, row m
+      if (m < M) v = rope_turn(v, w, n, rope_position(app, m), rope_freq(app, n));
+    }
     if (m < M) {
-      const uint16_t r = f32_to_bf16(v + (bias ? bf16_to_f32(bias[n]) : 0.0f));
+      const uint16_t r = f32_to_bf16(v);
       out[(int64_t)m * N + n] = r;
       append_store(app, m, n, r);
     }
@@ -845,7 +1022,7 @@ __global__ __launch_bounds__(kS16Threads, 2) void qkv_gemm_stream16_kernel(
 
 template <int MB, int D>
 static hipError_t launch_stream16(const void* x, const void* w, const void* bias, void* out, int M, int K, int N,
-                                  hipStream_t s, const KvAppend& app) {
+                                  hipStream_t s, const ProjEpilogue& app) {
   auto kern = qkv_gemm_stream16_kernel<MB, D>;
   const size_t lds = (size_t)4 * D * (1 + MB) * 512 * sizeof(uint16_t);
   static_assert((size_t)4 * D * (1 + MB) * 512 * 2 >= (size_t)4 * MB * 4 * 64 * 4, "reduction fits");
@@ -864,7 +1041,7 @@ constexpr int kMaxKsplit = 16;
 __global__ __launch_bounds__(256) void qkv_gemm_reduce_kernel(const float* __restrict__ part,
                                                               const uint16_t* __restrict__ bias,
                                                               uint16_t* __restrict__ out, int M, int N,
-                                                              int ksplit, KvAppend app) {
+                                                              int ksplit, ProjEpilogue app) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // 4 consecutive outputs
   const int64_t total = (int64_t)M * N;
   if (i >= total) return;
@@ -879,11 +1056,23 @@ __global__ __launch_bounds__(256) void qkv_gemm_reduce_kernel(const float* __res
 #pragma unroll
     for (int k = 0; k < 8; ++k) s += __builtin_bit_cast(f32x4_t, v[k]);
   }
+  if (bias) {
+    s[0] += bf16_to_f32(bias[n]);
+    s[1] += bf16_to_f32(bias[n + 1]);
+    s[2] += bf16_to_f32(bias[n + 2]);
+    s[3] += bf16_to_f32(bias[n + 3]);
+  }
+  if (app.inv_freq != nullptr && n < app.vcol) {  // two whole planes
+    const int p = rope_position(app, (int)(i / N));
+    const float t0 = rope_turn(s[0], s[1], n, p, rope_freq(app, n));
+    const float t1 = rope_turn(s[1], s[0], n + 1, p, rope_freq(app, n + 1));
+    const float t2 = rope_turn(s[2], s[3], n + 2, p, rope_freq(app, n + 2));
+    const float t3 = rope_turn(s[3], s[2], n + 3, p, rope_freq(app, n + 3));
+    s = f32x4_t{t0, t1, t2, t3};
+  }
   u32x2_t pk;
-  const float b0 = bias ? bf16_to_f32(bias[n]) : 0.0f, b1 = bias ? bf16_to_f32(bias[n + 1]) : 0.0f;
-  const float b2 = bias ? bf16_to_f32(bias[n + 2]) : 0.0f, b3 = bias ? bf16_to_f32(bias[n + 3]) : 0.0f;
-  pk[0] = pack_bf16(s[0] + b0, s[1] + b1);
-  pk[1] = pack_bf16(s[2] + b2, s[3] + b3);
+  pk[0] = pack_bf16(s[0], s[1]);
+  pk[1] = pack_bf16(s[2], s[3]);
   st8(out + i, pk);
   // four consecutive columns never straddle the K/V boundaries (multiples of d)
   if (app.k_cache != nullptr && n >= app.kcol) {
@@ -899,7 +1088,7 @@ __global__ __launch_bounds__(256) void qkv_gemm_reduce_kernel(const float* __res
 
 template <int BM, int BN, int BK, int WM, int WN, int KS>
 static hipError_t launch_gemm_bf16(const void* x, const void* w, const void* bias, void* out,
-                                   int M, int K, int N, hipStream_t s, const KvAppend& app) {
+                                   int M, int K, int N, hipStream_t s, const ProjEpilogue& app) {
   using C = GemmCfg<BM, BN, BK, WM, WN, KS>;
   const size_t lds = 2 * C::kLdsTile * sizeof(uint16_t);
   auto kern = qkv_gemm_bf16_kernel<BM, BN, BK, WM, WN, KS>;
@@ -951,7 +1140,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
 
 hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void* out, int64_t M,
                            int64_t K, int64_t N, bool bf16, void* ws, size_t ws_bytes, hipStream_t s,
-                           const KvAppend& app) {
+                           const ProjEpilogue& app) {
   if (!bf16) {
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     hipLaunchKernelGGL(qkv_gemm_f32_kernel, grid, dim3(256), 0, s, (const float*)x, (const float*)w,

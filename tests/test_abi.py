@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "gqa_attn_prefill",
+    for n in ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "qkv_proj_rope", "qkv_proj_append_rope",
+              "gqa_attn_prefill",
               "gqa_attn_prefill_workspace_bytes",
               "gqa_attn_decode", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode_paged",
               "gqa_attn_prefill_varlen", "gqa_attn_prefill_fp8", "gqa_attn_prefill_fp8_workspace_bytes",
@@ -43,7 +44,7 @@ def test_status_strings(lib):
     assert L.mqkv_status_string(1) == b"invalid argument"
     assert L.mqkv_status_string(2) == b"unsupported configuration"
     assert L.mqkv_status_string(3) == b"HIP runtime error"
-    assert L.mqkv_abi_version() == 107
+    assert L.mqkv_abi_version() == 108
 
 
 def proj(lib, **kw):
@@ -108,6 +109,46 @@ def test_qkv_proj_append_rejects(lib, kw, code):
 
 def test_qkv_proj_append_empty_is_noop(lib):
     assert proj_append(lib, B=0) == 0
+
+
+def proj_rope(lib, **kw):
+    a = dict(x=A, w=A, bias=None, out=A, pos=A, th=A, M=16, hidden=256, H_q=4, H_kv=2, d=64, dtype=BF16)
+    a.update(kw)
+    return lib.lib.qkv_proj_rope(a["x"], a["w"], a["bias"], a["out"], a["pos"], a["th"], a["M"], a["hidden"],
+                                 a["H_q"], a["H_kv"], a["d"], a["dtype"], a.get("ws"), a.get("wsb", 0), None)
+
+
+def proj_append_rope(lib, **kw):
+    a = dict(x=A, w=A, bias=None, out=A, kc=A, vc=A, lens=A, th=A, B=8, hidden=256, H_q=4, H_kv=2, d=64, Lmax=64,
+             dtype=BF16)
+    a.update(kw)
+    return lib.lib.qkv_proj_append_rope(a["x"], a["w"], a["bias"], a["out"], a["kc"], a["vc"], a["lens"], a["th"],
+                                        a["B"], a["hidden"], a["H_q"], a["H_kv"], a["d"], a["Lmax"], a["dtype"],
+                                        a.get("ws"), a.get("wsb", 0), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pos=None), INV), (dict(th=None), INV), (dict(pos=A + 2), INV), (dict(th=A + 1), INV),
+    (dict(x=None), INV), (dict(M=-1), INV), (dict(hidden=260), INV), (dict(H_q=3, H_kv=2), INV),
+    (dict(d=96), UNS), (dict(dtype=7), INV), (dict(M=1 << 40), UNS),
+])
+def test_qkv_proj_rope_rejects(lib, kw, code):
+    assert proj_rope(lib, **kw) == code
+    assert lib.lib.mqkv_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(th=None), INV), (dict(th=A + 2), INV), (dict(kc=None), INV), (dict(lens=A + 2), INV),
+    (dict(B=-1), INV), (dict(Lmax=0), INV), (dict(d=96), UNS), (dict(H_q=3, H_kv=2), INV),
+])
+def test_qkv_proj_append_rope_rejects(lib, kw, code):
+    assert proj_append_rope(lib, **kw) == code
+    assert lib.lib.mqkv_last_error() != b""
+
+
+def test_rope_calls_empty_are_noops(lib):
+    assert proj_rope(lib, M=0) == 0
+    assert proj_append_rope(lib, B=0) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
