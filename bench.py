@@ -106,11 +106,24 @@ class Timer:
         self.flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
         self.flush_out = torch.empty((), dtype=torch.float32, device=dev)
 
+    def spin_up(self, fn, seconds=0.05):
+        """Run fn back to back for `seconds` first: the GPU's clock ramps up over
+        several ms of sustained load (a long-context prefill measured 610 us in
+        bursts of 10 calls from idle and 508 us in bursts of 200), so every
+        figure here is taken at the steady clock of a sustained workload."""
+        t = self.torch
+        t0 = time.perf_counter()
+        while True:
+            for _ in range(3):
+                fn()
+            t.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return
+
     def warm(self, fn, n=20):
         t = self.torch
         with t.cuda.stream(self.stream):
-            for _ in range(3):
-                fn()
+            self.spin_up(fn)
             s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
             s.record(self.stream)
             for _ in range(n):
@@ -123,8 +136,7 @@ class Timer:
         t = self.torch
         ts = []
         with t.cuda.stream(self.stream):
-            for _ in range(2):
-                fn()
+            self.spin_up(fn)
             for _ in range(n):
                 t.sum(self.flush, dim=0, out=self.flush_out)
                 s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
@@ -368,13 +380,21 @@ def measure_configs(m, W, torch, np, dev, stream, timer, up, kv8):
         wsg = torch.empty(max(wsg, 16), dtype=torch.uint8, device=dev)
         wsp = torch.empty(m.prefill_workspace_bytes(wl.B, wl.L, wl.H_kv, wl.d), dtype=torch.uint8, device=dev)
         q, k, v = m.split_qkv(qkv, wl.H_q, wl.H_kv, wl.d)
+        pos = torch.from_numpy(W.prefill_positions(wl.B, wl.L)).to(dev)
+        th = torch.from_numpy(W.rope_inv_freq(wl.d)).to(dev)
         proj = lambda: m.qkv_proj(x, w, wl.H_q, wl.H_kv, wl.d, out=qkv, workspace=wsg)
+        proj_rope = lambda: m.qkv_proj_rope(x, w, pos, th, wl.H_q, wl.H_kv, wl.d, out=qkv, workspace=wsg)
         attn = lambda: m.gqa_attn_prefill(q, k, v, causal=True, out=o, workspace=wsp)
 
         def layer():
             proj()
             attn()
+
+        def layer_rope():
+            proj_rope()
+            attn()
         us_g, us_a, us_l = timer.warm(proj), timer.warm(attn), timer.warm(layer)
+        us_gr, us_lr = timer.warm(proj_rope), timer.warm(layer_rope)
         roof_g, fl_g, by_g = gemm_roof_us(M, wl.hidden, wl.N)
         fl_a = prefill_flops(wl.B, wl.H_q, wl.d, wl.L, wl.L, True)
         res[wl.name] = {
@@ -383,9 +403,10 @@ def measure_configs(m, W, torch, np, dev, stream, timer, up, kv8):
                          "frac": round(roof_g / us_g, 4)},
             "prefill": {"us": round(us_a, 2), "tflops": round(fl_a / us_a / 1e6, 2),
                         "frac": round(fl_a / us_a / 1e6 / PEAK_BF16_TFLOPS, 4)},
-            "layer_us": round(us_l, 2), "layer_tflops": round((fl_g + fl_a) / us_l / 1e6, 2)}
+            "layer_us": round(us_l, 2), "layer_tflops": round((fl_g + fl_a) / us_l / 1e6, 2),
+            "qkv_proj_rope_us": round(us_gr, 2), "layer_rope_us": round(us_lr, 2)}
         log(json.dumps({"config": wl.name, **res[wl.name]}))
-        del x, w, qkv, o, wsg, wsp, q, k, v
+        del x, w, qkv, o, wsg, wsp, q, k, v, pos, th
 
     # -- MQA decode: the 1024-step loop (projection + KV append, decode, lengths + 1)
     res["mqa_decode"] = decode_loop(m, W, torch, np, dev, stream, up)
@@ -486,9 +507,14 @@ def decode_loop(m, W, torch, np, dev, stream, up):
     scale = 1.0 / math.sqrt(wl.d)
     q_view = qkv[:, :wl.H_q * wl.d].unflatten(-1, (wl.H_q, wl.d))
 
-    def run_all():
+    th = torch.from_numpy(W.rope_inv_freq(wl.d)).to(dev)
+
+    def run_all(rope=False):
         for s in range(steps):
-            m.qkv_proj_append(xs[s], w, kc, vc, lens, wl.H_q, wl.H_kv, wl.d, out=qkv, workspace=ws_p)
+            if rope:
+                m.qkv_proj_append_rope(xs[s], w, kc, vc, lens, th, wl.H_q, wl.H_kv, wl.d, out=qkv, workspace=ws_p)
+            else:
+                m.qkv_proj_append(xs[s], w, kc, vc, lens, wl.H_q, wl.H_kv, wl.d, out=qkv, workspace=ws_p)
             m.gqa_attn_decode(q_view, kc, vc, lens, scale=scale, workspace=ws_d, out=o)
             lens.add_(1)
 
@@ -514,6 +540,14 @@ def decode_loop(m, W, torch, np, dev, stream, up):
             run_all()
         graphed = min(timed(graph.replay) for _ in range(3))
         same = bool(torch.equal(o, out_eager))
+        # the same loop with the rotary embedding in the projection epilogue
+        graph_r = torch.cuda.CUDAGraph()
+        lens.copy_(lens0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph_r, stream=stream):
+            run_all(rope=True)
+        graphed_r = min(timed(graph_r.replay) for _ in range(3))
+        del graph_r
         # one decode call at the final length (1040 keys), warm: the cache is resident
         lens.fill_(wl.len_hi)
         dec_us = 0.0
@@ -528,7 +562,7 @@ def decode_loop(m, W, torch, np, dev, stream, up):
     w_bytes = 2.0 * wl.hidden * wl.N
     kv_last = 2.0 * wl.B * wl.len_hi * wl.H_kv * wl.d * 2
     return {"steps": steps, "eager_us_per_step": round(eager, 2), "graph_us_per_step": round(graphed, 2),
-            "graph_speedup": round(eager / graphed, 2), "bytes_per_step_mb": round((kv_bytes + w_bytes) / 1e6, 2),
+            "graph_speedup": round(eager / graphed, 2), "graph_rope_us_per_step": round(graphed_r, 2), "bytes_per_step_mb": round((kv_bytes + w_bytes) / 1e6, 2),
             "graph_gbps": round((kv_bytes + w_bytes) / graphed / 1e3, 1),
             "graph_frac_hbm": round((kv_bytes + w_bytes) / graphed / 1e3 / PEAK_HBM_GBS, 4),
             "decode_at_1040_us": round(dec_us, 2), "decode_at_1040_gbps": round(kv_last / dec_us / 1e3, 1),

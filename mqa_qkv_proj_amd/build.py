@@ -26,7 +26,7 @@ ARCH = "gfx950"
 # otherwise, and the kernels do not rely on them.
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-I", CSRC] + os.environ.get("MQKV_EXTRA_FLAGS", "").split()
+            "-I", INCLUDE, "-I", CSRC]
 
 
 # Per-source extras.  The prefill kernels never form a NaN on valid inputs

@@ -59,9 +59,6 @@ constexpr int kRows = kWaves * 32;  // query rows per workgroup
 constexpr int kBK = 64;             // keys per K/V tile: two 32-key halves
 constexpr int kStages = 3;          // K/V tiles resident in LDS
 constexpr float kTau = 8.0f;        // lazy-rescale threshold (log2 units)
-#ifndef MQKV_PF_FILL_WAVES
-#define MQKV_PF_FILL_WAVES 4
-#endif
 
 // LDS image of one K/V tile.  Rows carry 16 bytes of padding, which keeps the
 // MFMA operand reads of 16 consecutive rows on distinct banks.  LDS-DMA copies
@@ -399,7 +396,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
   // Tile copies are issued by the first kFillWaves waves only: the hardware
   // favours the older wave of the two that share a SIMD, so those waves run
   // ahead and would otherwise wait at the tile barrier.
-  constexpr int kFillWaves = MQKV_PF_FILL_WAVES < NW ? MQKV_PF_FILL_WAVES : NW;
+  constexpr int kFillWaves = 4 < NW ? 4 : NW;
   constexpr int KCP = (S::kKCopies + kFillWaves - 1) / kFillWaves;  // K copies per filling wave
   constexpr int VCP = (S::kVCopies + kFillWaves - 1) / kFillWaves;  // V copies per filling wave
   extern __shared__ __align__(16) uint16_t smem[];

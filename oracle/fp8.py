@@ -58,11 +58,16 @@ def incoherent(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
 
 
 def e4m3(x: np.ndarray) -> np.ndarray:
-    """Round to the nearest e4m3 value (ties to even), saturating at +-448."""
-    import torch
+    """Round to the nearest e4m3 value (ties to even), saturating at +-448.
+
+    e4m3: 3 mantissa bits, so in the binade [2^e, 2^(e+1)) the values are
+    multiples of 2^(e-3); below the smallest normal 2^-6 the subnormals are
+    multiples of 2^-9.  |x| is clipped to the largest finite value 448 first."""
     x = np.clip(np.asarray(x, dtype=F64), -E4M3_MAX, E4M3_MAX)
-    t = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64)
-    return t.numpy()
+    a = np.abs(x)
+    _, ex = np.frexp(a)                            # a = m * 2^ex, m in [0.5, 1): binade ex - 1
+    q = np.exp2(np.maximum(ex - 1, -6) - 3.0)      # spacing of the e4m3 values around a
+    return np.copysign(np.rint(a / q) * q, x)      # np.rint rounds halves to even
 
 
 def _quantize(x: np.ndarray, amax: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
