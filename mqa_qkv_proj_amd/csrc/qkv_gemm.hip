@@ -9,6 +9,9 @@
 // chosen by shape in launch_qkv_gemm:
 //  * M <= 32, N <= 4096, K % 128 == 0: streaming kernel on 16-column blocks
 //    (W streamed through an LDS ring filled by LDS-DMA, no k split);
+//  * M <= 128, K % 256 == 0, N % 64 == 0 (for M <= 32 only on wide weights):
+//    8-wave workgroups over all of K, each wave streaming its own share of the
+//    rows, the waves' sums added in LDS (one kernel);
 //  * M <= 128 otherwise: register-staged skinny kernel, k split over
 //    workgroups with a fixed-order reduce kernel;
 //  * M > 128, K % 64 == 0, N % 8 == 0: LDS-DMA fed tiles (128 or 64 rows, 128
@@ -1033,6 +1036,154 @@ static hipError_t launch_stream16(const void* x, const void* w, const void* bias
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------- small M, wide workgroups
+// M <= 128 (short prompts, decode batches on wide weights): one kernel, no k split
+// across workgroups.  A workgroup of NW waves owns 64 columns of W (whole
+// 128-byte lines of each row) and a 16 MB-row tile of the output over all of
+// K: wave w streams the K/NW rows [w K/NW, (w + 1) K/NW) of the strip through
+// a ring of D LDS slots of its own (32 k rows x 64 columns, 4 KB), filled by
+// LDS-DMA D steps ahead, and takes its x fragments (the MFMA A operand, 8
+// consecutive k of one row per lane) straight from memory; no barrier until
+// the end, where the NW waves' sums are added in LDS in wave order.  MFMA
+// 16x16x32.  A slot stores k rows with index bits 2 and 3 swapped (so the
+// lanes of a B-operand read pair up k rows 8g..8g+7) and the 16-byte chunks of
+// slot row r at positions XOR 2((r >> 1) & 3), which puts the 8 rows a read
+// touches on distinct banks while row r + 8 keeps row r's offsets.
+constexpr int kWdBN = 64, kWdWaves = 8;
+__device__ __forceinline__ int wd_swz(int r) { return 2 * ((r >> 1) & 3); }
+template <int NW, int MB, int D>
+__global__ __launch_bounds__(NW * 64) void qkv_gemm_wide_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, int M, int K, int N, ProjEpilogue app) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kSlot = 32 * kWdBN;     // bf16 elements per slot
+  constexpr int kLoads = 4 + MB;        // vector-memory instructions per step (4 W copies, MB x loads)
+  constexpr int kAhead = (D - 1) * kLoads;
+  static_assert(kAhead <= 63, "vmcnt range");
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nrt = (M + 16 * MB - 1) / (16 * MB);
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int rt = lid % nrt, cs = lid / nrt;  // the row tiles of one strip are neighbours: W reuse in L2
+  const int n0 = cs * kWdBN, m0 = rt * 16 * MB;
+  const int kw = K / NW;                     // k rows per wave
+  const int nst = kw >> 5;                   // 32-row steps per wave
+  const uint32_t kbeg = (uint32_t)(wq * kw);
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)K * N * 2));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+  // W copy c of a step, lane l: slot row 8c + l/8, slot chunk l%8, holding
+  // chunk (l%8) ^ swz of k row (slot row with bits 2,3 swapped)
+  uint32_t w_lane[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int sr = 8 * c + (lane >> 3);
+    const int kr = (sr & ~12) | ((sr & 4) << 1) | ((sr & 8) >> 1);
+    w_lane[c] = (uint32_t)kr * N * 2 + (uint32_t)n0 * 2 + (uint32_t)(((lane & 7) ^ wd_swz(sr)) * 16);
+  }
+  // x block b: lane l holds row m0 + 16b + l%16, k group l/16; rows past M read zeros
+  uint32_t x_lane[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int row = m0 + b * 16 + (lane & 15);
+    x_lane[b] = row < M ? (uint32_t)row * K * 2 + (lane >> 4) * 16 : 0x80000000u;
+  }
+  uint16_t* ring = smem + wq * D * kSlot;
+  u32x4_t xf[D][MB];
+  auto issue = [&](int i, int slot) {
+    const uint32_t k0 = kbeg + (uint32_t)i * 32;
+    uint16_t* sp = ring + slot * kSlot;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dma16(wr, sp + c * 512, w_lane[c] + k0 * (uint32_t)N * 2, 0);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) xf[slot][b] = bld16(xr, x_lane[b] + k0 * 2);
+  };
+  // B operand of column block cb: lane group g (k rows 8g..8g+7 of column l%16)
+  // reads slot rows 16(g>>1) + 4(g&1) + j and, 8 rows on, the second half
+  const int bg = lane >> 4, bp = lane & 15;
+  const int br = 16 * (bg >> 1) + 4 * (bg & 1) + (bp >> 2);
+  int b_off[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+    b_off[cb] = br * kWdBN + (((2 * cb + ((bp & 3) >> 1)) ^ wd_swz(br)) * 8) + 4 * (bp & 1);
+
+  f32x4_t acc[MB][4];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[b][cb] = f32x4_t{};
+
+  static_for<0, D>([&](auto j) {
+    if (j < nst) issue(j, j);
+  });
+  for (int i0 = 0; i0 < nst; i0 += D) {
+    static_for<0, D>([&](auto j) {
+      const int i = i0 + j;
+      if (i < nst) {
+        if (i + D - 1 < nst) wait_vmcnt<kAhead>();
+        else wait_vmcnt<0>();
+        const uint16_t* sp = ring + j * kSlot;
+        u32x4_t bf[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) bf[cb] = lds_tr16_pair<8 * kWdBN * 2>(sp + b_off[cb]);
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc[b][cb] = mfma16_bf16(xf[j][b], bf[cb], acc[b][cb]);
+        if (i + D < nst) issue(i + D, j);
+      }
+    });
+  }
+  wait_vmcnt<0>();
+
+  // the NW waves' sums, added in wave order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr int kPer = MB * 4 * 4 * 64;  // floats per wave
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wq * kPer + ((b * 4 + cb) * 4 + e) * 64 + lane] = acc[b][cb][e];
+  __syncthreads();
+  static_assert(kPer % kThreads == 0, "outputs per thread");
+#pragma unroll
+  for (int q = 0; q < kPer / kThreads; ++q) {
+    const int idx = q * kThreads + tid;  // (b, cb, e, lane), lane fastest
+    const int ln = idx & 63, e = (idx >> 6) & 3, cb = (idx >> 8) & 3, b = idx >> 10;
+    float v = red[idx];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) v += red[wv * kPer + idx];
+    const int m = m0 + b * 16 + 4 * (ln >> 4) + e, n = n0 + cb * 16 + (ln & 15);
+    v += bias ? bf16_to_f32(bias[n]) : 0.0f;
+    if (app.inv_freq != nullptr && n0 + cb * 16 < app.vcol) {  // 16 columns, one side of vcol
+      const float pw = pair_partner(v);                        // thread tid ^ 1 holds column n ^ 1, row m
+      if (m < M) v = rope_turn(v, pw, n, rope_position(app, m), rope_freq(app, n));
+    }
+    if (m < M) {
+      const uint16_t r = f32_to_bf16(v);
+      out[(int64_t)m * N + n] = r;
+      append_store(app, m, n, r);
+    }
+  }
+}
+
+template <int NW, int MB, int D>
+static hipError_t launch_wide(const void* x, const void* w, const void* bias, void* out, int M, int K, int N,
+                              hipStream_t s, const ProjEpilogue& app) {
+  auto kern = qkv_gemm_wide_kernel<NW, MB, D>;
+  const size_t lds = (size_t)NW * D * 32 * kWdBN * sizeof(uint16_t);
+  static_assert((size_t)D * 32 * kWdBN * 2 >= (size_t)MB * 4 * 4 * 64 * 4, "reduction fits");
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int nblk = (N / kWdBN) * ((M + 16 * MB - 1) / (16 * MB));
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(NW * 64), lds, s, (const uint16_t*)x, (const uint16_t*)w,
+                     (const uint16_t*)bias, (uint16_t*)out, M, K, N, app);
+  return hipGetLastError();
+}
+
 // Sum the k-range partials in a fixed order, add the bias, round to bf16.  The
 // loads of 8 k ranges are issued together (branch-free: buffer loads past the
 // end return zeros), so the kernel waits for one memory round trip per 8
@@ -1117,6 +1268,24 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
     p.ok = true;
     return p;
   }
+  // Wide workgroups (8 waves over all of K, no partials).  Measured against
+  // the k-split skinny kernel + reduce: better at every M > 32 (TinyLlama
+  // width, M = 128: 14.7 -> 8.4 us warm, 20.2 -> 16.6 us cold); 16-row tiles
+  // while the grid stays within 256 workgroups (M = 64: 10.9 -> 6.3 us warm),
+  // 32-row tiles otherwise (a tile re-reads the whole strip of W).  At M <= 32
+  // only with at least 192 strips (N = 12288: 38.2 -> 32.5 us cold); narrower
+  // weights stream better split over k.
+  if (K % (kWdWaves * 32) == 0 && N % kWdBN == 0) {
+    const int64_t strips = N / kWdBN;
+    if (M > 32 || strips * ((M + 31) / 32) >= 192) {
+      p.wide = true;
+      p.wide_mb = (M > 32 && M <= 64 && strips * ((M + 15) / 16) <= 256) ? 1 : 2;
+      p.krange = (int)K;
+      p.ksplit = 1;
+      p.ok = true;
+      return p;
+    }
+  }
   if (N % kSkBN != 0) return SkinnyPlan{};
   const int64_t base = (N / kSkBN) * p.nbm;
   // about three workgroups per CU; each k range a multiple of the 128-deep chunk
@@ -1152,6 +1321,9 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
   if (p.ok && p.stream16)
     return M > 16 ? launch_stream16<2, 6>(x, w, bias, out, m, k, n, s, app)
                   : launch_stream16<1, 8>(x, w, bias, out, m, k, n, s, app);
+  if (p.ok && p.wide)
+    return p.wide_mb == 1 ? launch_wide<kWdWaves, 1, 2>(x, w, bias, out, m, k, n, s, app)
+                          : launch_wide<kWdWaves, 2, 2>(x, w, bias, out, m, k, n, s, app);
   if (p.ok && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
     const int64_t nblk = (N / kSkBN) * p.nbm * p.ksplit;
     hipLaunchKernelGGL(qkv_gemm_skinny_kernel, dim3((unsigned)nblk), dim3(kSkThreads), 0, s,

@@ -42,6 +42,7 @@ APPEND = [
     (24, 256, 4, 2, 64, 33, "bf16"),      # streaming kernel, two 16-row blocks
     (32, 1024, 32, 8, 128, 50, "bf16"),   # skinny, k split + reduce kernel
     (100, 128, 8, 2, 64, 20, "bf16"),     # skinny, one k range
+    (48, 512, 8, 2, 64, 20, "bf16"),      # 8-wave workgroups over all of K
     (300, 256, 8, 2, 64, 9, "bf16"),      # LDS-DMA tiles
     (200, 264, 4, 2, 64, 17, "bf16"),     # register-prefetched tiles (hidden % 64 != 0)
     (20, 128, 4, 2, 64, 12, "f32"),       # fp32 path

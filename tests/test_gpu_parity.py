@@ -38,6 +38,10 @@ PROJ = [  # M, hidden, H_q, H_kv, d, dtype
     (128, 512, 4, 2, 64, "bf16"), (100, 1024, 8, 1, 128, "bf16"), (8, 256, 64, 2, 128, "bf16"),
     (24, 384, 4, 2, 64, "bf16"), (32, 128, 12, 2, 128, "bf16"),
     (128, 256, 4, 2, 64, "f32"), (45, 100, 2, 1, 128, "f32"),
+    # 8-wave workgroups over all of K (hidden % 256 == 0): 16-row tiles (M <= 64, small
+    # grids), 32-row tiles, and M <= 32 on a 12288-column weight; ragged row tiles
+    (33, 512, 4, 2, 64, "bf16"), (97, 2048, 8, 2, 128, "bf16"), (64, 1024, 16, 2, 128, "bf16"),
+    (20, 512, 32, 32, 128, "bf16"),
 ]
 
 
