@@ -381,8 +381,8 @@ __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // map with `signs`), K arrives as per-tile e4m3 LDS images k8img with the tile
 // scale in row 0's padding, and the scores run on the fp8 MFMA 32x32x64; P and
 // V are as in the bf16 path.
-template <int D, bool CAUSAL, bool OUT_BF16, bool F8 = false, int NW = kWaves>
-__global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
+template <int D, bool CAUSAL, bool OUT_BF16, bool F8 = false, int NW = kWaves, int KP = 1>
+__global__ __launch_bounds__(NW * 64, KP == 1 ? 2 : 1) void attn_prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vimg,
     void* __restrict__ o, float* __restrict__ lse, int Lq_max, int Lkv_max, int Hq, int Hkv,
     int64_t q_stride, int64_t kv_stride, float c, int F, int n_hg, int n_qb, int ntiles,
@@ -393,6 +393,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
   constexpr int KS8 = D / 64;  // fp8 MFMA k-steps (64 bytes each)
   constexpr int KF = F8 ? 2 * KS8 : DS;  // 16-byte operand fragments per row of a half
   constexpr int DB = D / 32;  // 32-row blocks of O^T
+  // KP key parities: the waves form NW/KP groups of 32 query rows, and the
+  // wave of parity kp in a group takes the key tiles kp, kp + KP, ... of those
+  // rows; the KP partial results of a row are merged at the end (exact
+  // rescaling).  An LDS stage then holds KP consecutive tiles.
+  constexpr int RG = NW / KP;  // 32-row groups per workgroup
+  static_assert(NW % KP == 0 && (KP == 1 || !F8), "key parities");
+  constexpr int kStageP = KP * PrefillLds<D, F8>::kStage;  // LDS stage: KP tiles
   // Tile copies are issued by the first kFillWaves waves only: the hardware
   // favours the older wave of the two that share a SIMD, so those waves run
   // ahead and would otherwise wait at the tile barrier.
@@ -404,10 +411,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int wq = __builtin_amdgcn_readfirstlane(wave);
+  const int kp = wq / RG;  // this wave's key parity
 
   // ---- block -> (b, g, head group, query block), heaviest causal blocks first
   const int G = Hq / Hkv;
-  const int P = NW * 32 / F;  // positions per workgroup
+  const int P = RG * 32 / F;  // positions per workgroup
   int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int qb = n_qb - 1 - (lid % n_qb);
   lid /= n_qb;
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
   const int off = Lkv - Lq;
 
   // ---- this lane's query row (column of the S^T tile)
-  const int r = wave * 32 + l32;
+  const int r = (wave % RG) * 32 + l32;
   const int h = g * G + hg * F + r / P;
   const int pos = p0 + r % P;
   const bool valid = pos < Lq;
@@ -463,37 +471,46 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
                  : ch < D / 8 ? (uint32_t)row * row_bytes + (uint32_t)(g * D * 2) + ch * 16 : kNoCopy;
   }
   const uint8_t* k8base = F8 ? k8img + ((int64_t)b * Hkv + g) * ntiles * (S::kK * 2) : nullptr;
-  // A tile copy is split into numbered parts (K copies, then V copies) so that
-  // the pipelined steps can issue them one at a time between MFMAs.
-  constexpr int kParts = KCP + VCP;
-  __amdgpu_buffer_rsrc_t krs, vrs;
-  uint16_t* ks_dst = smem;
-  uint16_t* vs_dst = smem;
-  bool fill_on = false;
-  auto fill_begin = [&](int t, int st) {
-    fill_on = wq < kFillWaves && t < nt;
-    ks_dst = smem + st * S::kStage;
-    vs_dst = ks_dst + S::kK;
-    if constexpr (F8) {
-      krs = make_rsrc(k8base + (int64_t)t * (S::kK * 2), S::kK * 2);
-    } else {
-      const uint32_t k0b = (uint32_t)(t * kBK) * row_bytes;
-      krs = make_rsrc(kbase + k0b, kv_bytes - k0b);
+  // The copy of a stage (tiles u KP .. u KP + KP - 1) is split into numbered
+  // parts (per tile: K copies, then V copies) so that the pipelined steps can
+  // issue them one at a time between MFMAs.
+  constexpr int kTileParts = KCP + VCP;
+  constexpr int kParts = KP * kTileParts;
+  __amdgpu_buffer_rsrc_t krs[KP], vrs[KP];
+  uint16_t* ks_dst[KP];
+  uint16_t* vs_dst[KP];
+  bool fill_on[KP];
+  auto fill_begin = [&](int u, int st) {
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      const int t = u * KP + j;
+      fill_on[j] = wq < kFillWaves && t < nt;
+      ks_dst[j] = smem + st * kStageP + j * S::kStage;
+      vs_dst[j] = ks_dst[j] + S::kK;
+      const int tc = t < nt ? t : 0;  // descriptors of a tile that is not copied are never used
+      if constexpr (F8) {
+        krs[j] = make_rsrc(k8base + (int64_t)tc * (S::kK * 2), S::kK * 2);
+      } else {
+        const uint32_t k0b = (uint32_t)(tc * kBK) * row_bytes;
+        krs[j] = make_rsrc(kbase + k0b, kv_bytes - k0b);
+      }
+      vrs[j] = make_rsrc(vbase + (int64_t)tc * S::kV, S::kV * 2);
     }
-    vrs = make_rsrc(vbase + (int64_t)t * S::kV, S::kV * 2);
   };
   auto fill_part = [&](auto part) {
-    constexpr int i = part;
-    if constexpr (i < KCP) {
-      const int cp = wq + i * kFillWaves;
-      if (fill_on && cp < S::kKCopies) dma16(krs, ks_dst + cp * 512, koff[i], F8 ? cp * 1024 : 0);
-    } else if constexpr (i < kParts) {
-      const int cp = wq + (i - KCP) * kFillWaves;
-      if (fill_on && cp < S::kVCopies) dma16(vrs, vs_dst + cp * 512, (uint32_t)lane * 16, cp * 1024);
+    constexpr int j = part / kTileParts, i = part % kTileParts;
+    if constexpr (j < KP) {
+      if constexpr (i < KCP) {
+        const int cp = wq + i * kFillWaves;
+        if (fill_on[j] && cp < S::kKCopies) dma16(krs[j], ks_dst[j] + cp * 512, koff[i], F8 ? cp * 1024 : 0);
+      } else {
+        const int cp = wq + (i - KCP) * kFillWaves;
+        if (fill_on[j] && cp < S::kVCopies) dma16(vrs[j], vs_dst[j] + cp * 512, (uint32_t)lane * 16, cp * 1024);
+      }
     }
   };
-  auto fill = [&](int t, int st) {
-    fill_begin(t, st);
+  auto fill = [&](int u, int st) {
+    fill_begin(u, st);
     static_for<0, kParts>([&](auto i) { fill_part(i); });
   };
 
@@ -503,8 +520,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
   float m_run = -INFINITY;  // running max of S*c (log2 units)
   float l_run = 0.0f;       // this lane's share of the running sum
 
-  auto k_of = [&](int st) -> const uint16_t* { return smem + st * S::kStage; };
-  auto v_of = [&](int st) -> const uint16_t* { return smem + st * S::kStage + S::kK; };
+  // this wave's tile in stage st
+  auto k_of = [&](int st) -> const uint16_t* { return smem + st * kStageP + kp * S::kStage; };
+  auto v_of = [&](int st) -> const uint16_t* { return smem + st * kStageP + kp * S::kStage + S::kK; };
   // The V tile in stage st is V * 2^-s with its exponent s in row 0's padding
   // (0 unless the tile lies outside fp16's range).  acc holds O * l * 2^-sig;
   // before a tile's P.V it is brought to that tile's exponent by an exact
@@ -745,9 +763,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
 
   // Three LDS stages: while tile t is consumed, tile t + 1 is complete in LDS
   // (its first scores are computed under tile t's second half) and tile t + 2
-  // is being copied in.  One barrier per tile publishes the copy.
+  // is being copied in.  One barrier per tile publishes the copy.  With KP key
+  // parities the stages hold KP tiles each and this wave's tiles are
+  // kp, kp + KP, ...; every wave passes the same nu barriers.
+  const int nu = (nt + KP - 1) / KP;
   fill(0, 0);
-  if (nt > 1) fill(1, 1);
+  if (nu > 1) fill(1, 1);
   wait_dma();
   __syncthreads();
 
@@ -755,28 +776,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
   // one 32-key half is computed while the scores of the next half and the
   // P.V products of this half are in the matrix cores.
   const int t_mask = min(nt, mask_from / kBK);
-  int t = 0, st0 = 0;
+  const int tm = t_mask > kp ? (t_mask - kp + KP - 1) / KP : 0;  // this wave's unmasked tiles
+  const int ntw = nt > kp ? (nt - kp + KP - 1) / KP : 0;         // all of this wave's tiles
+  int u = 0, st0 = 0;
   f32x16_t sc = f32x16_t{};
   u32x4_t pf[2];
   u32x4_t kf[KF];
   u32x4_t pl = u32x4_t{0, 0, 0, 0};  // the step's carried P of keys 0..15 of the current half
   float ml = -INFINITY;
-  int sv_cur = v_exp_of(0);  // V exponent of tile t (read one tile ahead)
-  if (t_mask > 0) {
+  int sv_cur = v_exp_of(0);  // V exponent of this wave's current tile (read one tile ahead)
+  if (tm > 0) {
     cc = tile_c(0);
     sc = qk(k_of(0), 0);
     update_max(sc);
     if constexpr (!F8 && D == 128) first_p(sc, pl, ml);
     load_kf(kf, k_of(0), 1);
   }
-  for (; t + 1 < t_mask; ++t) {
+  for (; u + 1 < tm; ++u) {
     const int st1 = st0 == 2 ? 0 : st0 + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
-    fill_begin(t + 2, st2);
+    fill_begin(u + 2, st2);
     cc = tile_c(st0);
     v_rescale(sv_cur);
-    sv_cur = v_exp_of(st1);  // tile t + 1 is complete in LDS
-    // the second step computes the scores of tile t + 1 (stage st1), under that tile's scale
+    sv_cur = v_exp_of(st1);  // this wave's next tile is complete in LDS
+    // the second step computes the scores of the next tile (stage st1), under that tile's scale
     step(sc, pl, ml, kf, v_of(st0), 0, k_of(st1), 0, cc, std::true_type{}, std::integral_constant<int, 0>{});
     step(sc, pl, ml, kf, v_of(st0), 1, k_of(st1), 1, tile_c(st1), std::true_type{},
          std::integral_constant<int, 2 * DB>{});
@@ -785,10 +808,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
     __syncthreads();
     st0 = st1;
   }
-  if (t < t_mask) {  // last unmasked tile: the pipeline drains
+  if (u < tm) {  // last unmasked tile: the pipeline drains
     const int st1 = st0 == 2 ? 0 : st0 + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
-    if (t + 2 < nt) fill(t + 2, st2);
+    if (u + 2 < nu) fill(u + 2, st2);
     cc = tile_c(st0);
     v_rescale(sv_cur);
     step(sc, pl, ml, kf, v_of(st0), 0, k_of(st1), 0, cc, std::false_type{}, std::integral_constant<int, -1>{});
@@ -797,16 +820,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
     wait_dma();
     __syncthreads();
     st0 = st1;
-    ++t;
+    ++u;
   }
   // Tiles that cross some row's limit (at most a few per workgroup): masked,
   // one half after the other.
-  for (; t < nt; ++t) {
+  for (; u < ntw; ++u) {
     const int st1 = st0 == 2 ? 0 : st0 + 1;
     const int st2 = st1 == 2 ? 0 : st1 + 1;
-    if (t + 2 < nt) fill(t + 2, st2);
+    if (u + 2 < nu) fill(u + 2, st2);
     cc = tile_c(st0);
     v_rescale(v_exp_of(st0));
+    const int t = u * KP + kp;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       sc = qk(k_of(st0), j);
@@ -818,6 +842,51 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_prefill_bf16_kernel(
     wait_dma();
     __syncthreads();
     st0 = st1;
+  }
+  // no tile of this wave left: keep the barrier cadence and the copies
+  for (; u < nu; ++u) {
+    const int st1 = st0 == 2 ? 0 : st0 + 1;
+    const int st2 = st1 == 2 ? 0 : st1 + 1;
+    if (u + 2 < nu) fill(u + 2, st2);
+    wait_dma();
+    __syncthreads();
+    st0 = st1;
+  }
+
+  if constexpr (KP > 1) {
+    // Merge the key parities of each row (the stages are free now): the wave
+    // of parity 1 leaves its running max, sum, V exponent and accumulators in
+    // LDS; the wave of parity 0 brings both to the larger max and exponent.
+    static_assert(KP == 2, "two key parities");
+    constexpr int kRec = DB * 16 + 3;  // floats per lane
+    float* xr = reinterpret_cast<float*>(smem) + (wave % RG) * kRec * 64 + lane;
+    if (kp == 1) {
+      xr[0] = m_run;
+      xr[64] = l_run;
+      xr[128] = __int_as_float(sig);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xr[(3 + db * 16 + e) * 64] = acc[db][e];
+    }
+    __syncthreads();
+    if (kp == 1) return;
+    const float m1 = xr[0], l1 = xr[64];
+    const int s1 = __float_as_int(xr[128]);
+    const float M = fmaxf(m_run, m1);
+    // a side that has seen no key (max -inf) weighs 0, also when both have not
+    const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+    const int Sx = max(sig, s1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        acc[db][e] = __builtin_amdgcn_ldexpf(acc[db][e] * a0, sig - Sx) +
+                     __builtin_amdgcn_ldexpf(xr[(3 + db * 16 + e) * 64] * a1, s1 - Sx);
+    l_run = l_run * a0 + l1 * a1;
+    m_run = M;
+    sig = Sx;
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
@@ -936,13 +1005,20 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   // the longest key range.  Each row's arithmetic is the same either way.
   // Measured on the TinyLlama-shaped prefills (L = 2048 / 512 / 128): 8-11%
   // faster per call.
-  int nw = kWaves;
+  int nw = kWaves, kp = 1;
   if (D == 64) {
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (nblk < 2 * (int64_t)cus) nw = 4;
+    // Fewer 128-row blocks than CUs: 8 waves per block, each row group's key
+    // tiles split between two waves (even / odd tiles, merged at the end), so
+    // the longest block finishes in half the steps on a CU that would
+    // otherwise run it alone.  With more blocks than CUs the CUs are full
+    // anyway and the merge and doubled copies only cost (measured: L = 512 and
+    // 128 prefills 7% and 5% faster, L = 2048 7.5% slower with the split).
+    if (nw == 4 && grid(4, n_qb) <= cus) kp = 2;
   }
   if (nw != kWaves) nblk = grid(nw, n_qb);
   const int64_t nimg = (int64_t)a.B * a.Hkv * ntiles;
@@ -952,15 +1028,24 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefill_v_image_kernel<D>, dim3((unsigned)nimg), dim3((kBK / 4) * (D / 8)), 0, s,
                      (const uint16_t*)a.v, img, a.Lkv, a.Hkv, a.kv_stride, ntiles, a.cu_kv, a.total_kv);
   auto kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, kWaves>;
-  if constexpr (D == 64)
-    if (nw == 4) kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, 4>;
-  const size_t lds = PrefillLds<D>::kBytes;
+  size_t lds = PrefillLds<D>::kBytes;
+  int threads = kWaves * 64;
+  if constexpr (D == 64) {
+    if (nw == 4 && kp == 2) {  // 128 rows per workgroup: 4 row groups x 2 key parities
+      kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, 8, 2>;
+      lds = 2 * PrefillLds<D>::kBytes;
+      threads = 8 * 64;
+    } else if (nw == 4) {
+      kern = attn_prefill_bf16_kernel<D, CAUSAL, OUT_BF16, false, 4>;
+      threads = 4 * 64;
+    }
+  }
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   // scale 0 is run as a tiny positive scale: masked scores stay -inf after the
   // multiply and every visible score maps to exp2(0) = 1 exactly.
   const float c = fmaxf(a.scale * kLog2e, 1e-30f);
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(nw * 64), lds, s, (const uint16_t*)a.q,
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(threads), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, img, a.o, a.lse, a.Lq, a.Lkv, a.Hq, a.Hkv,
                      a.q_stride, a.kv_stride, c, F, n_hg, n_qb, ntiles, a.cu_q, a.cu_kv, a.total_q, a.total_kv,
                      nullptr, nullptr);

@@ -1,5 +1,5 @@
 """Prefill over a packed batch of variable-length sequences: parity with the
-oracle, bit-identity with one gqa_attn_prefill call per sequence, the LSE
+oracle, agreement with one gqa_attn_prefill call per sequence, the LSE
 layout, and the blind rows (no key visible) giving O = 0, LSE = -inf."""
 import math
 
@@ -54,14 +54,17 @@ def test_varlen_matches_oracle_and_per_sequence_calls(m, H_q, H_kv, d, causal, l
     assert_close(host(o), ref, "bf16", "varlen O (fp32 out)")
     # LSE bar as for the fixed-length call: the row sums come from fp16-rounded P
     assert_close(host(lse), ref_lse, "bf16", "varlen LSE", max_abs=1e-3, rel_l2=1e-4)
-    # one fixed-length call per sequence gives the same bits
+    # one fixed-length call per sequence: the same result.  The packed grid and
+    # a lone short sequence may pick different workgroup shapes (a small d=64
+    # grid splits each row block's keys between two waves), which sum in a
+    # different order, so the comparison is at the oracle's bar.
     for b in range(len(lq)):
         if lq[b] == 0:
             continue
         ob, lb = m.gqa_attn_prefill(qd[None, cq[b]:cq[b + 1]], kd[None, ck[b]:ck[b + 1]], vd[None, ck[b]:ck[b + 1]],
                                     causal=causal, scale=scale, return_lse=True, out_dtype=torch.float32)
-        assert torch.equal(o[cq[b]:cq[b + 1]], ob[0]), f"sequence {b}: O differs from its own call"
-        assert torch.equal(lse[:, cq[b]:cq[b + 1]], lb[0]), f"sequence {b}: LSE differs from its own call"
+        assert_close(host(ob[0]), host(o[cq[b]:cq[b + 1]]), "bf16", f"sequence {b}: its own call vs the batch")
+        assert np.abs(host(lb[0]) - host(lse[:, cq[b]:cq[b + 1]])).max() < 1e-3, f"sequence {b}: LSE"
 
 
 def test_varlen_blind_rows_and_empty_sequences(m):
