@@ -554,16 +554,20 @@ struct RopeTable {
       pos[k] = (k < rows && m < M) ? rope_position(app, m) : 0;
     }
   }
-  __device__ __forceinline__ void fill(const ProjEpilogue& app, float2* tab, int pitch, int tid) const {
+  // the rows [r0, r0 + nr) of the table, at tab[(row - r0) * pitch + plane]
+  __device__ __forceinline__ void fill(const ProjEpilogue& app, float2* tab, int pitch, int tid, int r0,
+                                       int nr) const {
     const int P = app.rope_d >> 1, groups = P >> 2, rows = BM * groups / THREADS;
     const int g = tid % groups, q = tid / groups;
 #pragma unroll
     for (int k = 0; k < kMaxRows; ++k) {
       if (k >= rows) break;
+      const int row = q + k * (THREADS / groups);
+      if (row < r0 || row >= r0 + nr) continue;
       float2 cs[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) rope_sincos((float)pos[k] * th[c], cs[c].y, cs[c].x);
-      float2* dst = tab + (q + k * (THREADS / groups)) * pitch + 4 * g;
+      float2* dst = tab + (row - r0) * pitch + 4 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) dst[c] = cs[c];
     }
@@ -573,14 +577,27 @@ struct RopeTable {
 // LDS of the tile epilogue: fp32 staging rows of BN + 8 floats (rows 4 apart
 // fall 32 banks apart), then the rotation table (BM rows of d/2 + 2 float2),
 // then the bias of the tile's columns (BN bf16).
-template <int BM, int BN>
+// The epilogue runs in PASSES passes of BM / PASSES rows when the whole
+// tile would need more LDS than the copy ring: a configuration that runs two
+// workgroups per CU keeps its LDS within half a CU's.
+template <int BM, int BN, int PASSES = 1>
 struct TileEpi {
+  static constexpr int kRows = BM / PASSES;  // rows staged per pass
   static constexpr int kPitch = BN + 8;
-  static constexpr size_t kStageBytes = (size_t)BM * kPitch * 4;
+  static constexpr size_t kStageBytes = (size_t)kRows * kPitch * 4;
+  __host__ __device__ static size_t table_bytes(bool rope, int d) { return rope ? (size_t)kRows * (d / 2 + 2) * 8 : 0; }
   static size_t bytes(bool rope, int d, bool bias) {
-    return kStageBytes + (rope ? (size_t)BM * (d / 2 + 2) * 8 : 0) + (bias ? (size_t)BN * 2 : 0);
+    return kStageBytes + table_bytes(rope, d) + (bias ? (size_t)BN * 2 : 0);
   }
+  static constexpr size_t kWorstBytes = kStageBytes + (size_t)kRows * 66 * 8 + (size_t)BN * 2;  // d = 128, bias
+  static_assert(BM % (32 * PASSES) == 0, "passes of whole 32-row blocks");
 };
+// Passes of a tile configuration: two where the ring leaves room for a second
+// workgroup on the CU (at most 80 KB) but the one-pass epilogue would not.
+template <int BM, int BN, size_t RING>
+constexpr int tile_epi_passes() {
+  return (RING <= 80 * 1024 && TileEpi<BM, BN, 1>::kWorstBytes > RING) ? 2 : 1;
+}
 
 template <int BM, int BN, int WM, int WN, int KW, int ST>
 __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
@@ -710,74 +727,83 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
   // Every thread then takes 8-column row pieces: bias, rotation, rounding to
   // bf16, one 16-byte store (and the cache append).  A piece holds 4 whole
   // planes of one head, so the rotation needs nothing from other threads.
-  using E = TileEpi<BM, BN>;
+  constexpr int kPasses = tile_epi_passes<BM, BN, L::kBytes>();
+  using E = TileEpi<BM, BN, kPasses>;
   float* stg = reinterpret_cast<float*>(smem);
   float2* tab = reinterpret_cast<float2*>(reinterpret_cast<char*>(smem) + E::kStageBytes);
   const int tpitch = (app.rope_d >> 1) + 2;  // float2 per table row: 16-byte aligned rows
   uint16_t* bstg = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(smem) + E::kStageBytes +
-                                               (rope ? (size_t)BM * tpitch * 8 : 0));
-  auto stage = [&](bool add) {
+                                               E::table_bytes(rope, app.rope_d));
+  // this wave's sums of the rows [r0, r0 + E::kRows) (whole 32-row blocks)
+  auto stage = [&](bool add, int r0) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int rb = wm * (32 * MI) + i * 32 - r0;
+      if (rb < 0 || rb >= E::kRows) continue;
 #pragma unroll
       for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float& d = stg[(wm * (32 * MI) + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4)) * E::kPitch + wn * (32 * NI) +
-                         j * 32 + l32];
+          float& d = stg[(rb + 8 * (e / 4) + 4 * hf + (e % 4)) * E::kPitch + wn * (32 * NI) + j * 32 + l32];
           d = add ? d + acc[i][j][e] : acc[i][j][e];
         }
+    }
   };
-  __syncthreads();  // every wave is done with the stages
-  if (kg == 0) stage(false);
-  if (rope) rtab.fill(app, tab, tpitch, tid);
-  if (bias && tid < BN / 8 && n0 + tid * 8 < N) st16(bstg + tid * 8, ld16(bias + n0 + tid * 8));
-#pragma unroll
-  for (int g = 1; g < KW; ++g) {
-    __syncthreads();
-    if (kg == g) stage(true);
-  }
-  __syncthreads();
-
-  constexpr int kPieces = BM * BN / 8, kPerRow = BN / 8;
+  constexpr int kPieces = E::kRows * BN / 8, kPerRow = BN / 8;
   static_assert(kPieces % L::kThreads == 0, "pieces per thread");
 #pragma unroll
-  for (int k = 0; k < kPieces / L::kThreads; ++k) {
-    const int c = tid + k * L::kThreads, r = c / kPerRow, cg = c % kPerRow;
-    const int gm = m0 + r, gn = n0 + cg * 8;
-    if (gm >= M || gn >= N) continue;  // N % 8 == 0: a piece is wholly in or out
-    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8);
-    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8 + 4);
-    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    if (bias) {
-      const u32x4_t bb = ld16(bstg + cg * 8);
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int r0 = ps * E::kRows;
+    __syncthreads();  // every wave is done with the stages, or with the previous pass's rows
+    if (kg == 0) stage(false, r0);
+    if (rope) rtab.fill(app, tab, tpitch, tid, r0, E::kRows);
+    if (ps == 0 && bias && tid < BN / 8 && n0 + tid * 8 < N) st16(bstg + tid * 8, ld16(bias + n0 + tid * 8));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] += __builtin_bit_cast(float, bb[q] << 16);
-        v[2 * q + 1] += __builtin_bit_cast(float, bb[q] & 0xffff0000u);
-      }
+    for (int g = 1; g < KW; ++g) {
+      __syncthreads();
+      if (kg == g) stage(true, r0);
     }
-    if (rope && gn < app.vcol) {
-      const float2* t = tab + r * tpitch + ((gn & (app.rope_d - 1)) >> 1);
-      const f32x4_t c01 = *reinterpret_cast<const f32x4_t*>(t), c23 = *reinterpret_cast<const f32x4_t*>(t + 2);
-      const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};  // (cos, sin) x 4
+    __syncthreads();
+
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float x0 = v[2 * q], x1 = v[2 * q + 1], cq = cs[2 * q], sq = cs[2 * q + 1];
-        v[2 * q] = __builtin_fmaf(x1, -sq, x0 * cq);      // rope_turn of the even column
-        v[2 * q + 1] = __builtin_fmaf(x0, sq, x1 * cq);   // and of the odd one
+    for (int k = 0; k < kPieces / L::kThreads; ++k) {
+      const int c = tid + k * L::kThreads, r = c / kPerRow, cg = c % kPerRow;
+      const int gm = m0 + r0 + r, gn = n0 + cg * 8;
+      if (gm >= M || gn >= N) continue;  // N % 8 == 0: a piece is wholly in or out
+      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8);
+      const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8 + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (bias) {
+        const u32x4_t bb = ld16(bstg + cg * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[2 * q] += __builtin_bit_cast(float, bb[q] << 16);
+          v[2 * q + 1] += __builtin_bit_cast(float, bb[q] & 0xffff0000u);
+        }
       }
-    }
-    const u32x4_t pk = u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
-                               pack_bf16(v[6], v[7])};
-    st16(out + (int64_t)gm * N + gn, pk);
-    if (app.k_cache != nullptr && gn >= app.kcol) {  // a piece never straddles the K/V boundaries
-      const int len = app.seq_lens[gm];
-      if (len >= 1 && len <= app.L_max) {
-        const bool is_k = gn < app.vcol;
-        uint16_t* cache = static_cast<uint16_t*>(is_k ? app.k_cache : app.v_cache);
-        st16(cache + ((int64_t)gm * app.L_max + (len - 1)) * (app.vcol - app.kcol) + (gn - (is_k ? app.kcol : app.vcol)),
-             pk);
+      if (rope && gn < app.vcol) {
+        const float2* t = tab + r * tpitch + ((gn & (app.rope_d - 1)) >> 1);
+        const f32x4_t c01 = *reinterpret_cast<const f32x4_t*>(t), c23 = *reinterpret_cast<const f32x4_t*>(t + 2);
+        const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};  // (cos, sin) x 4
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = v[2 * q], x1 = v[2 * q + 1], cq = cs[2 * q], sq = cs[2 * q + 1];
+          v[2 * q] = __builtin_fmaf(x1, -sq, x0 * cq);      // rope_turn of the even column
+          v[2 * q + 1] = __builtin_fmaf(x0, sq, x1 * cq);   // and of the odd one
+        }
+      }
+      const u32x4_t pk = u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
+                                 pack_bf16(v[6], v[7])};
+      st16(out + (int64_t)gm * N + gn, pk);
+      if (app.k_cache != nullptr && gn >= app.kcol) {  // a piece never straddles the K/V boundaries
+        const int len = app.seq_lens[gm];
+        if (len >= 1 && len <= app.L_max) {
+          const bool is_k = gn < app.vcol;
+          uint16_t* cache = static_cast<uint16_t*>(is_k ? app.k_cache : app.v_cache);
+          st16(cache + ((int64_t)gm * app.L_max + (len - 1)) * (app.vcol - app.kcol) +
+                   (gn - (is_k ? app.kcol : app.vcol)),
+               pk);
+        }
       }
     }
   }
@@ -788,7 +814,8 @@ static hipError_t launch_gemm_tiles(const void* x, const void* w, const void* bi
                                     hipStream_t s, const ProjEpilogue& app) {
   using L = TileCfg<BM, BN, WM, WN, KW, ST>;
   auto kern = qkv_gemm_tiles_kernel<BM, BN, WM, WN, KW, ST>;
-  const size_t lds = std::max(L::kBytes, TileEpi<BM, BN>::bytes(app.inv_freq != nullptr, app.rope_d, bias != nullptr));
+  using E = TileEpi<BM, BN, tile_epi_passes<BM, BN, L::kBytes>()>;
+  const size_t lds = std::max(L::kBytes, E::bytes(app.inv_freq != nullptr, app.rope_d, bias != nullptr));
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int nblk = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
