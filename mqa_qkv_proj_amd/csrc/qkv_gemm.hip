@@ -613,8 +613,14 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
   const int l32 = lane & 31, hf = lane >> 5;
 
   const int nbn = (N + BN - 1) / BN, nbm = (M + BM - 1) / BM;
+  // Tiles in groups of kGM row tiles, column-major inside a group: an XCD's
+  // contiguous share of ids covers a few columns of a few row tiles, so both
+  // the x rows and the W columns it reads are reused in its L2 (one row of
+  // tiles per XCD would stream all of W through every XCD).
+  constexpr int kGM = 8;
   const int lid = xcd_remap(blockIdx.x, nbn * nbm);
-  const int bm = lid / nbn, bn = lid % nbn;  // the n tiles of one m row are neighbours
+  const int grp = lid / (kGM * nbn), goff = lid % (kGM * nbn), gm0 = grp * kGM, gsz = min(kGM, nbm - gm0);
+  const int bm = gm0 + goff % gsz, bn = goff / gsz;
   const int m0 = bm * BM, n0 = bn * BN;
   const int nk = K / kTBK;
   // rotary embedding: this thread's positions and frequencies, loaded now
@@ -750,7 +756,6 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
     }
   };
   constexpr int kPieces = E::kRows * BN / 8, kPerRow = BN / 8;
-  static_assert(kPieces % L::kThreads == 0, "pieces per thread");
 #pragma unroll
   for (int ps = 0; ps < kPasses; ++ps) {
     const int r0 = ps * E::kRows;
@@ -766,10 +771,10 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
     __syncthreads();
 
 #pragma unroll
-    for (int k = 0; k < kPieces / L::kThreads; ++k) {
+    for (int k = 0; k < (kPieces + L::kThreads - 1) / L::kThreads; ++k) {
       const int c = tid + k * L::kThreads, r = c / kPerRow, cg = c % kPerRow;
       const int gm = m0 + r0 + r, gn = n0 + cg * 8;
-      if (gm >= M || gn >= N) continue;  // N % 8 == 0: a piece is wholly in or out
+      if (c >= kPieces || gm >= M || gn >= N) continue;  // N % 8 == 0: a piece is wholly in or out
       const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8);
       const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8 + 4);
       float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
