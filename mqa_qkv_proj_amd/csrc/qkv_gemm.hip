@@ -363,9 +363,13 @@ __global__ __launch_bounds__(256) void qkv_gemm_f32_kernel(const float* __restri
 // per row; W: consecutive k rows 16 banks apart, the lane groups of a read 8
 // banks apart); the lanes of a copy that fall on padding point past the
 // buffer, so they fetch nothing and land only on padding bytes, which are
-// never read.  All operand reads of a 16-deep k step are issued together and
-// waited for once, a step ahead of their MFMAs.  The epilogue stages the sums
-// in LDS and writes 16-byte row pieces (TileEpi).  Requires K % 64 == 0.
+// never read.  Every stage of the ring is an LDS array of its own, and the
+// operand reads are compiler builtins: the compiler then knows which stage
+// each read and each copy touches, so it waits only for the copies into the
+// stage being read (which the explicit per-tile wait has already retired) and
+// is free to issue the next k step's reads under the current step's MFMAs.
+// The epilogue stages the sums in LDS in 32-row passes over the freed stages
+// and writes 16-byte row pieces.  Requires K % 64 == 0.
 constexpr int kTBK = 64;
 constexpr int kTXld = kTBK + 8;  // x tile row pitch (bf16): 9 chunks of 16 B
 // W tile row pitch (bf16) for BN columns: the data rounded up to 16 dwords
@@ -385,121 +389,37 @@ struct TileCfg {
   static constexpr int kWld = tile_wpitch(BN);
   static constexpr int kX = BM * kTXld;
   static constexpr int kW = kTBK * kWld;
-  static constexpr int kStage = kX + kW;
+  static constexpr int kSink = kX + kW;    // 1 KB past the tiles: where surplus copies land
+  static constexpr int kStage = kX + kW + 512;
   static constexpr int kXChunks = kTXld / 8, kWChunks = kWld / 8;  // 16-byte chunks per row
   static constexpr int kXCopies = kX * 2 / 1024, kWCopies = kW * 2 / 1024;
-  static constexpr int kXcp = (kXCopies + kNW - 1) / kNW, kWcp = (kWCopies + kNW - 1) / kNW;  // per wave (at most)
+  static constexpr int kXcp = (kXCopies + kNW - 1) / kNW, kWcp = (kWCopies + kNW - 1) / kNW;  // per wave
+  static constexpr int kCopies = kXcp + kWcp;  // DMA instructions of every wave per k tile
   static constexpr size_t kBytes = (size_t)ST * kStage * sizeof(uint16_t);
   static_assert(kMI * WM * 32 == BM && kNI * WN * 32 == BN && kKS * KW * 16 == kTBK, "wave layout");
   static_assert(kX * 2 % 1024 == 0 && kW * 2 % 1024 == 0, "tiles are whole 1 KB copies");
   static_assert(kBytes <= 160 * 1024, "LDS");
-  // DMA instructions wave w issues per k tile
-  static constexpr int copies_of(int w) {
-    int c = 0;
-    for (int i = 0; i < kXcp; ++i) c += (w + kNW * i < kXCopies);
-    for (int i = 0; i < kWcp; ++i) c += (w + kNW * i < kWCopies);
-    return c;
-  }
 };
 
-// All operand fragments of one 16-deep k step, read in one asm block that
-// waits for itself once (a load written in asm is complete before the block
-// ends): MI x-row fragments at pa + 32 i rows (A), NI transposed W pairs at
-// pb + 32 j columns (B), the second read of a pair HI_BYTES (4 k rows) on.
-template <int MI, int NI, int A_STRIDE, int HI>
-struct StepFrags;
-#define MQKV_LDSADDR(p) ((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)(p))
-template <int A_STRIDE, int HI>
-struct StepFrags<1, 2, A_STRIDE, HI> {
-  __device__ static void read(const uint16_t* pa, const uint16_t* pb, u32x4_t (&a)[1], u32x4_t (&b)[2]) {
-    u32x2_t l0, h0, l1, h1;
-    asm volatile(
-        "ds_read_b128 %0, %5\n\t"
-        "ds_read_b64_tr_b16 %1, %6\n\t"
-        "ds_read_b64_tr_b16 %2, %6 offset:%7\n\t"
-        "ds_read_b64_tr_b16 %3, %6 offset:64\n\t"
-        "ds_read_b64_tr_b16 %4, %6 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
-        : "v"(MQKV_LDSADDR(pa)), "v"(MQKV_LDSADDR(pb)), "i"(HI), "i"(64 + HI)
-        : "memory");
-    b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
-    b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
-  }
-};
-template <int A_STRIDE, int HI>
-struct StepFrags<2, 2, A_STRIDE, HI> {
-  __device__ static void read(const uint16_t* pa, const uint16_t* pb, u32x4_t (&a)[2], u32x4_t (&b)[2]) {
-    u32x2_t l0, h0, l1, h1;
-    asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:%8\n\t"
-        "ds_read_b64_tr_b16 %2, %7\n\t"
-        "ds_read_b64_tr_b16 %3, %7 offset:%9\n\t"
-        "ds_read_b64_tr_b16 %4, %7 offset:64\n\t"
-        "ds_read_b64_tr_b16 %5, %7 offset:%10\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
-        : "v"(MQKV_LDSADDR(pa)), "v"(MQKV_LDSADDR(pb)), "i"(A_STRIDE), "i"(HI), "i"(64 + HI)
-        : "memory");
-    b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
-    b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
-  }
-};
-template <int A_STRIDE, int HI>
-struct StepFrags<1, 4, A_STRIDE, HI> {
-  __device__ static void read(const uint16_t* pa, const uint16_t* pb, u32x4_t (&a)[1], u32x4_t (&b)[4]) {
-    u32x2_t l0, h0, l1, h1, l2, h2, l3, h3;
-    asm volatile(
-        "ds_read_b128 %0, %9\n\t"
-        "ds_read_b64_tr_b16 %1, %10\n\t"
-        "ds_read_b64_tr_b16 %2, %10 offset:%11\n\t"
-        "ds_read_b64_tr_b16 %3, %10 offset:64\n\t"
-        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:128\n\t"
-        "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %7, %10 offset:192\n\t"
-        "ds_read_b64_tr_b16 %8, %10 offset:%14\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2), "=&v"(l3), "=&v"(h3)
-        : "v"(MQKV_LDSADDR(pa)), "v"(MQKV_LDSADDR(pb)), "i"(HI), "i"(64 + HI), "i"(128 + HI), "i"(192 + HI)
-        : "memory");
-    b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
-    b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
-    b[2] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-    b[3] = u32x4_t{l3[0], l3[1], h3[0], h3[1]};
-  }
-};
-template <int A_STRIDE, int HI>
-struct StepFrags<1, 5, A_STRIDE, HI> {
-  __device__ static void read(const uint16_t* pa, const uint16_t* pb, u32x4_t (&a)[1], u32x4_t (&b)[5]) {
-    u32x2_t l0, h0, l1, h1, l2, h2, l3, h3, l4, h4;
-    asm volatile(
-        "ds_read_b128 %0, %11\n\t"
-        "ds_read_b64_tr_b16 %1, %12\n\t"
-        "ds_read_b64_tr_b16 %2, %12 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %3, %12 offset:64\n\t"
-        "ds_read_b64_tr_b16 %4, %12 offset:%14\n\t"
-        "ds_read_b64_tr_b16 %5, %12 offset:128\n\t"
-        "ds_read_b64_tr_b16 %6, %12 offset:%15\n\t"
-        "ds_read_b64_tr_b16 %7, %12 offset:192\n\t"
-        "ds_read_b64_tr_b16 %8, %12 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %9, %12 offset:256\n\t"
-        "ds_read_b64_tr_b16 %10, %12 offset:%17\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2), "=&v"(l3), "=&v"(h3),
-          "=&v"(l4), "=&v"(h4)
-        : "v"(MQKV_LDSADDR(pa)), "v"(MQKV_LDSADDR(pb)), "i"(HI), "i"(64 + HI), "i"(128 + HI), "i"(192 + HI),
-          "i"(256 + HI)
-        : "memory");
-    b[0] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
-    b[1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
-    b[2] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-    b[3] = u32x4_t{l3[0], l3[1], h3[0], h3[1]};
-    b[4] = u32x4_t{l4[0], l4[1], h4[0], h4[1]};
-  }
-};
-#undef MQKV_LDSADDR
+// B-operand half of a 32x32x16 MFMA from a row-major W tile in LDS: a
+// transposing read of 4 k rows (lane 4j+q of each 16-lane group reads 4
+// columns of row j, lane i receives column i of the 4 rows).  As a builtin the
+// compiler knows which LDS array it reads and orders it after exactly the
+// copies into that array.
+__device__ __forceinline__ u32x2_t lds_tr16(const uint16_t* p) {
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p)));
+}
+// Compiler-level fence around a bare s_barrier: keeps LDS accesses on their
+// side of it (the barrier builtin alone does not order memory for the
+// optimizer).
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
 
 // B operand of a 32x32x16 MFMA from a row-major W tile: two transposing reads
 // (k rows r and r+4 of this lane's group; HI_BYTES apart) that wait for
@@ -574,38 +494,42 @@ struct RopeTable {
   }
 };
 
-// LDS of the tile epilogue: fp32 staging rows of BN + 8 floats (rows 4 apart
-// fall 32 banks apart), then the rotation table (BM rows of d/2 + 2 float2),
-// then the bias of the tile's columns (BN bf16).
-// The epilogue runs in PASSES passes of BM / PASSES rows when the whole
-// tile would need more LDS than the copy ring: a configuration that runs two
-// workgroups per CU keeps its LDS within half a CU's.
-template <int BM, int BN, int PASSES = 1>
-struct TileEpi {
-  static constexpr int kRows = BM / PASSES;  // rows staged per pass
+// Epilogue passes: the tile's rows are handled 32 at a time.  In a pass, the
+// k-step group g of every 32-row block in it writes its fp32 sums to stage g
+// (rows of BN + 8 floats: rows 4 apart fall 32 banks apart), the rotation
+// table of the pass's rows goes to stage KW (rows of d/2 + 2 float2) followed
+// by the tile's bias (BN bf16); then every thread takes 8-column row pieces.
+constexpr int kEpiRows = 32;
+template <int BM, int BN, int WM, int WN, int KW, int ST>
+struct TileEpiFit {
+  using L = TileCfg<BM, BN, WM, WN, KW, ST>;
   static constexpr int kPitch = BN + 8;
-  static constexpr size_t kStageBytes = (size_t)kRows * kPitch * 4;
-  __host__ __device__ static size_t table_bytes(bool rope, int d) { return rope ? (size_t)kRows * (d / 2 + 2) * 8 : 0; }
-  static size_t bytes(bool rope, int d, bool bias) {
-    return kStageBytes + table_bytes(rope, d) + (bias ? (size_t)BN * 2 : 0);
-  }
-  static constexpr size_t kWorstBytes = kStageBytes + (size_t)kRows * 66 * 8 + (size_t)BN * 2;  // d = 128, bias
-  static_assert(BM % (32 * PASSES) == 0, "passes of whole 32-row blocks");
+  static constexpr size_t kStageBytes = (size_t)L::kStage * 2;
+  static_assert(KW + 1 <= ST, "a stage per k-step group plus one for the table");
+  static_assert((size_t)kEpiRows * kPitch * 4 <= kStageBytes, "staging rows fit a stage");
+  static_assert((size_t)kEpiRows * (128 / 2 + 2) * 8 + BN * 2 <= kStageBytes, "table and bias fit a stage");
 };
-// Passes of a tile configuration: two where the ring leaves room for a second
-// workgroup on the CU (at most 80 KB) but the one-pass epilogue would not.
-template <int BM, int BN, size_t RING>
-constexpr int tile_epi_passes() {
-  return (RING <= 80 * 1024 && TileEpi<BM, BN, 1>::kWorstBytes > RING) ? 2 : 1;
-}
 
 template <int BM, int BN, int WM, int WN, int KW, int ST>
 __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ out, int M, int K, int N, ProjEpilogue app) {
   using L = TileCfg<BM, BN, WM, WN, KW, ST>;
+  using EF = TileEpiFit<BM, BN, WM, WN, KW, ST>;
   constexpr int MI = L::kMI, NI = L::kNI, NW = L::kNW;
-  extern __shared__ __align__(16) uint16_t smem[];
+  static_assert(ST >= 2 && ST <= 4, "ring of 2 to 4 stages");
+  // the ring: one LDS array per stage (unused arrays take 16 bytes)
+  __shared__ __align__(16) uint16_t ring0[L::kStage];
+  __shared__ __align__(16) uint16_t ring1[L::kStage];
+  __shared__ __align__(16) uint16_t ring2[ST > 2 ? L::kStage : 8];
+  __shared__ __align__(16) uint16_t ring3[ST > 3 ? L::kStage : 8];
+  auto stage = [&](auto sidx) -> uint16_t* {
+    constexpr int i = decltype(sidx)::value;
+    if constexpr (i == 0) return ring0;
+    else if constexpr (i == 1) return ring1;
+    else if constexpr (i == 2) return ring2;
+    else return ring3;
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wq = __builtin_amdgcn_readfirstlane(wave);
   const int pos = wave % (WM * WN), kg = wave / (WM * WN);  // tile position, k-step group
@@ -636,7 +560,7 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
   for (int i = 0; i < L::kXcp; ++i) {
     const int slot = (wave + NW * i) * 64 + lane;
     const int r = slot / L::kXChunks, ch = slot % L::kXChunks;
-    xoff[i] = ch < kTBK / 8 ? (uint32_t)r * xrow + ch * 16 : kNoCopy;
+    xoff[i] = (ch < kTBK / 8 && wave + NW * i < L::kXCopies) ? (uint32_t)r * xrow + ch * 16 : kNoCopy;
   }
 #pragma unroll
   for (int i = 0; i < L::kWcp; ++i) {
@@ -644,42 +568,37 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
     const int r = slot / L::kWChunks, ch = slot % L::kWChunks;
     // chunks of columns at or past N (a ragged last tile) fetch nothing: their
     // LDS columns feed only outputs that are not stored
-    woff[i] = (ch < BN / 8 && n0 + ch * 8 < N) ? (uint32_t)r * wrow + ch * 16 : kNoCopy;
+    woff[i] = (ch < BN / 8 && n0 + ch * 8 < N && wave + NW * i < L::kWCopies) ? (uint32_t)r * wrow + ch * 16
+                                                                              : kNoCopy;
   }
   // x rows at or past M and W rows past K lie past their buffer ends: they
   // fetch nothing, and their LDS rows only feed outputs that are not stored.
   const uint64_t xbytes = (uint64_t)M * K * 2, wbytes = (uint64_t)K * N * 2;
-  auto copy_tile = [&](int kt, int st) {
-    uint16_t* xs = smem + st * L::kStage;
+  // Every wave issues exactly L::kCopies copies per k tile, unconditionally:
+  // a wave's surplus copies fetch nothing (all offsets past the buffer) into
+  // the stage's sink, and the tiles past the last one (kt >= nk: the ring
+  // runs whole rounds) fetch nothing into a stage no tile reads again.  So
+  // one constant vmcnt retires a tile, and the compiler, which sees every
+  // copy and which stage it fills, needs no waits of its own before the reads.
+  auto copy_tile = [&](int kt, uint16_t* xs) {
     uint16_t* ws = xs + L::kX;
-    const uint64_t xb = (uint64_t)m0 * K * 2 + (uint64_t)kt * kTBK * 2;
-    const uint64_t wb = (uint64_t)kt * kTBK * N * 2 + (uint64_t)n0 * 2;
-    const __amdgpu_buffer_rsrc_t xr =
-        make_rsrc(reinterpret_cast<const char*>(x) + xb, (uint32_t)min(xbytes - xb, (uint64_t)0x7fffffff));
-    const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(reinterpret_cast<const char*>(w) + wb, (uint32_t)min(wbytes - wb, (uint64_t)0x7fffffff));
+    const bool live = kt < nk;
+    const uint64_t xb = live ? (uint64_t)m0 * K * 2 + (uint64_t)kt * kTBK * 2 : 0;
+    const uint64_t wb = live ? (uint64_t)kt * kTBK * N * 2 + (uint64_t)n0 * 2 : 0;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(reinterpret_cast<const char*>(x) + xb,
+                                                live ? (uint32_t)min(xbytes - xb, (uint64_t)0x7fffffff) : 0u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(reinterpret_cast<const char*>(w) + wb,
+                                                live ? (uint32_t)min(wbytes - wb, (uint64_t)0x7fffffff) : 0u);
 #pragma unroll
     for (int i = 0; i < L::kXcp; ++i) {
       const int cp = wq + NW * i;
-      if (cp < L::kXCopies) dma16(xr, xs + cp * 512, xoff[i], 0);
+      dma16(xr, cp < L::kXCopies ? xs + cp * 512 : xs + L::kSink, xoff[i], 0);
     }
 #pragma unroll
     for (int i = 0; i < L::kWcp; ++i) {
       const int cp = wq + NW * i;
-      if (cp < L::kWCopies) dma16(wr, ws + cp * 512, woff[i], 0);
+      dma16(wr, cp < L::kWCopies ? ws + cp * 512 : xs + L::kSink, woff[i], 0);
     }
-  };
-  // Wait until at most `ahead` later tiles of this wave's copies are still in
-  // flight (ahead <= ST - 2): an exact vmcnt per wave, since the waves issue
-  // different numbers of copies per tile.
-  auto wait_copies = [&](int ahead) {
-    static_for<0, NW>([&](auto wv) {
-      if (wq == wv) {
-        static_for<0, ST - 1>([&](auto a) {
-          if (ahead == a) wait_vmcnt<a * L::copies_of(wv)>();
-        });
-      }
-    });
   };
 
   f32x16_t acc[MI][NI];
@@ -688,96 +607,112 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = f32x16_t{};
 
-  // operand fragments of one 16-deep k step
+  // operand fragments of one 16-deep k step: MI x-row fragments (A), NI
+  // transposed W pairs (B: k rows r and r + 4 of the lane's group)
   const int bg = lane >> 4, bp = lane & 15;  // transposing-read lane group
   const int b_n = 16 * (bg & 1) + 4 * (bp & 3), b_k = 8 * (bg >> 1) + (bp >> 2);
-  using Frags = StepFrags<MI, NI, 32 * kTXld * 2, 4 * L::kWld * 2>;
-  auto frags = [&](const uint16_t* xs, const uint16_t* ws, int ks, u32x4_t (&a)[MI], u32x4_t (&b)[NI]) {
-    const uint16_t* pa = xs + (wm * (32 * MI) + l32) * kTXld + ks * 16 + hf * 8;
-    const uint16_t* pb = ws + (ks * 16 + b_k) * L::kWld + wn * (32 * NI) + b_n;
-    Frags::read(pa, pb, a, b);
+  // Every read indexes its stage array directly (one index, no chain of
+  // derived pointers), so the compiler keeps track of which array it reads.
+  const int a_idx = (wm * (32 * MI) + l32) * kTXld + hf * 8;
+  const int b_idx = L::kX + b_k * L::kWld + wn * (32 * NI) + b_n;
+  auto frags = [&](const uint16_t* st, int ks, u32x4_t (&a)[MI], u32x4_t (&b)[NI]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a[i] = ld16(st + (a_idx + ks * 16 + i * 32 * kTXld));
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int o = b_idx + ks * 16 * L::kWld + j * 32;
+      const u32x2_t lo = lds_tr16(st + o), hi = lds_tr16(st + (o + 4 * L::kWld));
+      b[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
   };
 
-  static_for<0, ST - 1>([&](auto s) {
-    if (s < nk) copy_tile(s, s);
-  });
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt % ST;
-    wait_copies(min(ST - 2, nk - 1 - kt));
-    // Tile kt is in LDS (every wave has waited for its own copies of it) and
-    // stage (kt - 1) % ST is free (every wave's reads of it completed inside
-    // their asm blocks).  A bare barrier: __syncthreads' workgroup fence would
-    // add a vmcnt(0) wait for the copies of the later tiles as well, which
-    // would leave only one tile of lookahead whatever ST is.
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + ST - 1 < nk) copy_tile(kt + ST - 1, (kt + ST - 1) % ST);
-    const uint16_t* xs = smem + st * L::kStage;
-    const uint16_t* ws = xs + L::kX;
-    u32x4_t a[2][MI], b[2][NI];
-    frags(xs, ws, kg, a[0], b[0]);
-    static_for<0, L::kKS>([&](auto kk) {
-      constexpr int cur = kk & 1;
-      if constexpr (kk + 1 < L::kKS) frags(xs, ws, (kk + 1) * KW + kg, a[cur ^ 1], b[cur ^ 1]);
+  static_for<0, ST - 1>([&](auto s) { copy_tile(s, stage(s)); });
+  // The k loop, unrolled over the ring so that every stage is named statically;
+  // it runs whole rounds of ST tiles, those past the last one without reads or
+  // MFMAs.
+  for (int kt0 = 0; kt0 < nk; kt0 += ST) {
+    static_for<0, ST>([&](auto s) {
+      const int kt = kt0 + s;
+      // Tile kt is in LDS once every wave has waited for its own copies of it
+      // and passed the barrier, which also tells that every wave's reads of
+      // the previous tile are done, so its stage may be refilled.  A bare
+      // barrier: __syncthreads' fence would also wait for the copies of the
+      // later tiles, which would leave one tile of lookahead whatever ST is.
+      wait_vmcnt<(ST - 2) * L::kCopies>();
+      bare_barrier();
+      constexpr int sn = (s + ST - 1) % ST;
+      copy_tile(kt + ST - 1, stage(std::integral_constant<int, sn>{}));
+      if (kt < nk) {  // uniform
+        const uint16_t* st = stage(s);
+        u32x4_t a[2][MI], b[2][NI];
+        frags(st, kg, a[0], b[0]);
+        static_for<0, L::kKS>([&](auto kk) {
+          constexpr int cur = kk & 1;
+          if constexpr (kk + 1 < L::kKS) frags(st, (kk + 1) * KW + kg, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+          for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = mfma32_bf16(a[cur][i], b[cur][j], acc[i][j]);
+            for (int j = 0; j < NI; ++j) acc[i][j] = mfma32_bf16(a[cur][i], b[cur][j], acc[i][j]);
+        });
+      }
     });
   }
 
-  // ---- epilogue.  The tile's sums are staged in LDS as fp32 rows (the stages
-  // are free now): k-step group 0 writes its sums, groups 1.. add theirs in
-  // group order (a fixed order, so the result does not depend on timing).
-  // Every thread then takes 8-column row pieces: bias, rotation, rounding to
-  // bf16, one 16-byte store (and the cache append).  A piece holds 4 whole
-  // planes of one head, so the rotation needs nothing from other threads.
-  constexpr int kPasses = tile_epi_passes<BM, BN, L::kBytes>();
-  using E = TileEpi<BM, BN, kPasses>;
-  float* stg = reinterpret_cast<float*>(smem);
-  float2* tab = reinterpret_cast<float2*>(reinterpret_cast<char*>(smem) + E::kStageBytes);
+  // ---- epilogue, in passes of 32 rows over the freed stages: k-step group g
+  // writes its sums to stage g, the rotation table and the bias go to stage
+  // KW; then every thread takes 8-column row pieces of the pass, adds the
+  // groups' sums in group order (a fixed order, so the result does not depend
+  // on timing), adds the bias, rotates, rounds to bf16 and writes one 16-byte
+  // piece (and the cache append).  A piece holds 4 whole planes of one head,
+  // so the rotation needs nothing from other threads.
+  constexpr int kPitch = EF::kPitch;
+  float2* tab = reinterpret_cast<float2*>(stage(std::integral_constant<int, KW>{}));
   const int tpitch = (app.rope_d >> 1) + 2;  // float2 per table row: 16-byte aligned rows
-  uint16_t* bstg = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(smem) + E::kStageBytes +
-                                               E::table_bytes(rope, app.rope_d));
-  // this wave's sums of the rows [r0, r0 + E::kRows) (whole 32-row blocks)
-  auto stage = [&](bool add, int r0) {
+  uint16_t* bstg = reinterpret_cast<uint16_t*>(tab + (rope ? kEpiRows * tpitch : 0));
+  constexpr int kPieces = kEpiRows * BN / 8, kPerRow = BN / 8;
+  wait_vmcnt<0>();  // the copies past the last tile (nothing fetched) have landed
+  static_for<0, BM / kEpiRows>([&](auto ps) {
+    constexpr int r0 = ps * kEpiRows;
+    // every wave is done with the ring, or with the previous pass's rows
+    wait_lgkm0();
+    bare_barrier();
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int rb = wm * (32 * MI) + i * 32 - r0;
-      if (rb < 0 || rb >= E::kRows) continue;
+      if (wm * (32 * MI) + i * 32 != r0) continue;  // the pass is one 32-row block
+      static_for<0, KW>([&](auto g) {
+        if (kg == g) {
+          float* stg = reinterpret_cast<float*>(stage(g));
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
+          for (int j = 0; j < NI; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float& d = stg[(rb + 8 * (e / 4) + 4 * hf + (e % 4)) * E::kPitch + wn * (32 * NI) + j * 32 + l32];
-          d = add ? d + acc[i][j][e] : acc[i][j][e];
+            for (int e = 0; e < 16; ++e)
+              stg[(8 * (e / 4) + 4 * hf + (e % 4)) * kPitch + wn * (32 * NI) + j * 32 + l32] = acc[i][j][e];
         }
+      });
     }
-  };
-  constexpr int kPieces = E::kRows * BN / 8, kPerRow = BN / 8;
-#pragma unroll
-  for (int ps = 0; ps < kPasses; ++ps) {
-    const int r0 = ps * E::kRows;
-    __syncthreads();  // every wave is done with the stages, or with the previous pass's rows
-    if (kg == 0) stage(false, r0);
-    if (rope) rtab.fill(app, tab, tpitch, tid, r0, E::kRows);
-    if (ps == 0 && bias && tid < BN / 8 && n0 + tid * 8 < N) st16(bstg + tid * 8, ld16(bias + n0 + tid * 8));
-#pragma unroll
-    for (int g = 1; g < KW; ++g) {
-      __syncthreads();
-      if (kg == g) stage(true, r0);
-    }
-    __syncthreads();
+    if (rope) rtab.fill(app, tab, tpitch, tid, r0, kEpiRows);
+    if (bias && tid < BN / 8 && n0 + tid * 8 < N) st16(bstg + tid * 8, ld16(bias + n0 + tid * 8));
+    wait_lgkm0();
+    bare_barrier();
 
 #pragma unroll
     for (int k = 0; k < (kPieces + L::kThreads - 1) / L::kThreads; ++k) {
       const int c = tid + k * L::kThreads, r = c / kPerRow, cg = c % kPerRow;
       const int gm = m0 + r0 + r, gn = n0 + cg * 8;
       if (c >= kPieces || gm >= M || gn >= N) continue;  // N % 8 == 0: a piece is wholly in or out
-      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8);
-      const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stg + r * E::kPitch + cg * 8 + 4);
-      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      static_for<0, KW>([&](auto g) {
+        const float* stg = reinterpret_cast<const float*>(stage(g)) + r * kPitch + cg * 8;
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stg);
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stg + 4);
+        if constexpr (g == 0) {
+          v[0] = lo[0], v[1] = lo[1], v[2] = lo[2], v[3] = lo[3];
+          v[4] = hi[0], v[5] = hi[1], v[6] = hi[2], v[7] = hi[3];
+        } else {
+          v[0] += lo[0], v[1] += lo[1], v[2] += lo[2], v[3] += lo[3];
+          v[4] += hi[0], v[5] += hi[1], v[6] += hi[2], v[7] += hi[3];
+        }
+      });
       if (bias) {
         const u32x4_t bb = ld16(bstg + cg * 8);
 #pragma unroll
@@ -811,21 +746,16 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
         }
       }
     }
-  }
+  });
 }
 
 template <int BM, int BN, int WM, int WN, int KW, int ST>
 static hipError_t launch_gemm_tiles(const void* x, const void* w, const void* bias, void* out, int M, int K, int N,
                                     hipStream_t s, const ProjEpilogue& app) {
   using L = TileCfg<BM, BN, WM, WN, KW, ST>;
-  auto kern = qkv_gemm_tiles_kernel<BM, BN, WM, WN, KW, ST>;
-  using E = TileEpi<BM, BN, tile_epi_passes<BM, BN, L::kBytes>()>;
-  const size_t lds = std::max(L::kBytes, E::bytes(app.inv_freq != nullptr, app.rope_d, bias != nullptr));
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   const int nblk = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3(nblk), dim3(L::kThreads), lds, s, (const uint16_t*)x, (const uint16_t*)w,
-                     (const uint16_t*)bias, (uint16_t*)out, M, K, N, app);
+  hipLaunchKernelGGL((qkv_gemm_tiles_kernel<BM, BN, WM, WN, KW, ST>), dim3(nblk), dim3(L::kThreads), 0, s,
+                     (const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out, M, K, N, app);
   return hipGetLastError();
 }
 
