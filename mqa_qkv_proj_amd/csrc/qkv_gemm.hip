@@ -668,7 +668,11 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
   constexpr int kPitch = EF::kPitch;
   float2* tab = reinterpret_cast<float2*>(stage(std::integral_constant<int, KW>{}));
   const int tpitch = (app.rope_d >> 1) + 2;  // float2 per table row: 16-byte aligned rows
-  uint16_t* bstg = reinterpret_cast<uint16_t*>(tab + (rope ? kEpiRows * tpitch : 0));
+  // rows of the table filled at once: as many whole 32-row passes as the stage
+  // holds beside the bias (all 128 at d = 64), so fewer passes pay for a fill
+  int tb_rows = kEpiRows;
+  while (tb_rows * 2 <= BM && (size_t)tb_rows * 2 * tpitch * 8 + BN * 2 <= EF::kStageBytes) tb_rows *= 2;
+  uint16_t* bstg = reinterpret_cast<uint16_t*>(tab + (rope ? tb_rows * tpitch : 0));
   constexpr int kPieces = kEpiRows * BN / 8, kPerRow = BN / 8;
   wait_vmcnt<0>();  // the copies past the last tile (nothing fetched) have landed
   static_for<0, BM / kEpiRows>([&](auto ps) {
@@ -690,7 +694,8 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
         }
       });
     }
-    if (rope) rtab.fill(app, tab, tpitch, tid, r0, kEpiRows);
+    const int tb0 = r0 - r0 % tb_rows;  // first row of the table block holding this pass
+    if (rope && r0 == tb0) rtab.fill(app, tab, tpitch, tid, r0, tb_rows);
     if (bias && tid < BN / 8 && n0 + tid * 8 < N) st16(bstg + tid * 8, ld16(bias + n0 + tid * 8));
     wait_lgkm0();
     bare_barrier();
@@ -722,7 +727,7 @@ __global__ __launch_bounds__(WM * WN * KW * 64, 1) void qkv_gemm_tiles_kernel(
         }
       }
       if (rope && gn < app.vcol) {
-        const float2* t = tab + r * tpitch + ((gn & (app.rope_d - 1)) >> 1);
+        const float2* t = tab + (r0 - tb0 + r) * tpitch + ((gn & (app.rope_d - 1)) >> 1);
         const f32x4_t c01 = *reinterpret_cast<const f32x4_t*>(t), c23 = *reinterpret_cast<const f32x4_t*>(t + 2);
         const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};  // (cos, sin) x 4
 #pragma unroll
@@ -1302,8 +1307,8 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
     // Tile shape: the one-workgroup-per-CU configuration with the most tiles
     // that still fit one round on the CUs (ties: the larger tile, which reads
     // fewer operand bytes per FLOP); shapes with more tiles than that run the
-    // 128 x 160 tile two workgroups per CU.  Measured on the 2560-column
-    // projection: M = 512 / 1024 / 2048 / 4096 -> 20.6 / 26.8 / 33.2 / 45.3 us.
+    // 128 x 160 tile two workgroups per CU, or 128 x 128 tiles when their
+    // rounds on the CUs take less time.
     int dev = 0, cus = 256;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1320,7 +1325,16 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
       case 1: return launch_gemm_tiles<128, 128, 2, 2, 2, 3>(x, w, bias, out, m, k, n, s, app);
       case 2: return launch_gemm_tiles<64, 160, 2, 1, 2, 4>(x, w, bias, out, m, k, n, s, app);
       case 3: return launch_gemm_tiles<64, 128, 2, 2, 2, 4>(x, w, bias, out, m, k, n, s, app);
-      default: return launch_gemm_tiles<128, 160, 4, 1, 1, 2>(x, w, bias, out, m, k, n, s, app);
+      default: {  // more tiles than CUs
+        // Rounds of 128 x 160 tiles two per CU against rounds of 128 x 128
+        // tiles one per CU; one round of the latter measured 0.58 of one of the
+        // former ([2048,4096] x [4096,6144]: 2 rounds 140 us against 3 rounds
+        // 127 us; M = 4096: 3 rounds 227 us against 6 rounds 252 us).
+        const int64_t r160 = (t160 + 2 * cus - 1) / (2 * cus), r128 = (t128 + cus - 1) / cus;
+        if (58 * r128 < 100 * r160)
+          return launch_gemm_tiles<128, 128, 2, 2, 2, 3>(x, w, bias, out, m, k, n, s, app);
+        return launch_gemm_tiles<128, 160, 4, 1, 1, 2>(x, w, bias, out, m, k, n, s, app);
+      }
     }
   }
   // Pick the largest tile that still gives the chip (256 CUs) a full wave of workgroups.

@@ -35,7 +35,9 @@ PROJ = [  # M, hidden, H_q, H_kv, d, dtype
     (1, 256, 4, 2, 64, "bf16"), (7, 512, 8, 1, 128, "bf16"), (33, 256, 4, 4, 64, "bf16"),
     (130, 384, 8, 2, 64, "bf16"), (300, 1024, 16, 2, 128, "bf16"), (1029, 264, 4, 2, 64, "bf16"),
     (1000, 192, 5, 1, 64, "bf16"), (4100, 256, 13, 1, 64, "bf16"),
-    (4133, 256, 32, 4, 64, "bf16"),  # more 128 x 160 tiles than CUs: two workgroups per CU
+    # more tiles than CUs: 128 x 128 tiles one per CU (M = 4133), 128 x 160 two per CU with a
+    # ragged last column tile (N = 6144)
+    (4133, 256, 32, 4, 64, "bf16"), (2100, 256, 32, 8, 128, "bf16"),
     (128, 512, 4, 2, 64, "bf16"), (100, 1024, 8, 1, 128, "bf16"), (8, 256, 64, 2, 128, "bf16"),
     (24, 384, 4, 2, 64, "bf16"), (32, 128, 12, 2, 128, "bf16"),
     (128, 256, 4, 2, 64, "f32"), (45, 100, 2, 1, 128, "f32"),

@@ -42,8 +42,9 @@ ROPE = [  # M, hidden, H_q, H_kv, d, dtype, bias: the kernel each case reaches
     (128, 2048, 32, 4, 64, "bf16", False),   # the same at the TinyLlama L=128 width
     (130, 384, 8, 2, 64, "bf16", False),     # LDS-DMA tiles
     (1029, 2048, 32, 4, 64, "bf16", True),   # LDS-DMA tiles, TinyLlama width, ragged M
-    (4133, 256, 32, 4, 64, "bf16", True),    # more tiles than CUs: two workgroups per CU, ragged M
-    (2100, 192, 16, 2, 128, "bf16", True),   # the same at d = 128
+    (4133, 256, 32, 4, 64, "bf16", True),    # more tiles than CUs: 128 x 128 tiles, ragged M
+    (2100, 192, 16, 2, 128, "bf16", True),   # more tiles than CUs: 128 x 160 tiles two per CU, d = 128
+    (2100, 128, 32, 8, 128, "bf16", True),   # the same with a ragged last column tile (N = 6144)
     (300, 264, 4, 2, 64, "bf16", False),     # register-prefetched tiles (hidden % 64 != 0)
     (128, 256, 4, 2, 64, "f32", True),       # fp32
     (45, 100, 2, 1, 128, "f32", False),      # fp32, ragged
@@ -122,7 +123,7 @@ APPEND = [  # B, hidden, H_q, H_kv, d, L_max, dtype
     (100, 128, 8, 2, 64, 20, "bf16"),     # skinny, one k range
     (64, 1024, 8, 2, 64, 20, "bf16"),     # 8-wave workgroups over all of K
     (300, 256, 8, 2, 64, 9, "bf16"),      # LDS-DMA tiles
-    (2100, 256, 32, 4, 64, 9, "bf16"),    # LDS-DMA tiles, two workgroups per CU
+    (2100, 256, 32, 4, 64, 9, "bf16"),    # LDS-DMA tiles, more tiles than CUs
     (200, 264, 4, 2, 64, 17, "bf16"),     # register-prefetched tiles
     (20, 128, 4, 2, 64, 12, "f32"),       # fp32
 ]
