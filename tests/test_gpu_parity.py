@@ -38,6 +38,8 @@ PROJ = [  # M, hidden, H_q, H_kv, d, dtype
     # more tiles than CUs: 128 x 128 tiles one per CU (M = 4133), 128 x 160 two per CU with a
     # ragged last column tile (N = 6144)
     (4133, 256, 32, 4, 64, "bf16"), (2100, 256, 32, 8, 128, "bf16"),
+    # the copy ring past the last k tile: one k tile (hidden 64) and two (hidden 128), tile path
+    (300, 64, 4, 2, 64, "bf16"), (517, 128, 8, 2, 64, "bf16"),
     (128, 512, 4, 2, 64, "bf16"), (100, 1024, 8, 1, 128, "bf16"), (8, 256, 64, 2, 128, "bf16"),
     (24, 384, 4, 2, 64, "bf16"), (32, 128, 12, 2, 128, "bf16"),
     (128, 256, 4, 2, 64, "f32"), (45, 100, 2, 1, 128, "f32"),

@@ -45,6 +45,7 @@ ROPE = [  # M, hidden, H_q, H_kv, d, dtype, bias: the kernel each case reaches
     (4133, 256, 32, 4, 64, "bf16", True),    # more tiles than CUs: 128 x 128 tiles, ragged M
     (2100, 192, 16, 2, 128, "bf16", True),   # more tiles than CUs: 128 x 160 tiles two per CU, d = 128
     (2100, 128, 32, 8, 128, "bf16", True),   # the same with a ragged last column tile (N = 6144)
+    (300, 64, 4, 2, 128, "bf16", True),      # LDS-DMA tiles, one k tile (hidden 64)
     (300, 264, 4, 2, 64, "bf16", False),     # register-prefetched tiles (hidden % 64 != 0)
     (128, 256, 4, 2, 64, "f32", True),       # fp32
     (45, 100, 2, 1, 128, "f32", False),      # fp32, ragged
