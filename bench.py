@@ -132,6 +132,30 @@ class Timer:
             e.synchronize()
         return s.elapsed_time(e) / n * 1e3  # us
 
+    def graphed(self, fn, n=20):
+        """fn called n times back to back inside one captured HIP graph, replayed:
+        the kernels' time without the host's launch gaps between them."""
+        t = self.torch
+        with t.cuda.stream(self.stream):
+            self.spin_up(fn)
+            t.cuda.synchronize()
+            g = t.cuda.CUDAGraph()
+            with t.cuda.graph(g, stream=self.stream):
+                for _ in range(n):
+                    fn()
+            best = None
+            for _ in range(3):
+                g.replay()  # warm replay, then the timed one
+                s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+                s.record(self.stream)
+                g.replay()
+                e.record(self.stream)
+                e.synchronize()
+                us = s.elapsed_time(e) / n * 1e3
+                best = us if best is None else min(best, us)
+            del g
+        return best
+
     def cold(self, fn, n=15):
         t = self.torch
         ts = []
@@ -395,6 +419,13 @@ def measure_configs(m, W, torch, np, dev, stream, timer, up, kv8):
             attn()
         us_g, us_a, us_l = timer.warm(proj), timer.warm(attn), timer.warm(layer)
         us_gr, us_lr = timer.warm(proj_rope), timer.warm(layer_rope)
+        layer()
+        torch.cuda.synchronize()
+        o_eager = o.clone()
+        us_lg = timer.graphed(layer)  # o now holds the last replay's output
+        torch.cuda.synchronize()
+        graph_same = bool(torch.equal(o, o_eager))
+        us_lrg = timer.graphed(layer_rope)
         roof_g, fl_g, by_g = gemm_roof_us(M, wl.hidden, wl.N)
         fl_a = prefill_flops(wl.B, wl.H_q, wl.d, wl.L, wl.L, True)
         res[wl.name] = {
@@ -404,7 +435,9 @@ def measure_configs(m, W, torch, np, dev, stream, timer, up, kv8):
             "prefill": {"us": round(us_a, 2), "tflops": round(fl_a / us_a / 1e6, 2),
                         "frac": round(fl_a / us_a / 1e6 / PEAK_BF16_TFLOPS, 4)},
             "layer_us": round(us_l, 2), "layer_tflops": round((fl_g + fl_a) / us_l / 1e6, 2),
-            "qkv_proj_rope_us": round(us_gr, 2), "layer_rope_us": round(us_lr, 2)}
+            "qkv_proj_rope_us": round(us_gr, 2), "layer_rope_us": round(us_lr, 2),
+            "layer_graph_us": round(us_lg, 2), "layer_rope_graph_us": round(us_lrg, 2),
+            "graph_output_equal": graph_same}
         log(json.dumps({"config": wl.name, **res[wl.name]}))
         del x, w, qkv, o, wsg, wsp, q, k, v, pos, th
 
