@@ -18,7 +18,8 @@ durations and the roofline figure come from it.
 
 Then every configuration is measured on its own (`configs`; skipped with
 --no-configs): the tiny fp32 layer, the TinyLlama-shaped layers (projection,
-prefill, whole layer), the MQA decode loop (eager and as one HIP graph), the
+prefill, whole layer eager and as one HIP graph), the MQA decode loop (eager
+and as one HIP graph), the
 Llama-2-7B decode sweep (cold caches) with its projections, and the four
 long-context prefills in bf16 and FP8.  Each carries its roofline fraction.
 
