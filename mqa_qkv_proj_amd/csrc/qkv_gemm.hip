@@ -1321,7 +1321,7 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
     for (int c = 0; c < 4; ++c)
       if (cand[c] <= cus && cand[c] > best) best = cand[c], pick = c;
     switch (pick) {
-      case 0: return launch_gemm_tiles<128, 160, 4, 1, 2, 4>(x, w, bias, out, m, k, n, s, app);
+      case 0: return launch_gemm_tiles<128, 160, 4, 1, 2, 3>(x, w, bias, out, m, k, n, s, app);
       case 1: return launch_gemm_tiles<128, 128, 2, 2, 2, 3>(x, w, bias, out, m, k, n, s, app);
       case 2: return launch_gemm_tiles<64, 160, 2, 1, 2, 4>(x, w, bias, out, m, k, n, s, app);
       case 3: return launch_gemm_tiles<64, 128, 2, 2, 2, 4>(x, w, bias, out, m, k, n, s, app);
