@@ -310,6 +310,9 @@ size_t gqa_attn_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int
  * resident workgroup, crossing sequence boundaries, so that ragged lengths
  * stay balanced.  Each unit writes a partial (max, sum, output) triple to
  * `workspace` and a second kernel combines them exactly (softmax rescaling).
+ * For short caches with kv_split = 0 the library may instead merge each
+ * segment's partials inside one workgroup and leave the workspace unused; the
+ * result is the same to within rounding.
  * workspace: >= gqa_attn_decode_workspace_bytes(...) bytes, 16-byte aligned;
  *   no initial contents needed; calls that overlap must not share one.
  */

@@ -390,6 +390,7 @@ mqkv_status decode_launch(const void* q, const void* k_cache, const void* v_cach
   mqkv::DecodeArgs a{q,     k_cache, v_cache, seq_lens, o,       lse,     B,
                      H_q,   H_kv,    d,       L_max,    q_tok_stride,     scale,
                      split, n_slot,  part_o,  part_ml,  bf16,    o_dtype == MQKV_BF16};
+  a.auto_split = kv_split == 0;
   return hip_status(mqkv::launch_decode(a, (hipStream_t)stream), "gqa_attn_decode launch");
 }
 
@@ -523,6 +524,7 @@ mqkv_status gqa_attn_decode_paged(const void* q, const void* k_pages, const void
   a.page_size = page_size;
   a.pages_per_seq = pages_per_seq;
   a.num_pages = num_pages;
+  a.auto_split = kv_split == 0;
   return hip_status(mqkv::launch_decode(a, (hipStream_t)stream), "gqa_attn_decode_paged launch");
 }
 

@@ -37,6 +37,13 @@ constexpr int kMinTiles = 4;  // balanced mode: at least this many tiles per wor
 constexpr int kWavesPerCU = 12;  // split-kernel workgroups resident per CU (3 per SIMD)
 constexpr int64_t kBalancedMinTiles = 16384;  // auto: balanced split from this many tiles at capacity
 constexpr int kShortSplit = 64;               // auto: keys per split below that
+constexpr int kNoExp = -(1 << 20);  // V exponent of a partial without keys (below any real one)
+// Fused small-cache decode: waves per workgroup; it is chosen for caches of at
+// most kFusedWaves tiles (one tile per wave), or of at most kFusedManyTiles
+// tiles when there are at least kFusedManySegs segments to fill the chip.
+constexpr int kFusedWaves = 8;
+constexpr int kFusedManyTiles = 32;
+constexpr int kFusedManySegs = 128;
 
 template <int D>
 struct DecodeLds {
@@ -133,23 +140,46 @@ __device__ __forceinline__ int64_t balanced_tpw(int64_t total, int nwg) {
 // Per unit, MFMA 16x16x32 layout: A (16 x 32): lane l holds row l%16, k slot
 // group l/16; B (32 x 16): column l%16, the same k group; D (16 x 16): column
 // l%16, rows 4*(l/16) + i.
-template <int D, bool STREAM>
-__global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
+// NW = 1: the split kernel (one wave per workgroup, partials to the workspace).
+// NW > 1: the fused small-cache kernel (see attn_decode_fused_bf16 below):
+// one workgroup per segment, its NW waves take contiguous tile ranges, and
+// their partials are merged in LDS into O and LSE (OUT_BF16: the output type).
+template <int D, bool STREAM, int NW = 1, bool OUT_BF16 = true>
+__global__ __launch_bounds__(64 * NW, NW == 1 ? 3 : 1) void attn_decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_ml,
     int B, int Hq, int Hkv, int Lmax, int64_t q_stride, float c, int split, int n_slot, int n_qblk,
-    const int32_t* __restrict__ block_table, int page_size, int pages_per_seq, int num_pages) {
+    const int32_t* __restrict__ block_table, int page_size, int pages_per_seq, int num_pages,
+    void* __restrict__ o_out = nullptr, float* __restrict__ lse_out = nullptr) {
   using S = DecodeLds<D>;
   constexpr int DS = D / 32;                       // k-steps of the score MFMA
   constexpr int DB = D / 16;                       // 16-row blocks of O^T
   constexpr int VTASK = (kTK / 4) * (D / 8) / 64;  // V 4x8 blocks per lane
+  constexpr int kVtElems = (int)(S::kBytes / sizeof(uint16_t));
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* Vt = smem;
+  const int wave = NW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+  uint16_t* Vt = smem + wave * kVtElems;  // this wave's V^T staging
 
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const int G = Hq / Hkv;
   const int64_t row_stride = (int64_t)Hkv * D;
   const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // Fused mode: a wave's partial (its O^T accumulators at scale 2^-sig, the row
+  // max and sum) as a record of 4 DB + 3 floats per lane, lane-fastest, in the
+  // wave's own V^T region (free once its last tile is done).
+  constexpr int kRec = 4 * DB + 3;
+  static_assert(NW == 1 || (size_t)kRec * 64 * 4 <= S::kBytes, "a wave's record fits its V^T region");
+  float* rec = reinterpret_cast<float*>(Vt);
+  auto emit_lds = [&](const f32x4_t (&acc)[DB], float m, float l, int sg) {
+    wave_lds_sync();  // this wave's last V^T reads are done
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rec[(db * 4 + e) * 64 + lane] = acc[db][e];
+    rec[(4 * DB) * 64 + lane] = m;
+    rec[(4 * DB + 1) * 64 + lane] = l;
+    rec[(4 * DB + 2) * 64 + lane] = __int_as_float(sg);
+  };
 
   // Process tiles [tb, tb + ntile) of segment (b, g, qblk) and write its partial to `slot`.
   auto unit = [&](int b, int g, int qblk, int tb, int ntile, int slot) {
@@ -321,7 +351,9 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
 
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    if (hvalid) {
+    if constexpr (NW > 1) {
+      emit_lds(acc, m_run, l_tot, sig);
+    } else if (hvalid) {
       const int64_t pidx = ((int64_t)b * Hq + h) * n_slot + slot;
       float* po = part_o + pidx * D;
 #pragma unroll
@@ -332,6 +364,71 @@ __global__ __launch_bounds__(64, 3) void attn_decode_split_bf16_kernel(
         st16(part_ml + pidx * 4, u32x4_t{__float_as_uint(m_run), __float_as_uint(l_tot), (uint32_t)sig, 0u});
     }
   };
+
+  if constexpr (NW > 1) {
+    // Fused mode: workgroup = segment (b, g, qblk); wave w takes tiles
+    // [w ntb / NW, (w + 1) ntb / NW) of it (none when the segment is short).
+    const int seg_id = blockIdx.x;
+    const int qblk = seg_id % n_qblk, bg = seg_id / n_qblk;
+    const int b = bg / Hkv, g = bg % Hkv;
+    const int ntb = (seq_len(seq_lens, b, Lmax) + kTK - 1) / kTK;
+    const int tb = (int)((int64_t)wave * ntb / NW), te = (int)((int64_t)(wave + 1) * ntb / NW);
+    if (te > tb) {
+      unit(b, g, qblk, tb, te - tb, 0);
+    } else {  // no keys for this wave: a record that weighs nothing
+      f32x4_t zero[DB];
+#pragma unroll
+      for (int i = 0; i < DB; ++i) zero[i] = f32x4_t{};
+      emit_lds(zero, -INFINITY, 0.0f, kNoExp);
+    }
+    __syncthreads();
+    // Merge, exactly as the combine kernel does: the largest max M and V
+    // exponent S over the waves, O = sum_w 2^(m_w - M) 2^(s_w - S) acc_w / L,
+    // L = sum_w 2^(m_w - M) l_w, then O 2^S.  Wave w' merges the 16-row blocks
+    // db = w', w' + NW, ...; lane (head column l16, group g4) as in a record.
+    const int col = qblk * 16 + l16;
+    const bool hvalid = col < G;
+    const int h = g * G + (hvalid ? col : 0);
+    const float* recs = reinterpret_cast<const float*>(smem);
+    constexpr int kRegion = kVtElems / 2;  // floats per wave region
+    float M = -INFINITY;
+    int Sx = kNoExp;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      M = fmaxf(M, recs[w * kRegion + (4 * DB) * 64 + lane]);
+      Sx = max(Sx, __float_as_int(recs[w * kRegion + (4 * DB + 2) * 64 + lane]));
+    }
+    float L = 0.0f, wt[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = recs[w * kRegion + (4 * DB) * 64 + lane];
+      const float a = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      L = __builtin_fmaf(a, recs[w * kRegion + (4 * DB + 1) * 64 + lane], L);
+      const int sw = __float_as_int(recs[w * kRegion + (4 * DB + 2) * 64 + lane]);
+      wt[w] = a == 0.0f ? 0.0f : __builtin_amdgcn_ldexpf(a, sw - Sx);
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no keys: O = 0
+    const int osh = L > 0.0f ? Sx : 0;
+    for (int db = wave; db < DB; db += NW) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v = __builtin_fmaf(wt[w], recs[w * kRegion + (db * 4 + e) * 64 + lane], v);
+        const float r = __builtin_amdgcn_ldexpf(v * inv, osh);
+        if (hvalid) {
+          const int64_t oi = ((int64_t)b * Hq + h) * D + db * 16 + 4 * g4 + e;
+          if constexpr (OUT_BF16)
+            static_cast<uint16_t*>(o_out)[oi] = f32_to_bf16(r);
+          else
+            static_cast<float*>(o_out)[oi] = r;
+        }
+      }
+    }
+    if (lse_out != nullptr && wave == 0 && g4 == 0 && hvalid)
+      lse_out[(int64_t)b * Hq + h] = (M + __builtin_log2f(L)) * kLn2;
+    return;
+  }
 
   // Work assignment; a single call site keeps one copy of the unit code.
   const int per_seq = Hkv * n_qblk;
@@ -615,7 +712,33 @@ hipError_t launch_split_bf16(const DecodeArgs& a, hipStream_t s, int& nwg) {
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64), lds, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_lens, a.part_o, a.part_ml, a.B,
                      a.Hq, a.Hkv, a.Lmax, a.q_stride, fmaxf(a.scale * kLog2e, 1e-30f), a.split, a.n_slot,
-                     n_qblk, a.block_table, a.page_size, a.pages_per_seq, a.num_pages);
+                     n_qblk, a.block_table, a.page_size, a.pages_per_seq, a.num_pages, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+// Fused small-cache decode: one workgroup of kFusedWaves waves per (sequence,
+// KV head, block of 16 query heads); the waves split the segment's tiles and
+// merge their partials in LDS, so there is no workspace traffic and no second
+// kernel.  For short caches the split path's cost is latency (one or two tiles
+// per wave, then the combine launch and its round trips); here it is one
+// launch.
+template <int D>
+hipError_t launch_fused_bf16(const DecodeArgs& a, hipStream_t s) {
+  const int n_qblk = (a.Hq / a.Hkv + 15) / 16;
+  const int64_t nblk = (int64_t)a.B * a.Hkv * n_qblk;
+  if (nblk > 0x7fffffff || nblk < 1) return hipErrorInvalidValue;
+  const bool stream = (int64_t)a.B * a.Lmax * a.Hkv * D * 4 >= kStreamBytes;
+  const size_t lds = (size_t)kFusedWaves * DecodeLds<D>::kBytes;
+  auto kern = stream ? (a.out_bf16 ? attn_decode_split_bf16_kernel<D, true, kFusedWaves, true>
+                                   : attn_decode_split_bf16_kernel<D, true, kFusedWaves, false>)
+                     : (a.out_bf16 ? attn_decode_split_bf16_kernel<D, false, kFusedWaves, true>
+                                   : attn_decode_split_bf16_kernel<D, false, kFusedWaves, false>);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * kFusedWaves), lds, s, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.seq_lens, a.part_o, a.part_ml, a.B,
+                     a.Hq, a.Hkv, a.Lmax, a.q_stride, fmaxf(a.scale * kLog2e, 1e-30f), a.split, a.n_slot,
+                     n_qblk, a.block_table, a.page_size, a.pages_per_seq, a.num_pages, a.o, a.lse);
   return hipGetLastError();
 }
 
@@ -647,6 +770,16 @@ int decode_slots(int B, int Hq, int Hkv, int Lmax, int kv_split, bool bf16) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  // The library's own split on a short cache: the fused kernel instead, where
+  // it is the faster one.  A wave's tiles are a chain of dependent loads, so
+  // with few segments it pays only at one tile per wave; with many segments
+  // the chip is full and the saved combine launch and workspace round trip win.
+  if (a.in_bf16 && a.auto_split && a.split > 0) {
+    const int64_t ntile = ((int64_t)a.Lmax + kTK - 1) / kTK;
+    const int64_t nseg = (int64_t)a.B * a.Hkv * ((a.Hq / a.Hkv + 15) / 16);
+    if (ntile <= kFusedWaves || (nseg >= kFusedManySegs && ntile <= kFusedManyTiles))
+      return a.d == 64 ? launch_fused_bf16<64>(a, s) : launch_fused_bf16<128>(a, s);
+  }
   hipError_t e;
   int nwg = 1;
   if (a.in_bf16)

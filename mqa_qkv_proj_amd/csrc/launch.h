@@ -93,6 +93,9 @@ struct DecodeArgs {
   // (Lmax = pages_per_seq * page_size).  nullptr: contiguous [B, Lmax, Hkv, d].
   const int32_t* block_table = nullptr;
   int page_size = 0, pages_per_seq = 0, num_pages = 0;
+  // The caller left the split to the library (kv_split = 0): on short caches
+  // the fused kernel then runs instead of the split kernel and the combine.
+  bool auto_split = false;
 };
 // The library's choice for kv_split == 0 (0 = balanced work split, else keys
 // per split), and the partial slots per (sequence, query head) a call needs.

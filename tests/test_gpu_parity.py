@@ -245,6 +245,11 @@ DECODE = [  # B, H_q, H_kv, d, L_max, lens, split
     (4, 4, 4, 64, 200, [200, 5, 64, 65], 64),
     (2, 6, 3, 64, 130, [129, 130], 0),
     (1, 64, 1, 128, 100, [100], 64),     # G = 64 > 32: two query blocks
+    # the library's choice on short caches: one workgroup per segment that
+    # merges its waves' partials in LDS (no workspace, no second kernel)
+    (1, 64, 1, 128, 200, [200], 0),      # four 16-head query blocks
+    (64, 32, 8, 128, 600, [600, 1, 31, 32, 33] + [(i * 97) % 600 + 1 for i in range(59)], 0),
+    (40, 32, 4, 64, 1000, [1000, 999, 1, 2] + [(i * 211) % 1000 + 1 for i in range(36)], 0),
 ]
 
 
@@ -265,6 +270,27 @@ def test_decode_matches_oracle(m, B, H_q, H_kv, d, L_max, lens, split, dtype):
     ref_o, ref_l = oracle.decode(q, kc, vc, seq, scale)
     assert_close(host(o), ref_o, dtype, "decode O")
     assert_close(host(lse), ref_l, dtype, "decode LSE", max_abs=1e-3 if dtype == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,d,L_max", [(6, 8, 2, 128, 256), (64, 32, 8, 128, 600), (40, 32, 4, 64, 1000),
+                                                 (3, 8, 2, 128, 300)])
+def test_decode_bf16_output_is_rounded_f32_output(m, B, H_q, H_kv, d, L_max):
+    """The bf16 output is the fp32 output rounded to nearest even, bit for bit
+    (short caches through the in-LDS merge, the last case through the split
+    kernels and their combine)."""
+    t = torch()
+    say("decode bf16 output", B, H_q, H_kv, d, L_max)
+    rng = np.random.default_rng([41, B, d])
+    lens = rng.integers(1, L_max + 1, size=B).astype(np.int32)
+    lens[0] = L_max
+    kd = dev(W.round_bf16(W.normal(41, 1, (B, L_max, H_kv, d))), "bf16")
+    vd = dev(W.round_bf16(W.normal(41, 2, (B, L_max, H_kv, d))), "bf16")
+    qd = dev(W.round_bf16(W.normal(41, 3, (B, H_q, d))), "bf16")
+    ld = t.from_numpy(lens).cuda()
+    o32, l32 = m.gqa_attn_decode(qd, kd, vd, ld, return_lse=True, out_dtype=t.float32)
+    o16, l16 = m.gqa_attn_decode(qd, kd, vd, ld, return_lse=True, out_dtype=t.bfloat16)
+    assert t.equal(o16, o32.to(t.bfloat16)), "bf16 output must be the rounded fp32 output"
+    assert t.equal(l16, l32), "LSE must not depend on the output type"
 
 
 @pytest.mark.parametrize("B,H_q,H_kv,L_max", [(64, 16, 8, 1024), (64, 64, 2, 4096)])
