@@ -47,6 +47,10 @@ PROJ = [  # M, hidden, H_q, H_kv, d, dtype
     # grids), 32-row tiles, and M <= 32 on a 12288-column weight; ragged row tiles
     (33, 512, 4, 2, 64, "bf16"), (97, 2048, 8, 2, 128, "bf16"), (64, 1024, 16, 2, 128, "bf16"),
     (20, 512, 32, 32, 128, "bf16"),
+    # M <= 32 on decode-width weights (5120-10240 columns, K = 1024..4096): the skinny
+    # kernel with a k split and the reduce kernel, ragged M down to one row
+    (32, 4096, 32, 8, 128, "bf16"), (17, 3072, 24, 8, 128, "bf16"), (1, 1024, 40, 4, 128, "bf16"),
+    (9, 2048, 40, 4, 128, "bf16"), (32, 1024, 64, 8, 128, "bf16"),
 ]
 
 

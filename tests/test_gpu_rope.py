@@ -38,6 +38,7 @@ ROPE = [  # M, hidden, H_q, H_kv, d, dtype, bias: the kernel each case reaches
     (33, 256, 4, 4, 64, "bf16", True),       # skinny, one k range (direct epilogue)
     (100, 1024, 8, 1, 128, "bf16", False),   # skinny, k split (rotation in the reduce kernel)
     (32, 4096, 32, 8, 128, "bf16", True),    # skinny + reduce at the Llama-2-7B decode width
+    (17, 3072, 24, 8, 128, "bf16", True),    # the same, N = 5120, ragged M
     (97, 2048, 8, 2, 128, "bf16", True),     # 8-wave workgroups over all of K, ragged row tile
     (128, 2048, 32, 4, 64, "bf16", False),   # the same at the TinyLlama L=128 width
     (130, 384, 8, 2, 64, "bf16", False),     # LDS-DMA tiles
@@ -121,6 +122,7 @@ def test_zero_frequencies_give_qkv_proj(m, M, hidden, d):
 APPEND = [  # B, hidden, H_q, H_kv, d, L_max, dtype
     (8, 2048, 16, 1, 128, 40, "bf16"),    # the MQA decode shape: streaming kernel
     (32, 4096, 32, 8, 128, 50, "bf16"),   # Llama-2-7B GQA-8 decode: skinny + reduce
+    (16, 1024, 64, 8, 128, 30, "bf16"),   # the same at N = 10240, half the rows
     (100, 128, 8, 2, 64, 20, "bf16"),     # skinny, one k range
     (64, 1024, 8, 2, 64, 20, "bf16"),     # 8-wave workgroups over all of K
     (300, 256, 8, 2, 64, 9, "bf16"),      # LDS-DMA tiles
