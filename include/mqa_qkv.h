@@ -46,15 +46,17 @@
  *     [0, L_max]), so no device value leads outside them.
  *   - dtypes: MQKV_BF16 (bf16 storage, fp32 accumulation, round-to-nearest-
  *     even outputs) or MQKV_F32 (fp32 throughout).
- *   - bf16 attention multiplies P by V on fp16 matrix cores; each tile of V
- *     (64 keys in prefill, 32 in decode) is converted as V * 2^-s with a
- *     power-of-two exponent s of its own (s = 0 when the tile lies inside
- *     fp16's range) and the accumulator follows with exact power-of-two
- *     rescales, so every finite bf16 V, however large or small, gives a finite
- *     result.  Values at least 2^-29 of their tile's largest |v| convert
- *     exactly; smaller ones are rounded with an absolute error of at most
- *     max(2^-39 * that largest |v|, 2^-25) (a prefill tile's largest |v|
- *     includes keys a causal row does not see).
+ *   - bf16 prefill multiplies P by V on fp16 matrix cores; each 64-key tile
+ *     of V is converted as V * 2^-s with a power-of-two exponent s of its own
+ *     (s = 0 when the tile lies inside fp16's range) and the accumulator
+ *     follows with exact power-of-two rescales, so every finite bf16 V,
+ *     however large or small, gives a finite result.  Values at least 2^-29
+ *     of their tile's largest |v| convert exactly; smaller ones are rounded
+ *     with an absolute error of at most max(2^-39 * that largest |v|, 2^-25)
+ *     (a tile's largest |v| includes keys a causal row does not see).  bf16
+ *     decode multiplies on bf16 matrix cores, where every finite bf16 V is an
+ *     exact operand, with P carried as the sum of two bf16 parts (about 16
+ *     bits).
  *   - Alignment: every data pointer 16-byte aligned; element strides multiples
  *     of 8 (bf16) or 4 (fp32) elements.
  */

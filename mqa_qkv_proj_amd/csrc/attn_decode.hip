@@ -13,10 +13,11 @@
 // Split kernel (bf16): single-wave workgroups.  Each K/V row is read from HBM
 // once and serves all G query heads of its group through MFMA 16x16x32:
 // S^T = K . Q^T (bf16, the heads as the 16 columns) and O^T += V^T . P^T
-// (fp16, P rounded to fp16 as in the prefill kernel).  K rows are loaded
-// straight into the MFMA operand registers; V rows are staged through the
-// wave's LDS, transposed and converted to fp16.  Tiles are 32 keys; the next
-// tile's loads are in flight while the current one is finished.
+// (bf16: P = P_hi + P_lo as two bf16 MFMAs, so P keeps about 16 bits, and any
+// finite bf16 V is an exact operand).  K rows are loaded straight into the
+// MFMA operand registers; V rows are staged through the wave's LDS and
+// transposed.  Tiles are 32 keys; the next tile's loads are in flight while
+// the current one is finished.
 // Work assignment: for large caches the tiles of every (sequence, KV head)
 // are laid end to end and each resident workgroup streams an equal share of
 // them, crossing sequence ends, so ragged lengths stay balanced over the
@@ -37,7 +38,6 @@ constexpr int kMinTiles = 4;  // balanced mode: at least this many tiles per wor
 constexpr int kWavesPerCU = 12;  // split-kernel workgroups resident per CU (3 per SIMD)
 constexpr int64_t kBalancedMinTiles = 16384;  // auto: balanced split from this many tiles at capacity
 constexpr int kShortSplit = 64;               // auto: keys per split below that
-constexpr int kNoExp = -(1 << 20);  // V exponent of a partial without keys (below any real one)
 // Fused small-cache decode: waves per workgroup; it is chosen for caches of at
 // most kFusedWaves tiles (one tile per wave), or of at most kFusedManyTiles
 // tiles when there are at least kFusedManySegs segments to fill the chip.
@@ -47,7 +47,7 @@ constexpr int kFusedManySegs = 128;
 
 template <int D>
 struct DecodeLds {
-  static constexpr int kVld = kTK + 8;  // V^T row stride (fp16 elements)
+  static constexpr int kVld = kTK + 8;  // V^T row stride (bf16 elements)
   static constexpr size_t kBytes = (size_t)D * kVld * sizeof(uint16_t);
 };
 
@@ -55,11 +55,6 @@ struct DecodeLds {
 // kg holds keys {4kg..4kg+3} of the first 16-key block then the same of the
 // second block, so those eight keys are stored contiguously.
 __device__ __forceinline__ int vt_pos32(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
-
-__device__ __forceinline__ f32x4_t mfma16_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
 
 // A K/V cache row is read once per call.  When the caches are large (STREAM),
 // rows are loaded with the non-temporal hint so the stream does not allocate in
@@ -163,14 +158,13 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 3 : 1) void attn_decode_split_bf
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const int G = Hq / Hkv;
   const int64_t row_stride = (int64_t)Hkv * D;
-  const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-  // Fused mode: a wave's partial (its O^T accumulators at scale 2^-sig, the row
-  // max and sum) as a record of 4 DB + 3 floats per lane, lane-fastest, in the
-  // wave's own V^T region (free once its last tile is done).
-  constexpr int kRec = 4 * DB + 3;
+  // Fused mode: a wave's partial (its O^T accumulators, the row max and sum)
+  // as a record of 4 DB + 2 floats per lane, lane-fastest, in the wave's own
+  // V^T region (free once its last tile is done).
+  constexpr int kRec = 4 * DB + 2;
   static_assert(NW == 1 || (size_t)kRec * 64 * 4 <= S::kBytes, "a wave's record fits its V^T region");
   float* rec = reinterpret_cast<float*>(Vt);
-  auto emit_lds = [&](const f32x4_t (&acc)[DB], float m, float l, int sg) {
+  auto emit_lds = [&](const f32x4_t (&acc)[DB], float m, float l) {
     wave_lds_sync();  // this wave's last V^T reads are done
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -178,7 +172,6 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 3 : 1) void attn_decode_split_bf
       for (int e = 0; e < 4; ++e) rec[(db * 4 + e) * 64 + lane] = acc[db][e];
     rec[(4 * DB) * 64 + lane] = m;
     rec[(4 * DB + 1) * 64 + lane] = l;
-    rec[(4 * DB + 2) * 64 + lane] = __int_as_float(sg);
   };
 
   // Process tiles [tb, tb + ntile) of segment (b, g, qblk) and write its partial to `slot`.
@@ -251,20 +244,9 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 3 : 1) void attn_decode_split_bf
       off_next[0] = block_off(k0 + kTK);
       off_next[1] = block_off(k0 + kTK + 16);
     };
-    // V^T of the tile in fp16 as V * 2^-s, s = the tile's exponent (returned,
-    // wave-uniform); s = 0 for values inside fp16's range
-    auto store_v = [&]() -> int {
-      uint32_t em = 0;
-#pragma unroll
-      for (int j = 0; j < VTASK; ++j)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) em = max(em, bf16x2_expmax(rv[j][jj][e]));
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) em = max(em, (uint32_t)__shfl_xor((int)em, o, 64));
-      const int sv = __builtin_amdgcn_readfirstlane(v_tile_exp(em));
-      auto cv = [&](float x) { return __builtin_amdgcn_ldexpf(x, -sv); };
+    // V^T of the tile in LDS as the raw bf16 values (P.V runs on bf16 matrix
+    // cores, where any finite bf16 V is an exact operand)
+    auto store_v = [&]() {
 #pragma unroll
       for (int j = 0; j < VTASK; ++j) {
         const int ti = lane + j * 64;
@@ -272,35 +254,27 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 3 : 1) void attn_decode_split_bf
         const int cpos = vt_pos32(a * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          // dimension 2e of keys 4a..4a+3 (the low halves), then dimension 2e + 1
           u32x2_t lo, hi;
-          lo[0] = pack_f16(cv(bf16lo(rv[j][0][e])), cv(bf16lo(rv[j][1][e])));
-          lo[1] = pack_f16(cv(bf16lo(rv[j][2][e])), cv(bf16lo(rv[j][3][e])));
-          hi[0] = pack_f16(cv(bf16hi(rv[j][0][e])), cv(bf16hi(rv[j][1][e])));
-          hi[1] = pack_f16(cv(bf16hi(rv[j][2][e])), cv(bf16hi(rv[j][3][e])));
+          lo[0] = __builtin_amdgcn_perm(rv[j][1][e], rv[j][0][e], 0x05040100u);
+          lo[1] = __builtin_amdgcn_perm(rv[j][3][e], rv[j][2][e], 0x05040100u);
+          hi[0] = __builtin_amdgcn_perm(rv[j][1][e], rv[j][0][e], 0x07060302u);
+          hi[1] = __builtin_amdgcn_perm(rv[j][3][e], rv[j][2][e], 0x07060302u);
           st8(Vt + (dg * 8 + 2 * e) * S::kVld + cpos, lo);
           st8(Vt + (dg * 8 + 2 * e + 1) * S::kVld + cpos, hi);
         }
       }
-      return sv;
     };
 
     f32x4_t acc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) acc[i] = f32x4_t{};
     float m_run = -INFINITY, l_run = 0.0f;
-    int sig = 0;  // acc holds O * 2^-sig: the exponent of the V tiles accumulated so far
 
     load_tile(0);
     for (int t = 0; t < nt; ++t) {
       wave_lds_sync();  // the previous tile's V^T reads are done before overwriting
-      const int sv = store_v();
-      if (sv != sig) {  // exact power-of-two rescale to this tile's V exponent
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][e] = __builtin_amdgcn_ldexpf(acc[i][e], sig - sv);
-        sig = sv;
-      }
+      store_v();
       wave_lds_sync();
       const int k0 = kbeg + t * kTK;
       f32x4_t sb[2] = {f32x4_t{}, f32x4_t{}};
@@ -333,26 +307,32 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 3 : 1) void attn_decode_split_bf
 #pragma unroll
         for (int i = 0; i < DB; ++i) acc[i] *= alpha;
       }
-      // P^T operand: slots 0-3 = keys 4*g4+i of block 0, slots 4-7 = the same of block 1
-      u32x4_t pf;
+      // P^T operand: slots 0-3 = keys 4*g4+i of block 0, slots 4-7 = the same of block 1.
+      // P = P_hi + P_lo, both bf16 (P_lo the rounding residual of P_hi): two
+      // bf16 MFMAs carry P to about 16 bits, against fp32 P's row sum
+      u32x4_t ph, pl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int kb = e >> 1, i = (e & 1) * 2;
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[kb][i], c, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[kb][i + 1], c, -m_run));
-        const uint32_t w = pack_f16(p0, p1);
-        pf[e] = w;
-        l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), ones, l_run, false);
+        const uint32_t w = pack_bf16(p0, p1);
+        ph[e] = w;
+        pl[e] = pack_bf16(p0 - bf16lo(w), p1 - bf16hi(w));
+        l_run += p0 + p1;
       }
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        acc[db] = mfma16_f16(ld16(Vt + (db * 16 + l16) * S::kVld + g4 * 8), pf, acc[db]);
+      for (int db = 0; db < DB; ++db) {
+        const u32x4_t vf = ld16(Vt + (db * 16 + l16) * S::kVld + g4 * 8);
+        acc[db] = mfma16_bf16(vf, ph, acc[db]);
+        acc[db] = mfma16_bf16(vf, pl, acc[db]);
+      }
     }
 
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     if constexpr (NW > 1) {
-      emit_lds(acc, m_run, l_tot, sig);
+      emit_lds(acc, m_run, l_tot);
     } else if (hvalid) {
       const int64_t pidx = ((int64_t)b * Hq + h) * n_slot + slot;
       float* po = part_o + pidx * D;
@@ -361,7 +341,7 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 3 : 1) void attn_decode_split_bf
         st16(po + db * 16 + 4 * g4, u32x4_t{__float_as_uint(acc[db][0]), __float_as_uint(acc[db][1]),
                                             __float_as_uint(acc[db][2]), __float_as_uint(acc[db][3])});
       if (g4 == 0)
-        st16(part_ml + pidx * 4, u32x4_t{__float_as_uint(m_run), __float_as_uint(l_tot), (uint32_t)sig, 0u});
+        st16(part_ml + pidx * 4, u32x4_t{__float_as_uint(m_run), __float_as_uint(l_tot), 0u, 0u});
     }
   };
 
@@ -379,43 +359,36 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 3 : 1) void attn_decode_split_bf
       f32x4_t zero[DB];
 #pragma unroll
       for (int i = 0; i < DB; ++i) zero[i] = f32x4_t{};
-      emit_lds(zero, -INFINITY, 0.0f, kNoExp);
+      emit_lds(zero, -INFINITY, 0.0f);
     }
     __syncthreads();
-    // Merge, exactly as the combine kernel does: the largest max M and V
-    // exponent S over the waves, O = sum_w 2^(m_w - M) 2^(s_w - S) acc_w / L,
-    // L = sum_w 2^(m_w - M) l_w, then O 2^S.  Wave w' merges the 16-row blocks
-    // db = w', w' + NW, ...; lane (head column l16, group g4) as in a record.
+    // Merge, exactly as the combine kernel does: the largest max M over the
+    // waves, O = sum_w 2^(m_w - M) acc_w / L, L = sum_w 2^(m_w - M) l_w.  Wave
+    // w' merges the 16-row blocks db = w', w' + NW, ...; lane (head column
+    // l16, group g4) as in a record.
     const int col = qblk * 16 + l16;
     const bool hvalid = col < G;
     const int h = g * G + (hvalid ? col : 0);
     const float* recs = reinterpret_cast<const float*>(smem);
     constexpr int kRegion = kVtElems / 2;  // floats per wave region
     float M = -INFINITY;
-    int Sx = kNoExp;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      M = fmaxf(M, recs[w * kRegion + (4 * DB) * 64 + lane]);
-      Sx = max(Sx, __float_as_int(recs[w * kRegion + (4 * DB + 2) * 64 + lane]));
-    }
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, recs[w * kRegion + (4 * DB) * 64 + lane]);
     float L = 0.0f, wt[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float mw = recs[w * kRegion + (4 * DB) * 64 + lane];
-      const float a = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-      L = __builtin_fmaf(a, recs[w * kRegion + (4 * DB + 1) * 64 + lane], L);
-      const int sw = __float_as_int(recs[w * kRegion + (4 * DB + 2) * 64 + lane]);
-      wt[w] = a == 0.0f ? 0.0f : __builtin_amdgcn_ldexpf(a, sw - Sx);
+      wt[w] = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      L = __builtin_fmaf(wt[w], recs[w * kRegion + (4 * DB + 1) * 64 + lane], L);
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no keys: O = 0
-    const int osh = L > 0.0f ? Sx : 0;
     for (int db = wave; db < DB; db += NW) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) v = __builtin_fmaf(wt[w], recs[w * kRegion + (db * 4 + e) * 64 + lane], v);
-        const float r = __builtin_amdgcn_ldexpf(v * inv, osh);
+        const float r = v * inv;
         if (hvalid) {
           const int64_t oi = ((int64_t)b * Hq + h) * D + db * 16 + 4 * g4 + e;
           if constexpr (OUT_BF16)
@@ -549,12 +522,9 @@ __global__ __launch_bounds__(64) void attn_decode_split_f32_kernel(
 // Combine the partials of every unit: one wave per (sequence, query head).
 // The number of units of (b, h) follows from the same work split the split
 // kernel used (one pass over seq_lens).  Then, 16 units at a time, every lane
-// loads one unit's (max, sum, V exponent) and its D/64 elements of all 16
-// units' partial outputs at once, so the statistics and the outputs cost one
-// round trip together; the weights are applied once the wave's maximum is
-// known.  A unit's partial output is stored at the scale 2^-s of its V
-// exponent s; the sum is kept at the largest exponent seen, with exact
-// power-of-two rescaling (all exponents 0 for V inside fp16's range).
+// loads one unit's (max, sum) and its D/64 elements of all 16 units' partial
+// outputs at once, so the statistics and the outputs cost one round trip
+// together; the weights are applied once the wave's maximum is known.
 // A sequence with no keys has no units: O = 0, LSE = -inf.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
@@ -574,13 +544,11 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
   // count (stale or never written) are replaced below, never used.
   const int pre = min(U, n_slot);
   float m_pre = -INFINITY, l_pre = 0.0f, v_pre[U][EPL] = {};
-  int s_pre = 0;
   if (pre > 0) {
     const int sl = lane < pre ? lane : 0;
     const u32x4_t st = ld16(ml + 4 * sl);
     m_pre = __uint_as_float(st[0]);
     l_pre = __uint_as_float(st[1]);
-    s_pre = (int)st[2];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -614,21 +582,17 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     n = min(n, n_slot);
   }
 
-  constexpr int kNoUnit = -(1 << 20);  // V exponent of a lane without a unit (below any real one)
   float M = -INFINITY, L = 0.0f;  // running max (log2 units) and sum over the rounds so far
-  int Sx = INT_MIN;               // largest V exponent so far: acc holds O * L * 2^-Sx
-  float acc[EPL];
+  float acc[EPL];                 // O * L
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
   for (int c0 = 0; c0 < n; c0 += U) {
     const int cnt = min(U, n - c0);
     // this lane's unit statistics (lanes >= cnt: none) and every unit's outputs
     float m_l, l_l, v[U][EPL];
-    int s_l;
     if (c0 == 0) {
       m_l = lane < cnt ? m_pre : -INFINITY;
       l_l = lane < cnt ? l_pre : 0.0f;
-      s_l = lane < cnt ? s_pre : kNoUnit;
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -638,48 +602,37 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
       const u32x4_t st = ld16(ml + 4 * sl);
       m_l = lane < cnt ? __uint_as_float(st[0]) : -INFINITY;
       l_l = lane < cnt ? __uint_as_float(st[1]) : 0.0f;
-      s_l = lane < cnt ? (int)st[2] : kNoUnit;
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) v[u][e] = u < cnt ? po[(int64_t)(c0 + u) * D + e * 64 + lane] : 0.0f;
     }
     float mr = m_l;
-    int sr = s_l;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      mr = fmaxf(mr, __shfl_xor(mr, off, 64));
-      sr = max(sr, __shfl_xor(sr, off, 64));
-    }
+    for (int off = 32; off > 0; off >>= 1) mr = fmaxf(mr, __shfl_xor(mr, off, 64));
     const float Mn = fmaxf(M, mr);
-    const int Sn = max(Sx, sr);
     // rescale what the earlier rounds accumulated (no earlier round: factor 1)
     const float a = M == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-    const int ash = Sx == INT_MIN ? 0 : Sx - Sn;
     const float w = lane < cnt ? __builtin_amdgcn_exp2f(m_l - Mn) : 0.0f;
-    // weight of the unit's output: w * 2^(s - Sn), exactly w when s = Sn
-    const float wo = lane < cnt ? __builtin_amdgcn_ldexpf(w, s_l - Sn) : 0.0f;
     float lw = w * l_l;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off, 64);
     L = L * a + lw;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = __builtin_amdgcn_ldexpf(acc[e] * a, ash);
+    for (int e = 0; e < EPL; ++e) acc[e] *= a;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wu = __shfl(wo, u, 64);
+      const float wu = __shfl(w, u, 64);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(wu, v[u][e], acc[e]);
     }
     M = Mn;
-    Sx = Sn;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no keys: O = 0
-  const int osh = Sx == INT_MIN ? 0 : Sx;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const int64_t oi = bh * D + e * 64 + lane;
-    const float r = __builtin_amdgcn_ldexpf(acc[e] * inv, osh);
+    const float r = acc[e] * inv;
     if constexpr (OUT_BF16)
       static_cast<uint16_t*>(o)[oi] = f32_to_bf16(r);
     else

@@ -1,19 +1,20 @@
 """V beyond the 16-bit operand range, and decode of empty sequences.
 
-Every bf16 attention path multiplies P by V on fp16 matrix cores.  Each V tile
-is converted as V * 2^-s with its own power-of-two exponent s (0 inside fp16's
-range), and the accumulator follows with exact power-of-two rescales, so any
-finite bf16 V gives a finite, exact-to-rounding result:
+The bf16 prefill paths multiply P by V on fp16 matrix cores: each V tile is
+converted as V * 2^-s with its own power-of-two exponent s (0 inside fp16's
+range), and the accumulator follows with exact power-of-two rescales.  The
+bf16 decode multiplies on bf16 matrix cores, where V needs no conversion.
+Either way any finite bf16 V gives a finite, exact-to-rounding result:
 
 * O is linear in V (the oracle's own pin), so scaling V by 2^e must scale the
   kernel's fp32 output by exactly 2^e and leave the LSE bit-identical: the same
-  fp16 operands, the same sums, only the exponent moves.  Checked for e = 20
+  significands, the same sums, only the exponent moves.  Checked for e = 20
   (|v| up to ~4e6, beyond fp16's 65504) and e = -40 (tiny values that fp16
   would flush), on every entry point;
 * V mixing magnitudes from 1e-12 to 3e30 within one head matches the fp64
-  oracle within the bf16 bar scaled to the data's magnitude.  One exponent
-  serves a whole tile, so a value far below its tile's largest |v| is held
-  to that largest value: each output row must be within 5e-3 (the bar's 2e-2
+  oracle within the bf16 bar scaled to the data's magnitude.  In the prefill
+  one exponent serves a whole tile, so a value far below its tile's largest
+  |v| is held to that largest value: each output row must be within 5e-3 (the bar's 2e-2
   at the O(4) magnitude of N(0,1) data) of the largest |v| in the V tiles the
   row reads -- for a prefill row the whole 64-key tiles up to its last
   visible key, masked keys of the diagonal tile included; for decode the
