@@ -20,8 +20,10 @@ Then every configuration is measured on its own (`configs`; skipped with
 --no-configs): the tiny fp32 layer, the TinyLlama-shaped layers (projection,
 prefill, whole layer eager and as one HIP graph), the MQA decode loop (eager
 and as one HIP graph), the
-Llama-2-7B decode sweep (cold caches) with its projections, and the four
-long-context prefills in bf16 and FP8.  Each carries its roofline fraction.
+Llama-2-7B decode sweep (cold caches) with its projections, the four
+long-context prefills in bf16 and FP8, and two packed variable-length batches
+(persistent heaviest-first workers against the per-row-block grid).  Each
+carries its roofline fraction.
 
 Prints ONE JSON line: `value` is the whole step's algorithmic TFLOP/s (prefill
 + GEMM + decode FLOPs over the step time); `roofline` is the dominant kernel
@@ -515,6 +517,35 @@ def measure_configs(m, W, torch, np, dev, stream, timer, up, kv8):
         log(json.dumps({"config": name, **res[name]}))
         del q, k, v, o, wsp, ws8
         torch.cuda.empty_cache()
+    # -- packed variable-length batches (causal): the persistent heaviest-first
+    #    workers (workspace with the row-block schedule) against the grid of one
+    #    workgroup per row block (workspace of V images only).  TinyLlama heads
+    #    over 8 sequences of U{128..2048} tokens; long-context heads over 16
+    #    sequences of U{256..8192}
+    for name, n, lo, hi, H_q, H_kv, d, seed in (("varlen_tinyllama_8", 8, 128, 2048, 32, 4, 64, 1007),
+                                                 ("varlen_long_16", 16, 256, 8192, 16, 4, 128, 1008)):
+        lens = np.random.default_rng(seed).integers(lo, hi, size=n, endpoint=True).astype(np.int32)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        tot, L = int(cu[-1]), int(lens.max())
+        g = torch.Generator(device=dev).manual_seed(seed)
+        q = torch.randn(tot, H_q, d, generator=g, device=dev).to(torch.bfloat16)
+        k = torch.randn(tot, H_kv, d, generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn(tot, H_kv, d, generator=g, device=dev).to(torch.bfloat16)
+        cu_d = torch.from_numpy(cu).to(dev)
+        o = torch.empty_like(q)
+        ws_s = torch.empty(m.prefill_varlen_workspace_bytes(n, L, tot, H_q, H_kv, d), dtype=torch.uint8, device=dev)
+        ws_g = torch.empty(m.prefill_workspace_bytes(n, L, H_kv, d), dtype=torch.uint8, device=dev)
+        fl = sum(prefill_flops(1, H_q, d, int(x), int(x), True) for x in lens)
+        us_s = timer.warm(lambda: m.gqa_attn_prefill_varlen(q, k, v, cu_d, cu_d, L, L, out=o, workspace=ws_s))
+        us_g = timer.warm(lambda: m.gqa_attn_prefill_varlen(q, k, v, cu_d, cu_d, L, L, out=o, workspace=ws_g))
+        res[name] = {"lengths": lens.tolist(), "H_q": H_q, "H_kv": H_kv, "d": d,
+                     "scheduled": {"us": round(us_s, 2), "tflops": round(fl / us_s / 1e6, 1),
+                                   "frac": round(fl / us_s / 1e6 / PEAK_BF16_TFLOPS, 4)},
+                     "grid": {"us": round(us_g, 2), "tflops": round(fl / us_g / 1e6, 1)},
+                     "speedup": round(us_g / us_s, 3)}
+        log(json.dumps({"config": name, **res[name]}))
+        del q, k, v, o, ws_s, ws_g
+        torch.cuda.empty_cache()
     res["seconds"] = round(time.time() - t_cfg, 1)
     return res
 
@@ -645,7 +676,8 @@ def extra_sweep(m, W, torch, np, dev, timer):
     cu_d = torch.from_numpy(cu).to(dev)
     o = torch.empty_like(q)
     L = int(lens.max())
-    ws = torch.empty(m.prefill_workspace_bytes(len(lens), L, H_kv, d), dtype=torch.uint8, device=dev)
+    ws = torch.empty(m.prefill_varlen_workspace_bytes(len(lens), L, tot, H_q, H_kv, d), dtype=torch.uint8,
+                     device=dev)
     fl = sum(4.0 * H_q * d * n * (n + 1) / 2 for n in lens.tolist())
     us_v = timer.warm(lambda: m.gqa_attn_prefill_varlen(q, k, v, cu_d, cu_d, L, L, causal=True, out=o, workspace=ws))
     views = [(q[None, cu[b]:cu[b + 1]], k[None, cu[b]:cu[b + 1]], v[None, cu[b]:cu[b + 1]], o[None, cu[b]:cu[b + 1]])

@@ -233,13 +233,33 @@ mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* 
  *                 outside the buffers.
  * o    [total_q, H_q, d] contiguous, dtype o_dtype (bf16 or fp32)
  * lse  [H_q, total_q] fp32 natural-log normalisers, or NULL
- * workspace: gqa_attn_prefill_workspace_bytes(B, max_L_kv, H_kv, d, MQKV_BF16) bytes
+ * workspace: at least gqa_attn_prefill_workspace_bytes(B, max_L_kv, H_kv, d,
+ *   MQKV_BF16) bytes (the V images).  With at least
+ *   gqa_attn_prefill_varlen_workspace_bytes(B, max_L_kv, total_q, H_q, H_kv, d)
+ *   bytes (nonzero for B <= 1024) and lengths that differ (total_q !=
+ *   B*max_L_q or total_kv != B*max_L_kv) the call also plans a schedule
+ *   there: every row block of the batch (a sequence's query block of one KV
+ *   head group) is listed by the key tiles it runs, most first, and
+ *   persistent workgroups, one per resident slot of the GPU, take the list in
+ *   that order, each claiming its next block with one atomic increment of a
+ *   counter in the workspace (the FlashAttention-3 page's closing section
+ *   lists persistent kernels and variable-length batches among its further
+ *   optimisations).  Otherwise the grid has one workgroup per row block of a
+ *   max_L_q sequence, sequence by sequence, the heaviest blocks of each
+ *   sequence first.  Either way each row is computed alike (d = 128:
+ *   bit-identical results; d = 64 small batches may split a block's keys
+ *   between two waves on the grid path, which rounds differently).  With
+ *   malformed cu_seqlens (decreasing, or lengths summing past total_q) rows
+ *   may be left unwritten; no access leaves the buffers.
  * A query row that sees no key (a sequence with no keys, or L_q > L_kv under
  * the causal mask) gets O = 0 and LSE = -inf.  Each sequence's result is
  * bit-identical to a gqa_attn_prefill call on that sequence alone.
  * fp32 inputs return MQKV_ERR_UNSUPPORTED.  B == 0, max_L_q == 0 or
  * total_q == 0 is a no-op; max_L_kv >= 1, total_kv >= 1.
  */
+size_t gqa_attn_prefill_varlen_workspace_bytes(int32_t B, int32_t max_L_kv, int32_t total_q, int32_t H_q,
+                                               int32_t H_kv, int32_t d);
+
 mqkv_status gqa_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                                     int32_t B, int32_t max_L_q, int32_t max_L_kv, int32_t total_q,

@@ -30,6 +30,7 @@ MQKV_F32, MQKV_BF16 = 0, 1
 EXPORTS = ("qkv_proj", "qkv_proj_workspace_bytes", "qkv_proj_append", "qkv_proj_rope", "qkv_proj_append_rope",
            "gqa_attn_prefill_workspace_bytes",
            "gqa_attn_prefill", "gqa_attn_decode_paged", "gqa_attn_prefill_varlen",
+           "gqa_attn_prefill_varlen_workspace_bytes",
            "gqa_attn_prefill_fp8_workspace_bytes", "gqa_attn_prefill_fp8",
            "gqa_attn_decode_workspace_bytes", "gqa_attn_decode", "gqa_attn_decode_noalloc", "mqkv_status_string",
            "mqkv_last_error", "mqkv_abi_version")
@@ -73,6 +74,8 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                             i64, i64, i32, f32, i32, i32, vp, sz, vp]
     lib.gqa_attn_prefill_varlen.restype = i32
+    lib.gqa_attn_prefill_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.gqa_attn_prefill_varlen_workspace_bytes.restype = sz
     lib.gqa_attn_prefill_fp8_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.gqa_attn_prefill_fp8_workspace_bytes.restype = sz
     lib.gqa_attn_prefill_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, i64, i32,
@@ -293,6 +296,12 @@ def prefill_workspace_bytes(B: int, L_kv: int, H_kv: int, d: int, dtype_code: in
     return int(lib.gqa_attn_prefill_workspace_bytes(B, L_kv, H_kv, d, dtype_code))
 
 
+def prefill_varlen_workspace_bytes(B: int, max_L_kv: int, total_q: int, H_q: int, H_kv: int, d: int) -> int:
+    """Workspace of a packed-batch prefill that also holds its row-block schedule
+    (persistent heaviest-first workers); 0 when none is planned (B > 1024)."""
+    return int(lib.gqa_attn_prefill_varlen_workspace_bytes(B, max_L_kv, total_q, H_q, H_kv, d))
+
+
 def gqa_attn_prefill(q, k, v, causal: bool = True, scale: Optional[float] = None,
                      return_lse: bool = False, out_dtype=None, out=None, workspace=None):
     """Exact grouped-query attention over whole sequences.
@@ -336,13 +345,15 @@ def gqa_attn_prefill(q, k, v, causal: bool = True, scale: Optional[float] = None
 
 def gqa_attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_L_q: int, max_L_kv: int,
                             causal: bool = True, scale: Optional[float] = None, return_lse: bool = False,
-                            out_dtype=None, out=None, workspace=None):
+                            out_dtype=None, out=None, workspace=None, schedule: bool = True):
     """Exact grouped-query attention over a packed batch of variable-length sequences.
 
     q [total_q, H_q, d], k/v [total_kv, H_kv, d] (token strides may be views into
     qkv); cu_seqlens_q / cu_seqlens_kv [B+1] int32 on the device.  Sequence b owns
     tokens [cu[b], cu[b+1]).  Returns o [total_q, H_q, d] and, if asked,
-    lse [H_q, total_q] float32."""
+    lse [H_q, total_q] float32.  When the workspace is allocated here, `schedule`
+    sizes it for the row-block schedule (persistent heaviest-first workers);
+    schedule=False sizes it for the V images only (one workgroup per row block)."""
     torch = _torch()
     _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_kv, out, workspace)
     total_q, H_q, d = q.shape
@@ -370,7 +381,9 @@ def gqa_attn_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_L_q: int, 
         raise ValueError("out must be a contiguous [total_q, H_q, d] tensor of out_dtype")
     lse = torch.empty(H_q, total_q, dtype=torch.float32, device=q.device) if return_lse else None
     if workspace is None:
-        need = prefill_workspace_bytes(max(B, 0), max_L_kv, H_kv, d, _dtype_code(q.dtype))
+        need = prefill_varlen_workspace_bytes(max(B, 0), max_L_kv, total_q, H_q, H_kv, d) if schedule else 0
+        if need == 0:
+            need = prefill_workspace_bytes(max(B, 0), max_L_kv, H_kv, d, _dtype_code(q.dtype))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = lib.gqa_attn_prefill_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                      lse.data_ptr() if lse is not None else None, cu_seqlens_q.data_ptr(),

@@ -241,6 +241,13 @@ mqkv_status gqa_attn_prefill(const void* q, const void* k, const void* v, void* 
   return hip_status(mqkv::launch_prefill(a, (hipStream_t)stream), "gqa_attn_prefill launch");
 }
 
+size_t gqa_attn_prefill_varlen_workspace_bytes(int32_t B, int32_t max_L_kv, int32_t total_q, int32_t H_q,
+                                               int32_t H_kv, int32_t d) {
+  if (B < 1 || max_L_kv < 1 || total_q < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || (d != 64 && d != 128))
+    return 0;
+  return mqkv::prefill_varlen_workspace_bytes(B, max_L_kv, total_q, H_q, H_kv, d);
+}
+
 mqkv_status gqa_attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B,
                                     int32_t max_L_q, int32_t max_L_kv, int32_t total_q, int32_t total_kv,

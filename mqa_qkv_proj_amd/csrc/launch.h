@@ -71,6 +71,9 @@ struct PrefillArgs {
 };
 size_t prefill_fp8_workspace_bytes(int B, int Lq, int Lkv, int Hq, int Hkv, int d);
 size_t prefill_workspace_bytes(int B, int Lkv, int Hkv, int d, bool bf16);
+// V images plus the row-block schedule of a packed batch (persistent
+// workers); 0 when no schedule is planned for the shape (B > 1024).
+size_t prefill_varlen_workspace_bytes(int B, int Lkv_max, int total_q, int Hq, int Hkv, int d);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 struct DecodeArgs {

@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
               "gqa_attn_prefill",
               "gqa_attn_prefill_workspace_bytes",
               "gqa_attn_decode", "gqa_attn_decode_workspace_bytes", "gqa_attn_decode_paged",
-              "gqa_attn_prefill_varlen", "gqa_attn_prefill_fp8", "gqa_attn_prefill_fp8_workspace_bytes",
+              "gqa_attn_prefill_varlen", "gqa_attn_prefill_varlen_workspace_bytes",
+              "gqa_attn_prefill_fp8", "gqa_attn_prefill_fp8_workspace_bytes",
               "mqkv_status_string", "mqkv_last_error", "mqkv_abi_version"):
         assert n in names
 
@@ -213,6 +214,29 @@ def test_prefill_workspace_query(lib):
     assert f(2, 100, 4, 128, 0) == 0          # fp32 inputs need none
     assert f(2, 100, 4, 96) == 0              # unsupported d
     assert f(2, 0, 4, 128) == 0               # L_kv < 1
+
+
+def test_prefill_varlen_workspace_query(lib):
+    """The packed-batch workspace: the V images (256-byte aligned), then a
+    4-word header and one (sequence, query block) pair of int32 per row block.
+    Row blocks hold P = W*32/F query positions (W = 8 waves at d = 128, 4 at
+    d = 64; F = the largest power of two dividing G, at most 32), and the list
+    holds B + ceil(total_q / P) of them, enough for any lengths summing to
+    total_q."""
+    f = lib.prefill_varlen_workspace_bytes
+    img = lib.prefill_workspace_bytes
+    r256 = lambda n: (n + 255) // 256 * 256
+    # d = 64, G = 8: F = 8, P = 4*32/8 = 16; cap = 8 + 8000/16 = 508 pairs
+    assert f(8, 2048, 8000, 32, 4, 64) == r256(img(8, 2048, 4, 64)) + r256(4 * (4 + 2 * 508))
+    # d = 128, G = 4: F = 4, P = 8*32/4 = 64; cap = 3 + ceil(1000/64) = 19
+    assert f(3, 700, 1000, 16, 4, 128) == r256(img(3, 700, 4, 128)) + r256(4 * (4 + 2 * 19))
+    # G = 6: F = 2, P = 128 at d = 128
+    assert f(2, 100, 300, 12, 2, 128) == r256(img(2, 100, 2, 128)) + r256(4 * (4 + 2 * (2 + 3)))
+    assert f(1024, 64, 10, 8, 2, 128) > 0
+    assert f(1025, 64, 10, 8, 2, 128) == 0    # no schedule past 1024 sequences
+    assert f(0, 64, 10, 8, 2, 128) == 0
+    assert f(2, 64, 10, 8, 3, 128) == 0       # H_q % H_kv
+    assert f(2, 64, 10, 8, 2, 96) == 0        # d
 
 
 def test_decode_workspace_query(lib):

@@ -106,3 +106,94 @@ def test_varlen_bf16_output_on_qkv_views(m):
     o = m.gqa_attn_prefill_varlen(q, k, v, cu_d, cu_d, max(lens), max(lens), causal=True)
     ref, _ = oracle.attention_varlen(host(q), host(k), host(v), cu, cu, True, 1.0 / math.sqrt(d))
     assert_close(host(o), ref, "bf16", "varlen on qkv views")
+
+
+# H_q, H_kv, d, causal, L_q lengths, L_kv lengths (None: the same), seed
+SCHEDULED = [
+    # 300 sequences (some empty): the planning scans run over more sequences than threads, and the
+    # list holds more row blocks than there are persistent workers, so each worker claims several
+    (8, 2, 128, True, "many", None, 101),
+    (8, 2, 128, False, [200, 77, 0, 513, 64], [90, 300, 5, 513, 1], 102),
+    # the TinyLlama-shaped batch: 8 sequences of 128..2048 tokens, four KV heads of 8 query heads
+    (32, 4, 64, True, "tinyllama8", None, 103),
+    # a long and a short causal sequence
+    (32, 4, 64, True, [2048, 1000], None, 104),
+]
+
+
+def _lengths(spec, seed):
+    rng = np.random.default_rng(seed)
+    if spec == "many":
+        lens = rng.integers(0, 300, size=300, endpoint=True)
+        lens[[0, 17, 299]] = 0
+        return lens.tolist()
+    if spec == "tinyllama8":
+        return rng.integers(128, 2048, size=8, endpoint=True).tolist()
+    return spec
+
+
+@pytest.mark.parametrize("H_q,H_kv,d,causal,lq,lk,seed", SCHEDULED)
+def test_varlen_schedule_matches_grid_path_and_oracle(m, H_q, H_kv, d, causal, lq, lk, seed):
+    """The persistent heaviest-first workers (workspace with a schedule) against
+    the grid of one workgroup per row block (workspace of V images only): the
+    same per-row arithmetic, so bit-identical outputs and LSE; sampled
+    sequences against the oracle."""
+    import torch
+    lq = _lengths(lq, seed)
+    lk = lq if lk is None else lk
+    say("prefill varlen schedule", H_q, H_kv, d, causal, len(lq), "sequences", sum(lq), "queries")
+    cq, ck = _cu(lq), _cu(lk)
+    tq, tk = int(cq[-1]), int(ck[-1])
+    q = W.round_bf16(W.normal(seed, 1, (tq, H_q, d)))
+    k = W.round_bf16(W.normal(seed, 2, (tk, H_kv, d)))
+    v = W.round_bf16(W.normal(seed, 3, (tk, H_kv, d)))
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    cqd, ckd = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    scale = 1.0 / math.sqrt(d)
+    B = len(lq)
+    need = m.prefill_varlen_workspace_bytes(B, max(lk), tq, H_q, H_kv, d)
+    assert need > m.prefill_workspace_bytes(B, max(lk), H_kv, d)
+    # stale bytes everywhere, the schedule's header included: the plan rewrites all it reads
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    kw = dict(causal=causal, scale=scale, return_lse=True, out_dtype=torch.float32)
+    o_s, l_s = m.gqa_attn_prefill_varlen(qd, kd, vd, cqd, ckd, max(lq), max(lk), workspace=ws, **kw)
+    o_s2, l_s2 = m.gqa_attn_prefill_varlen(qd, kd, vd, cqd, ckd, max(lq), max(lk), workspace=ws, **kw)
+    o_g, l_g = m.gqa_attn_prefill_varlen(qd, kd, vd, cqd, ckd, max(lq), max(lk), schedule=False, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_s2) and torch.equal(l_s, l_s2), "a second call on the same workspace differs"
+    assert torch.equal(o_s, o_g), "scheduled and grid outputs differ"
+    assert torch.equal(l_s, l_g), "scheduled and grid LSE differ"
+    # oracle on the longest sequence and a few others
+    order = np.argsort(lq)[::-1]
+    pick = [int(b) for b in order[:2]] + [int(b) for b in np.random.default_rng(seed).choice(B, min(B, 3), False)]
+    got, gl = host(o_s), host(l_s)
+    for b in sorted(set(pick)):
+        if lq[b] == 0:
+            continue
+        sl_q, sl_k = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        ref, ref_lse = oracle.attention_varlen(q[sl_q], k[sl_k], v[sl_k], _cu([lq[b]]), _cu([lk[b]]), causal, scale)
+        assert_close(got[sl_q], ref, "bf16", f"scheduled sequence {b} ({lq[b]} x {lk[b]})")
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isinf(gl[:, sl_q]), ~fin)
+        assert_close(gl[:, sl_q][fin], ref_lse[fin], "bf16", f"scheduled sequence {b} LSE", max_abs=1e-3, rel_l2=1e-4)
+
+
+@pytest.mark.parametrize("B,L", [(1, 2048), (2, 1024)])
+def test_varlen_equal_lengths_equal_fixed_length_call(m, B, L):
+    """Packed sequences all at the maximum length (TinyLlama-shaped heads) take
+    the grid even with a schedule-sized workspace, and equal the fixed-length
+    call on the same rows bit for bit."""
+    import torch
+    H_q, H_kv, d = 32, 4, 64
+    say("prefill varlen equal lengths vs fixed length", B, L, H_q, H_kv, d)
+    q = dev(W.round_bf16(W.normal(105, 1, (B * L, H_q, d))), "bf16")
+    k = dev(W.round_bf16(W.normal(105, 2, (B * L, H_kv, d))), "bf16")
+    v = dev(W.round_bf16(W.normal(105, 3, (B * L, H_kv, d))), "bf16")
+    cu = torch.arange(0, B * L + 1, L, dtype=torch.int32, device="cuda")
+    o_p, l_p = m.gqa_attn_prefill_varlen(q, k, v, cu, cu, L, L, causal=True, return_lse=True)
+    o_f, l_f = m.gqa_attn_prefill(q.view(B, L, H_q, d), k.view(B, L, H_kv, d), v.view(B, L, H_kv, d),
+                                  causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p, o_f.view(B * L, H_q, d))
+    # LSE [H_q, total_q] against [B, H_q, L]
+    assert torch.equal(l_p, l_f.permute(1, 0, 2).reshape(H_q, B * L))
