@@ -11,6 +11,7 @@ struct SkinnyPlan {
   bool stream16;  // 16-column streaming kernel (M <= 32, K % 128 == 0), no k split
   bool wide;      // 8-wave workgroups over all of K (K % 256 == 0, N % 64 == 0), no k split
   int wide_mb;    // 16-row blocks per wide tile (1 or 2)
+  int rt_ns;      // > 0: register-transpose kernel, 32-row k steps per wave (ksplit k ranges)
   int nbm;        // 32-row blocks
   int ksplit;     // k ranges
   int krange;     // rows of W per k range (a multiple of 128)

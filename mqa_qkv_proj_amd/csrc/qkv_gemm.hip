@@ -883,6 +883,136 @@ __global__ __launch_bounds__(kSkThreads) void qkv_gemm_skinny_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------- decode width, register transpose
+// M <= 32, K % 256 == 0, N % 64 == 0, too wide for the 16-column stream (the
+// grouped-query decode projections): the weight is the whole cost.  MFMA
+// 16x16x32 wants eight consecutive k of one column per lane, and W is stored
+// k-major, so each lane loads eight 8-byte row pieces (rows kb*8 .. kb*8+7 of
+// a 32-row step, columns 4j .. 4j+3) and builds the operands of four MFMAs
+// from them with byte permutes: MFMA t takes column 4j + t in lane j.  The
+// outputs of the four MFMAs are four interleaved column sets, so nothing
+// passes through LDS and no barrier is needed until the end: a wave loads its
+// whole slice (NS steps) at once and multiplies as the pieces arrive.  A
+// workgroup of 8 waves covers 64 columns and a k range of 8*NS*32 rows (wave
+// w: the w-th eighth); the waves' sums are added in LDS in wave order and
+// written as one fp32 partial per k range, which qkv_gemm_reduce_kernel adds
+// (fixed order) with the bias and epilogue.
+constexpr int kRtBN = 64, kRtWaves = 8, kRtStep = 32;
+
+__device__ __forceinline__ u32x2_t bld8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+template <int MB, int NS>
+__global__ __launch_bounds__(kRtWaves * 64) void qkv_gemm_rt_kernel(const uint16_t* __restrict__ x,
+                                                                    const uint16_t* __restrict__ w,
+                                                                    float* __restrict__ part, int M, int K, int N,
+                                                                    int nbn) {
+  constexpr int R = MB * 16;  // rows of x covered
+  __shared__ __align__(16) float red[4 * R * kRtBN];  // four waves' sums
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, kb = lane >> 4;
+  // neighbouring column strips of one k range go to one XCD
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bn = lid % nbn, ks = lid / nbn;
+  const int n0 = bn * kRtBN;
+  const int kw = (ks * kRtWaves + wave) * (NS * kRtStep) + kb * 8;  // this lane's first row of W
+  const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, (uint32_t)((int64_t)K * N * 2));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, xbytes);
+  u32x2_t wv[NS][8];
+  u32x4_t xv[NS][MB];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      wv[s][r] = bld8(wr, (uint32_t)(((int64_t)(kw + s * kRtStep + r) * N + n0 + 4 * j) * 2));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = mb * 16 + j;
+      xv[s][mb] = bld16(xr, m < M ? (uint32_t)(((int64_t)m * K + kw + s * kRtStep) * 2) : xbytes);
+    }
+  }
+  f32x4_t acc[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[mb][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // column 4j + t of rows 0..7: dword q packs rows 2q (low half) and 2q + 1
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      u32x4_t b;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b[q] = __builtin_amdgcn_perm(wv[s][2 * q + 1][t >> 1], wv[s][2 * q][t >> 1], sel);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][t] = mfma16_bf16(xv[s][mb], b, acc[mb][t]);
+    }
+  }
+  // acc[mb][t][e] = sum for row mb*16 + 4kb + e, column n0 + 4j + t.  The
+  // eight waves' sums are added pairwise through LDS in a fixed order (wave w
+  // adds wave w + 4's, then w + 2's, then w + 1's, each staged in LDS slot w),
+  // and wave 0 writes the partial: four
+  // consecutive columns per (row, lane), 16-byte stores.
+  auto put = [&](int to) {
+    float* dst = red + to * (R * kRtBN) + lane * 4;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        st16(dst + (mb * 4 + e) * 256,
+             u32x4_t{__float_as_uint(acc[mb][0][e]), __float_as_uint(acc[mb][1][e]), __float_as_uint(acc[mb][2][e]),
+                     __float_as_uint(acc[mb][3][e])});
+  };
+  auto take = [&](int from) {
+    const float* src = red + from * (R * kRtBN) + lane * 4;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x4_t v = __builtin_bit_cast(f32x4_t, ld16(src + (mb * 4 + e) * 256));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[mb][t][e] += v[t];
+      }
+  };
+#pragma unroll
+  for (int half = 4; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) put(wave - half);
+    __syncthreads();
+    if (wave < half) take(wave);
+    __syncthreads();
+  }
+  if (wave != 0) return;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = mb * 16 + 4 * kb + e;
+      if (row < M)
+        st16(part + ((int64_t)ks * M + row) * N + n0 + 4 * j,
+             u32x4_t{__float_as_uint(acc[mb][0][e]), __float_as_uint(acc[mb][1][e]), __float_as_uint(acc[mb][2][e]),
+                     __float_as_uint(acc[mb][3][e])});
+    }
+}
+
+template <int MB>
+static hipError_t launch_rt(const SkinnyPlan& p, const void* x, const void* w, void* ws, int M, int K, int N,
+                            hipStream_t s) {
+  const int nbn = N / kRtBN;
+  const dim3 grid((unsigned)(nbn * p.ksplit)), block(kRtWaves * 64);
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, (const uint16_t*)x, (const uint16_t*)w, (float*)ws, M, K, N, nbn);
+  };
+  switch (p.rt_ns) {
+    case 1: args(qkv_gemm_rt_kernel<MB, 1>); break;
+    case 2: args(qkv_gemm_rt_kernel<MB, 2>); break;
+    default: args(qkv_gemm_rt_kernel<MB, 4>); break;
+  }
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------------------- skinny M <= 32, streamed
 // M <= 32 with K % 128 == 0 and a narrow W: the weight is the whole cost, so a
 // workgroup owns 16 columns of W over all of K and streams them.  Its 4 waves
@@ -1253,6 +1383,30 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N) {
       return p;
     }
   }
+  // Register-transpose kernel (M <= 32): 8 waves per 64 columns, each wave
+  // NS = 4, 2 or 1 steps of 32 rows.  A CU streams its workgroups' bytes at a
+  // rate bounded by the loads it keeps in flight, so the choice minimises the
+  // bytes of the busiest CU (workgroups spread over 256 CUs, rounded up, times
+  // 64 columns x 256 NS rows), counting the fp32 partials written and read
+  // back as bytes spread over all CUs.
+  if (M <= 32 && K % 256 == 0 && N % kRtBN == 0) {
+    const int64_t strips = N / kRtBN;
+    int ns = 0;
+    int64_t best = 0;
+    for (int c = 4; c >= 1; c /= 2) {
+      if (K % (256 * c) != 0) continue;
+      const int64_t ksp = K / (256 * c);
+      const int64_t cost = (strips * ksp + 255) / 256 * (256 * c * kRtBN * 2) + ksp * M * N * 8 / 256;
+      if (ns == 0 || cost < best) ns = c, best = cost;
+    }
+    p.rt_ns = ns;
+    p.krange = 256 * ns;
+    p.ksplit = (int)(K / p.krange);
+    if (p.ksplit * M * N * 4 >= ((int64_t)1 << 31)) return SkinnyPlan{};
+    p.ws_bytes = (size_t)p.ksplit * M * N * 4;
+    p.ok = true;
+    return p;
+  }
   if (N % kSkBN != 0) return SkinnyPlan{};
   const int64_t base = (N / kSkBN) * p.nbm;
   // about three workgroups per CU; each k range a multiple of the 128-deep chunk
@@ -1291,7 +1445,15 @@ hipError_t launch_qkv_gemm(const void* x, const void* w, const void* bias, void*
   if (p.ok && p.wide)
     return p.wide_mb == 1 ? launch_wide<kWdWaves, 1, 2>(x, w, bias, out, m, k, n, s, app)
                           : launch_wide<kWdWaves, 2, 2>(x, w, bias, out, m, k, n, s, app);
-  if (p.ok && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
+  if (p.ok && p.rt_ns > 0 && ws != nullptr && ws_bytes >= p.ws_bytes) {
+    hipError_t e = M > 16 ? launch_rt<2>(p, x, w, ws, m, k, n, s) : launch_rt<1>(p, x, w, ws, m, k, n, s);
+    if (e != hipSuccess) return e;
+    const int64_t quads = (M * N + 3) / 4;
+    hipLaunchKernelGGL(qkv_gemm_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                       (const float*)ws, (const uint16_t*)bias, (uint16_t*)out, m, n, p.ksplit, app);
+    return hipGetLastError();
+  }
+  if (p.ok && p.rt_ns == 0 && (p.ksplit == 1 || (ws != nullptr && ws_bytes >= p.ws_bytes))) {
     const int64_t nblk = (N / kSkBN) * p.nbm * p.ksplit;
     hipLaunchKernelGGL(qkv_gemm_skinny_kernel, dim3((unsigned)nblk), dim3(kSkThreads), 0, s,
                        (const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias, (uint16_t*)out,

@@ -47,10 +47,13 @@ PROJ = [  # M, hidden, H_q, H_kv, d, dtype
     # grids), 32-row tiles, and M <= 32 on a 12288-column weight; ragged row tiles
     (33, 512, 4, 2, 64, "bf16"), (97, 2048, 8, 2, 128, "bf16"), (64, 1024, 16, 2, 128, "bf16"),
     (20, 512, 32, 32, 128, "bf16"),
-    # M <= 32 on decode-width weights (5120-10240 columns, K = 1024..4096): the skinny
-    # kernel with a k split and the reduce kernel, ragged M down to one row
+    # M <= 32 on decode-width weights (5120-10240 columns, K = 1024..4096): the register-
+    # transpose kernel (one and two 16-row blocks; 1, 2 and 4 k steps per wave; one k range
+    # at K = 256) and the reduce kernel, ragged M down to one row
     (32, 4096, 32, 8, 128, "bf16"), (17, 3072, 24, 8, 128, "bf16"), (1, 1024, 40, 4, 128, "bf16"),
-    (9, 2048, 40, 4, 128, "bf16"), (32, 1024, 64, 8, 128, "bf16"),
+    (9, 2048, 40, 4, 128, "bf16"), (32, 1024, 64, 8, 128, "bf16"), (8, 256, 64, 2, 128, "bf16"),
+    # the skinny split-K kernel: hidden not a multiple of 256 (M <= 32 on a wide weight; M > 32)
+    (20, 640, 64, 2, 128, "bf16"), (40, 384, 4, 2, 64, "bf16"),
 ]
 
 
