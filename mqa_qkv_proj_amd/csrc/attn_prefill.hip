@@ -73,14 +73,24 @@ constexpr int kPlanBins = 1024;  // cost classes of the counting sort
 template <int D, bool F8 = false>
 struct PrefillLds {
   // K row pitch in 16-bit units: bf16 rows of D + 8 elements, or (F8) e4m3 rows
-  // of D + 16 bytes whose padding also carries the tile's quantisation scale
-  static constexpr int kKld = F8 ? (D + 16) / 2 : D + 8;
+  // of D + 16 bytes whose padding also carries the tile's quantisation scale.
+  // d = 64 bf16 rows carry no padding: their 16-byte chunks are swizzled
+  // instead (kSwizzle), which keeps a stage at 17 KB so that three 4-wave
+  // workgroups share a CU's LDS.
+  static constexpr bool kSwizzle = D == 64 && !F8;
+  static constexpr int kKld = F8 ? (D + 16) / 2 : kSwizzle ? D : D + 8;
   static constexpr int kVld = kBK + 8;  // V^T row pitch (fp16 elements)
   static constexpr int kK = kBK * kKld;
   static constexpr int kV = D * kVld;
   static constexpr int kStage = kK + kV;
   static constexpr size_t kBytes = kStages * kStage * sizeof(uint16_t);
   static constexpr int kKChunks = kKld / 8;  // 16-byte chunks per K row, padding included
+  // Position of chunk c of K row r in its LDS row (kSwizzle): c ^ ((r / 2) % 8).
+  // The 16 rows that one 16-lane pass of a ds_read_b128 reads (rows r0 .. r0+15,
+  // one chunk each) then cover all 16 16-byte bank groups: a 128-byte row
+  // spans 8 groups, so group = 8 (r % 2) + position, and positions differ for
+  // the 8 rows of each parity.
+  static __device__ __forceinline__ int kpos(int r, int c) { return kSwizzle ? c ^ ((r >> 1) & 7) : c; }
   static constexpr int kKCopies = kK * 2 / 1024;
   static constexpr int kVCopies = kV * 2 / 1024;
   static_assert(kK * 2 % 1024 == 0 && kV * 2 % 1024 == 0, "tile images are whole 1 KB copies");
@@ -599,7 +609,10 @@ __global__ __launch_bounds__(NW * 64, KP == 1 ? 2 : 1) void attn_prefill_bf16_ke
 #pragma unroll
   for (int i = 0; i < KCP; ++i) {
     const int slot = (wave + i * kFillWaves) * 64 + lane;
-    const int row = slot / S::kKChunks, ch = slot % S::kKChunks;
+    // this lane's 16 bytes land on LDS chunk position `pos` of row `row`; it
+    // fetches the K chunk that belongs there
+    const int row = slot / S::kKChunks, pos = slot % S::kKChunks;
+    const int ch = S::kSwizzle ? S::kpos(row, pos) : pos;
     koff[i] = F8 ? (uint32_t)lane * 16
                  : ch < D / 8 ? (uint32_t)row * row_bytes + (uint32_t)(g * D * 2) + ch * 16 : kNoCopy;
   }
@@ -684,6 +697,7 @@ __global__ __launch_bounds__(NW * 64, KP == 1 ? 2 : 1) void attn_prefill_bf16_ke
   auto kfrag = [&](const uint16_t* ks, int r, int f) -> u32x4_t {
     if constexpr (F8)
       return ld16(reinterpret_cast<const char*>(ks) + r * S::kKld * 2 + (f >> 1) * 64 + hf * 32 + (f & 1) * 16);
+    if constexpr (S::kSwizzle) return ld16(ks + r * S::kKld + S::kpos(r, 2 * f + hf) * 8);
     return ld16(ks + r * S::kKld + f * 16 + hf * 8);
   };
   // score MFMA over fragments [f, f + 1] (F8) or fragment f (bf16)
@@ -1228,20 +1242,22 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   };
   int n_qb = 0;
   int64_t nblk = grid(kWaves, n_qb);
-  // Small d=64 grids (under two 8-wave workgroups per CU) run 4-wave
-  // workgroups instead: two of them fit a CU (LDS 55 KB each), and with the
-  // heaviest causal blocks dispatched first a CU then pairs a heavy block
-  // with a light one, where an 8-wave workgroup alone would hold the CU for
-  // the longest key range.  Each row's arithmetic is the same either way.
-  // Measured on the TinyLlama-shaped prefills (L = 2048 / 512 / 128): 8-11%
-  // faster per call.
+  // d=64 grids run 4-wave workgroups: three of them fit a CU (LDS 51 KB
+  // each with the swizzled K rows, 141 VGPRs), twelve waves where one 8-wave
+  // workgroup (141 VGPRs) leaves eight; with the heaviest causal blocks
+  // dispatched first a CU also pairs heavy blocks with light ones, where an
+  // 8-wave workgroup alone would hold the CU for the longest key range.  Each
+  // row's arithmetic is the same either way (bit-identical outputs).
+  // Measured against 8-wave workgroups on the TinyLlama-shaped prefills:
+  // L = 2048 / 512 / 128 8-11% faster per call with two per CU; with three per
+  // CU, B = 4 at L = 2048 and B = 8 at L = 1024 6% and 8% faster.
   int nw = kWaves, kp = 1;
   if (D == 64) {
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    if (nblk < 2 * (int64_t)cus) nw = 4;
+    nw = 4;
     // Fewer 128-row blocks than CUs: 8 waves per block, each row group's key
     // tiles split between two waves (even / odd tiles, merged at the end), so
     // the longest block finishes in half the steps on a CU that would

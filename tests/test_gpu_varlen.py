@@ -197,3 +197,40 @@ def test_varlen_equal_lengths_equal_fixed_length_call(m, B, L):
     assert torch.equal(o_p, o_f.view(B * L, H_q, d))
     # LSE [H_q, total_q] against [B, H_q, L]
     assert torch.equal(l_p, l_f.permute(1, 0, 2).reshape(H_q, B * L))
+
+
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_varlen_schedule_at_the_sequence_limit(m, B):
+    """1024 sequences: the largest batch the schedule is planned for (its LDS
+    scans and binary search at full size); 1025: no schedule size exists, and
+    the call runs the grid.  Short causal prompts of 0..48 tokens, d = 128,
+    two KV heads of four query heads; the schedule against the grid bit for
+    bit, and sampled sequences against the oracle."""
+    import torch
+    H_q, H_kv, d = 8, 2, 128
+    lens = np.random.default_rng(B).integers(0, 48, size=B, endpoint=True)
+    lens[[0, B // 2]] = 0
+    lq = lens.tolist()
+    say("prefill varlen at the sequence limit", B, "sequences", sum(lq), "tokens")
+    cq = _cu(lq)
+    tq = int(cq[-1])
+    q = W.round_bf16(W.normal(106, 1, (tq, H_q, d)))
+    k = W.round_bf16(W.normal(106, 2, (tq, H_kv, d)))
+    v = W.round_bf16(W.normal(106, 3, (tq, H_kv, d)))
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    cqd = torch.from_numpy(cq).cuda()
+    need = m.prefill_varlen_workspace_bytes(B, max(lq), tq, H_q, H_kv, d)
+    assert (need > 0) == (B <= 1024)
+    o_s = m.gqa_attn_prefill_varlen(qd, kd, vd, cqd, cqd, max(lq), max(lq), out_dtype=torch.float32)
+    o_g = m.gqa_attn_prefill_varlen(qd, kd, vd, cqd, cqd, max(lq), max(lq), out_dtype=torch.float32,
+                                    schedule=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_g)
+    got = host(o_s)
+    scale = 1.0 / math.sqrt(d)
+    for b in (1, 2, B // 2 + 1, B - 1):
+        if lq[b] == 0:
+            continue
+        sl = slice(cq[b], cq[b + 1])
+        ref, _ = oracle.attention_varlen(q[sl], k[sl], v[sl], _cu([lq[b]]), _cu([lq[b]]), True, scale)
+        assert_close(got[sl], ref, "bf16", f"sequence {b} of {B} ({lq[b]} tokens)")
