@@ -234,3 +234,39 @@ def test_varlen_schedule_at_the_sequence_limit(m, B):
         sl = slice(cq[b], cq[b + 1])
         ref, _ = oracle.attention_varlen(q[sl], k[sl], v[sl], _cu([lq[b]]), _cu([lq[b]]), True, scale)
         assert_close(got[sl], ref, "bf16", f"sequence {b} of {B} ({lq[b]} tokens)")
+
+
+def test_varlen_schedule_replays_from_a_captured_graph(m):
+    """The scheduled packed prefill captured in a HIP graph: the plan rewrites
+    the list and zeroes the claim counter with kernel stores on every call (no
+    memset node), so each replay, with other work and synchronisations
+    between them, equals the eager call bit for bit."""
+    import torch
+    H_q, H_kv, d = 32, 4, 64
+    lq = np.random.default_rng(107).integers(16, 700, size=6, endpoint=True).tolist()
+    say("prefill varlen schedule in a graph", lq)
+    cq = _cu(lq)
+    tq = int(cq[-1])
+    q = dev(W.round_bf16(W.normal(107, 1, (tq, H_q, d))), "bf16")
+    k = dev(W.round_bf16(W.normal(107, 2, (tq, H_kv, d))), "bf16")
+    v = dev(W.round_bf16(W.normal(107, 3, (tq, H_kv, d))), "bf16")
+    cqd = torch.from_numpy(cq).cuda()
+    ws = torch.empty(m.prefill_varlen_workspace_bytes(len(lq), max(lq), tq, H_q, H_kv, d), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty(tq, H_q, d, dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    call = lambda: m.gqa_attn_prefill_varlen(q, k, v, cqd, cqd, max(lq), max(lq), out=o, workspace=ws)
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    ref = o.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for i in range(3):
+        o.zero_()
+        ws.fill_(0xFF)  # stale schedule and counter bytes
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref), f"replay {i}"
