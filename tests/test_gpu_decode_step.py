@@ -35,12 +35,14 @@ def _lens(rng, B, L_max, skip=True):
 
 
 # B, hidden, H_q, H_kv, d, L_max, dtype: the cases reach every projection kernel
-# (16-column streaming; skinny with and without a k split, whose append sits in
-# the reduce kernel; 64x128 LDS-DMA tiles; register-prefetched tiles; fp32).
+# (16-column streaming; register transpose + reduce; skinny with and without a
+# k split; 8-wave workgroups over all of K; LDS-DMA tiles; register-prefetched
+# tiles; fp32).  With a k split the append sits in the reduce kernel.
 APPEND = [
     (8, 512, 16, 1, 128, 40, "bf16"),     # streaming kernel, one 16-row block
     (24, 256, 4, 2, 64, 33, "bf16"),      # streaming kernel, two 16-row blocks
-    (32, 1024, 32, 8, 128, 50, "bf16"),   # skinny, k split + reduce kernel
+    (32, 1024, 32, 8, 128, 50, "bf16"),   # register transpose, k split + reduce kernel
+    (20, 640, 64, 2, 128, 24, "bf16"),    # skinny, k split + reduce kernel (hidden % 256 != 0)
     (100, 128, 8, 2, 64, 20, "bf16"),     # skinny, one k range
     (48, 512, 8, 2, 64, 20, "bf16"),      # 8-wave workgroups over all of K
     (300, 256, 8, 2, 64, 9, "bf16"),      # LDS-DMA tiles

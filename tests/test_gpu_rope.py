@@ -35,9 +35,11 @@ def _t(a, dtype="int32"):
 ROPE = [  # M, hidden, H_q, H_kv, d, dtype, bias: the kernel each case reaches
     (7, 512, 8, 1, 128, "bf16", False),      # streaming, one 16-row block
     (24, 384, 4, 2, 64, "bf16", True),       # streaming, two 16-row blocks
-    (33, 256, 4, 4, 64, "bf16", True),       # skinny, one k range (direct epilogue)
-    (100, 1024, 8, 1, 128, "bf16", False),   # skinny, k split (rotation in the reduce kernel)
-    (32, 4096, 32, 8, 128, "bf16", True),    # skinny + reduce at the Llama-2-7B decode width
+    (33, 256, 4, 4, 64, "bf16", True),       # 8-wave workgroups over all of K, M just above 32
+    (100, 1024, 8, 1, 128, "bf16", False),   # the same, 32-row tiles
+    (100, 128, 8, 2, 64, "bf16", True),      # skinny, one k range (rotation in its own epilogue)
+    (40, 640, 8, 2, 64, "bf16", False),      # skinny, k split (rotation in the reduce kernel)
+    (32, 4096, 32, 8, 128, "bf16", True),    # register transpose + reduce at the Llama-2-7B decode width
     (17, 3072, 24, 8, 128, "bf16", True),    # the same, N = 5120, ragged M
     (97, 2048, 8, 2, 128, "bf16", True),     # 8-wave workgroups over all of K, ragged row tile
     (128, 2048, 32, 4, 64, "bf16", False),   # the same at the TinyLlama L=128 width
