@@ -131,12 +131,15 @@ def test_decode_steps_match_oracle(m, B, hidden, H_q, H_kv, d, L_max):
         lens = lens + 1
 
 
-def test_decode_step_graph_replays_match_eager(m):
+@pytest.mark.parametrize("B,hidden,H_q,H_kv,d,L_max,steps", [
+    (8, 2048, 16, 1, 128, 48, 5),     # MQA: 16-column streaming projection
+    (32, 4096, 32, 8, 128, 96, 4),    # Llama-2-7B GQA-8 width: register transpose + reduce kernel
+])
+def test_decode_step_graph_replays_match_eager(m, B, hidden, H_q, H_kv, d, L_max, steps):
     """The whole step (project + append, decode, lengths + 1) captured once as a
     HIP graph and replayed: every replay equals the same step run eagerly, with
     eager work and synchronisations between the replays."""
     import torch
-    B, hidden, H_q, H_kv, d, L_max, steps = 8, 2048, 16, 1, 128, 48, 5
     N = (H_q + 2 * H_kv) * d
     say("decode step graph", B, hidden, H_q, H_kv, d, L_max, steps)
     xs, w, kc0, vc0, lens0 = _decode_step_inputs(B, hidden, H_q, H_kv, d, L_max, steps, 61)
