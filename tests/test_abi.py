@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -425,3 +426,23 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import mqa_qkv_proj_amd"], cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "build.py" in r.stderr
+
+
+def test_prefill_varlen_schedule_capacity_bound(lib):
+    """The schedule's list holds B + ceil(total_q / P) row blocks: enough for any
+    lengths that sum to total_q, since ceil(L / P) <= L / P + 1 per sequence.
+    Checked on random and extreme length mixes against the size the library
+    reports (the list bytes past the 256-aligned V images)."""
+    rng = np.random.default_rng(5)
+    r256 = lambda n: (n + 255) // 256 * 256
+    for H_q, H_kv, d, P in ((32, 4, 64, 16), (16, 4, 128, 64), (12, 2, 128, 128), (64, 2, 64, 4)):
+        for _ in range(50):
+            B = int(rng.integers(1, 1025))
+            lens = rng.integers(0, 3000, size=B)
+            if rng.random() < 0.3:  # every sequence one token past a multiple of P
+                lens = (rng.integers(0, 20, size=B) * P + 1)
+            total_q, L_kv = int(lens.sum()), int(max(1, lens.max()))
+            blocks = int(sum((int(n) + P - 1) // P for n in lens))
+            size = lib.prefill_varlen_workspace_bytes(B, L_kv, total_q, H_q, H_kv, d)
+            list_bytes = size - r256(lib.prefill_workspace_bytes(B, L_kv, H_kv, d))
+            assert list_bytes >= 4 * (4 + 2 * blocks), (H_q, H_kv, d, B, total_q, blocks)
