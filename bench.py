@@ -732,7 +732,7 @@ def cpu_baseline(W, seconds, main_only):
     del q, k, v, inp
 
     if not main_only:
-        share = (seconds - budget) / 5.0
+        share = (seconds - budget) / 6.0
 
         def timed_until(fn, limit):
             n, t = 0, time.perf_counter()
@@ -781,6 +781,26 @@ def cpu_baseline(W, seconds, main_only):
             per[wl.name] = {"gbps": round(by / dt / 1e9, 4), "seconds": round(dt, 2),
                             "sample": f"{n} decode step(s) of sequences 0..{nb - 1}"}
             del din
+
+        # packed variable-length batches: whole sequences, shortest first, one at a time
+        for name, nseq, lo, hi, H_q, H_kv, d, seed in (("varlen_tinyllama_8", 8, 128, 2048, 32, 4, 64, 1007),
+                                                        ("varlen_long_16", 16, 256, 8192, 16, 4, 128, 1008)):
+            lens = sorted(np.random.default_rng(seed).integers(lo, hi, size=nseq, endpoint=True).tolist())
+            rng = np.random.default_rng(seed)
+            fl, done, t = 0.0, 0, time.perf_counter()
+            for n in lens:
+                qs = rng.standard_normal((n, H_q, d), dtype=np.float32)
+                ks = rng.standard_normal((n, H_kv, d), dtype=np.float32)
+                vs = rng.standard_normal((n, H_kv, d), dtype=np.float32)
+                cu = np.array([0, n], dtype=np.int32)
+                oracle.attention_varlen(qs, ks, vs, cu, cu, True, 1.0 / math.sqrt(d))
+                fl += prefill_flops(1, H_q, d, n, n, True)
+                done += 1
+                if time.perf_counter() - t >= share / 2.0:
+                    break
+            dt = time.perf_counter() - t
+            per[name] = {"tflops": round(fl / dt / 1e12, 6), "seconds": round(dt, 2),
+                         "sample": f"{done} of the {nseq} sequences, shortest first"}
     total = sum(p["seconds"] for p in per.values())
     try:
         affinity = len(os.sched_getaffinity(0))
