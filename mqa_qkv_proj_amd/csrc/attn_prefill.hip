@@ -795,14 +795,14 @@ __global__ __launch_bounds__(NW * 64, KP == 1 ? 2 : 1) void attn_prefill_bf16_ke
   // P.V MFMA by a row-sum step and one K read, so the vector and LDS units
   // work while the matrix cores run and every operand is in flight long
   // before it is used.  Fences keep the compiler from regrouping.
-  // With bf16 scores and d = 128 (SPREAD) a half's exponentials are split
-  // between two steps: those of its first 16 keys are computed under the
-  // previous step's P.V MFMAs (carried in `pl`, their max in `ml`, with the
-  // half's score scale `cn`), the rest under its own score MFMAs, which
-  // spreads the vector work evenly under the matrix work (measured 1-3%
-  // faster).  Otherwise every exponential of the half follows the score
-  // MFMAs: with fp8 scores (two MFMAs per step) the split measured 8% slower,
-  // with d = 64 (half the MFMAs per step) 6% slower.
+  // With bf16 scores (SPREAD) a half's exponentials are split between two
+  // steps: those of its first 16 keys are computed under the previous step's
+  // P.V MFMAs (carried in `pl`, their max in `ml`, with the half's score scale
+  // `cn`), the rest under its own score MFMAs, which spreads the vector work
+  // evenly under the matrix work (measured 1-3% faster at d = 128, and 1-3% at
+  // d = 64 with three workgroups per CU, where two per CU had made it 6%
+  // slower).  With fp8 scores (two MFMAs per step) every exponential of the
+  // half follows the score MFMAs: the split measured 8% slower there.
   // P is computed with the running max as it stands, while the half's row max
   // is folded in beside it; only if some row's max grew by more than kTau
   // (rare after the first half) is the max raised, O and l rescaled and P
@@ -813,7 +813,7 @@ __global__ __launch_bounds__(NW * 64, KP == 1 ? 2 : 1) void attn_prefill_bf16_ke
                   const uint16_t* kn, int jn, float cn, auto next_tag, auto part0) {
     constexpr bool NEXT = decltype(next_tag)::value;
     constexpr int PART0 = part0;
-    constexpr bool SPREAD = !F8 && D == 128;
+    constexpr bool SPREAD = !F8;
     u32x4_t pf[2];
     u32x4_t vf[2 * DB];
     f32x16_t sn = f32x16_t{};
@@ -936,7 +936,7 @@ __global__ __launch_bounds__(NW * 64, KP == 1 ? 2 : 1) void attn_prefill_bf16_ke
     cc = tile_c(0);
     sc = qk(k_of(0), 0);
     update_max(sc);
-    if constexpr (!F8 && D == 128) first_p(sc, pl, ml);
+    if constexpr (!F8) first_p(sc, pl, ml);
     load_kf(kf, k_of(0), 1);
   }
   for (; u + 1 < tm; ++u) {
@@ -1243,8 +1243,8 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   int n_qb = 0;
   int64_t nblk = grid(kWaves, n_qb);
   // d=64 grids run 4-wave workgroups: three of them fit a CU (LDS 51 KB
-  // each with the swizzled K rows, 141 VGPRs), twelve waves where one 8-wave
-  // workgroup (141 VGPRs) leaves eight; with the heaviest causal blocks
+  // each with the swizzled K rows, 149 VGPRs), twelve waves where one 8-wave
+  // workgroup (149 VGPRs) leaves eight; with the heaviest causal blocks
   // dispatched first a CU also pairs heavy blocks with light ones, where an
   // 8-wave workgroup alone would hold the CU for the longest key range.  Each
   // row's arithmetic is the same either way (bit-identical outputs).
