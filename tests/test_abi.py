@@ -446,3 +446,46 @@ def test_prefill_varlen_schedule_capacity_bound(lib):
             size = lib.prefill_varlen_workspace_bytes(B, L_kv, total_q, H_q, H_kv, d)
             list_bytes = size - r256(lib.prefill_workspace_bytes(B, L_kv, H_kv, d))
             assert list_bytes >= 4 * (4 + 2 * blocks), (H_q, H_kv, d, B, total_q, blocks)
+
+
+def test_plain_c_caller_links_and_queries(lib, tmp_path):
+    """A C99 program built against include/mqa_qkv.h and linked with the
+    library: the size queries and status calls answer as through the binding,
+    and an invalid call returns MQKV_ERR_INVALID with a message (no GPU work)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "mqa_qkv.h"
+int main(void) {
+  printf("%d\n", mqkv_abi_version());
+  printf("%zu\n", gqa_attn_prefill_workspace_bytes(2, 100, 4, 128, MQKV_BF16));
+  printf("%zu\n", gqa_attn_prefill_varlen_workspace_bytes(8, 2048, 8000, 32, 4, 64));
+  printf("%zu\n", gqa_attn_decode_workspace_bytes(32, 32, 8, 128, 4096, 0));
+  printf("%zu\n", qkv_proj_workspace_bytes(32, 4096, 32, 8, 128, MQKV_BF16));
+  mqkv_status st = gqa_attn_prefill(0, 0, 0, 0, 0, 1, 8, 8, 4, 2, 64, 512, 256, 1, 0.125f, MQKV_BF16,
+                                    MQKV_BF16, 0, 0, 0);
+  printf("%d %s\n", (int)st, mqkv_status_string(st));
+  printf("%d\n", mqkv_last_error()[0] != 0);
+  return 0;
+}
+''')
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(lib.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                        "-L", libdir, "-lmqa_qkv", f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    lines = out.stdout.split("\n")
+    assert int(lines[0]) == lib.lib.mqkv_abi_version()
+    assert int(lines[1]) == lib.prefill_workspace_bytes(2, 100, 4, 128)
+    assert int(lines[2]) == lib.prefill_varlen_workspace_bytes(8, 2048, 8000, 32, 4, 64)
+    assert int(lines[3]) == lib.decode_workspace_bytes(32, 32, 8, 128, 4096, 0)
+    assert int(lines[4]) == lib.qkv_proj_workspace_bytes(32, 4096, 32, 8, 128)
+    assert lines[5].startswith("1 ")  # NULL operands: MQKV_ERR_INVALID
+    assert lines[6] == "1"
