@@ -118,6 +118,8 @@ SCHEDULED = [
     (32, 4, 64, True, "tinyllama8", None, 103),
     # a long and a short causal sequence
     (32, 4, 64, True, [2048, 1000], None, 104),
+    # d = 64, not causal, key lengths unlike the query lengths (one sequence without keys)
+    (16, 2, 64, False, [700, 33, 129, 0, 257], [64, 900, 129, 5, 0], 108),
 ]
 
 
