@@ -20,7 +20,9 @@ Then every configuration is measured on its own (`configs`; skipped with
 --no-configs): the tiny fp32 layer, the TinyLlama-shaped layers (projection,
 prefill, whole layer eager and as one HIP graph), the MQA decode loop (eager
 and as one HIP graph), the
-Llama-2-7B decode sweep (cold caches) with its projections, the four
+Llama-2-7B decode sweep (cold caches) with its projections and, for GQA-8,
+the whole decode step (projection with RoPE and KV append, decode) eager and
+as one HIP graph, the four
 long-context prefills in bf16 and FP8, and two packed variable-length batches
 (persistent heaviest-first workers against the per-row-block grid).  Each
 carries its roofline fraction.
@@ -479,7 +481,48 @@ def measure_configs(m, W, torch, np, dev, stream, timer, up, kv8):
         proj = lambda: m.qkv_proj(x, w, wl.H_q, wl.H_kv, wl.d, out=qkv, workspace=wsg)
         gus_c, gus_w = timer.cold(proj), timer.warm(proj)
         roof_g, _, by_g = gemm_roof_us(wl.B, wl.hidden, wl.N)
+        step_rec = {}
+        if hkv == 8:
+            # the whole decode step as the model runs it: the projection with the
+            # rotary embedding and the new token's K/V appended to the caches, the
+            # decode on the q view, lengths + 1; 20 steps eagerly and as one
+            # captured HIP graph (lengths restored before each run)
+            th = torch.from_numpy(W.rope_inv_freq(wl.d)).to(dev)
+            lens_s = lens.clone()
+            qv = qkv[:, :wl.H_q * wl.d].unflatten(-1, (wl.H_q, wl.d))
+            nsteps = 20
+
+            def steps_run():
+                for _ in range(nsteps):
+                    m.qkv_proj_append_rope(x, w, kc, vc, lens_s, th, wl.H_q, wl.H_kv, wl.d, out=qkv, workspace=wsg)
+                    m.gqa_attn_decode(qv, kc, vc, lens_s, workspace=wsd, out=o)
+                    lens_s.add_(1)
+
+            def steps_timed(fn):
+                lens_s.copy_(lens)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / nsteps
+
+            with torch.cuda.stream(stream):
+                steps_timed(steps_run)  # warm-up
+                st_eager = min(steps_timed(steps_run) for _ in range(3))
+                graph = torch.cuda.CUDAGraph()
+                lens_s.copy_(lens)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph, stream=stream):
+                    steps_run()
+                st_graph = min(steps_timed(graph.replay) for _ in range(3))
+                del graph
+            step_rec = {"decode_step_rope_append": {
+                "steps": nsteps, "eager_us_per_step": round(st_eager, 2), "graph_us_per_step": round(st_graph, 2),
+                "note": "qkv_proj_append_rope + gqa_attn_decode + lengths + 1, caches warm from the runs above"}}
         res[wl.name] = {
+            **step_rec,
             "decode": {"us_cold": round(us_c, 2), "gbps_cold": round(by / us_c / 1e3, 1),
                        "frac_cold": round(by / us_c / 1e3 / PEAK_HBM_GBS, 4), "us_warm": round(us_w, 2),
                        "mbytes": round(by / 1e6, 2)},
