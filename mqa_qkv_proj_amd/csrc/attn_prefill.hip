@@ -11,7 +11,7 @@
 //  * One workgroup = 8 waves = 256 query rows of one KV head: F query heads of
 //    the group x (256/F) positions, F = the largest power of two dividing
 //    G = H_q/H_kv (at most 32).  Every LDS K/V tile is reused by all F heads.
-//    Small d=64 grids use 4-wave workgroups (128 rows), two per CU.
+//    d=64 grids use 4-wave workgroups (128 rows), three per CU.
 //  * Scores are computed transposed, S^T = K . Q^T: the accumulator then holds
 //    one query per lane column, so the row max and row sum are in-lane
 //    reductions plus one exchange with the lane 32 away.  Q stays in VGPRs.
@@ -33,16 +33,23 @@
 //    the tile being consumed, the next tile (complete) and the tile being
 //    copied in, with one barrier per 64-key tile.
 //  * Tiles reach LDS by LDS-DMA (buffer loads that write LDS directly): no
-//    staging registers and no LDS store instructions.  K rows keep 16 bytes of
-//    padding per row (the pad lanes of a copy point past the buffer, so they
-//    fetch nothing and land only on padding) so that the operand reads of 16
-//    consecutive rows hit distinct banks; the V^T images carry the same padding.  The copies are issued by
-//    the four older waves, between the MFMAs of the pipelined steps.
+//    staging registers and no LDS store instructions.  d=128 K rows keep 16
+//    bytes of padding per row (the pad lanes of a copy point past the buffer,
+//    so they fetch nothing and land only on padding) so that the operand reads
+//    of 16 consecutive rows hit distinct banks; d=64 K rows are unpadded with
+//    their 16-byte chunks swizzled to the same effect; the V^T images carry
+//    padding.  The copies are issued by the four older waves, between the
+//    MFMAs of the pipelined steps.
 //  * Causal: tiles beyond the block's diagonal are never visited, only tiles
 //    that cross a row's limit are masked (a separate, unpipelined loop), and
 //    the heaviest query blocks are dispatched first.  Workgroup ids are
 //    remapped so that each XCD serves a contiguous range of (batch, KV head)
 //    blocks and keeps their K/V in its L2.
+//  * Packed batches of unequal lengths (with a workspace that holds a
+//    schedule): one workgroup of the V-image pre-pass lists the row blocks of
+//    the whole batch heaviest first, and persistent workgroups claim them in
+//    that order with an atomic counter (FlashAttention-3 page, closing
+//    section: persistent kernels, variable length).
 // fp32 inputs use a plain one-row-per-thread kernel (fp32 throughout).
 #include <type_traits>
 
